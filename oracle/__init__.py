@@ -1,0 +1,15 @@
+"""fp64 CPU oracle for the Nystrom self-attention forward (test infrastructure only).
+
+Only tests/, the package smoke check and the benchmark's CPU-baseline leg import this
+package. It shares no code with the HIP library.
+"""
+from .nystrom import (  # noqa: F401
+    depthwise_conv_seq,
+    exact_attention_head,
+    iterative_pinv,
+    nystrom_forward,
+    nystrom_head,
+    pinv_scaling,
+    segment_means,
+    softmax_rows,
+)
