@@ -1,0 +1,206 @@
+"""Benchmark of the Nystrom self-attention forward on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+
+Workload: B=16, H=8, n=4096, d=64, m=64 landmarks (segments of 64 tokens), depthwise
+conv width 33, 6 pseudo-inverse iterations, bf16 I/O; seeded synthetic Q, K, V ~ N(0,1)
+and conv weights (stand-ins for the GLUE/IMDB/LRA inputs of the pages, which are not
+available). A step is one full forward (segment means, landmark kernel and iterative
+pseudo-inverse, landmark context, output softmax times Y, conv skip) with inputs already
+resident in HBM; consecutive steps alternate between two independently seeded input
+sets so no step starts with its inputs cache-resident.
+
+Prints one JSON line: tokens/s (tokens = B*n per forward), the per-stage kernel times
+from HIP events recorded by the library on the forward's stream, the HBM roofline of the
+dominant kernel, and the fp64 CPU oracle timed on the host on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Nyström attn fwd tokens/s at n=4096,m=64,d=64; % of binding roofline"
+HBM_PEAK_GBS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "efficient_transformer_attention_segment_amd", "csrc")
+STAGES = ("segment_means", "pinv", "context", "output")
+# kernel name (as rocprofv3 reports it) of each stage
+STAGE_KERNEL = {"segment_means": "segmeans_kernel", "pinv": "pinv_kernel",
+                "context": "flash_kernel", "output": "output_kernel"}
+
+
+def stage_bytes(cfg) -> dict:
+    """Algorithmic HBM bytes per launch of each stage (inputs read once, output written
+    once; the small landmark-sized workspace traffic is not counted)."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    tok = cfg.bh * cfg.n * cfg.d * e
+    return {"segment_means": 2 * tok,      # read Q, K
+            "pinv": 0,                     # landmark-sized only (compute/latency bound)
+            "context": 2 * tok,            # read K, V
+            "output": 3 * tok}             # read Q, V; write out
+
+
+def source_hash(stage: str) -> str:
+    files = {"segment_means": ["segmeans.hip"], "pinv": ["context.hip"],
+             "context": ["context.hip"], "output": ["output.hip"]}[stage] + ["nys_common.h"]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(stage: str, cfg_name: str):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None when the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(PROFILES, f"{STAGE_KERNEL[stage]}_{cfg_name}_counters.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as fh:
+        rec = json.load(fh)
+    if rec.get("source_hash") != source_hash(stage):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def cpu_baseline(cfg, x, budget_s: float = 12.0) -> dict:
+    """Time the fp64 oracle (untuned) on the host: whole forwards of the workload,
+    repeated until about budget_s seconds have passed."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    # one sampled block of heads per pass: every (b, h) of the workload
+    heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        oracle.nystrom_forward(x.q, x.k, x.v, x.w, cfg.m, cfg.pinv_iters, heads=heads)
+        passes += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": passes * cfg.tokens / dt, "unit": "tokens/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{passes} full forward(s) of the workload ({cfg.bh} heads) in "
+                      f"{dt:.1f} s, numpy fp64, BLAS threads={cores}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="long")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(the forward shards over (batch, head) without communication; see the "
+              "design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from efficient_transformer_attention_segment_amd import NystromAttention
+    from efficient_transformer_attention_segment_amd import inputs as gen
+
+    cfg = gen.CONFIGS[args.config]
+    sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
+    torch.cuda.set_device(0)
+
+    def dev(a):
+        if cfg.dtype == gen.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    dev_sets = [(dev(s.q_dev), dev(s.k_dev), dev(s.v_dev), torch.from_numpy(s.w).cuda())
+                for s in sets]
+    dt = torch.bfloat16 if cfg.dtype == gen.BF16 else torch.float32
+    outs = [torch.empty(cfg.B, cfg.H, cfg.n, cfg.d, dtype=dt, device="cuda") for _ in sets]
+    att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, cfg.conv_width,
+                           cfg.pinv_iters, cfg.dtype)
+
+    def step(i):
+        q, k, v, w = dev_sets[i % 2]
+        att.forward(q, k, v, w, out=outs[i % 2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        step(i)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+
+    # per-stage kernel times: HIP events the library records on the forward's stream
+    att.profile_enable(args.steps)
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = np.array(att.profile_read(args.steps), dtype=np.float64)
+    stage_ms = {s: float(prof[:, j].mean()) for j, s in enumerate(STAGES)}
+
+    if args.copy_calibration:
+        a = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    tokens = cfg.tokens
+    value = tokens / (ms * 1e-3)
+    sbytes = stage_bytes(cfg)
+    dom = max((s for s in STAGES if sbytes[s] > 0), key=lambda s: stage_ms[s])
+    achieved = sbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
+    path_bytes = 4 * cfg.bh * cfg.n * cfg.d * (2 if cfg.dtype == "bf16" else 4)
+    path_roof_ms = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    rec = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"nystrom_attention_forward_B{cfg.B}_H{cfg.H}_n{cfg.n}_"
+                               f"d{cfg.d}_m{cfg.m}_conv{cfg.conv_width}_iters{cfg.pinv_iters}",
+                   "B": cfg.B, "H": cfg.H, "n": cfg.n, "d": cfg.d, "m": cfg.m,
+                   "conv_width": cfg.conv_width, "pinv_iters": cfg.pinv_iters,
+                   "inputs": "two alternating seeded N(0,1) sets"},
+        "roofline": {"kernel": STAGE_KERNEL[dom], "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic(dom, args.config)},
+        "stages_ms": stage_ms,
+        "stage_algorithmic_bytes": sbytes,
+        "path_roofline": {"bound": "hbm", "compulsory_bytes": path_bytes,
+                          "roofline_ms": path_roof_ms, "frac": path_roof_ms / ms},
+    }
+    if not args.no_cpu_baseline:
+        rec["cpu_baseline"] = cpu_baseline(cfg, sets[0])
+    att.close()
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

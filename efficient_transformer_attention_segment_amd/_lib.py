@@ -1,0 +1,206 @@
+"""ctypes binding of libnysattn.so (the C ABI in include/nys_attn.h).
+
+Argument marshalling only: every step of the forward pass runs in the HIP library.
+The functions keep the C names; ``NystromAttention`` wraps a plan for torch tensors
+(PyTorch supplies device memory and the current stream, nothing else).
+There is no fallback: if the shared library is missing or fails to load, importing this
+module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+# torch ships its own HIP runtime (same soname as /opt/rocm's). Import it first so that
+# libnysattn.so binds to the runtime torch already loaded: two HIP runtimes in one
+# process do not share the device.
+import torch  # noqa: F401  (load order matters)
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libnysattn.so")
+
+NYS_F32, NYS_BF16 = 0, 1
+STATUS = {0: "NYS_OK", 1: "NYS_E_ARG", 2: "NYS_E_UNSUPPORTED", 3: "NYS_E_NOMEM",
+          4: "NYS_E_DEVICE", 5: "NYS_E_LAUNCH"}
+NYS_OK, NYS_E_ARG, NYS_E_UNSUPPORTED, NYS_E_NOMEM, NYS_E_DEVICE, NYS_E_LAUNCH = range(6)
+
+# symbol name -> (restype, argtypes), mirroring include/nys_attn.h
+_c_int, _c_void_p, _c_size_t = ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+
+
+class Taps(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in
+                ("q_land", "k_land", "a_s", "z", "w", "y", "attn")]
+
+
+SIGNATURES = {
+    "nys_attn_create": (_c_int, [ctypes.POINTER(_c_void_p), _c_int, _c_int, _c_int, _c_int,
+                                 _c_int, _c_int, _c_int, _c_int]),
+    "nys_attn_forward": (_c_int, [_c_void_p] * 7),
+    "nys_attn_forward_debug": (_c_int, [_c_void_p] * 7 + [ctypes.POINTER(Taps)]),
+    "nys_attn_workspace_bytes": (_c_size_t, [_c_void_p]),
+    "nys_attn_profile_enable": (_c_int, [_c_void_p, _c_int]),
+    "nys_attn_profile_read": (_c_int, [_c_void_p, ctypes.POINTER(ctypes.c_float), _c_int,
+                                       ctypes.POINTER(_c_int)]),
+    "nys_attn_destroy": (None, [_c_void_p]),
+    "nys_attn_last_error": (ctypes.c_char_p, []),
+}
+
+
+class NysError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str):
+        super().__init__(f"{where}: {STATUS.get(status, status)}: {detail}")
+        self.status = status
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    if not os.path.exists(path):
+        raise ImportError(
+            f"{path} is missing: build it with `python -m "
+            "efficient_transformer_attention_segment_amd.build` (hipcc, gfx950)")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_LIB = load_library()
+
+
+def lib() -> ctypes.CDLL:
+    return _LIB
+
+
+# ------------------------------------------------------------------ C-named functions
+def nys_attn_last_error() -> str:
+    return _LIB.nys_attn_last_error().decode()
+
+
+def _check(status: int, where: str):
+    if status != NYS_OK:
+        raise NysError(status, where, nys_attn_last_error())
+
+
+def nys_attn_create(B, H, n, d, m, conv_width=33, pinv_iters=6, dtype=NYS_BF16) -> int:
+    plan = _c_void_p()
+    _check(_LIB.nys_attn_create(ctypes.byref(plan), B, H, n, d, m, conv_width, pinv_iters,
+                                dtype), "nys_attn_create")
+    return plan.value
+
+
+def nys_attn_forward(plan, q, k, v, conv_w, out, stream) -> None:
+    _check(_LIB.nys_attn_forward(plan, q, k, v, conv_w, out, stream), "nys_attn_forward")
+
+
+def nys_attn_forward_debug(plan, q, k, v, conv_w, out, stream, taps: Taps | None) -> None:
+    _check(_LIB.nys_attn_forward_debug(plan, q, k, v, conv_w, out, stream,
+                                       ctypes.byref(taps) if taps is not None else None),
+           "nys_attn_forward_debug")
+
+
+def nys_attn_workspace_bytes(plan) -> int:
+    return int(_LIB.nys_attn_workspace_bytes(plan))
+
+
+def nys_attn_profile_enable(plan, max_calls: int) -> None:
+    _check(_LIB.nys_attn_profile_enable(plan, max_calls), "nys_attn_profile_enable")
+
+
+NYS_ATTN_STAGES = 4  # segment means, pseudo-inverse, landmark context, output
+
+
+def nys_attn_profile_read(plan, max_calls: int):
+    S = NYS_ATTN_STAGES
+    buf = (ctypes.c_float * (S * max(max_calls, 1)))()
+    n = _c_int(0)
+    _check(_LIB.nys_attn_profile_read(plan, buf, max_calls, ctypes.byref(n)),
+           "nys_attn_profile_read")
+    return [tuple(buf[S * i:S * i + S]) for i in range(n.value)]
+
+
+def nys_attn_destroy(plan) -> None:
+    _LIB.nys_attn_destroy(plan)
+
+
+# ------------------------------------------------------------------ torch wrapper
+class NystromAttention:
+    """One plan: fixed (B, H, n, d, m, conv width, iterations, dtype).
+
+    ``forward(q, k, v, conv_w, out=None, taps=None)`` takes CUDA/HIP torch tensors
+    [B, H, n, d] (bf16 or fp32, contiguous) and fp32 conv weights [H, W]; it enqueues on
+    torch's current stream and returns ``out``.
+    """
+
+    def __init__(self, B, H, n, d, m, conv_width=33, pinv_iters=6, dtype="bf16"):
+        self.shape = (B, H, n, d)
+        self.m, self.conv_width, self.pinv_iters = m, conv_width, pinv_iters
+        self.dtype = dtype
+        code = NYS_BF16 if dtype == "bf16" else NYS_F32
+        self.plan = nys_attn_create(B, H, n, d, m, conv_width, pinv_iters, code)
+
+    def close(self):
+        if self.plan:
+            nys_attn_destroy(self.plan)
+            self.plan = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @property
+    def workspace_bytes(self) -> int:
+        return nys_attn_workspace_bytes(self.plan)
+
+    def _torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def _check(self, name, t, shape, dtype):
+        import torch
+        if not isinstance(t, torch.Tensor):
+            raise TypeError(f"{name} must be a torch tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be a device tensor")
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if t.dtype != dtype:
+            raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+    def forward(self, q, k, v, conv_w, out=None, taps: dict | None = None):
+        import torch
+        dt = self._torch_dtype()
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            self._check(name, t, self.shape, dt)
+        self._check("conv_w", conv_w, (self.shape[1], self.conv_width), torch.float32)
+        if out is None:
+            out = torch.empty(self.shape, dtype=dt, device=q.device)
+        else:
+            self._check("out", out, self.shape, dt)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        args = (self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), conv_w.data_ptr(),
+                out.data_ptr(), stream)
+        if taps is None:
+            nys_attn_forward(*args)
+        else:
+            t = Taps()
+            for key, val in taps.items():
+                if val is not None:
+                    if val.dtype != torch.float32 or not val.is_contiguous():
+                        raise ValueError(f"tap {key} must be contiguous fp32")
+                    setattr(t, key, val.data_ptr())
+            nys_attn_forward_debug(*args, t)
+        return out
+
+    __call__ = forward
+
+    def profile_enable(self, max_calls: int):
+        nys_attn_profile_enable(self.plan, max_calls)
+
+    def profile_read(self, max_calls: int):
+        return nys_attn_profile_read(self.plan, max_calls)

@@ -1,0 +1,229 @@
+// Device helpers shared by the Nystrom attention kernels. CDNA4 (gfx950) only.
+//
+// Matrix products use the wave64 MFMA v_mfma_f32_32x32x16_bf16 (fp32 accumulate).
+// Operand layout of that instruction, as used throughout:
+//   A (32 x 16): lane l holds row (l % 32), k-slots (l / 32, e) for e = 0..7
+//   B (16 x 32): lane l holds column (l % 32), k-slots (l / 32, e)
+//   C (32 x 32): lane l, register r holds row 8*(r/4) + 4*(l/32) + (r%4), column l % 32
+// A and B map k-slot (l/32, e) to the same k, so any consistent assignment of logical k
+// indices to the slots of both operands gives the same contraction. The kernels use that
+// freedom to feed an accumulator straight back in as an operand (see kslot_perm).
+//
+// Values that need more than bf16's 8-bit mantissa are carried as a bf16 pair
+// hi = bf16(x), lo = bf16(x - hi) (about 17 significant bits); a product of two such
+// values is formed as hi*hi + hi*lo + lo*hi with fp32 accumulation.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nys {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) __bf16 bf16x4;
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;  // finite "minus infinity" for running maxima
+
+struct Pair8 {  // an MFMA operand as a hi/lo bf16 pair
+  bf16x8 hi, lo;
+};
+
+__device__ __forceinline__ f32x16 mfma(const bf16x8& a, const bf16x8& b, const f32x16& c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// c += a * b for hi/lo pairs; kA / kB say whether a / b carry a nonzero lo part.
+template <bool kA, bool kB>
+__device__ __forceinline__ f32x16 mfma_pair(const Pair8& a, const Pair8& b, f32x16 c) {
+  if constexpr (kA) c = mfma(a.lo, b.hi, c);
+  if constexpr (kB) c = mfma(a.hi, b.lo, c);
+  return mfma(a.hi, b.hi, c);
+}
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ bf16x8 zero8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
+__device__ __forceinline__ __bf16 bf16_rne(float x) { return (__bf16)x; }
+
+__device__ __forceinline__ Pair8 split8(const float* x) {
+  Pair8 p;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    __bf16 h = bf16_rne(x[e]);
+    p.hi[e] = h;
+    p.lo[e] = bf16_rne(x[e] - (float)h);
+  }
+  return p;
+}
+
+__device__ __forceinline__ void split1(float x, uint16_t& hi, uint16_t& lo) {
+  __bf16 h = bf16_rne(x);
+  __bf16 l = bf16_rne(x - (float)h);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ void st8(uint16_t* p, const bf16x8& v) {
+  *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
+}
+
+// Eight consecutive input elements as an MFMA operand. bf16 inputs are exact in the hi
+// part; fp32 inputs are split into hi/lo. Out-of-range rows read as zero.
+template <typename Tin>
+struct Input;
+
+template <>
+struct Input<uint16_t> {
+  static constexpr bool kSplit = false;
+  __device__ __forceinline__ static Pair8 load8(const uint16_t* p, bool valid) {
+    Pair8 r;
+    r.hi = valid ? ld8(p) : zero8();
+    r.lo = zero8();
+    return r;
+  }
+  __device__ __forceinline__ static void load_raw(const uint16_t* p, bool valid, float* out8) {
+    u32x4 u = valid ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out8[2 * i] = __uint_as_float(u[i] << 16);
+      out8[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+  }
+};
+
+template <>
+struct Input<float> {
+  static constexpr bool kSplit = true;
+  __device__ __forceinline__ static Pair8 load8(const float* p, bool valid) {
+    float x[8];
+    load_raw(p, valid, x);
+    return split8(x);
+  }
+  __device__ __forceinline__ static void load_raw(const float* p, bool valid, float* out8) {
+    f32x4 a = valid ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 b = valid ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out8[i] = a[i];
+      out8[4 + i] = b[i];
+    }
+  }
+};
+
+// Position of logical index t inside a 16-wide k-step when an accumulator's rows are
+// reused as the k dimension of the next product. Accumulator register r of lane half h
+// holds row 8*(r/4) + 4*h + (r%4); read as eight k-slots per half for one 16-row step,
+// slot (h, e) then carries row 8*(e/4) + 4*h + (e%4). Storing the other operand with
+// rows permuted by this map (swap bits 2 and 3 of the index) lines both up.
+__device__ __forceinline__ int kslot_perm(int t) {
+  return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Map a linear block index to (head, part) so that all parts of one head run on the
+// same XCD (blocks are dispatched round-robin over the 8 XCDs) and share its L2.
+__device__ __forceinline__ void xcd_map(int b, int heads, int parts, int& head, int& part) {
+  if ((heads & 7) == 0) {
+    const int x = b & 7, slot = b >> 3;
+    head = x + 8 * (slot / parts);
+    part = slot % parts;
+  } else {
+    head = b / parts;
+    part = b % parts;
+  }
+}
+
+// ---------------------------------------------------------------- 32x32 tile helpers
+// acc(32x32) = A[row0:+32, 0:K] * B[0:K, col0:+32] with A given as row-major hi/lo
+// planes (leading dimension lda) and B given through its transpose, i.e. planes holding
+// B^T row-major (ldb), so both operands are read as 16-byte runs along k.
+__device__ __forceinline__ f32x16 gemm_tile(const uint16_t* ahi, const uint16_t* alo, int lda,
+                                            const uint16_t* bhi, const uint16_t* blo, int ldb,
+                                            int row0, int col0, int K, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  const size_t oa = (size_t)(row0 + r) * lda + 8 * h;
+  const size_t ob = (size_t)(col0 + r) * ldb + 8 * h;
+  f32x16 acc = zero16();
+#pragma unroll 8
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    Pair8 a{ld8(ahi + oa + k0), ld8(alo + oa + k0)};
+    Pair8 b{ld8(bhi + ob + k0), ld8(blo + ob + k0)};
+    acc = mfma_pair<true, true>(a, b, acc);
+  }
+  return acc;
+}
+
+// Element (i, j) held by register rr of an accumulator tile at (row0, col0).
+__device__ __forceinline__ int acc_row(int row0, int rr, int lane) {
+  return row0 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+}
+
+__device__ __forceinline__ void store_rows_hl(uint16_t* hi, uint16_t* lo, int ld, int row0,
+                                              int col0, const f32x16& v, int lane) {
+  const int j = col0 + (lane & 31);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    uint16_t a, b;
+    split1(v[rr], a, b);
+    const size_t o = (size_t)acc_row(row0, rr, lane) * ld + j;
+    hi[o] = a;
+    lo[o] = b;
+  }
+}
+
+// Store the transpose: element (i, j) goes to [j][i]; rows come in runs of four.
+__device__ __forceinline__ void store_cols_hl(uint16_t* hi, uint16_t* lo, int ld, int row0,
+                                              int col0, const f32x16& v, int lane) {
+  const int j = col0 + (lane & 31);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint16_t a[4], b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split1(v[4 * g + e], a[e], b[e]);
+    const size_t o = (size_t)j * ld + row0 + 8 * g + 4 * (lane >> 5);
+    *reinterpret_cast<u32x2*>(hi + o) =
+        u32x2{(uint32_t)a[0] | ((uint32_t)a[1] << 16), (uint32_t)a[2] | ((uint32_t)a[3] << 16)};
+    *reinterpret_cast<u32x2*>(lo + o) =
+        u32x2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+  }
+}
+
+__device__ __forceinline__ void store_rows_f32(float* p, int ld, int row0, int col0,
+                                               const f32x16& v, int lane) {
+  const int j = col0 + (lane & 31);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) p[(size_t)acc_row(row0, rr, lane) * ld + j] = v[rr];
+}
+
+}  // namespace nys

@@ -1,0 +1,71 @@
+// Kernel argument blocks and host launchers of the three stages of the forward pass.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nys {
+
+// Stage 1: segment means of Q and K.
+struct SegArgs {
+  int BH, n, m, mp, l;
+  float* qt;       // [BH][mp][d]
+  float* kt;       // [BH][mp][d]
+  uint16_t* qt_hl; // [BH][2][mp][d] hi plane then lo plane
+  uint16_t* kt_hl; // [BH][2][mp][d]
+};
+
+// Stage 2: landmark kernel + iterative pseudo-inverse (one block per head) and the
+// landmark context split over n (BH * C blocks, partial softmax states).
+struct CtxArgs {
+  const void* k;
+  const void* v;
+  const uint16_t* qt_hl;  // [BH][2][mp][d]
+  const uint16_t* kt_hl;  // [BH][2][mp][d]
+  float* a_s;             // [BH][mp][mp]  logits, then A_S
+  float* z;               // [BH][mp][mp]  final Z (fp32)
+  uint16_t* planes;       // [BH][kPlanes][mp][mp]  hi/lo bf16 operand planes
+  float* own;             // [BH][2][mp][mp]  fp32 X, X^2 (global-memory pinv variant)
+  uint16_t* z_hl;         // [BH][2][mp][mp]  final Z, row-major hi/lo
+  float* part_w;          // [BH][C][d][mp]   per-chunk unnormalised (Bbar V)^T
+  float* part_ml;         // [BH][C][2][mp]   per-chunk running max (log2 units), sum
+  int BH, n, d, m, mp, iters, chunk, C, LG, TG;
+  float scale;            // 1/sqrt(d)
+  float scale_log2e;      // log2(e)/sqrt(d)
+};
+
+// Number of hi/lo bf16 mp x mp planes per head in CtxArgs::planes.
+constexpr int kPlanes = 18;
+
+// Stage 3: merge of the partial states into W and Y = Z W (prologue of every block),
+// then softmax(Q Kt^T s) Y plus the depthwise conv of V, stored in the I/O dtype;
+// optionally the fp32 W, Y and attention part for inspection.
+struct OutArgs {
+  const void* q;
+  const void* v;
+  const float* conv_w;    // [H][W]
+  void* out;              // [BH][n][d]
+  float* attn_tap;        // [BH][n][d] or nullptr
+  float* w_tap;           // [BH][mp][d] or nullptr (written by each head's first block)
+  float* y_tap;           // [BH][mp][d] or nullptr
+  const uint16_t* kt_hl;  // [BH][2][mp][d]
+  const uint16_t* z_hl;   // [BH][2][mp][mp]
+  const float* part_w;    // [BH][C][d][mp]
+  const float* part_ml;   // [BH][C][2][mp]
+  int BH, H, n, m, mp, W, half, tok_per_block, G, C;
+  float scale_log2e;
+};
+
+hipError_t launch_segmeans(bool bf16, int d, const void* q, const void* k, const SegArgs& a,
+                           hipStream_t s);
+hipError_t launch_pinv(int d, const CtxArgs& a, hipStream_t s);
+hipError_t launch_flash(bool bf16, int d, const CtxArgs& a, hipStream_t s);
+hipError_t launch_output(bool bf16, int d, int conv_ksteps, const OutArgs& a, hipStream_t s);
+
+// Dynamic LDS each launch needs (bytes), and one-time kernel attribute setup.
+size_t context_lds_bytes(bool bf16, int d, int mp, int LG, int TG);
+size_t output_lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C);
+hipError_t configure_context(bool bf16, int d, size_t flash_lds);
+hipError_t configure_output(bool bf16, int d, int conv_ksteps, size_t out_lds);
+
+}  // namespace nys

@@ -1,0 +1,329 @@
+// Host side of the C ABI declared in include/nys_attn.h: argument validation (before
+// any HIP call), device check, workspace sizing and carving, the launch sequence on the
+// caller's stream (segment means, pseudo-inverse, landmark context, output), debug taps
+// and stage timing.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <new>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "nys_attn.h"
+#include "nys_kernels.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+nys_status fail(nys_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+constexpr int kStages = 4;  // segment means, pseudo-inverse, landmark context, output
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+long long round_up(long long a, long long b) { return ((a + b - 1) / b) * b; }
+
+}  // namespace
+
+struct nys_attn_plan {
+  int B, H, n, d, m, mp, W, half, iters, ks;
+  nys_dtype dtype;
+  int BH, chunk, C, LG, TG, tok_per_block, G;
+  int device;
+  char* ws;
+  size_t ws_bytes;
+  nys::SegArgs seg;
+  nys::CtxArgs ctx;
+  nys::OutArgs out;
+  int prof_max, prof_count;
+  std::vector<hipEvent_t> prof_ev;  // kStages + 1 per recorded call
+};
+
+static nys_status validate_shape(int B, int H, int n, int d, int m, int W, int iters,
+                                 nys_dtype dtype) {
+  if (B < 0 || H < 0) return fail(NYS_E_ARG, "B and H must be >= 0");
+  if (n < 1) return fail(NYS_E_ARG, "n must be >= 1");
+  if (m < 1 || m > n) return fail(NYS_E_ARG, "need 1 <= m <= n");
+  if (m > 256) return fail(NYS_E_UNSUPPORTED, "m > 256 is not built");
+  if (n % m != 0) return fail(NYS_E_UNSUPPORTED, "n must be a multiple of m (equal segments)");
+  if (d < 1) return fail(NYS_E_ARG, "d must be >= 1");
+  if (d != 32 && d != 64 && d != 128) return fail(NYS_E_UNSUPPORTED, "d must be 32, 64 or 128");
+  if (W < 1 || (W % 2) == 0) return fail(NYS_E_ARG, "conv_width must be odd and >= 1");
+  if (W > 65) return fail(NYS_E_UNSUPPORTED, "conv_width > 65 is not built");
+  if (iters < 0 || iters > 100) return fail(NYS_E_ARG, "pinv_iters must be in [0, 100]");
+  if (dtype != NYS_F32 && dtype != NYS_BF16) return fail(NYS_E_ARG, "unknown dtype");
+  if ((long long)n * d >= (1LL << 31)) return fail(NYS_E_UNSUPPORTED, "n*d must be < 2^31");
+  if ((long long)B * H >= (1LL << 24)) return fail(NYS_E_UNSUPPORTED, "B*H too large");
+  return NYS_OK;
+}
+
+extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n, int d, int m,
+                                      int conv_width, int pinv_iters, nys_dtype dtype) {
+  if (plan == nullptr) return fail(NYS_E_ARG, "plan out-pointer is NULL");
+  *plan = nullptr;
+  nys_status st = validate_shape(B, H, n, d, m, conv_width, pinv_iters, dtype);
+  if (st != NYS_OK) return st;
+
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(NYS_E_DEVICE, "no HIP device available");
+  }
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(NYS_E_DEVICE, "hipGetDevice failed");
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+    return fail(NYS_E_DEVICE, "hipGetDeviceProperties failed");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(NYS_E_DEVICE, std::string("device is ") + prop.gcnArchName + ", need gfx950");
+
+  nys_attn_plan* p = new (std::nothrow) nys_attn_plan();
+  if (p == nullptr) return fail(NYS_E_NOMEM, "host allocation failed");
+  p->B = B; p->H = H; p->n = n; p->d = d; p->m = m; p->W = conv_width;
+  p->half = (conv_width - 1) / 2; p->iters = pinv_iters; p->dtype = dtype;
+  p->device = dev;
+  p->BH = B * H;
+  p->mp = (int)round_up(m, 32);
+  p->LG = p->mp / 32;
+  p->TG = p->LG >= 4 ? 1 : 4 / p->LG;
+  const int step = 32 * p->TG;
+  const long long work = (long long)p->BH * n;
+  // about 1024 context blocks, at most 16 chunks per head (bounds the merge)
+  p->chunk = (int)round_up(std::max<long long>({(long long)step, (work + 1023) / 1024,
+                                                 ((long long)n + 15) / 16}), step);
+  p->chunk = (int)std::min<long long>(p->chunk, round_up(n, step));
+  p->C = ceil_div(n, p->chunk);
+  p->tok_per_block = (int)round_up(std::max<long long>(128, (work + 511) / 512), 128);
+  p->tok_per_block = (int)std::min<long long>(p->tok_per_block, round_up(n, 128));
+  p->G = ceil_div(n, p->tok_per_block);
+  p->ks = (p->half == 0) ? 2 : (p->half <= 16 ? 4 : 6);
+  const bool bf16 = dtype == NYS_BF16;
+
+  const size_t flash_lds = nys::context_lds_bytes(bf16, d, p->mp, p->LG, p->TG);
+  const size_t out_lds = nys::output_lds_bytes(bf16, d, p->mp, p->ks, p->C);
+  const size_t max_lds = (size_t)prop.sharedMemPerBlock;
+  if (flash_lds > max_lds || out_lds > max_lds || (size_t)12 * 64 * 64 * 2 > max_lds) {
+    delete p;
+    return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
+  }
+  if (nys::configure_context(bf16, d, flash_lds) != hipSuccess ||
+      nys::configure_output(bf16, d, p->ks, out_lds) != hipSuccess) {
+    (void)hipGetLastError();
+    delete p;
+    return fail(NYS_E_LAUNCH, "could not set kernel LDS limits");
+  }
+
+  // workspace carve
+  const size_t BHs = (size_t)p->BH, mp = (size_t)p->mp, dd = (size_t)d;
+  const size_t P = mp * mp;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return o;
+  };
+  const size_t o_qt = take(BHs * mp * dd * 4), o_kt = take(BHs * mp * dd * 4);
+  const size_t o_qhl = take(BHs * 2 * mp * dd * 2), o_khl = take(BHs * 2 * mp * dd * 2);
+  const size_t o_as = take(BHs * P * 4), o_z = take(BHs * P * 4);
+  const size_t o_pl = take(p->mp > 64 ? BHs * nys::kPlanes * P * 2 : 0);
+  const size_t o_own = take(p->mp > 64 ? BHs * 2 * P * 4 : 0);
+  const size_t o_zhl = take(BHs * 2 * P * 2);
+  const size_t o_pw = take(BHs * p->C * mp * dd * 4), o_pml = take(BHs * p->C * 2 * mp * 4);
+  const size_t o_w = take(BHs * mp * dd * 4), o_y = take(BHs * mp * dd * 4);
+  p->ws_bytes = off;
+  p->ws = nullptr;
+
+  const char* fault = std::getenv("NYS_FAULT");
+  if (fault != nullptr && std::strcmp(fault, "alloc") == 0) {
+    delete p;
+    return fail(NYS_E_NOMEM, "workspace allocation failed (NYS_FAULT=alloc)");
+  }
+  if (p->ws_bytes > 0) {
+    if (hipMalloc(reinterpret_cast<void**>(&p->ws), p->ws_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      delete p;
+      return fail(NYS_E_NOMEM, "workspace allocation failed");
+    }
+    if (hipMemset(p->ws, 0, p->ws_bytes) != hipSuccess) {
+      (void)hipFree(p->ws);
+      delete p;
+      return fail(NYS_E_LAUNCH, "workspace clear failed");
+    }
+  }
+  char* ws = p->ws;
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  auto U = [&](size_t o) { return reinterpret_cast<uint16_t*>(ws + o); };
+
+  p->seg = nys::SegArgs{p->BH, n, m, p->mp, n / m, F(o_qt), F(o_kt), U(o_qhl), U(o_khl)};
+
+  nys::CtxArgs& c = p->ctx;
+  std::memset(&c, 0, sizeof(c));
+  c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
+  c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.z_hl = U(o_zhl);
+  c.part_w = F(o_pw); c.part_ml = F(o_pml);
+  c.BH = p->BH; c.n = n; c.d = d; c.m = m; c.mp = p->mp; c.iters = pinv_iters;
+  c.chunk = p->chunk; c.C = p->C; c.LG = p->LG; c.TG = p->TG;
+  c.scale = 1.0f / std::sqrt((float)d);
+  c.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)d));
+
+  nys::OutArgs& o = p->out;
+  std::memset(&o, 0, sizeof(o));
+  o.kt_hl = U(o_khl); o.z_hl = U(o_zhl); o.part_w = F(o_pw); o.part_ml = F(o_pml);
+  o.w_tap = F(o_w); o.y_tap = F(o_y);  // enabled per call (debug forwards only)
+  o.BH = p->BH; o.H = H; o.n = n; o.m = m; o.mp = p->mp; o.W = conv_width; o.half = p->half;
+  o.tok_per_block = p->tok_per_block; o.G = p->G; o.C = p->C;
+  o.scale_log2e = c.scale_log2e;
+
+  p->prof_max = 0;
+  p->prof_count = 0;
+  *plan = p;
+  g_err.clear();
+  return NYS_OK;
+}
+
+static bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, const void* v,
+                               const float* conv_w, void* out, void* stream,
+                               const nys_attn_taps* taps) {
+  if (p == nullptr) return fail(NYS_E_ARG, "plan is NULL");
+  if (p->BH == 0) return NYS_OK;
+  if (!q || !k || !v || !out || !conv_w) return fail(NYS_E_ARG, "NULL tensor pointer");
+  auto misaligned = [](const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) != 0; };
+  if (misaligned(q) || misaligned(k) || misaligned(v) || misaligned(out))
+    return fail(NYS_E_ARG, "q, k, v and out must be 16-byte aligned");
+  const size_t bytes = (size_t)p->BH * p->n * p->d * (p->dtype == NYS_BF16 ? 2 : 4);
+  if (ranges_overlap(out, bytes, q, bytes) || ranges_overlap(out, bytes, k, bytes) ||
+      ranges_overlap(out, bytes, v, bytes))
+    return fail(NYS_E_ARG, "out overlaps q, k or v");
+  if (taps && taps->attn && misaligned(taps->attn))
+    return fail(NYS_E_ARG, "taps->attn must be 16-byte aligned");
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const bool bf16 = p->dtype == NYS_BF16;
+  const bool prof = p->prof_count < p->prof_max;
+  hipEvent_t* ev = prof ? &p->prof_ev[(kStages + 1) * p->prof_count] : nullptr;
+  auto chk = [&](hipError_t e, const char* what) -> bool {
+    if (e != hipSuccess) {
+      g_err = std::string(what) + ": " + hipGetErrorString(e);
+      return false;
+    }
+    return true;
+  };
+  auto mark = [&](int i) { return !prof || chk(hipEventRecord(ev[i], s), "event record"); };
+  nys::CtxArgs c = p->ctx;
+  c.k = k;
+  c.v = v;
+  nys::OutArgs o = p->out;
+  o.q = q;
+  o.v = v;
+  o.conv_w = conv_w;
+  o.out = out;
+  o.attn_tap = taps ? taps->attn : nullptr;
+  if (!taps || (!taps->w && !taps->y)) o.w_tap = o.y_tap = nullptr;
+  if (!mark(0) || !chk(nys::launch_segmeans(bf16, p->d, q, k, p->seg, s), "segment means launch") ||
+      !mark(1) || !chk(nys::launch_pinv(p->d, c, s), "pseudo-inverse launch") ||
+      !mark(2) || !chk(nys::launch_flash(bf16, p->d, c, s), "landmark context launch") ||
+      !mark(3) || !chk(nys::launch_output(bf16, p->d, p->ks, o, s), "output launch") ||
+      !mark(4))
+    return NYS_E_LAUNCH;
+  if (prof) p->prof_count++;
+
+  if (taps) {
+    const size_t mp = p->mp, m = p->m, dd = p->d, BH = p->BH;
+    auto copy_md = [&](float* dst, const float* src) {
+      if (!dst) return true;
+      return chk(hipMemcpy2DAsync(dst, m * dd * 4, src, mp * dd * 4, m * dd * 4, BH,
+                                  hipMemcpyDeviceToDevice, s),
+                 "tap copy");
+    };
+    auto copy_mm = [&](float* dst, const float* src) {
+      if (!dst) return true;
+      for (size_t b = 0; b < BH; ++b)
+        if (!chk(hipMemcpy2DAsync(dst + b * m * m, m * 4, src + b * mp * mp, mp * 4, m * 4, m,
+                                  hipMemcpyDeviceToDevice, s),
+                 "tap copy"))
+          return false;
+      return true;
+    };
+    if (!copy_md(taps->q_land, p->seg.qt) || !copy_md(taps->k_land, p->seg.kt) ||
+        !copy_md(taps->w, p->out.w_tap) || !copy_md(taps->y, p->out.y_tap) ||
+        !copy_mm(taps->a_s, p->ctx.a_s) || !copy_mm(taps->z, p->ctx.z))
+      return NYS_E_LAUNCH;
+  }
+  return NYS_OK;
+}
+
+extern "C" nys_status nys_attn_forward(nys_attn_plan* plan, const void* q, const void* k,
+                                       const void* v, const float* conv_w, void* out,
+                                       void* stream) {
+  return forward_impl(plan, q, k, v, conv_w, out, stream, nullptr);
+}
+
+extern "C" nys_status nys_attn_forward_debug(nys_attn_plan* plan, const void* q, const void* k,
+                                             const void* v, const float* conv_w, void* out,
+                                             void* stream, const nys_attn_taps* taps) {
+  return forward_impl(plan, q, k, v, conv_w, out, stream, taps);
+}
+
+extern "C" size_t nys_attn_workspace_bytes(const nys_attn_plan* plan) {
+  return plan ? plan->ws_bytes : 0;
+}
+
+extern "C" nys_status nys_attn_profile_enable(nys_attn_plan* p, int max_calls) {
+  if (p == nullptr || max_calls < 0 || max_calls > 100000)
+    return fail(NYS_E_ARG, "profile_enable: bad plan or max_calls");
+  for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
+  p->prof_ev.clear();
+  p->prof_ev.resize((kStages + 1) * (size_t)max_calls);
+  for (auto& e : p->prof_ev)
+    if (hipEventCreate(&e) != hipSuccess) {
+      p->prof_max = 0;
+      return fail(NYS_E_LAUNCH, "event creation failed");
+    }
+  p->prof_max = max_calls;
+  p->prof_count = 0;
+  return NYS_OK;
+}
+
+extern "C" nys_status nys_attn_profile_read(nys_attn_plan* p, float* stage_ms, int max_calls,
+                                            int* n_calls) {
+  if (p == nullptr || n_calls == nullptr || (stage_ms == nullptr && max_calls > 0))
+    return fail(NYS_E_ARG, "profile_read: NULL argument");
+  const int n = std::min(p->prof_count, max_calls);
+  for (int i = 0; i < n; ++i) {
+    hipEvent_t* ev = &p->prof_ev[(kStages + 1) * i];
+    if (hipEventSynchronize(ev[kStages]) != hipSuccess)
+      return fail(NYS_E_LAUNCH, "event sync failed");
+    for (int j = 0; j < kStages; ++j) {
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev[j], ev[j + 1]) != hipSuccess)
+        return fail(NYS_E_LAUNCH, "event elapsed failed");
+      stage_ms[kStages * i + j] = ms;
+    }
+  }
+  *n_calls = n;
+  p->prof_count = 0;
+  return NYS_OK;
+}
+
+extern "C" void nys_attn_destroy(nys_attn_plan* p) {
+  if (p == nullptr) return;
+  (void)hipDeviceSynchronize();
+  for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
+  if (p->ws) (void)hipFree(p->ws);
+  delete p;
+}
+
+extern "C" const char* nys_attn_last_error(void) { return g_err.c_str(); }

@@ -71,8 +71,9 @@ METRIC_CONFIG = "long"
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    rounded = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    # finite inputs cannot overflow 32 bits here (largest is 0xFF7FFFFF + 0x8000)
+    rounded = (u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)
     return rounded.astype(np.uint16)
 
 
@@ -165,15 +166,18 @@ def make_inputs(cfg: Config, seed: int | None = None, family: str = "iid") -> In
 
 def make_well_conditioned_square(n: int, d: int, seed: int, scale: float = 0.5,
                                  dtype: str = F32, B: int = 1, H: int = 1,
-                                 conv_width: int = 33) -> Inputs:
-    """Inputs for the m = n case (one token per segment): small-magnitude Q, K so the
-    n x n softmax kernel is well conditioned."""
+                                 conv_width: int = 33, tied: bool = False) -> Inputs:
+    """Inputs for the m = n case (one token per segment). With ``tied`` K = Q, so the
+    logits are largest on the diagonal and the n x n softmax kernel stays close to a
+    scaled identity (small condition number)."""
     cfg = Config(f"square_n{n}", B, H, n, d, n, conv_width=conv_width, dtype=dtype,
                  seed=seed)
     rng = np.random.default_rng(seed)
     shape = (B, H, n, d)
     q = rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
     k = rng.standard_normal(shape, dtype=np.float32) * np.float32(scale)
+    if tied:
+        k = q.copy()
     v = rng.standard_normal(shape, dtype=np.float32)
     w = conv_weights(rng, H, conv_width)
     return _assemble(cfg, q, k, v, w)

@@ -1,0 +1,119 @@
+/*
+ * nys_attn.h - C ABI of the MI355X (gfx950) Nystrom self-attention forward.
+ *
+ * Operation (review page "Nystromformer: A Nystrom-Based Algorithm for Approximating
+ * Self-Attention", section "Proposed method"): for every (batch b, head h) with
+ * Q, K, V in R^{n x d} and s = 1/sqrt(d),
+ *
+ *   Qt, Kt  = segment means of Q, K over m contiguous segments of l = n/m tokens
+ *   F       = softmax_row(s Q Kt^T)          (n x m)
+ *   A_S     = softmax_row(s Qt Kt^T)         (m x m)
+ *   Bbar    = softmax_row(s Qt K^T)          (m x n)
+ *   Z       = pinv_iters steps of Z <- 1/4 Z (13I - X(15I - X(7I - X))), X = A_S Z,
+ *             from Z_0 = A_S^T / (||A_S||_1 ||A_S||_inf)   (approximates A_S^+)
+ *   out     = F (Z (Bbar V)) + dwconv(V)
+ *
+ * where dwconv(V)[t, :] = sum_{k<W} w[h][k] V[t + k - (W-1)/2, :] with V = 0 outside
+ * [0, n) (a depthwise convolution along the sequence, one filter per head shared by
+ * the d features). The n x n matrices are never formed: time and memory are linear in
+ * n (page, "Main findings").
+ *
+ * Conventions for every entry point:
+ *  - All functions return a status; nothing throws across this boundary. On failure,
+ *    nys_attn_last_error() returns a thread-local description of the last error.
+ *  - Arguments are validated on the host before any HIP call.
+ *  - Device pointers are plain device addresses (hipMalloc or equivalent) on the
+ *    device that was current when the plan was created. The caller owns every tensor.
+ */
+#ifndef NYS_ATTN_H
+#define NYS_ATTN_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Opaque plan: holds the shapes and the device workspace of one problem size. */
+typedef struct nys_attn_plan nys_attn_plan;
+
+/* Element type of q, k, v and out. */
+typedef enum { NYS_F32 = 0, NYS_BF16 = 1 } nys_dtype;
+
+typedef enum {
+  NYS_OK = 0,
+  NYS_E_ARG = 1,         /* invalid argument (null pointer, bad shape, misalignment) */
+  NYS_E_UNSUPPORTED = 2, /* valid but not built: n % m != 0, d not in {32,64,128}, ... */
+  NYS_E_NOMEM = 3,       /* device workspace allocation failed                         */
+  NYS_E_DEVICE = 4,      /* no HIP device, or the current device is not gfx950          */
+  NYS_E_LAUNCH = 5       /* a kernel launch or a HIP runtime call failed                */
+} nys_status;
+
+/* Optional fp32 device buffers filled by nys_attn_forward_debug; each may be NULL.
+ * Layouts (row-major, BH = B*H, heads in b-major order):
+ *   q_land, k_land : [BH][m][d]   segment means Qt, Kt
+ *   a_s, z         : [BH][m][m]   landmark kernel A_S and its iterative inverse Z
+ *   w              : [BH][m][d]   Bbar V
+ *   y              : [BH][m][d]   Z (Bbar V)
+ *   attn           : [BH][n][d]   F Y, the attention part without the conv skip   */
+typedef struct {
+  float *q_land, *k_land, *a_s, *z, *w, *y, *attn;
+} nys_attn_taps;
+
+/* Create a plan for one problem size and allocate its device workspace on the current
+ * device.
+ *   B, H >= 0 (B*H == 0 is an empty problem: forward does nothing);
+ *   n >= 1; 1 <= m <= 256, m <= n, n % m == 0 (else NYS_E_UNSUPPORTED);
+ *   d in {32, 64, 128} (other positive d: NYS_E_UNSUPPORTED);
+ *   conv_width odd, 1 <= conv_width <= 65;
+ *   0 <= pinv_iters <= 100;  dtype NYS_F32 or NYS_BF16; n*d < 2^31.
+ * On success *plan is set; on failure *plan = NULL (when plan itself is non-NULL).
+ * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED, NYS_E_DEVICE (no device / not gfx950, checked
+ * after argument validation), NYS_E_NOMEM. */
+nys_status nys_attn_create(nys_attn_plan **plan, int B, int H, int n, int d, int m,
+                           int conv_width, int pinv_iters, nys_dtype dtype);
+
+/* Enqueue one forward pass on `stream` (a hipStream_t; NULL = the default stream).
+ *   q, k, v, out : device, [B][H][n][d] contiguous, d fastest, element type = dtype,
+ *                  16-byte aligned; out must not overlap q, k or v.
+ *   conv_w       : device, fp32 [H][conv_width], 16-byte aligned not required.
+ * Asynchronous: returns after the launches; device faults surface at the caller's next
+ * synchronisation. A plan serves one forward at a time (its workspace is shared):
+ * forwards on one plan must be ordered on a stream. No NaN/Inf checks.
+ * Errors: NYS_E_ARG (null/misaligned/overlapping pointers), NYS_E_LAUNCH. */
+nys_status nys_attn_forward(nys_attn_plan *plan, const void *q, const void *k,
+                            const void *v, const float *conv_w, void *out, void *stream);
+
+/* nys_attn_forward plus copies of the intermediates into the non-NULL fields of
+ * `taps` (layouts above). taps may be NULL. Same errors as nys_attn_forward. */
+nys_status nys_attn_forward_debug(nys_attn_plan *plan, const void *q, const void *k,
+                                  const void *v, const float *conv_w, void *out,
+                                  void *stream, const nys_attn_taps *taps);
+
+/* Bytes of device workspace the plan owns (0 for a NULL plan). */
+size_t nys_attn_workspace_bytes(const nys_attn_plan *plan);
+
+/* Stage timing for benchmarks. After nys_attn_profile_enable(plan, max_calls), each of
+ * the next max_calls forwards records HIP events around its NYS_ATTN_STAGES kernels on
+ * the forward's stream: 0 segment means, 1 landmark kernel + pseudo-inverse, 2 landmark
+ * context (split over n), 3 output (merge, Y = Z W, softmax times Y, conv skip).
+ * nys_attn_profile_read waits for those events and writes, for call i, the durations in
+ * milliseconds to stage_ms[NYS_ATTN_STAGES*i + 0..3]; *n_calls receives the number of
+ * recorded calls (at most max_calls), after which recording restarts from zero.
+ * Errors: NYS_E_ARG, NYS_E_LAUNCH. */
+#define NYS_ATTN_STAGES 4
+nys_status nys_attn_profile_enable(nys_attn_plan *plan, int max_calls);
+nys_status nys_attn_profile_read(nys_attn_plan *plan, float *stage_ms, int max_calls,
+                                 int *n_calls);
+
+/* Wait for the device, then free the workspace and the plan. NULL-safe. */
+void nys_attn_destroy(nys_attn_plan *plan);
+
+/* Thread-local description of the last failure in this thread ("" if none). */
+const char *nys_attn_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NYS_ATTN_H */

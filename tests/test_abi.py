@@ -1,0 +1,86 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every
+function include/nys_attn.h declares, and validates arguments before touching HIP."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from efficient_transformer_attention_segment_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nys_attn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nys_attn_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_api():
+    names = declared_functions()
+    assert {"nys_attn_create", "nys_attn_forward", "nys_attn_destroy",
+            "nys_attn_forward_debug", "nys_attn_workspace_bytes",
+            "nys_attn_last_error"} <= set(names)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(_lib.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def _create(*args):
+    plan = ctypes.c_void_p(12345)
+    st = _lib.lib().nys_attn_create(ctypes.byref(plan), *args)
+    return st, plan.value
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 64, 32, 8, 33, 6, -1), _lib.NYS_E_ARG),          # bad dtype
+    ((-1, 1, 64, 32, 8, 33, 6, 1), _lib.NYS_E_ARG),          # B < 0
+    ((1, 1, 0, 32, 8, 33, 6, 1), _lib.NYS_E_ARG),            # n = 0
+    ((1, 1, 64, 32, 0, 33, 6, 1), _lib.NYS_E_ARG),           # m = 0
+    ((1, 1, 64, 32, 128, 33, 6, 1), _lib.NYS_E_ARG),         # m > n
+    ((1, 1, 64, 32, 8, 32, 6, 1), _lib.NYS_E_ARG),           # even conv width
+    ((1, 1, 64, 32, 8, 0, 6, 1), _lib.NYS_E_ARG),            # conv width 0
+    ((1, 1, 64, 32, 8, 33, -1, 1), _lib.NYS_E_ARG),          # iterations < 0
+    ((1, 1, 64, 32, 8, 33, 101, 1), _lib.NYS_E_ARG),         # iterations > 100
+    ((1, 1, 64, 0, 8, 33, 6, 1), _lib.NYS_E_ARG),            # d = 0
+    ((1, 1, 60, 32, 8, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),   # n % m != 0
+    ((1, 1, 64, 48, 8, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),   # d not built
+    ((1, 1, 1024, 32, 512, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),  # m > 256
+    ((1, 1, 64, 32, 8, 67, 6, 1), _lib.NYS_E_UNSUPPORTED),   # conv width > 65
+])
+def test_create_rejects_before_any_device_call(args, status):
+    st, plan = _create(*args)
+    assert st == status
+    assert plan is None  # *plan set to NULL on failure
+    assert _lib.nys_attn_last_error() != ""
+
+
+def test_create_null_plan_pointer():
+    assert _lib.lib().nys_attn_create(None, 1, 1, 64, 32, 8, 33, 6, 1) == _lib.NYS_E_ARG
+
+
+def test_null_safe_entry_points():
+    L = _lib.lib()
+    L.nys_attn_destroy(None)
+    assert L.nys_attn_workspace_bytes(None) == 0
+    assert L.nys_attn_forward(None, None, None, None, None, None, None) == _lib.NYS_E_ARG
+    assert L.nys_attn_forward_debug(None, None, None, None, None, None, None,
+                                    None) == _lib.NYS_E_ARG
+    assert L.nys_attn_profile_enable(None, 4) == _lib.NYS_E_ARG
+    n = ctypes.c_int(0)
+    assert L.nys_attn_profile_read(None, None, 0, ctypes.byref(n)) == _lib.NYS_E_ARG
+
+
+def test_valid_shape_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    st, plan = _create(1, 1, 64, 32, 8, 33, 6, 1)
+    assert st == _lib.NYS_E_DEVICE and plan is None
+    assert "device" in _lib.nys_attn_last_error()
