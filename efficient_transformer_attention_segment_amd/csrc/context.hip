@@ -30,18 +30,6 @@ __device__ __forceinline__ void store_cols_f32(float* p, int ld, int row0, int c
         f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
 }
 
-__device__ __forceinline__ float half_max(float x) {  // over the 32 lanes of a half-wave
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
-}
-
-__device__ __forceinline__ float half_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
 __device__ __forceinline__ float block_max(float x, float* red, int tid, int nw) {
   x = wave_max(x);
   __syncthreads();
@@ -312,6 +300,169 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
   }
 }
 
+// ------------------------------------------------------------------ pinv, mp <= 64
+// Compile-time specialisation for MP in {32, 64}: one 32x32 tile per wave (waves beyond
+// the tile count only join the barriers), every loop unrolled, all operand planes in LDS.
+// Z and the X^2/T plane are updated in place, so results are held in registers across
+// the barrier that precedes their store.
+template <int MP, int D>
+__global__ __launch_bounds__(256) void pinv_lds_kernel(CtxArgs a) {
+  constexpr int NT = MP / 32, NTILES = NT * NT, KD = D / 16, KM = MP / 16;
+  constexpr int P = MP * MP;
+  // LDS plane rows padded by 16 bytes: a 32-lane operand fetch then touches every bank
+  // once instead of a few banks many times
+  constexpr int LD = MP + 8, PL = MP * LD;
+  extern __shared__ __align__(16) char lds[];
+  __shared__ float red_part[MP * NT];  // [row][column tile]
+  __shared__ float red_col[NT * MP];   // [row tile][column]
+  __shared__ float red[16];
+  uint16_t* pl = reinterpret_cast<uint16_t*>(lds);
+  auto plane = [&](int idx) { return pl + idx * PL; };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31;
+  const int bh = blockIdx.x, m = a.m;
+  const bool mine = wave < NTILES;
+  const int row0 = 32 * (wave / NT), tj = wave % NT, col0 = 32 * tj;
+  const int jcol = col0 + r32;
+
+  // 1. scaled logits (log2 units)
+  f32x16 at = zero16();
+  if (mine) {
+    const uint16_t* qh = a.qt_hl + (size_t)bh * 2 * MP * D;
+    const uint16_t* kh = a.kt_hl + (size_t)bh * 2 * MP * D;
+    at = gemm_tile_k<KD>(qh, qh + MP * D, D, kh, kh + MP * D, D, row0, col0, lane) * a.scale_log2e;
+  }
+  // 2. row softmax over the m real landmarks (padded rows/columns become 0)
+  if (mine) {
+    float mx[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) mx[rr] = half_max(jcol < m ? at[rr] : kNegBig);
+    if (r32 == 0)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) red_part[acc_row(row0, rr, lane) * NT + tj] = mx[rr];
+  }
+  __syncthreads();
+  if (mine) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int i = acc_row(row0, rr, lane);
+      float mx = red_part[i * NT];
+#pragma unroll
+      for (int c = 1; c < NT; ++c) mx = fmaxf(mx, red_part[i * NT + c]);
+      at[rr] = (i < m && jcol < m) ? fast_exp2(at[rr] - mx) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (mine) {
+    float sm[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) sm[rr] = half_sum(at[rr]);
+    if (r32 == 0)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) red_part[acc_row(row0, rr, lane) * NT + tj] = sm[rr];
+  }
+  __syncthreads();
+  if (mine) {
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int i = acc_row(row0, rr, lane);
+      float sm = red_part[i * NT];
+#pragma unroll
+      for (int c = 1; c < NT; ++c) sm += red_part[i * NT + c];
+      at[rr] = i < m ? at[rr] * (1.f / sm) : 0.f;
+    }
+  }
+  __syncthreads();
+  // abs row sums (partials per column tile) and abs column sums (per row tile)
+  if (mine) {
+    float rs[16], cs = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      rs[rr] = half_sum(fabsf(at[rr]));
+      cs += fabsf(at[rr]);
+    }
+    cs += __shfl_xor(cs, 32);
+    if (r32 == 0)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) red_part[acc_row(row0, rr, lane) * NT + tj] = rs[rr];
+    if (lane < 32) red_col[(row0 / 32) * MP + jcol] = cs;
+  }
+  __syncthreads();
+  float rmax = 0.f, cmax = 0.f;
+  if (tid < m) {
+#pragma unroll
+    for (int c = 0; c < NT; ++c) {
+      rmax += red_part[tid * NT + c];
+      cmax += red_col[c * MP + tid];
+    }
+  }
+  rmax = wave_max(rmax);
+  cmax = wave_max(cmax);
+  if (lane == 0) {
+    red[wave] = rmax;
+    red[8 + wave] = cmax;
+  }
+  __syncthreads();
+  rmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  cmax = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
+  const float alpha = 1.0f / (cmax * rmax);
+  // 3. A_S (fp32 copy), its operand plane, Z_0 = alpha A_S^T (row-major and transposed)
+  if (mine) {
+    store_rows_f32(a.a_s + (size_t)bh * P, MP, row0, col0, at, lane);
+    store_rows_hl(plane(kPA), plane(kPA + 1), LD, row0, col0, at, lane);
+    const f32x16 zv = at * alpha;
+    store_rows_hl(plane(kPZc), plane(kPZc + 1), LD, row0, col0, zv, lane);
+    store_cols_hl(plane(kPZr), plane(kPZr + 1), LD, row0, col0, zv, lane);
+    if (a.iters == 0) store_cols_f32(a.z + (size_t)bh * P, MP, row0, col0, zv, lane);
+  }
+  __syncthreads();
+  // 4. iterations
+  for (int it = 0; it < a.iters; ++it) {
+    f32x16 x, x2, acc;
+    if (mine) {  // X = A Z
+      x = gemm_tile_k<KM>(plane(kPA), plane(kPA + 1), LD, plane(kPZc), plane(kPZc + 1), LD,
+                          row0, col0, lane);
+      store_rows_hl(plane(kPXr), plane(kPXr + 1), LD, row0, col0, x, lane);
+      store_cols_hl(plane(kPXc), plane(kPXc + 1), LD, row0, col0, x, lane);
+    }
+    __syncthreads();
+    if (mine) {  // X^2 = X X
+      x2 = gemm_tile_k<KM>(plane(kPXr), plane(kPXr + 1), LD, plane(kPXc), plane(kPXc + 1), LD,
+                           row0, col0, lane);
+      store_cols_hl(plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, x2, lane);
+    }
+    __syncthreads();
+    if (mine)  // X^3 = X X^2
+      acc = gemm_tile_k<KM>(plane(kPXr), plane(kPXr + 1), LD, plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, lane);
+    __syncthreads();
+    if (mine) {  // T = 13I - 15X + 7X^2 - X^3  (= 13I - X(15I - X(7I - X)))
+      f32x16 tv;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const float diag = (acc_row(row0, rr, lane) == jcol) ? 13.f : 0.f;
+        tv[rr] = diag - 15.f * x[rr] + 7.f * x2[rr] - acc[rr];
+      }
+      store_cols_hl(plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, tv, lane);
+    }
+    __syncthreads();
+    if (mine)  // Z T
+      acc = gemm_tile_k<KM>(plane(kPZr), plane(kPZr + 1), LD, plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, lane);
+    __syncthreads();
+    if (mine) {  // Z <- Z T / 4
+      const f32x16 zv = acc * 0.25f;
+      store_rows_hl(plane(kPZr), plane(kPZr + 1), LD, row0, col0, zv, lane);
+      store_cols_hl(plane(kPZc), plane(kPZc + 1), LD, row0, col0, zv, lane);
+      if (it == a.iters - 1) store_rows_f32(a.z + (size_t)bh * P, MP, row0, col0, zv, lane);
+    }
+    __syncthreads();
+  }
+  // 5. Z (row-major hi/lo, unpadded) for the output stage
+  uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
+  for (int e = tid; e < 2 * P / 8; e += 256) {
+    const int which = e / (P / 8), r = (e % (P / 8)) / (MP / 8), c8 = (e % (MP / 8)) * 8;
+    st8(dst + (size_t)which * P + r * MP + c8, ld8(plane(kPZr + which) + r * LD + c8));
+  }
+}
+
 template <bool kLds, int TPW, int D>
 __global__ __launch_bounds__(kLds ? 256 : 1024) void pinv_kernel(CtxArgs a) {
   extern __shared__ __align__(16) char lds[];
@@ -325,12 +476,14 @@ __global__ __launch_bounds__(kLds ? 256 : 1024) void pinv_kernel(CtxArgs a) {
 }
 
 // ------------------------------------------------------------------ flash
-template <typename Tin, int D>
+// NCH: 8-element V chunks each thread stages per step (D / (16 * LG), rounded up).
+template <typename Tin, int D, int NCH>
 __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
   extern __shared__ __align__(16) char lds[];
   constexpr bool kS = Input<Tin>::kSplit;
-  constexpr int KD = D / 16;   // k-steps over features
-  constexpr int FT = D / 32;   // feature tiles of the accumulator
+  constexpr int KD = D / 16;       // k-steps over features
+  constexpr int FT = D / 32;       // feature tiles of the accumulator
+  constexpr int VR = D + 8;        // LDS row stride (elements) of the row-major V tile
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthreads = blockDim.x;
   const int r32 = lane & 31, h = lane >> 5;
   const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
@@ -356,36 +509,52 @@ __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
   float M = kNegBig, L = 0.f;
 
   const int step = 32 * TG;
-  const int vs = step + 8;  // LDS row stride (elements) of the transposed V tile
-  uint16_t* vt = reinterpret_cast<uint16_t*>(lds);
-  uint16_t* vt_lo = vt + (size_t)D * vs;
-  for (int base = c0; base < c1; base += step) {
-    __syncthreads();
-    // V tile -> LDS, transposed to [feature][token], tokens permuted inside 16-groups
-    for (int qi = tid; qi < step * (D / 8); qi += nthreads) {
-      const int tl = qi / (D / 8), cf = qi % (D / 8), tok = base + tl;
-      float x[8];
-      Input<Tin>::load_raw(V + (size_t)tok * D + cf * 8, tok < a.n, x);
-      const int pos = (tl & ~15) | kslot_perm(tl & 15);
+  const int nchunks = step * (D / 8);
+  uint16_t* vt = reinterpret_cast<uint16_t*>(lds);  // [step][VR] V rows (hi)
+  uint16_t* vt_lo = vt + (size_t)step * VR;          // fp32 input only
+  // transposed-read addressing (see lds_tr16): lane 4j + q of each 16-lane group points
+  // at token row j, feature column 16*(group & 1) + 4q of the feature tile
+  const int trj = (lane & 15) >> 2;
+  const int trcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+
+  auto load_v = [&](int base, Chunk<Tin>* vc) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t hb, lb;
-        if constexpr (kS) {
-          split1(x[e], hb, lb);
-          vt_lo[(size_t)(cf * 8 + e) * vs + pos] = lb;
-        } else {
-          hb = (uint16_t)(__float_as_uint(x[e]) >> 16);
-        }
-        vt[(size_t)(cf * 8 + e) * vs + pos] = hb;
+    for (int u = 0; u < NCH; ++u) {
+      const int qi = tid + nthreads * u;
+      const int row = qi / (D / 8), cf = qi % (D / 8), tok = base + row;
+      vc[u].load(V + (size_t)tok * D + cf * 8, qi < nchunks && tok < a.n);
+    }
+  };
+  auto store_v = [&](const Chunk<Tin>* vc) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int qi = tid + nthreads * u;
+      if (qi < nchunks) {
+        const int row = qi / (D / 8), cf = qi % (D / 8);
+        vc[u].store(vt + (size_t)row * VR + cf * 8, vt_lo + (size_t)row * VR + cf * 8);
       }
     }
-    const int tok_k = base + 32 * tg + r32;
-    Pair8 ka[KD];
+  };
+  auto load_k = [&](int base, Pair8* ka) {
+    const int tok = base + 32 * tg + r32;
 #pragma unroll
     for (int s = 0; s < KD; ++s)
-      ka[s] = Input<Tin>::load8(K + (size_t)tok_k * D + 16 * s + 8 * h, tok_k < a.n);
-    __syncthreads();
+      ka[s] = Input<Tin>::load8(K + (size_t)tok * D + 16 * s + 8 * h, tok < a.n);
+  };
 
+  Chunk<Tin> vc[NCH];
+  Pair8 ka[KD];
+  load_v(c0, vc);
+  load_k(c0, ka);
+  store_v(vc);
+  __syncthreads();
+  for (int base = c0; base < c1; base += step) {
+    const bool more = base + step < c1;
+    Pair8 kn[KD];
+    if (more) {  // next step's K and V, in flight during this step's products
+      load_v(base + step, vc);
+      load_k(base + step, kn);
+    }
     // scores: rows = 32 tokens, columns = 32 landmarks
     f32x16 S = zero16();
 #pragma unroll
@@ -419,14 +588,22 @@ __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const Pair8 pb = split8(&p[8 * s2]);
+      const size_t r0 = (size_t)(32 * tg + 16 * s2 + 4 * h + trj) * VR + trcol;
 #pragma unroll
       for (int f = 0; f < FT; ++f) {
-        const size_t o = (size_t)(32 * f + r32) * vs + 32 * tg + 16 * s2 + 8 * h;
+        const size_t o = r0 + 32 * f;
         Pair8 va;
-        va.hi = ld8(vt + o);
-        va.lo = kS ? ld8(vt_lo + o) : zero8();
+        va.hi = lds_tr16x2(vt + o, vt + o + 8 * VR);
+        va.lo = kS ? lds_tr16x2(vt_lo + o, vt_lo + o + 8 * VR) : zero8();
         wacc[f] = mfma_pair<kS, true>(va, pb, wacc[f]);
       }
+    }
+    if (more) {
+      __syncthreads();  // every wave is done with this step's V tile
+      store_v(vc);
+#pragma unroll
+      for (int s = 0; s < KD; ++s) ka[s] = kn[s];
+      __syncthreads();
     }
   }
   L += __shfl_xor(L, 32);
@@ -479,19 +656,21 @@ __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
 static bool pinv_in_lds(int mp) { return mp <= 64; }
 
 size_t context_lds_bytes(bool bf16, int d, int mp, int LG, int TG) {
-  const size_t vbytes = (bf16 ? 1 : 2) * (size_t)d * (32 * TG + 8) * 2;
+  const size_t vbytes = (bf16 ? 1 : 2) * (size_t)(32 * TG) * (d + 8) * 2;
   const size_t mbytes = (size_t)LG * (TG - 1) * ((d / 32) * 16 * 64 + 128) * 4;
   return vbytes > mbytes ? vbytes : mbytes;
 }
 
 static size_t pinv_lds_bytes(int mp) {
-  return pinv_in_lds(mp) ? (size_t)kLdsPlanes * mp * mp * 2 : 0;
+  return pinv_in_lds(mp) ? (size_t)kLdsPlanes * mp * (mp + 8) * 2 : 0;
 }
 
 template <int D>
 static hipError_t launch_pinv_t(const CtxArgs& a, hipStream_t s) {
-  if (pinv_in_lds(a.mp))
-    hipLaunchKernelGGL((pinv_kernel<true, 1, D>), dim3(a.BH), dim3(256), pinv_lds_bytes(a.mp), s, a);
+  if (a.mp == 32)
+    hipLaunchKernelGGL((pinv_lds_kernel<32, D>), dim3(a.BH), dim3(256), pinv_lds_bytes(32), s, a);
+  else if (a.mp == 64)
+    hipLaunchKernelGGL((pinv_lds_kernel<64, D>), dim3(a.BH), dim3(256), pinv_lds_bytes(64), s, a);
   else
     hipLaunchKernelGGL((pinv_kernel<false, 4, D>), dim3(a.BH), dim3(1024), 0, s, a);
   return hipGetLastError();
@@ -503,10 +682,21 @@ hipError_t launch_pinv(int d, const CtxArgs& a, hipStream_t s) {
   return launch_pinv_t<128>(a, s);
 }
 
+static int flash_nch(int d, int LG) {
+  const int n = (d + 16 * LG - 1) / (16 * LG);
+  return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8;
+}
+
 template <typename Tin, int D>
 static hipError_t launch_flash_t(const CtxArgs& a, hipStream_t s) {
   const size_t flds = context_lds_bytes(Input<Tin>::kSplit == false, D, a.mp, a.LG, a.TG);
-  hipLaunchKernelGGL((flash_kernel<Tin, D>), dim3(a.BH * a.C), dim3(64 * a.LG * a.TG), flds, s, a);
+  const dim3 grid(a.BH * a.C), block(64 * a.LG * a.TG);
+  switch (flash_nch(D, a.LG)) {
+    case 1: hipLaunchKernelGGL((flash_kernel<Tin, D, 1>), grid, block, flds, s, a); break;
+    case 2: hipLaunchKernelGGL((flash_kernel<Tin, D, 2>), grid, block, flds, s, a); break;
+    case 4: hipLaunchKernelGGL((flash_kernel<Tin, D, 4>), grid, block, flds, s, a); break;
+    default: hipLaunchKernelGGL((flash_kernel<Tin, D, 8>), grid, block, flds, s, a); break;
+  }
   return hipGetLastError();
 }
 
@@ -523,16 +713,21 @@ hipError_t launch_flash(bool bf16, int d, const CtxArgs& a, hipStream_t s) {
 
 template <int D>
 static hipError_t set_pinv_attr() {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&pinv_kernel<true, 1, D>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize,
-                                     (int)pinv_lds_bytes(64));
-  return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&pinv_lds_kernel<64, D>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)pinv_lds_bytes(64));
 }
 
 template <typename Tin, int D>
 static hipError_t set_flash_attr(size_t bytes) {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&flash_kernel<Tin, D>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  const void* fns[] = {reinterpret_cast<const void*>(&flash_kernel<Tin, D, 1>),
+                       reinterpret_cast<const void*>(&flash_kernel<Tin, D, 2>),
+                       reinterpret_cast<const void*>(&flash_kernel<Tin, D, 4>),
+                       reinterpret_cast<const void*>(&flash_kernel<Tin, D, 8>)};
+  for (const void* f : fns) {
+    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t configure_context(bool bf16, int d, size_t flash_lds) {

@@ -85,6 +85,24 @@ __device__ __forceinline__ void st8(uint16_t* p, const bf16x8& v) {
   *reinterpret_cast<u32x4*>(p) = __builtin_bit_cast(u32x4, v);
 }
 
+// LDS transpose read (ds_read_b64_tr_b16). Within each 16-lane group, lane k = 4j + q
+// supplies the address of four consecutive 16-bit elements; result lane 4q + c receives
+// element c of the lanes 4*0+q, 4*1+q, 4*2+q, 4*3+q, i.e. with lane 4j + q pointing at
+// row T + j, column F(q) of a row-major tile, lane 4q + c gets rows T..T+3 of column
+// F(q) + c: four consecutive k values of one operand row.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+__device__ __forceinline__ u32x2 lds_tr16(const uint16_t* p) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uint16_t*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Eight k values as two transposed reads (k 0..3 from p0, k 4..7 from p1).
+__device__ __forceinline__ bf16x8 lds_tr16x2(const uint16_t* p0, const uint16_t* p1) {
+  const u32x2 a = lds_tr16(p0), b = lds_tr16(p1);
+  return __builtin_bit_cast(bf16x8, u32x4{a[0], a[1], b[0], b[1]});
+}
+
 // Eight consecutive input elements as an MFMA operand. bf16 inputs are exact in the hi
 // part; fp32 inputs are split into hi/lo. Out-of-range rows read as zero.
 template <typename Tin>
@@ -128,6 +146,37 @@ struct Input<float> {
   }
 };
 
+// Staging of eight consecutive input elements into a row-major bf16 LDS tile (fp32
+// inputs are split into a hi tile and a lo tile).
+template <typename Tin>
+struct Chunk;
+
+template <>
+struct Chunk<uint16_t> {
+  u32x4 v;
+  __device__ __forceinline__ void load(const uint16_t* p, bool valid) {
+    v = valid ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
+  }
+  __device__ __forceinline__ void store(uint16_t* hi, uint16_t* /*lo*/) const {
+    *reinterpret_cast<u32x4*>(hi) = v;
+  }
+};
+
+template <>
+struct Chunk<float> {
+  f32x4 a, b;
+  __device__ __forceinline__ void load(const float* p, bool valid) {
+    a = valid ? *reinterpret_cast<const f32x4*>(p) : f32x4{0.f, 0.f, 0.f, 0.f};
+    b = valid ? *reinterpret_cast<const f32x4*>(p + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ __forceinline__ void store(uint16_t* hi, uint16_t* lo) const {
+    float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const Pair8 p = split8(x);
+    st8(hi, p.hi);
+    st8(lo, p.lo);
+  }
+};
+
 // Position of logical index t inside a 16-wide k-step when an accumulator's rows are
 // reused as the k dimension of the next product. Accumulator register r of lane half h
 // holds row 8*(r/4) + 4*h + (r%4); read as eight k-slots per half for one 16-row step,
@@ -150,6 +199,34 @@ __device__ __forceinline__ float wave_sum(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// DPP lane moves within 16-lane rows (VALU, no LDS round trip).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppQuadXor1 = 0xb1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4e;  // quad_perm [2,3,0,1]
+constexpr int kDppRowRor4 = 0x124;  // rotate right by 4 within the row
+constexpr int kDppRowRor8 = 0x128;  // rotate right by 8 within the row
+
+// Max / sum over the 32 lanes of a half-wave (lanes 0-31 or 32-63): four DPP steps
+// reduce each 16-lane row, one exchange combines the two rows.
+__device__ __forceinline__ float half_max(float x) {
+  x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppRowRor4>(x));
+  x = fmaxf(x, dpp_mov<kDppRowRor8>(x));
+  return fmaxf(x, __shfl_xor(x, 16));
+}
+
+__device__ __forceinline__ float half_sum(float x) {
+  x += dpp_mov<kDppQuadXor1>(x);
+  x += dpp_mov<kDppQuadXor2>(x);
+  x += dpp_mov<kDppRowRor4>(x);
+  x += dpp_mov<kDppRowRor8>(x);
+  return x + __shfl_xor(x, 16);
+}
 
 // Map a linear block index to (head, part) so that all parts of one head run on the
 // same XCD (blocks are dispatched round-robin over the 8 XCDs) and share its L2.
@@ -181,6 +258,27 @@ __device__ __forceinline__ f32x16 gemm_tile(const uint16_t* ahi, const uint16_t*
     Pair8 b{ld8(bhi + ob + k0), ld8(blo + ob + k0)};
     acc = mfma_pair<true, true>(a, b, acc);
   }
+  return acc;
+}
+
+// Same product with a compile-time number of 16-wide k-steps: every operand load is
+// issued before the first MFMA, so one memory latency covers the whole tile.
+template <int KSTEPS>
+__device__ __forceinline__ f32x16 gemm_tile_k(const uint16_t* ahi, const uint16_t* alo, int lda,
+                                              const uint16_t* bhi, const uint16_t* blo, int ldb,
+                                              int row0, int col0, int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  const size_t oa = (size_t)(row0 + r) * lda + 8 * h;
+  const size_t ob = (size_t)(col0 + r) * ldb + 8 * h;
+  Pair8 a[KSTEPS], b[KSTEPS];
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) {
+    a[s] = Pair8{ld8(ahi + oa + 16 * s), ld8(alo + oa + 16 * s)};
+    b[s] = Pair8{ld8(bhi + ob + 16 * s), ld8(blo + ob + 16 * s)};
+  }
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int s = 0; s < KSTEPS; ++s) acc = mfma_pair<true, true>(a[s], b[s], acc);
   return acc;
 }
 

@@ -20,8 +20,10 @@
 //  * O^T += Y^T P^T on MFMA, P fed straight from the score registers (hi/lo bf16) and Y^T
 //    (hi/lo, landmark index permuted to match) from LDS;
 //  * the convolution as a banded product O^T += V_ext^T T^T on MFMA, with the 33-tap
-//    filter expanded per lane into the B operand once per block and V staged in LDS
-//    transposed (feature-major) with its 16-row halo;
+//    filter expanded per lane into the B operand once per block; V is staged row-major
+//    in LDS with its 16-row halo (16-byte writes) and read feature-major with LDS
+//    transpose reads; the next step's V rows and Q are loaded into registers while the
+//    current step computes;
 //  * bf16 (RNE) or fp32 store: each lane writes d/2 contiguous features of its token.
 #include "nys_common.h"
 #include "nys_kernels.h"
@@ -41,7 +43,8 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   constexpr bool kS = Input<Tin>::kSplit;
   constexpr int KD = D / 16, FT = D / 32;
   constexpr int EXT = 96 + 16 * KS;  // staged V rows per 128-token step (with halo)
-  constexpr int VS = EXT + 8;        // LDS row stride (elements) of the transposed V
+  constexpr int VR = D + 8;          // LDS row stride (elements) of the row-major V tile
+  constexpr int NCH = (EXT * (D / 8) + 255) / 256;  // 8-element V chunks per thread
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, h = lane >> 5;
   const int mp = a.mp, YS = mp + 8;
@@ -59,8 +62,8 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   uint16_t* wtl = un;                                // [2][D][YS]  W^T hi, lo
   float* wgt = reinterpret_cast<float*>(un + (size_t)2 * D * YS);  // [C][mp]
   uint16_t* kl = un;                                 // [2][mp][KR] Kt hi, lo (kKtLds)
-  uint16_t* vt = kl + (kKtLds ? (size_t)2 * mp * KR : 0);  // [D][VS] V^T (hi)
-  uint16_t* vt_lo = vt + (size_t)D * VS;           // [D][VS]     V^T lo (fp32 input only)
+  uint16_t* vt = kl + (kKtLds ? (size_t)2 * mp * KR : 0);  // [EXT][VR] V rows (hi)
+  uint16_t* vt_lo = vt + (size_t)EXT * VR;         // [EXT][VR]   V rows lo (fp32 input only)
   const bool taps = grp == 0;
 
   {
@@ -168,31 +171,54 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   const Tin* Q = static_cast<const Tin*>(a.q) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
 
-  for (int T0 = t_begin; T0 < t_end; T0 += 128) {
-    __syncthreads();
+  // transposed-read addressing of the conv operand (see lds_tr16): lane k = 4j + q of
+  // each 16-lane group points at row j, column F(q) of the feature tile
+  const int grp16 = lane >> 4, trj = (lane & 15) >> 2, trq = lane & 3;
+  const int trcol = (D / 2) * (trq & 1) + 8 * (grp16 & 1) + 4 * (trq >> 1);
+
+  auto load_v = [&](int T0, Chunk<Tin>* vc) {
     const int e0 = T0 - a.half;
-    for (int qi = tid; qi < EXT * (D / 8); qi += 256) {
-      const int u = qi / (D / 8), cf = qi % (D / 8), tok = e0 + u;
-      float x[8];
-      Input<Tin>::load_raw(V + (size_t)tok * D + cf * 8, tok >= 0 && tok < a.n, x);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        uint16_t hb, lb;
-        if constexpr (kS) {
-          split1(x[e], hb, lb);
-          vt_lo[(size_t)(cf * 8 + e) * VS + u] = lb;
-        } else {
-          hb = (uint16_t)(__float_as_uint(x[e]) >> 16);
-        }
-        vt[(size_t)(cf * 8 + e) * VS + u] = hb;
+    for (int u = 0; u < NCH; ++u) {
+      const int qi = tid + 256 * u;
+      const int row = qi / (D / 8), cf = qi % (D / 8), tok = e0 + row;
+      vc[u].load(V + (size_t)tok * D + cf * 8, qi < EXT * (D / 8) && tok >= 0 && tok < a.n);
+    }
+  };
+  auto store_v = [&](const Chunk<Tin>* vc) {
+#pragma unroll
+    for (int u = 0; u < NCH; ++u) {
+      const int qi = tid + 256 * u;
+      if (qi < EXT * (D / 8)) {
+        const int row = qi / (D / 8), cf = qi % (D / 8);
+        vc[u].store(vt + (size_t)row * VR + cf * 8, vt_lo + (size_t)row * VR + cf * 8);
       }
+    }
+  };
+  auto load_q = [&](int T0, Pair8* qb) {
+    const int tq = T0 + 32 * wave + r32;
+#pragma unroll
+    for (int s = 0; s < KD; ++s)
+      qb[s] = Input<Tin>::load8(Q + (size_t)tq * D + 16 * s + 8 * h, tq < t_end);
+  };
+
+  Chunk<Tin> vc[NCH];
+  Pair8 qb[KD];
+  load_v(t_begin, vc);
+  load_q(t_begin, qb);
+  __syncthreads();  // prologue done with the region the V tile reuses
+  store_v(vc);
+  __syncthreads();
+
+  for (int T0 = t_begin; T0 < t_end; T0 += 128) {
+    const bool more = T0 + 128 < t_end;
+    Pair8 qn[KD];
+    if (more) {  // next step's V rows and Q, in flight during this step's products
+      load_v(T0 + 128, vc);
+      load_q(T0 + 128, qn);
     }
     const int tq = T0 + 32 * wave + r32;
     const bool qok = tq < t_end;
-    Pair8 qb[KD];
-#pragma unroll
-    for (int s = 0; s < KD; ++s) qb[s] = Input<Tin>::load8(Q + (size_t)tq * D + 16 * s + 8 * h, qok);
-    __syncthreads();
 
     f32x16 oacc[FT];
 #pragma unroll
@@ -264,14 +290,16 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
               f32x4{oacc[f][4 * q4], oacc[f][4 * q4 + 1], oacc[f][4 * q4 + 2], oacc[f][4 * q4 + 3]};
     }
 
+    // conv: A operand V_ext^T (features x ext tokens) by transposed reads of the V rows
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-      const size_t rowoff = (size_t)out_feature<D>(f, r32) * VS + 32 * wave + 8 * h;
+      const int col = trcol + 16 * f;
 #pragma unroll
       for (int s = 0; s < KS; ++s) {
+        const size_t r0 = (size_t)(32 * wave + 16 * s + 8 * h + trj) * VR + col;
         Pair8 va;
-        va.hi = ld8(vt + rowoff + 16 * s);
-        va.lo = kS ? ld8(vt_lo + rowoff + 16 * s) : zero8();
+        va.hi = lds_tr16x2(vt + r0, vt + r0 + 4 * VR);
+        va.lo = kS ? lds_tr16x2(vt_lo + r0, vt_lo + r0 + 4 * VR) : zero8();
         oacc[f] = mfma_pair<kS, true>(va, wb[s], oacc[f]);
       }
     }
@@ -300,6 +328,13 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
         }
       }
     }
+    if (more) {
+      __syncthreads();  // every wave is done with this step's V tile
+      store_v(vc);
+#pragma unroll
+      for (int s = 0; s < KD; ++s) qb[s] = qn[s];
+      __syncthreads();
+    }
   }
 }
 
@@ -311,7 +346,7 @@ static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, bool k
   const size_t yl = (size_t)2 * d * (mp + 8) * 2;
   const size_t prologue = yl + (size_t)C * mp * 4;
   const size_t main = ((kt_lds ? (size_t)2 * mp * (d + 8) : 0) +
-                       (bf16 ? 1 : 2) * (size_t)d * (ext + 8)) * 2;
+                       (bf16 ? 1 : 2) * ext * (size_t)(d + 8)) * 2;
   return yl + (prologue > main ? prologue : main);
 }
 

@@ -110,7 +110,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   const size_t flash_lds = nys::context_lds_bytes(bf16, d, p->mp, p->LG, p->TG);
   const size_t out_lds = nys::output_lds_bytes(bf16, d, p->mp, p->ks, p->C);
   const size_t max_lds = (size_t)prop.sharedMemPerBlock;
-  if (flash_lds > max_lds || out_lds > max_lds || (size_t)12 * 64 * 64 * 2 > max_lds) {
+  if (flash_lds > max_lds || out_lds > max_lds || (size_t)12 * 64 * 72 * 2 > max_lds) {
     delete p;
     return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
   }
