@@ -494,13 +494,21 @@ __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
   const Tin* K = static_cast<const Tin*>(a.k) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
 
+  // landmark operand, with s*log2(e) folded in so the scores come out in log2 units
   Pair8 qb[KD];
   {
-    const uint16_t* qh = a.qt_hl + (size_t)bh * 2 * mp * D + (size_t)(32 * g + r32) * D + 8 * h;
+    const float* qs = a.qt + ((size_t)bh * mp + 32 * g + r32) * D + 8 * h;
 #pragma unroll
     for (int s = 0; s < KD; ++s) {
-      qb[s].hi = ld8(qh + 16 * s);
-      qb[s].lo = ld8(qh + (size_t)mp * D + 16 * s);
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(qs + 16 * s);
+      const f32x4 u1 = *reinterpret_cast<const f32x4*>(qs + 16 * s + 4);
+      float x[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        x[q] = u0[q] * a.scale_log2e;
+        x[4 + q] = u1[q] * a.scale_log2e;
+      }
+      qb[s] = split8(x);
     }
   }
   f32x16 wacc[FT];
@@ -555,36 +563,53 @@ __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
       load_v(base + step, vc);
       load_k(base + step, kn);
     }
-    // scores: rows = 32 tokens, columns = 32 landmarks
+    // scores (log2 units): rows = 32 tokens, columns = 32 landmarks
     f32x16 S = zero16();
 #pragma unroll
     for (int s = 0; s < KD; ++s) S = mfma_pair<kS, true>(ka[s], qb[s], S);
 
-    float x[16];
+    // online softmax over tokens per landmark; only the chunk's last step can be partial
+    const bool partial = base + 32 * tg + 32 > c1;
     float mx = kNegBig;
-    unsigned okmask = 0;
+    if (!partial) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int tok = base + 32 * tg + 8 * (rr >> 2) + 4 * h + (rr & 3);
-      const bool ok = tok < c1;
-      okmask |= (ok ? 1u : 0u) << rr;
-      x[rr] = S[rr] * a.scale_log2e;
-      if (ok) mx = fmaxf(mx, x[rr]);
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, S[rr]);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int tok = base + 32 * tg + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        if (tok >= c1) S[rr] = kNegBig;
+        mx = fmaxf(mx, S[rr]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(M, mx);
-    const float corr = fast_exp2(M - mn);
+    // lazy rescaling: keep the reference maximum while every lane's new maximum stays
+    // within 2^8 of it (probabilities then stay <= 256); the state (M, L, acc) is exact
+    // for any reference point
+    if (__any(mx > M + 8.f)) {
+      const float mn = fmaxf(M, mx);
+      const float corr = fast_exp2(M - mn);
+      L *= corr;
+#pragma unroll
+      for (int f = 0; f < FT; ++f) wacc[f] *= corr;
+      M = mn;
+    }
     float p[16];
     float ps = 0.f;
+    if (!partial) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      p[rr] = ((okmask >> rr) & 1u) ? fast_exp2(x[rr] - mn) : 0.f;
-      ps += p[rr];
+      for (int rr = 0; rr < 16; ++rr) {
+        p[rr] = fast_exp2(S[rr] - M);
+        ps += p[rr];
+      }
+    } else {  // masked tokens contribute exactly 0 (M may still be the -1e30 start value)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        p[rr] = S[rr] > 0.5f * kNegBig ? fast_exp2(S[rr] - M) : 0.f;
+        ps += p[rr];
+      }
     }
-    L = L * corr + ps;
-    M = mn;
-#pragma unroll
-    for (int f = 0; f < FT; ++f) wacc[f] *= corr;
+    L += ps;
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const Pair8 pb = split8(&p[8 * s2]);

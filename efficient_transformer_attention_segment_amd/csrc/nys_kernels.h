@@ -20,6 +20,7 @@ struct SegArgs {
 struct CtxArgs {
   const void* k;
   const void* v;
+  const float* qt;        // [BH][mp][d]  landmarks Qt (fp32)
   const uint16_t* qt_hl;  // [BH][2][mp][d]
   const uint16_t* kt_hl;  // [BH][2][mp][d]
   float* a_s;             // [BH][mp][mp]  logits, then A_S
@@ -48,6 +49,7 @@ struct OutArgs {
   float* attn_tap;        // [BH][n][d] or nullptr
   float* w_tap;           // [BH][mp][d] or nullptr (written by each head's first block)
   float* y_tap;           // [BH][mp][d] or nullptr
+  const float* kt;        // [BH][mp][d]      landmarks Kt (fp32)
   const uint16_t* kt_hl;  // [BH][2][mp][d]
   const uint16_t* z_hl;   // [BH][2][mp][mp]
   const float* part_w;    // [BH][C][d][mp]

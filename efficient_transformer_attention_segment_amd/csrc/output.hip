@@ -7,23 +7,23 @@
 // Prologue of every block (4 waves, one head): merge the C partial states of the
 // landmark context (per landmark, weights exp2(M_c - M*) / sum_c exp2(M_c - M*) L_c,
 // fixed chunk order) into W^T in LDS, form Y = Z W on MFMA and keep Y^T (hi/lo bf16,
-// landmark index permuted to match the score registers) in LDS.
+// landmark index permuted to match the score registers) in LDS; stage Kt (hi/lo, with
+// s*log2(e) folded in) and the conv filter's MFMA operand in LDS.
 //
 // The block then walks a contiguous token range of its head in steps of 128 tokens;
 // each wave owns 32 tokens per step. Per wave and step:
-//  * scores S^T = Kt Q^T (landmarks x tokens) on MFMA, Kt as hi/lo bf16 staged in LDS
-//    once per block (read from L2 when it does not fit), Q read straight into the B
+//  * scores S^T = Kt Q^T (landmarks x tokens) on MFMA, Q read straight into the B
 //    operand;
-//  * softmax over the landmarks, one landmark tile at a time with a running max/sum
-//    (each lane holds one token, so the normaliser is lane-local plus one exchange with
-//    the partner half-wave);
-//  * O^T += Y^T P^T on MFMA, P fed straight from the score registers (hi/lo bf16) and Y^T
-//    (hi/lo, landmark index permuted to match) from LDS;
-//  * the convolution as a banded product O^T += V_ext^T T^T on MFMA, with the 33-tap
-//    filter expanded per lane into the B operand once per block; V is staged row-major
-//    in LDS with its 16-row halo (16-byte writes) and read feature-major with LDS
-//    transpose reads; the next step's V rows and Q are loaded into registers while the
-//    current step computes;
+//  * softmax over the landmarks. Each lane holds one token, so the normaliser is
+//    lane-local plus one exchange with the partner half-wave. With at most two landmark
+//    tiles (NT = 1, 2) all scores stay in registers: max, exponentials, sum, then the
+//    probabilities scaled by 1/sum feed the product directly (no accumulator
+//    rescaling). Larger m runs an online softmax over landmark tiles (NT = 0);
+//  * O^T += Y^T P^T on MFMA, P fed straight from the score registers (hi/lo bf16);
+//  * the convolution as a banded product O^T += V_ext^T T^T on MFMA, with the filter
+//    expanded per lane into the B operand once per block; V is staged row-major in LDS
+//    with its halo (16-byte writes) and read feature-major with LDS transpose reads;
+//    the next step's V rows and Q are loaded into registers while this step computes;
 //  * bf16 (RNE) or fp32 store: each lane writes d/2 contiguous features of its token.
 #include "nys_common.h"
 #include "nys_kernels.h"
@@ -37,33 +37,45 @@ __device__ __forceinline__ int out_feature(int f, int i) {
   return (D / 2) * ((i >> 2) & 1) + 16 * f + 4 * (i >> 3) + (i & 3);
 }
 
-template <typename Tin, int D, int KS, bool kKtLds>
+// Landmark index held by score register rr of landmark tile lt.
+__device__ __forceinline__ int score_landmark(int lt, int rr, int h) {
+  return 32 * lt + 8 * (rr >> 2) + 4 * h + (rr & 3);
+}
+
+// NT: landmark tiles handled with all scores in registers (1 or 2), or 0 for the
+// online softmax over a runtime number of tiles. kFull: m == 32 * NT (no masking).
+template <typename Tin, int D, int KS, bool kKtLds, int NT, bool kFull>
 __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   extern __shared__ __align__(16) char lds[];
   constexpr bool kS = Input<Tin>::kSplit;
   constexpr int KD = D / 16, FT = D / 32;
   constexpr int EXT = 96 + 16 * KS;  // staged V rows per 128-token step (with halo)
   constexpr int VR = D + 8;          // LDS row stride (elements) of the row-major V tile
+  constexpr int KR = D + 8;          // LDS row stride of the Kt planes
   constexpr int NCH = (EXT * (D / 8) + 255) / 256;  // 8-element V chunks per thread
+  static_assert(NT == 0 || kKtLds, "register-resident softmax expects Kt in LDS");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, h = lane >> 5;
-  const int mp = a.mp, YS = mp + 8;
-  constexpr int KR = D + 8;  // LDS row stride of the Kt planes
+  const int mp = NT > 0 ? 32 * NT : a.mp;
+  const int YS = mp + 8;
   int bh, grp;
   xcd_map(blockIdx.x, a.BH, a.G, bh, grp);
   const int head = bh % a.H;
   const int t_begin = grp * a.tok_per_block;
   const int t_end = min(a.n, t_begin + a.tok_per_block);
+  // scores in log2 units: folded into Kt when it is staged (NT > 0), else applied here
+  const float score_scale = NT > 0 ? 1.f : a.scale_log2e;
 
-  uint16_t* yl = reinterpret_cast<uint16_t*>(lds);  // [2][D][YS]  Y^T hi, lo
-  // region after yl, used first by the prologue (W^T planes, chunk weights), then by
-  // the main loop (Kt planes when kKtLds, transposed V tile)
-  uint16_t* un = yl + (size_t)2 * D * YS;
-  uint16_t* wtl = un;                                // [2][D][YS]  W^T hi, lo
+  uint16_t* yl = reinterpret_cast<uint16_t*>(lds);     // [2][D][YS]  Y^T hi, lo
+  uint16_t* wl = yl + (size_t)2 * D * YS;              // [KS][2][64][8] conv B operand
+  // region used first by the prologue (W^T planes, chunk weights), then by the main
+  // loop (Kt planes when kKtLds, V rows)
+  uint16_t* un = wl + (size_t)KS * 2 * 64 * 8;
+  uint16_t* wtl = un;                                  // [2][D][YS]  W^T hi, lo
   float* wgt = reinterpret_cast<float*>(un + (size_t)2 * D * YS);  // [C][mp]
-  uint16_t* kl = un;                                 // [2][mp][KR] Kt hi, lo (kKtLds)
+  uint16_t* kl = un;                                   // [2][mp][KR] Kt hi, lo
   uint16_t* vt = kl + (kKtLds ? (size_t)2 * mp * KR : 0);  // [EXT][VR] V rows (hi)
-  uint16_t* vt_lo = vt + (size_t)EXT * VR;         // [EXT][VR]   V rows lo (fp32 input only)
+  uint16_t* vt_lo = vt + (size_t)EXT * VR;             // V rows lo (fp32 input only)
   const bool taps = grp == 0;
 
   {
@@ -96,6 +108,22 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
       }
       const float inv = 1.f / den;
       for (int c = 0; c < C; ++c) wgt[c * mp + j] *= inv;
+    }
+    // conv filter as the B operand of the banded product (identical for every wave)
+    if (tid < 64) {
+      const float* w = a.conv_w + (size_t)head * a.W;
+#pragma unroll
+      for (int s = 0; s < KS; ++s) {
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int k = 16 * s + 8 * h + e - r32;
+          x[e] = (k >= 0 && k < a.W) ? w[k] : 0.f;
+        }
+        const Pair8 p = split8(x);
+        st8(wl + ((size_t)(2 * s) * 64 + lane) * 8, p.hi);
+        st8(wl + ((size_t)(2 * s + 1) * 64 + lane) * 8, p.lo);
+      }
     }
     __syncthreads();
     // W^T[f][j] = sum_c wgt[c][j] * partial_c^T[f][j], four landmarks per thread
@@ -146,35 +174,38 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     }
     __syncthreads();
     if constexpr (kKtLds) {
-      const uint16_t* ksrc = a.kt_hl + (size_t)bh * 2 * mp * D;
-      for (int e = tid; e < 2 * mp * (D / 8); e += 256) {
-        const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
-        st8(kl + (size_t)row * KR + c8, ld8(ksrc + (size_t)row * D + c8));
-      }
-    }
-  }
-  Pair8 wb[KS];
-  {
-    const float* w = a.conv_w + (size_t)head * a.W;
+      if constexpr (NT > 0) {  // from the fp32 landmarks, scaled to log2 units, then split
+        const float* ksrc = a.kt + (size_t)bh * mp * D;
+        for (int e = tid; e < mp * (D / 8); e += 256) {
+          const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+          const f32x4 u0 = *reinterpret_cast<const f32x4*>(ksrc + (size_t)row * D + c8);
+          const f32x4 u1 = *reinterpret_cast<const f32x4*>(ksrc + (size_t)row * D + c8 + 4);
+          float x[8];
 #pragma unroll
-    for (int s = 0; s < KS; ++s) {
-      float x[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int k = 16 * s + 8 * h + e - r32;
-        x[e] = (k >= 0 && k < a.W) ? w[k] : 0.f;
+          for (int q = 0; q < 4; ++q) {
+            x[q] = u0[q] * a.scale_log2e;
+            x[4 + q] = u1[q] * a.scale_log2e;
+          }
+          const Pair8 p = split8(x);
+          st8(kl + (size_t)row * KR + c8, p.hi);
+          st8(kl + (size_t)mp * KR + (size_t)row * KR + c8, p.lo);
+        }
+      } else {
+        const uint16_t* ksrc = a.kt_hl + (size_t)bh * 2 * mp * D;
+        for (int e = tid; e < 2 * mp * (D / 8); e += 256) {
+          const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+          st8(kl + (size_t)row * KR + c8, ld8(ksrc + (size_t)row * D + c8));
+        }
       }
-      wb[s] = split8(x);
     }
   }
   const uint16_t* khl = a.kt_hl + (size_t)bh * 2 * mp * D;
   const Tin* Q = static_cast<const Tin*>(a.q) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
-
   // transposed-read addressing of the conv operand (see lds_tr16): lane k = 4j + q of
   // each 16-lane group points at row j, column F(q) of the feature tile
-  const int grp16 = lane >> 4, trj = (lane & 15) >> 2, trq = lane & 3;
-  const int trcol = (D / 2) * (trq & 1) + 8 * (grp16 & 1) + 4 * (trq >> 1);
+  const int trj = (lane & 15) >> 2, trq = lane & 3;
+  const int trcol = (D / 2) * (trq & 1) + 8 * ((lane >> 4) & 1) + 4 * (trq >> 1);
 
   auto load_v = [&](int T0, Chunk<Tin>* vc) {
     const int e0 = T0 - a.half;
@@ -201,6 +232,36 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     for (int s = 0; s < KD; ++s)
       qb[s] = Input<Tin>::load8(Q + (size_t)tq * D + 16 * s + 8 * h, tq < t_end);
   };
+  // scores of landmark tile lt (landmarks x tokens)
+  auto scores = [&](int lt, const Pair8* qb) -> f32x16 {
+    f32x16 S = zero16();
+    if constexpr (kKtLds) {
+      const uint16_t* kp = kl + (size_t)(32 * lt + r32) * KR + 8 * h;
+#pragma unroll
+      for (int s = 0; s < KD; ++s) {
+        const Pair8 ka{ld8(kp + 16 * s), ld8(kp + (size_t)mp * KR + 16 * s)};
+        S = mfma_pair<true, kS>(ka, qb[s], S);
+      }
+    } else {
+      const uint16_t* kp = khl + (size_t)(32 * lt + r32) * D + 8 * h;
+      Pair8 ka[KD];
+#pragma unroll
+      for (int s = 0; s < KD; ++s) ka[s] = Pair8{ld8(kp + 16 * s), ld8(kp + (size_t)mp * D + 16 * s)};
+#pragma unroll
+      for (int s = 0; s < KD; ++s) S = mfma_pair<true, kS>(ka[s], qb[s], S);
+    }
+    return S;
+  };
+  // O^T += Y^T P^T for the 16 landmarks of k-step 2*lt + s2 (P values p[0..7])
+  auto add_py = [&](f32x16* oacc, int lt, int s2, const float* p) {
+    const Pair8 pb = split8(p);
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+      const uint16_t* yp = yl + (size_t)out_feature<D>(f, r32) * YS + 32 * lt + 16 * s2 + 8 * h;
+      const Pair8 ya{ld8(yp), ld8(yp + (size_t)D * YS)};
+      oacc[f] = mfma_pair<true, true>(ya, pb, oacc[f]);
+    }
+  };
 
   Chunk<Tin> vc[NCH];
   Pair8 qb[KD];
@@ -223,62 +284,71 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     f32x16 oacc[FT];
 #pragma unroll
     for (int f = 0; f < FT; ++f) oacc[f] = zero16();
-    float M = kNegBig, L = 0.f;
-    for (int lt = 0; lt < mp / 32; ++lt) {
-      f32x16 S = zero16();
-      if constexpr (kKtLds) {
-        const uint16_t* kp = kl + (size_t)(32 * lt + r32) * KR + 8 * h;
+    if constexpr (NT > 0) {
+      // all scores in registers: max, exponentials, sum, then normalised P
+      f32x16 S[NT];
 #pragma unroll
-        for (int s = 0; s < KD; ++s) {
-          const Pair8 ka{ld8(kp + 16 * s), ld8(kp + (size_t)mp * KR + 16 * s)};
-          S = mfma_pair<true, kS>(ka, qb[s], S);
-        }
-      } else {
-        const uint16_t* kp = khl + (size_t)(32 * lt + r32) * D + 8 * h;
-        Pair8 ka[KD];
-#pragma unroll
-        for (int s = 0; s < KD; ++s) ka[s] = Pair8{ld8(kp + 16 * s), ld8(kp + (size_t)mp * D + 16 * s)};
-#pragma unroll
-        for (int s = 0; s < KD; ++s) S = mfma_pair<true, kS>(ka[s], qb[s], S);
-      }
-      float x[16];
+      for (int lt = 0; lt < NT; ++lt) S[lt] = scores(lt, qb);
       float mx = kNegBig;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int lm = 32 * lt + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        x[rr] = S[rr] * a.scale_log2e;
-        if (lm < a.m) mx = fmaxf(mx, x[rr]);
-      }
+      for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          if (kFull || score_landmark(lt, rr, h) < a.m) mx = fmaxf(mx, S[lt][rr]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mn = fmaxf(M, mx);
-      const float corr = fast_exp2(M - mn);
-      float p[16];
       float ps = 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int lm = 32 * lt + 8 * (rr >> 2) + 4 * h + (rr & 3);
-        p[rr] = lm < a.m ? fast_exp2(x[rr] - mn) : 0.f;
-        ps += p[rr];
-      }
-      L = L * corr + ps;
-      M = mn;
+      for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
-      for (int f = 0; f < FT; ++f) oacc[f] *= corr;
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const Pair8 pb = split8(&p[8 * s2]);
-#pragma unroll
-        for (int f = 0; f < FT; ++f) {
-          const uint16_t* yp = yl + (size_t)out_feature<D>(f, r32) * YS + 32 * lt + 16 * s2 + 8 * h;
-          const Pair8 ya{ld8(yp), ld8(yp + (size_t)D * YS)};
-          oacc[f] = mfma_pair<true, true>(ya, pb, oacc[f]);
+        for (int rr = 0; rr < 16; ++rr) {
+          const float e = (kFull || score_landmark(lt, rr, h) < a.m) ? fast_exp2(S[lt][rr] - mx) : 0.f;
+          S[lt][rr] = e;
+          ps += e;
         }
-      }
-    }
-    L += __shfl_xor(L, 32);
-    const float inv = 1.f / L;
+      ps += __shfl_xor(ps, 32);
+      const float inv = 1.f / ps;
 #pragma unroll
-    for (int f = 0; f < FT; ++f) oacc[f] *= inv;
+      for (int lt = 0; lt < NT; ++lt)
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) {
+          float p[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) p[e] = S[lt][8 * s2 + e] * inv;
+          add_py(oacc, lt, s2, p);
+        }
+    } else {
+      float M = kNegBig, L = 0.f;
+      for (int lt = 0; lt < mp / 32; ++lt) {
+        const f32x16 S = scores(lt, qb);
+        float x[16];
+        float mx = kNegBig;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          x[rr] = S[rr] * score_scale;
+          if (score_landmark(lt, rr, h) < a.m) mx = fmaxf(mx, x[rr]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float mn = fmaxf(M, mx);
+        const float corr = fast_exp2(M - mn);
+        float p[16];
+        float ps = 0.f;
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+          p[rr] = score_landmark(lt, rr, h) < a.m ? fast_exp2(x[rr] - mn) : 0.f;
+          ps += p[rr];
+        }
+        L = L * corr + ps;
+        M = mn;
+#pragma unroll
+        for (int f = 0; f < FT; ++f) oacc[f] *= corr;
+#pragma unroll
+        for (int s2 = 0; s2 < 2; ++s2) add_py(oacc, lt, s2, &p[8 * s2]);
+      }
+      L += __shfl_xor(L, 32);
+      const float inv = 1.f / L;
+#pragma unroll
+      for (int f = 0; f < FT; ++f) oacc[f] *= inv;
+    }
 
     if (a.attn_tap != nullptr && qok) {
       float* tp = a.attn_tap + ((size_t)bh * a.n + tq) * D + (D / 2) * h;
@@ -292,15 +362,16 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
 
     // conv: A operand V_ext^T (features x ext tokens) by transposed reads of the V rows
 #pragma unroll
-    for (int f = 0; f < FT; ++f) {
-      const int col = trcol + 16 * f;
+    for (int s = 0; s < KS; ++s) {
+      const Pair8 wb{ld8(wl + ((size_t)(2 * s) * 64 + lane) * 8),
+                     ld8(wl + ((size_t)(2 * s + 1) * 64 + lane) * 8)};
+      const size_t r0 = (size_t)(32 * wave + 16 * s + 8 * h + trj) * VR + trcol;
 #pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        const size_t r0 = (size_t)(32 * wave + 16 * s + 8 * h + trj) * VR + col;
+      for (int f = 0; f < FT; ++f) {
         Pair8 va;
-        va.hi = lds_tr16x2(vt + r0, vt + r0 + 4 * VR);
-        va.lo = kS ? lds_tr16x2(vt_lo + r0, vt_lo + r0 + 4 * VR) : zero8();
-        oacc[f] = mfma_pair<kS, true>(va, wb[s], oacc[f]);
+        va.hi = lds_tr16x2(vt + r0 + 16 * f, vt + r0 + 16 * f + 4 * VR);
+        va.lo = kS ? lds_tr16x2(vt_lo + r0 + 16 * f, vt_lo + r0 + 16 * f + 4 * VR) : zero8();
+        oacc[f] = mfma_pair<kS, true>(va, wb, oacc[f]);
       }
     }
 
@@ -338,16 +409,18 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ host side
 // LDS budget of one block; Kt goes to LDS only when everything fits in 160 KiB.
 constexpr size_t kLdsLimit = 160 * 1024;
 
 static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, bool kt_lds) {
   const size_t ext = 96 + 16 * (size_t)conv_ksteps;
   const size_t yl = (size_t)2 * d * (mp + 8) * 2;
+  const size_t wl = (size_t)conv_ksteps * 2 * 64 * 8 * 2;
   const size_t prologue = yl + (size_t)C * mp * 4;
   const size_t main = ((kt_lds ? (size_t)2 * mp * (d + 8) : 0) +
                        (bf16 ? 1 : 2) * ext * (size_t)(d + 8)) * 2;
-  return yl + (prologue > main ? prologue : main);
+  return yl + wl + (prologue > main ? prologue : main);
 }
 
 static bool kt_in_lds(bool bf16, int d, int mp, int conv_ksteps, int C) {
@@ -358,15 +431,31 @@ size_t output_lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C) {
   return lds_bytes(bf16, d, mp, conv_ksteps, C, kt_in_lds(bf16, d, mp, conv_ksteps, C));
 }
 
+// Kernel variant for a shape: register-resident softmax for m <= 64 with the usual
+// conv width (k-steps 4), online softmax otherwise.
+template <typename Tin, int D, int KS>
+static const void* pick_kernel(const OutArgs& a, bool kt_lds) {
+  if constexpr (KS == 4) {
+    if (a.mp <= 64 && kt_lds) {
+      const bool full = a.m == a.mp;
+      if (a.mp == 32)
+        return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true>)
+                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false>);
+      return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true>)
+                  : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false>);
+    }
+  }
+  return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false>)
+                : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false>);
+}
+
 template <typename Tin, int D, int KS>
 static hipError_t launch_t(const OutArgs& a, hipStream_t s) {
   constexpr bool kBf16 = !Input<Tin>::kSplit;
   const size_t lds = output_lds_bytes(kBf16, D, a.mp, KS, a.C);
-  if (kt_in_lds(kBf16, D, a.mp, KS, a.C))
-    hipLaunchKernelGGL((output_kernel<Tin, D, KS, true>), dim3(a.BH * a.G), dim3(256), lds, s, a);
-  else
-    hipLaunchKernelGGL((output_kernel<Tin, D, KS, false>), dim3(a.BH * a.G), dim3(256), lds, s, a);
-  return hipGetLastError();
+  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, a.mp, KS, a.C));
+  void* args[] = {const_cast<OutArgs*>(&a)};
+  return hipLaunchKernel(fn, dim3(a.BH * a.G), dim3(256), args, lds, s);
 }
 
 template <typename Tin, int D>
@@ -389,11 +478,22 @@ hipError_t launch_output(bool bf16, int d, int ks, const OutArgs& a, hipStream_t
 
 template <typename Tin, int D, int KS>
 static hipError_t attr_t(size_t bytes) {
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true>),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-  if (e != hipSuccess) return e;
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  const void* fns[6] = {
+      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false>),
+      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false>)};
+  int nf = 2;
+  if constexpr (KS == 4) {
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false>);
+  }
+  for (int i = 0; i < nf; ++i) {
+    const hipError_t e =
+        hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <typename Tin, int D>

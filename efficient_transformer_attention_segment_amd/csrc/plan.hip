@@ -166,7 +166,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
 
   nys::CtxArgs& c = p->ctx;
   std::memset(&c, 0, sizeof(c));
-  c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
+  c.qt = F(o_qt); c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
   c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.z_hl = U(o_zhl);
   c.part_w = F(o_pw); c.part_ml = F(o_pml);
   c.BH = p->BH; c.n = n; c.d = d; c.m = m; c.mp = p->mp; c.iters = pinv_iters;
@@ -176,7 +176,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
 
   nys::OutArgs& o = p->out;
   std::memset(&o, 0, sizeof(o));
-  o.kt_hl = U(o_khl); o.z_hl = U(o_zhl); o.part_w = F(o_pw); o.part_ml = F(o_pml);
+  o.kt = F(o_kt); o.kt_hl = U(o_khl); o.z_hl = U(o_zhl); o.part_w = F(o_pw); o.part_ml = F(o_pml);
   o.w_tap = F(o_w); o.y_tap = F(o_y);  // enabled per call (debug forwards only)
   o.BH = p->BH; o.H = H; o.n = n; o.m = m; o.mp = p->mp; o.W = conv_width; o.half = p->half;
   o.tok_per_block = p->tok_per_block; o.G = p->G; o.C = p->C;

@@ -57,6 +57,10 @@ SMALL = {
     "f32_d128": gen.Config("f32d128", 1, 2, 256, 128, 32, dtype=gen.F32, seed=33),
     "f32_d64_m64": gen.Config("f32d64", 2, 2, 640, 64, 64, dtype=gen.F32, seed=34),
     "odd_bh": gen.Config("odd", 3, 3, 384, 64, 32, seed=35),
+    # last context chunk holds 8 tokens: whole token groups of that step are masked
+    "tail8": gen.Config("tail8", 1, 2, 136, 64, 8, seed=36),
+    "m40_pad": gen.Config("m40", 1, 2, 200, 64, 40, seed=37),
+    "m64_d32": gen.Config("m64d32", 2, 2, 1024, 32, 64, seed=38),
 }
 
 
