@@ -1,20 +1,25 @@
 // Stage 2 of the forward pass (Nystromformer review page, "Proposed method"):
 //
-//  * pinv_kernel   one block per head: A_S = softmax_row(s Qt Kt^T), the scaling
-//                  alpha = 1/(||A_S||_1 ||A_S||_inf), Z_0 = alpha A_S^T, then `iters`
-//                  steps of Z <- 1/4 Z (13I - X(15I - X(7I - X))), X = A_S Z, every
-//                  m x m product on MFMA. For mp <= 64 all operand planes live in LDS
-//                  (4 waves); larger mp keeps them in global memory (16 waves).
-//  * flash_kernel  BH * C blocks: the right factor softmax_row(s Qt K^T) V, computed
-//                  without forming the m x n matrix: each block streams one chunk of K/V
-//                  tiles, keeps a running max / sum per landmark (online softmax over n)
-//                  and an unnormalised m x d accumulator; it writes that partial state
-//                  (feature-major, so the merge reads it as W^T).
+//  * pseudo-inverse   one block per head: A_S = softmax_row(s Qt Kt^T), the scaling
+//                     alpha = 1/(||A_S||_1 ||A_S||_inf), Z_0 = alpha A_S^T, then `iters`
+//                     steps of Z <- 1/4 Z (13I - X(15I - X(7I - X))), X = A_S Z, every
+//                     m x m product on MFMA. For mp <= 64 the operand planes live in LDS
+//                     (4 waves) and these blocks ride at the front of the context launch;
+//                     larger mp keeps them in global memory (pinv_global_kernel, 16
+//                     waves, its own launch).
+//  * landmark context BH * C blocks: the right factor softmax_row(s Qt K^T) V, computed
+//                     without forming the m x n matrix: each block streams one chunk of
+//                     K/V tiles, keeps a running max / sum per landmark (online softmax
+//                     over n) and an unnormalised m x d accumulator; it writes that
+//                     partial state (feature-major, so the merge reads it as W^T).
 //
-// Blocks never exchange data inside a kernel: on MI355X each XCD has its own L2, and a
-// device-scope hand-off costs an L2 write-back plus invalidate per block. The output
-// stage merges the C partial states (fixed chunk order, log-sum-exp rescaling) and
-// forms Y = Z W in its prologue.
+// The two need only the segment means, so one launch overlaps the latency-bound
+// pseudo-inverse with the bandwidth-bound context stream. Blocks never exchange data
+// inside a kernel: on MI355X each XCD has its own L2, and a device-scope hand-off costs
+// an L2 write-back plus invalidate per block. The output stage merges the C partial
+// states (fixed chunk order, log-sum-exp rescaling) and forms Y = Z W in its prologue.
+#include <algorithm>
+
 #include "nys_common.h"
 #include "nys_kernels.h"
 
@@ -41,15 +46,15 @@ __device__ __forceinline__ float block_max(float x, float* red, int tid, int nw)
 }
 
 // ------------------------------------------------------------------ pinv
-// Plane pairs (hi, lo) per head. In LDS mode they are LDS arrays, otherwise a slice of
-// CtxArgs::planes. Z and the X^2/T plane are updated in place: every wave first computes
-// all of its tiles into registers, the block synchronises, then the tiles are written.
-// LDS variant: 12 planes. Global variant adds a second Z pair and a separate T pair.
-enum { kPA = 0, kPZr = 2, kPZc = 4, kPXr = 6, kPXc = 8, kPX2T = 10, kLdsPlanes = 12,
-       kGZr1 = 12, kGZc1 = 14, kGT = 16 };
+// Variant for 64 < mp <= 256 (one block of 16 waves per head, up to four tiles per wave):
+// hi/lo operand planes in a slice of CtxArgs::planes, 18 of them (row- and column-major
+// copies, a second Z pair and a separate T pair, so that no plane is read and rewritten
+// by one product).
+enum { kPA = 0, kPZr = 2, kPZc = 4, kPXr = 6, kPXc = 8, kPX2T = 10, kGZr1 = 12, kGZc1 = 14,
+       kGT = 16 };
 static_assert(kPlanes == 18, "plane count");
 
-template <bool kLds, int TPW>
+template <int TPW>
 __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl, float* red,
                                           float* red_part, float* red_col) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -63,7 +68,7 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
 
   // 1. logits Qt Kt^T (both landmark sets as hi/lo planes, K = d), scaled to log2
   //    units, held in registers: tile t = wave + nw*u of the mp x mp matrix.
-  constexpr int TPW0 = kLds ? 1 : 4;  // tiles per wave for mp <= 64 / mp <= 256
+  constexpr int TPW0 = 4;  // tiles per wave (mp <= 256, 16 waves)
   f32x16 at[TPW0];
   {
     const uint16_t* qh = a.qt_hl + (size_t)bh * 2 * mp * dd;
@@ -185,56 +190,7 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
   __syncthreads();
 
   // 5. iterations. Each wave owns tiles t = wave + nw*u.
-  if constexpr (kLds) {
-    // mp <= 64: one tile per wave. Z and the X^2/T plane are updated in place: the
-    // products are held in registers across a barrier before they are written.
-    static_assert(TPW == 1, "LDS variant holds one tile per wave");
-    const int t = wave;
-    const bool mine = t < ntiles;
-    const int row0 = 32 * (t / nt), col0 = 32 * (t % nt);
-    const int j = col0 + (lane & 31);
-    for (int it = 0; it < a.iters; ++it) {
-      f32x16 x, x2, acc;
-      if (mine) {  // X = A Z
-        x = gemm_tile(plane(kPA), plane(kPA + 1), mp, plane(kPZc), plane(kPZc + 1), mp, row0,
-                      col0, mp, lane);
-        store_rows_hl(plane(kPXr), plane(kPXr + 1), mp, row0, col0, x, lane);
-        store_cols_hl(plane(kPXc), plane(kPXc + 1), mp, row0, col0, x, lane);
-      }
-      __syncthreads();
-      if (mine) {  // X^2 = X X
-        x2 = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPXc), plane(kPXc + 1), mp, row0,
-                       col0, mp, lane);
-        store_cols_hl(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, x2, lane);
-      }
-      __syncthreads();
-      if (mine)  // X^3 = X X^2
-        acc = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPX2T), plane(kPX2T + 1), mp,
-                        row0, col0, mp, lane);
-      __syncthreads();
-      if (mine) {  // T = 13I - 15X + 7X^2 - X^3  (= 13I - X(15I - X(7I - X)))
-        f32x16 tv;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const float diag = (acc_row(row0, rr, lane) == j) ? 13.f : 0.f;
-          tv[rr] = diag - 15.f * x[rr] + 7.f * x2[rr] - acc[rr];
-        }
-        store_cols_hl(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, tv, lane);
-      }
-      __syncthreads();
-      if (mine)  // Z T
-        acc = gemm_tile(plane(kPZr), plane(kPZr + 1), mp, plane(kPX2T), plane(kPX2T + 1), mp,
-                        row0, col0, mp, lane);
-      __syncthreads();
-      if (mine) {  // Z <- Z T / 4
-        const f32x16 zv = acc * 0.25f;
-        store_rows_hl(plane(kPZr), plane(kPZr + 1), mp, row0, col0, zv, lane);
-        store_cols_hl(plane(kPZc), plane(kPZc + 1), mp, row0, col0, zv, lane);
-        if (it == a.iters - 1) store_rows_f32(a.z + (size_t)bh * P, mp, row0, col0, zv, lane);
-      }
-      __syncthreads();
-    }
-  } else {
+  {
     // mp > 64: planes in global memory; Z and T get separate (ping-pong) planes so every
     // product is written as soon as it is formed. fp32 X, X^2 of the own tiles go to
     // per-head scratch and are read back by the same wave.
@@ -287,10 +243,10 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
       }
       __syncthreads();
     }
-  }
+    }
   // 6. hand Z (row-major hi/lo) to the Y = Z W product of the output stage
   {
-    const int zfin = kLds ? kPZr : ((a.iters & 1) ? kGZr1 : kPZr);
+    const int zfin = (a.iters & 1) ? kGZr1 : kPZr;
     uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
     const int n8 = (int)(P / 8);
     for (int e = tid; e < 2 * n8; e += nthreads) {
@@ -302,89 +258,147 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
 
 // ------------------------------------------------------------------ pinv, mp <= 64
 // Compile-time specialisation for MP in {32, 64}: one 32x32 tile per wave (waves beyond
-// the tile count only join the barriers), every loop unrolled, all operand planes in LDS.
-// Z and the X^2/T plane are updated in place, so results are held in registers across
-// the barrier that precedes their store.
-template <int MP, int D>
-__global__ __launch_bounds__(256) void pinv_lds_kernel(CtxArgs a) {
-  constexpr int NT = MP / 32, NTILES = NT * NT, KD = D / 16, KM = MP / 16;
-  constexpr int P = MP * MP;
-  // LDS plane rows padded by 16 bytes: a 32-lane operand fetch then touches every bank
-  // once instead of a few banks many times
-  constexpr int LD = MP + 8, PL = MP * LD;
-  extern __shared__ __align__(16) char lds[];
-  __shared__ float red_part[MP * NT];  // [row][column tile]
-  __shared__ float red_col[NT * MP];   // [row tile][column]
-  __shared__ float red[16];
-  uint16_t* pl = reinterpret_cast<uint16_t*>(lds);
-  auto plane = [&](int idx) { return pl + idx * PL; };
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31;
-  const int bh = blockIdx.x, m = a.m;
-  const bool mine = wave < NTILES;
-  const int row0 = 32 * (wave / NT), tj = wave % NT, col0 = 32 * tj;
-  const int jcol = col0 + r32;
+// the tile count only join the barriers), every loop unrolled, operand planes in LDS.
+//
+// Every m x m matrix lives in LDS once, row-major (hi and lo planes), with the 16-byte
+// chunks of each row permuted (swz_off). A product C = A B is formed transposed on MFMA
+// (C^T = B^T A^T): rows of A are read as 16-byte runs, columns of B with LDS transpose
+// reads, and the result comes out one row of C per lane (16 values in four runs of four
+// columns), which is stored as 8-byte row runs.
+template <int MP>
+__device__ __forceinline__ int swz(int r, int c) {
+  return swz_off<MP / 8>(r, c);
+}
 
-  // 1. scaled logits (log2 units)
+// Column of register rr in the row-per-lane layout of a tile at column col0.
+__device__ __forceinline__ int row_tile_col(int col0, int rr, int lane) {
+  return col0 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+}
+
+// C[row0:+32, col0:+32] of C = A B for MP x MP planes, row-per-lane layout: lane l holds
+// row row0 + l % 32, register rr column row_tile_col(col0, rr, l).
+template <int MP>
+__device__ __forceinline__ f32x16 prod_rows(const uint16_t* ahi, const uint16_t* alo,
+                                            const uint16_t* bhi, const uint16_t* blo,
+                                            int row0, int col0, int lane) {
+  constexpr int KS = MP / 16;
+  const int r = lane & 31, h = lane >> 5;
+  // transposed reads: lane 4j + q of each 16-lane group addresses row k0 + j, column
+  // col0 + 16 * (group & 1) + 4q; the result lane then holds column col0 + lane % 32
+  const int trj = (lane & 15) >> 2, trc = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  Pair8 ao[KS], bo[KS];
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    const int k0 = 16 * s + 8 * h;
+    bo[s] = Pair8{ld8(ahi + swz<MP>(row0 + r, k0)), ld8(alo + swz<MP>(row0 + r, k0))};
+    ao[s].hi = lds_tr16x2(bhi + swz<MP>(k0 + trj, trc), bhi + swz<MP>(k0 + 4 + trj, trc));
+    ao[s].lo = lds_tr16x2(blo + swz<MP>(k0 + trj, trc), blo + swz<MP>(k0 + 4 + trj, trc));
+  }
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) acc = mfma_pair<true, true>(ao[s], bo[s], acc);
+  return acc;
+}
+
+// Store a row-per-lane tile into swizzled hi/lo planes (four 8-byte runs per plane).
+template <int MP>
+__device__ __forceinline__ void store_row_tile(uint16_t* hi, uint16_t* lo, int row0, int col0,
+                                               const f32x16& v, int lane) {
+  const int i = row0 + (lane & 31), h = lane >> 5;
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint16_t a[4], b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split1(v[4 * g + e], a[e], b[e]);
+    const int o = swz<MP>(i, col0 + 8 * g + 4 * h);
+    *reinterpret_cast<u32x2*>(hi + o) =
+        u32x2{(uint32_t)a[0] | ((uint32_t)a[1] << 16), (uint32_t)a[2] | ((uint32_t)a[3] << 16)};
+    *reinterpret_cast<u32x2*>(lo + o) =
+        u32x2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+  }
+}
+
+// Row-per-lane tile to a row-major fp32 matrix in global memory (ld = MP).
+template <int MP>
+__device__ __forceinline__ void store_row_tile_f32(float* p, int row0, int col0, const f32x16& v,
+                                                   int lane) {
+  float* q = p + (size_t)(row0 + (lane & 31)) * MP + col0 + 4 * (lane >> 5);
+#pragma unroll
+  for (int g = 0; g < 4; ++g)
+    *reinterpret_cast<f32x4*>(q + 8 * g) = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
+}
+
+enum { kQA = 0, kQZ = 2, kQX = 4, kQT = 6, kQPlanes = 8 };
+
+template <int MP>
+constexpr size_t pinv_lds_planes_bytes() { return (size_t)kQPlanes * MP * MP * 2; }
+
+template <int MP, int D>
+__device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t* pl,
+                                              float* red_part, float* red_col, float* red) {
+  constexpr int NT = MP / 32, NTILES = NT * NT, KD = D / 16;
+  constexpr int P = MP * MP;
+  auto plane = [&](int idx) { return pl + idx * P; };
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  const int m = a.m;
+  const bool mine = wave < NTILES;
+  const int row0 = 32 * (wave / NT), ti = wave / NT, tj = wave % NT, col0 = 32 * tj;
+  const int irow = row0 + r32;  // the row this lane holds
+
+  // 1. scaled logits (log2 units), row-per-lane: the product Kt Qt^T read transposed
   f32x16 at = zero16();
   if (mine) {
     const uint16_t* qh = a.qt_hl + (size_t)bh * 2 * MP * D;
     const uint16_t* kh = a.kt_hl + (size_t)bh * 2 * MP * D;
-    at = gemm_tile_k<KD>(qh, qh + MP * D, D, kh, kh + MP * D, D, row0, col0, lane) * a.scale_log2e;
+    at = gemm_tile_k<KD>(kh, kh + MP * D, D, qh, qh + MP * D, D, col0, row0, lane) * a.scale_log2e;
   }
-  // 2. row softmax over the m real landmarks (padded rows/columns become 0)
+  // 2. row softmax over the m real landmarks (padded rows/columns become 0). A lane
+  // holds 16 of the row's columns, its partner lane (l ^ 32) the other 16 of the tile.
   if (mine) {
-    float mx[16];
+    float mx = kNegBig;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) mx[rr] = half_max(jcol < m ? at[rr] : kNegBig);
-    if (r32 == 0)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) red_part[acc_row(row0, rr, lane) * NT + tj] = mx[rr];
+    for (int rr = 0; rr < 16; ++rr)
+      if (row_tile_col(col0, rr, lane) < m) mx = fmaxf(mx, at[rr]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    if (h == 0) red_part[irow * NT + tj] = mx;
   }
   __syncthreads();
+  float sm = 0.f;
   if (mine) {
+    float mx = red_part[irow * NT];
+#pragma unroll
+    for (int c = 1; c < NT; ++c) mx = fmaxf(mx, red_part[irow * NT + c]);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int i = acc_row(row0, rr, lane);
-      float mx = red_part[i * NT];
-#pragma unroll
-      for (int c = 1; c < NT; ++c) mx = fmaxf(mx, red_part[i * NT + c]);
-      at[rr] = (i < m && jcol < m) ? fast_exp2(at[rr] - mx) : 0.f;
+      at[rr] = (irow < m && row_tile_col(col0, rr, lane) < m) ? fast_exp2(at[rr] - mx) : 0.f;
+      sm += at[rr];
     }
+    sm += __shfl_xor(sm, 32);
   }
+  __syncthreads();  // every wave has read the maxima
+  if (mine && h == 0) red_part[irow * NT + tj] = sm;
   __syncthreads();
   if (mine) {
-    float sm[16];
+    float rsum = red_part[irow * NT];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) sm[rr] = half_sum(at[rr]);
-    if (r32 == 0)
+    for (int c = 1; c < NT; ++c) rsum += red_part[irow * NT + c];
+    const float inv = irow < m ? 1.f / rsum : 0.f;
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) red_part[acc_row(row0, rr, lane) * NT + tj] = sm[rr];
+    for (int rr = 0; rr < 16; ++rr) at[rr] *= inv;
   }
   __syncthreads();
+  // abs row sums (partials per column tile) and abs column sums (partials per row tile)
   if (mine) {
+    float rs = 0.f;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) rs += fabsf(at[rr]);
+    rs += __shfl_xor(rs, 32);
+    if (h == 0) red_part[irow * NT + tj] = rs;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int i = acc_row(row0, rr, lane);
-      float sm = red_part[i * NT];
-#pragma unroll
-      for (int c = 1; c < NT; ++c) sm += red_part[i * NT + c];
-      at[rr] = i < m ? at[rr] * (1.f / sm) : 0.f;
+      const float cs = half_sum(fabsf(at[rr]));
+      if (r32 == 0) red_col[ti * MP + row_tile_col(col0, rr, lane)] = cs;
     }
-  }
-  __syncthreads();
-  // abs row sums (partials per column tile) and abs column sums (per row tile)
-  if (mine) {
-    float rs[16], cs = 0.f;
-#pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      rs[rr] = half_sum(fabsf(at[rr]));
-      cs += fabsf(at[rr]);
-    }
-    cs += __shfl_xor(cs, 32);
-    if (r32 == 0)
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) red_part[acc_row(row0, rr, lane) * NT + tj] = rs[rr];
-    if (lane < 32) red_col[(row0 / 32) * MP + jcol] = cs;
   }
   __syncthreads();
   float rmax = 0.f, cmax = 0.f;
@@ -405,81 +419,131 @@ __global__ __launch_bounds__(256) void pinv_lds_kernel(CtxArgs a) {
   rmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   cmax = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
   const float alpha = 1.0f / (cmax * rmax);
-  // 3. A_S (fp32 copy), its operand plane, Z_0 = alpha A_S^T (row-major and transposed)
+  // 3. A_S (fp32 copy and operand planes), Z_0 = alpha A_S^T
   if (mine) {
-    store_rows_f32(a.a_s + (size_t)bh * P, MP, row0, col0, at, lane);
-    store_rows_hl(plane(kPA), plane(kPA + 1), LD, row0, col0, at, lane);
-    const f32x16 zv = at * alpha;
-    store_rows_hl(plane(kPZc), plane(kPZc + 1), LD, row0, col0, zv, lane);
-    store_cols_hl(plane(kPZr), plane(kPZr + 1), LD, row0, col0, zv, lane);
-    if (a.iters == 0) store_cols_f32(a.z + (size_t)bh * P, MP, row0, col0, zv, lane);
+    store_row_tile_f32<MP>(a.a_s + (size_t)bh * P, row0, col0, at, lane);
+    store_row_tile<MP>(plane(kQA), plane(kQA + 1), row0, col0, at, lane);
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {  // element (i, j) of A goes to Z_0[j][i]
+      const int j = row_tile_col(col0, rr, lane);
+      uint16_t hb, lb;
+      const float zv = alpha * at[rr];
+      split1(zv, hb, lb);
+      plane(kQZ)[swz<MP>(j, irow)] = hb;
+      plane(kQZ + 1)[swz<MP>(j, irow)] = lb;
+      if (a.iters == 0) a.z[(size_t)bh * P + (size_t)j * MP + irow] = zv;
+    }
   }
   __syncthreads();
-  // 4. iterations
+  // 4. iterations Z <- 1/4 Z (13I - 15X + 7X^2 - X^3), X = A Z
   for (int it = 0; it < a.iters; ++it) {
     f32x16 x, x2, acc;
     if (mine) {  // X = A Z
-      x = gemm_tile_k<KM>(plane(kPA), plane(kPA + 1), LD, plane(kPZc), plane(kPZc + 1), LD,
-                          row0, col0, lane);
-      store_rows_hl(plane(kPXr), plane(kPXr + 1), LD, row0, col0, x, lane);
-      store_cols_hl(plane(kPXc), plane(kPXc + 1), LD, row0, col0, x, lane);
+      x = prod_rows<MP>(plane(kQA), plane(kQA + 1), plane(kQZ), plane(kQZ + 1), row0, col0, lane);
+      store_row_tile<MP>(plane(kQX), plane(kQX + 1), row0, col0, x, lane);
     }
     __syncthreads();
-    if (mine) {  // X^2 = X X
-      x2 = gemm_tile_k<KM>(plane(kPXr), plane(kPXr + 1), LD, plane(kPXc), plane(kPXc + 1), LD,
-                           row0, col0, lane);
-      store_cols_hl(plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, x2, lane);
+    if (mine) {  // X^2 = X X, parked in the T planes
+      x2 = prod_rows<MP>(plane(kQX), plane(kQX + 1), plane(kQX), plane(kQX + 1), row0, col0, lane);
+      store_row_tile<MP>(plane(kQT), plane(kQT + 1), row0, col0, x2, lane);
     }
     __syncthreads();
     if (mine)  // X^3 = X X^2
-      acc = gemm_tile_k<KM>(plane(kPXr), plane(kPXr + 1), LD, plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, lane);
+      acc = prod_rows<MP>(plane(kQX), plane(kQX + 1), plane(kQT), plane(kQT + 1), row0, col0, lane);
     __syncthreads();
     if (mine) {  // T = 13I - 15X + 7X^2 - X^3  (= 13I - X(15I - X(7I - X)))
       f32x16 tv;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const float diag = (acc_row(row0, rr, lane) == jcol) ? 13.f : 0.f;
+        const float diag = (irow == row_tile_col(col0, rr, lane)) ? 13.f : 0.f;
         tv[rr] = diag - 15.f * x[rr] + 7.f * x2[rr] - acc[rr];
       }
-      store_cols_hl(plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, tv, lane);
+      store_row_tile<MP>(plane(kQT), plane(kQT + 1), row0, col0, tv, lane);
     }
     __syncthreads();
     if (mine)  // Z T
-      acc = gemm_tile_k<KM>(plane(kPZr), plane(kPZr + 1), LD, plane(kPX2T), plane(kPX2T + 1), LD, row0, col0, lane);
+      acc = prod_rows<MP>(plane(kQZ), plane(kQZ + 1), plane(kQT), plane(kQT + 1), row0, col0, lane);
     __syncthreads();
     if (mine) {  // Z <- Z T / 4
       const f32x16 zv = acc * 0.25f;
-      store_rows_hl(plane(kPZr), plane(kPZr + 1), LD, row0, col0, zv, lane);
-      store_cols_hl(plane(kPZc), plane(kPZc + 1), LD, row0, col0, zv, lane);
-      if (it == a.iters - 1) store_rows_f32(a.z + (size_t)bh * P, MP, row0, col0, zv, lane);
+      store_row_tile<MP>(plane(kQZ), plane(kQZ + 1), row0, col0, zv, lane);
+      if (it == a.iters - 1) store_row_tile_f32<MP>(a.z + (size_t)bh * P, row0, col0, zv, lane);
     }
     __syncthreads();
   }
-  // 5. Z (row-major hi/lo, unpadded) for the output stage
+  // 5. Z (row-major hi/lo, unpermuted) for the output stage
   uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
-  for (int e = tid; e < 2 * P / 8; e += 256) {
+  for (int e = tid; e < 2 * P / 8; e += blockDim.x) {
     const int which = e / (P / 8), r = (e % (P / 8)) / (MP / 8), c8 = (e % (MP / 8)) * 8;
-    st8(dst + (size_t)which * P + r * MP + c8, ld8(plane(kPZr + which) + r * LD + c8));
+    st8(dst + (size_t)which * P + r * MP + c8, ld8(plane(kQZ + which) + swz<MP>(r, c8)));
   }
 }
 
-template <bool kLds, int TPW, int D>
-__global__ __launch_bounds__(kLds ? 256 : 1024) void pinv_kernel(CtxArgs a) {
-  extern __shared__ __align__(16) char lds[];
+
+template <int D>
+__global__ __launch_bounds__(1024) void pinv_global_kernel(CtxArgs a) {
   __shared__ float red[32];
   __shared__ float red_part[256 * 8];  // [row][column tile] partial max / sums
   __shared__ float red_col[8 * 256];   // [row tile][column] partial column sums
   const int bh = blockIdx.x;
-  uint16_t* pl = kLds ? reinterpret_cast<uint16_t*>(lds)
-                      : a.planes + (size_t)bh * kPlanes * a.mp * a.mp;
-  pinv_body<kLds, TPW>(a, bh, pl, red, red_part, red_col);
+  pinv_body<4>(a, bh, a.planes + (size_t)bh * kPlanes * a.mp * a.mp, red, red_part, red_col);
 }
 
-// ------------------------------------------------------------------ flash
+// Merge the TG token groups of each landmark group (fixed order) and write the block's
+// partial state: W^T [feature][landmark] unnormalised, running max (log2 units) and sum.
+// mb: LDS scratch of LG * (TG - 1) slots; the caller synchronises before reusing LDS.
+template <int D>
+__device__ __forceinline__ void flash_store_partial(const CtxArgs& a, int bh, int c,
+                                                    f32x16* wacc, float M, float L, float* mb) {
+  constexpr int FT = D / 32;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31, h = lane >> 5;
+  const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG, mp = a.mp;
+  const int slot_floats = FT * 16 * 64 + 128;
+  if (tg > 0) {
+    float* sb = mb + (size_t)(g * (TG - 1) + tg - 1) * slot_floats;
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) sb[(f * 16 + rr) * 64 + lane] = wacc[f][rr];
+    sb[FT * 16 * 64 + lane] = M;
+    sb[FT * 16 * 64 + 64 + lane] = L;
+  }
+  __syncthreads();
+  if (tg == 0) {
+    for (int o = 1; o < TG; ++o) {
+      const float* sb = mb + (size_t)(g * (TG - 1) + o - 1) * slot_floats;
+      const float mo = sb[FT * 16 * 64 + lane], lo = sb[FT * 16 * 64 + 64 + lane];
+      const float mn = fmaxf(M, mo);
+      const float ca = fast_exp2(M - mn), cb = fast_exp2(mo - mn);
+      L = L * ca + lo * cb;
+      M = mn;
+#pragma unroll
+      for (int f = 0; f < FT; ++f)
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr)
+          wacc[f][rr] = wacc[f][rr] * ca + sb[(f * 16 + rr) * 64 + lane] * cb;
+    }
+    // partial W^T: [feature][landmark], 32 consecutive landmarks per register
+    const int lm = 32 * g + r32;
+    float* pw = a.part_w + ((size_t)bh * a.C + c) * D * mp + lm;
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr)
+        pw[(size_t)(32 * f + acc_row(0, rr, lane)) * mp] = wacc[f][rr];
+    if (h == 0) {
+      float* pm = a.part_ml + ((size_t)bh * a.C + c) * 2 * mp;
+      pm[lm] = M;
+      pm[mp + lm] = L;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ context, fp32
+// Register staging (fp32 inputs are split into hi/lo bf16 tiles on the way to LDS).
 // NCH: 8-element V chunks each thread stages per step (D / (16 * LG), rounded up).
 template <typename Tin, int D, int NCH>
-__global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
-  extern __shared__ __align__(16) char lds[];
+__device__ __forceinline__ void flash_reg_body(const CtxArgs& a, int blk, char* lds) {
   constexpr bool kS = Input<Tin>::kSplit;
   constexpr int KD = D / 16;       // k-steps over features
   constexpr int FT = D / 32;       // feature tiles of the accumulator
@@ -489,7 +553,7 @@ __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
   const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
   const int mp = a.mp;
   int bh, c;
-  xcd_map(blockIdx.x, a.BH, a.C, bh, c);
+  xcd_map(blk, a.BH, a.C, bh, c);
   const int c0 = c * a.chunk, c1 = min(a.n, c0 + a.chunk);
   const Tin* K = static_cast<const Tin*>(a.k) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
@@ -632,72 +696,210 @@ __global__ __launch_bounds__(512) void flash_kernel(CtxArgs a) {
     }
   }
   L += __shfl_xor(L, 32);
+  __syncthreads();  // LDS becomes the merge buffer
+  flash_store_partial<D>(a, bh, c, wacc, M, L, reinterpret_cast<float*>(lds));
+}
 
-  // merge the TG token groups of each landmark group (fixed order)
-  __syncthreads();
-  float* mb = reinterpret_cast<float*>(lds);
-  const int slot_floats = FT * 16 * 64 + 128;
-  if (tg > 0) {
-    float* sb = mb + (size_t)(g * (TG - 1) + tg - 1) * slot_floats;
+// ------------------------------------------------------------------ context, bf16
+// K and V tiles of `step` tokens stream through a ring of ring_stages LDS slots filled
+// by LDS-DMA (no registers held for data in flight): while tile t is consumed, tiles
+// t+1 .. t+stages-1 are in flight. Each tile is row-major with permuted 16-byte chunks
+// (swz_off); a wave's DMA instruction i covers slots [64 (i W + wave), +64) of the tile,
+// slot s holding row s / CPR, chunk (s % CPR) ^ key. Slots past the tile's real chunks
+// (and rows past the chunk end) load a valid row of the head whose values are masked.
+template <int D>
+__device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char* lds) {
+  constexpr int KD = D / 16;       // k-steps over features
+  constexpr int FT = D / 32;       // feature tiles of the accumulator
+  constexpr int CPR = D / 8;       // 16-byte chunks per row
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
+  const int mp = a.mp;
+  int bh, c;
+  xcd_map(blk, a.BH, a.C, bh, c);
+  const int c0 = c * a.chunk, c1 = min(a.n, c0 + a.chunk);
+  const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)bh * a.n * D;
+  const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)bh * a.n * D;
+
+  const int step = 32 * TG;
+  const int NI = a.ring_ni, S = a.ring_stages;
+  const int tile_elems = nw * NI * 512;  // 1 KiB (512 bf16) per wave instruction
+  const int real = step * CPR;
+  const int nsteps = (c1 - c0 + step - 1) / step;
+  uint16_t* ring = reinterpret_cast<uint16_t*>(lds);
+  auto issue = [&](int t) {
+    const int base = c0 + t * step;
+    uint16_t* dk = ring + (size_t)(t % S) * 2 * tile_elems;
+    uint16_t* dv = dk + tile_elems;
+    for (int i = 0; i < NI; ++i) {
+      const int b = i * nw + wave, s = 64 * b + lane;
+      const int r = s / CPR, ch = (s % CPR) ^ chunk_key<CPR>(r);
+      const int tok = (s < real && base + r < c1) ? base + r : c0;
+      const size_t off = (size_t)tok * D + 8 * ch;
+      dma16(K + off, dk + 512 * b);
+      dma16(V + off, dv + 512 * b);
+    }
+  };
+  // ring prologue first: its loads overlap the landmark operand set-up below
+  for (int t = 0; t < S - 1 && t < nsteps; ++t) issue(t);
+
+  // landmark operand, with s*log2(e) folded in so the scores come out in log2 units
+  Pair8 qb[KD];
+  {
+    const float* qs = a.qt + ((size_t)bh * mp + 32 * g + r32) * D + 8 * h;
 #pragma unroll
-    for (int f = 0; f < FT; ++f)
+    for (int s = 0; s < KD; ++s) {
+      const f32x4 u0 = *reinterpret_cast<const f32x4*>(qs + 16 * s);
+      const f32x4 u1 = *reinterpret_cast<const f32x4*>(qs + 16 * s + 4);
+      float x[8];
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) sb[(f * 16 + rr) * 64 + lane] = wacc[f][rr];
-    sb[FT * 16 * 64 + lane] = M;
-    sb[FT * 16 * 64 + 64 + lane] = L;
+      for (int q = 0; q < 4; ++q) {
+        x[q] = u0[q] * a.scale_log2e;
+        x[4 + q] = u1[q] * a.scale_log2e;
+      }
+      qb[s] = split8(x);
+    }
   }
-  __syncthreads();
-  if (tg == 0) {
-    for (int o = 1; o < TG; ++o) {
-      const float* sb = mb + (size_t)(g * (TG - 1) + o - 1) * slot_floats;
-      const float mo = sb[FT * 16 * 64 + lane], lo = sb[FT * 16 * 64 + 64 + lane];
-      const float mn = fmaxf(M, mo);
-      const float ca = fast_exp2(M - mn), cb = fast_exp2(mo - mn);
-      L = L * ca + lo * cb;
+  f32x16 wacc[FT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) wacc[f] = zero16();
+  float M = kNegBig, L = 0.f;
+  // transposed-read addressing (see lds_tr16): lane 4j + q of each 16-lane group points
+  // at token row j, feature column 16*(group & 1) + 4q of the feature tile
+  const int trj = (lane & 15) >> 2;
+  const int trcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  const int krow = 32 * tg + r32;
+
+  for (int t = 0; t < nsteps; ++t) {
+    // tile t is complete once only the DMA of later tiles is outstanding (any other
+    // younger load only makes the count conservative)
+    wait_dma_barrier(2 * NI * min(nsteps - 1 - t, S - 2));
+    if (t + S - 1 < nsteps) issue(t + S - 1);  // refills the slot consumed at t - 1
+    const int base = c0 + t * step;
+    const uint16_t* kt = ring + (size_t)(t % S) * 2 * tile_elems;
+    const uint16_t* vt = kt + tile_elems;
+
+    // scores (log2 units): rows = 32 tokens, columns = 32 landmarks
+    f32x16 Sc = zero16();
+#pragma unroll
+    for (int s = 0; s < KD; ++s) {
+      const Pair8 ka{ld8(kt + swz_off<CPR>(krow, 16 * s + 8 * h)), zero8()};
+      Sc = mfma_pair<false, true>(ka, qb[s], Sc);
+    }
+    // online softmax over tokens per landmark; only the chunk's last step can be partial
+    const bool partial = base + 32 * tg + 32 > c1;
+    float mx = kNegBig;
+    if (!partial) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, Sc[rr]);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int tok = base + 32 * tg + 8 * (rr >> 2) + 4 * h + (rr & 3);
+        if (tok >= c1) Sc[rr] = kNegBig;
+        mx = fmaxf(mx, Sc[rr]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // lazy rescaling: keep the reference maximum while every lane's new maximum stays
+    // within 2^8 of it (probabilities then stay <= 256); the state (M, L, acc) is exact
+    // for any reference point
+    if (__any(mx > M + 8.f)) {
+      const float mn = fmaxf(M, mx);
+      const float corr = fast_exp2(M - mn);
+      L *= corr;
+#pragma unroll
+      for (int f = 0; f < FT; ++f) wacc[f] *= corr;
       M = mn;
-#pragma unroll
-      for (int f = 0; f < FT; ++f)
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr)
-          wacc[f][rr] = wacc[f][rr] * ca + sb[(f * 16 + rr) * 64 + lane] * cb;
     }
-    // partial W^T: [feature][landmark], 32 consecutive landmarks per register
-    const int lm = 32 * g + r32;
-    float* pw = a.part_w + ((size_t)bh * a.C + c) * D * mp + lm;
+    float p[16];
+    float ps = 0.f;
+    if (!partial) {
 #pragma unroll
-    for (int f = 0; f < FT; ++f)
+      for (int rr = 0; rr < 16; ++rr) {
+        p[rr] = fast_exp2(Sc[rr] - M);
+        ps += p[rr];
+      }
+    } else {  // masked tokens contribute exactly 0 (M may still be the -1e30 start value)
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr)
-        pw[(size_t)(32 * f + acc_row(0, rr, lane)) * mp] = wacc[f][rr];
-    if (h == 0) {
-      float* pm = a.part_ml + ((size_t)bh * a.C + c) * 2 * mp;
-      pm[lm] = M;
-      pm[mp + lm] = L;
+      for (int rr = 0; rr < 16; ++rr) {
+        p[rr] = Sc[rr] > 0.5f * kNegBig ? fast_exp2(Sc[rr] - M) : 0.f;
+        ps += p[rr];
+      }
+    }
+    L += ps;
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) {
+      const Pair8 pb = split8(&p[8 * s2]);
+      const int row = 32 * tg + 16 * s2 + 4 * h + trj;
+#pragma unroll
+      for (int f = 0; f < FT; ++f) {
+        const int col = 32 * f + trcol;
+        const Pair8 va{lds_tr16x2(vt + swz_off<CPR>(row, col), vt + swz_off<CPR>(row + 8, col)),
+                       zero8()};
+        wacc[f] = mfma_pair<false, true>(va, pb, wacc[f]);
+      }
     }
   }
+  L += __shfl_xor(L, 32);
+  __syncthreads();  // ring drained (the last wait was for everything); LDS becomes scratch
+  flash_store_partial<D>(a, bh, c, wacc, M, L, reinterpret_cast<float*>(lds));
+}
+
+// ------------------------------------------------------------------ context launch
+// MP > 0: blocks [0, BH) run the pseudo-inverse of their head (mp = MP), the rest the
+// landmark context; MP == 0: context blocks only. NCH applies to fp32 inputs.
+template <typename Tin, int D, int MP, int NCH>
+__global__ __launch_bounds__(MP > 0 ? 256 : 512, MP > 0 ? 2 : 1) void context_kernel(CtxArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  int blk = blockIdx.x;
+  if constexpr (MP > 0) {
+    __shared__ float red_part[MP * (MP / 32)];  // [row][column tile]
+    __shared__ float red_col[(MP / 32) * MP];   // [row tile][column]
+    __shared__ float red[16];
+    if (blk < a.npinv) {
+      pinv_lds_body<MP, D>(a, blk, reinterpret_cast<uint16_t*>(lds), red_part, red_col, red);
+      return;
+    }
+    blk -= a.npinv;
+  }
+  if constexpr (Input<Tin>::kSplit) flash_reg_body<Tin, D, NCH>(a, blk, lds);
+  else flash_ring_body<D>(a, blk, lds);
 }
 
 // ------------------------------------------------------------------ host side
 static bool pinv_in_lds(int mp) { return mp <= 64; }
 
-size_t context_lds_bytes(bool bf16, int d, int mp, int LG, int TG) {
-  const size_t vbytes = (bf16 ? 1 : 2) * (size_t)(32 * TG) * (d + 8) * 2;
-  const size_t mbytes = (size_t)LG * (TG - 1) * ((d / 32) * 16 * 64 + 128) * 4;
-  return vbytes > mbytes ? vbytes : mbytes;
+static size_t pinv_lds_bytes(int mp) {
+  return pinv_in_lds(mp) ? (size_t)kQPlanes * mp * mp * 2 : 0;
 }
 
-static size_t pinv_lds_bytes(int mp) {
-  return pinv_in_lds(mp) ? (size_t)kLdsPlanes * mp * (mp + 8) * 2 : 0;
+void context_ring_geometry(int d, CtxArgs& a) {
+  const int nw = a.LG * a.TG, step = 32 * a.TG, chunks = step * (d / 8);
+  a.ring_ni = (chunks + 64 * nw - 1) / (64 * nw);
+  const size_t stage = (size_t)2 * nw * a.ring_ni * 1024;
+  // 64 KiB keeps two blocks per CU next to the fused pseudo-inverse's planes
+  const size_t budget = std::max<size_t>(64 * 1024, pinv_lds_bytes(a.mp));
+  a.ring_stages = (int)std::min<size_t>(4, std::max<size_t>(2, budget / stage));
+}
+
+size_t context_lds_bytes(bool bf16, int d, const CtxArgs& a) {
+  const int LG = a.LG, TG = a.TG;
+  size_t main;
+  if (bf16) {
+    main = (size_t)a.ring_stages * 2 * (LG * TG) * a.ring_ni * 1024;
+  } else {
+    main = (size_t)2 * (32 * TG) * (d + 8) * 2;
+  }
+  const size_t merge = (size_t)LG * (TG - 1) * ((d / 32) * 16 * 64 + 128) * 4;
+  const size_t pinv = context_fuses_pinv(a.mp) ? pinv_lds_bytes(a.mp) : 0;
+  return std::max({main, merge, pinv});
 }
 
 template <int D>
 static hipError_t launch_pinv_t(const CtxArgs& a, hipStream_t s) {
-  if (a.mp == 32)
-    hipLaunchKernelGGL((pinv_lds_kernel<32, D>), dim3(a.BH), dim3(256), pinv_lds_bytes(32), s, a);
-  else if (a.mp == 64)
-    hipLaunchKernelGGL((pinv_lds_kernel<64, D>), dim3(a.BH), dim3(256), pinv_lds_bytes(64), s, a);
-  else
-    hipLaunchKernelGGL((pinv_kernel<false, 4, D>), dim3(a.BH), dim3(1024), 0, s, a);
+  hipLaunchKernelGGL((pinv_global_kernel<D>), dim3(a.BH), dim3(1024), 0, s, a);
   return hipGetLastError();
 }
 
@@ -712,63 +914,51 @@ static int flash_nch(int d, int LG) {
   return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8;
 }
 
+// Every kernel instance a (dtype, d) pair can launch: MP in {32, 64, 0} for the fused
+// pseudo-inverse, NCH for fp32 staging.
 template <typename Tin, int D>
-static hipError_t launch_flash_t(const CtxArgs& a, hipStream_t s) {
-  const size_t flds = context_lds_bytes(Input<Tin>::kSplit == false, D, a.mp, a.LG, a.TG);
-  const dim3 grid(a.BH * a.C), block(64 * a.LG * a.TG);
-  switch (flash_nch(D, a.LG)) {
-    case 1: hipLaunchKernelGGL((flash_kernel<Tin, D, 1>), grid, block, flds, s, a); break;
-    case 2: hipLaunchKernelGGL((flash_kernel<Tin, D, 2>), grid, block, flds, s, a); break;
-    case 4: hipLaunchKernelGGL((flash_kernel<Tin, D, 4>), grid, block, flds, s, a); break;
-    default: hipLaunchKernelGGL((flash_kernel<Tin, D, 8>), grid, block, flds, s, a); break;
+static const void* context_fn(int mp, int LG) {
+  if constexpr (!Input<Tin>::kSplit) {
+    if (mp == 32) return reinterpret_cast<const void*>(&context_kernel<Tin, D, 32, 1>);
+    if (mp == 64) return reinterpret_cast<const void*>(&context_kernel<Tin, D, 64, 1>);
+    return reinterpret_cast<const void*>(&context_kernel<Tin, D, 0, 1>);
+  } else {
+#define NYS_NCH(MP)                                                                     \
+  switch (flash_nch(D, LG)) {                                                           \
+    case 1: return reinterpret_cast<const void*>(&context_kernel<Tin, D, MP, 1>);       \
+    case 2: return reinterpret_cast<const void*>(&context_kernel<Tin, D, MP, 2>);       \
+    case 4: return reinterpret_cast<const void*>(&context_kernel<Tin, D, MP, 4>);       \
+    default: return reinterpret_cast<const void*>(&context_kernel<Tin, D, MP, 8>);      \
   }
-  return hipGetLastError();
+    if (mp == 32) { NYS_NCH(32) }
+    if (mp == 64) { NYS_NCH(64) }
+    NYS_NCH(0)
+#undef NYS_NCH
+  }
 }
 
-hipError_t launch_flash(bool bf16, int d, const CtxArgs& a, hipStream_t s) {
+static const void* context_fn(bool bf16, int d, int mp, int LG) {
   if (bf16) {
-    if (d == 32) return launch_flash_t<uint16_t, 32>(a, s);
-    if (d == 64) return launch_flash_t<uint16_t, 64>(a, s);
-    return launch_flash_t<uint16_t, 128>(a, s);
+    if (d == 32) return context_fn<uint16_t, 32>(mp, LG);
+    if (d == 64) return context_fn<uint16_t, 64>(mp, LG);
+    return context_fn<uint16_t, 128>(mp, LG);
   }
-  if (d == 32) return launch_flash_t<float, 32>(a, s);
-  if (d == 64) return launch_flash_t<float, 64>(a, s);
-  return launch_flash_t<float, 128>(a, s);
+  if (d == 32) return context_fn<float, 32>(mp, LG);
+  if (d == 64) return context_fn<float, 64>(mp, LG);
+  return context_fn<float, 128>(mp, LG);
 }
 
-template <int D>
-static hipError_t set_pinv_attr() {
-  return hipFuncSetAttribute(reinterpret_cast<const void*>(&pinv_lds_kernel<64, D>),
-                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)pinv_lds_bytes(64));
+hipError_t launch_context(bool bf16, int d, const CtxArgs& a, hipStream_t s) {
+  const void* fn = context_fn(bf16, d, a.mp, a.LG);
+  const dim3 grid(a.npinv + a.BH * a.C), block(64 * a.LG * a.TG);
+  void* args[] = {const_cast<CtxArgs*>(&a)};
+  return hipLaunchKernel(fn, grid, block, args, context_lds_bytes(bf16, d, a), s);
 }
 
-template <typename Tin, int D>
-static hipError_t set_flash_attr(size_t bytes) {
-  const void* fns[] = {reinterpret_cast<const void*>(&flash_kernel<Tin, D, 1>),
-                       reinterpret_cast<const void*>(&flash_kernel<Tin, D, 2>),
-                       reinterpret_cast<const void*>(&flash_kernel<Tin, D, 4>),
-                       reinterpret_cast<const void*>(&flash_kernel<Tin, D, 8>)};
-  for (const void* f : fns) {
-    const hipError_t e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
-}
-
-hipError_t configure_context(bool bf16, int d, size_t flash_lds) {
-  hipError_t e;
-  if (d == 32) e = set_pinv_attr<32>();
-  else if (d == 64) e = set_pinv_attr<64>();
-  else e = set_pinv_attr<128>();
-  if (e != hipSuccess) return e;
-  if (bf16) {
-    if (d == 32) return set_flash_attr<uint16_t, 32>(flash_lds);
-    if (d == 64) return set_flash_attr<uint16_t, 64>(flash_lds);
-    return set_flash_attr<uint16_t, 128>(flash_lds);
-  }
-  if (d == 32) return set_flash_attr<float, 32>(flash_lds);
-  if (d == 64) return set_flash_attr<float, 64>(flash_lds);
-  return set_flash_attr<float, 128>(flash_lds);
+hipError_t configure_context(bool bf16, int d, int mp, size_t ctx_lds) {
+  const int LG = mp / 32;
+  return hipFuncSetAttribute(context_fn(bf16, d, mp, LG),
+                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)ctx_lds);
 }
 
 }  // namespace nys

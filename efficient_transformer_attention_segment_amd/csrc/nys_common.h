@@ -228,6 +228,57 @@ __device__ __forceinline__ float half_sum(float x) {
   return x + __shfl_xor(x, 16);
 }
 
+// ---------------------------------------------------------------- LDS-DMA staging
+// global_load_lds_dwordx4: every lane moves 16 bytes from its own global address to LDS
+// at (M0 base) + 16 * lane, so one wave instruction fills 1 KiB of LDS contiguously and
+// any permutation of 16-byte chunks is free on the global side. Issued through inline
+// asm: the caller tracks completion itself with wait_dma_barrier. dst_lds must be
+// wave-uniform.
+__device__ __forceinline__ void dma16(const void* src, void* dst_lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_lds);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
+// Wait until at most n vector-memory loads of this wave are outstanding, then a
+// workgroup barrier. Loads complete in issue order, so when the n youngest loads are
+// the DMA of later tiles, every older tile is in LDS; after the barrier that holds for
+// every wave's share. No compiler fence is involved: the "memory" clobber keeps LDS
+// accesses on their side of it. n is wave-uniform and at most 32.
+template <int N>
+__device__ __forceinline__ void wait_vm_barrier_n() {
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_dma_barrier(int n) {
+  switch (n) {
+#define NYS_WAIT_CASE(N) case N: wait_vm_barrier_n<N>(); break;
+    NYS_WAIT_CASE(1) NYS_WAIT_CASE(2) NYS_WAIT_CASE(3) NYS_WAIT_CASE(4) NYS_WAIT_CASE(5)
+    NYS_WAIT_CASE(6) NYS_WAIT_CASE(7) NYS_WAIT_CASE(8) NYS_WAIT_CASE(10) NYS_WAIT_CASE(12)
+    NYS_WAIT_CASE(14) NYS_WAIT_CASE(16) NYS_WAIT_CASE(20) NYS_WAIT_CASE(24) NYS_WAIT_CASE(28)
+    NYS_WAIT_CASE(32)
+#undef NYS_WAIT_CASE
+    default: wait_vm_barrier_n<0>(); break;  // any other count: wait for everything
+  }
+}
+
+// 16-byte chunk permutation of row-major bf16 tiles with cpr chunks per row (4, 8 or
+// 16): chunk c of row r is stored at chunk c ^ chunk_key(r). With it, eight consecutive
+// rows read at one chunk (16-byte operand fetches) hit eight distinct 16-byte bank
+// groups, and four consecutive rows read at one aligned 32-byte column pair (transposed
+// reads) hit four distinct 32-byte bank groups.
+template <int CPR>
+__device__ __forceinline__ int chunk_key(int r) {
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "chunks per row");
+  if constexpr (CPR == 4) return 2 * ((r >> 1) & 1) + ((r >> 2) & 1);
+  else return 2 * (r & 3) + ((r >> 2) & 1);
+}
+
+// Element offset of (r, c) in a permuted row-major tile of CPR chunks per row.
+template <int CPR>
+__device__ __forceinline__ int swz_off(int r, int c) {
+  return r * (8 * CPR) + (((c >> 3) ^ chunk_key<CPR>(r)) << 3) + (c & 7);
+}
+
 // Map a linear block index to (head, part) so that all parts of one head run on the
 // same XCD (blocks are dispatched round-robin over the 8 XCDs) and share its L2.
 __device__ __forceinline__ void xcd_map(int b, int heads, int parts, int& head, int& part) {

@@ -16,7 +16,8 @@ struct SegArgs {
 };
 
 // Stage 2: landmark kernel + iterative pseudo-inverse (one block per head) and the
-// landmark context split over n (BH * C blocks, partial softmax states).
+// landmark context split over n (BH * C blocks, partial softmax states). For mp <= 64 both
+// run in one launch: blocks [0, npinv) form the pseudo-inverse, the rest the context.
 struct CtxArgs {
   const void* k;
   const void* v;
@@ -31,6 +32,9 @@ struct CtxArgs {
   float* part_w;          // [BH][C][d][mp]   per-chunk unnormalised (Bbar V)^T
   float* part_ml;         // [BH][C][2][mp]   per-chunk running max (log2 units), sum
   int BH, n, d, m, mp, iters, chunk, C, LG, TG;
+  int npinv;              // pseudo-inverse blocks at the front of the context grid (0 or BH)
+  int ring_ni;            // bf16 context: 1 KiB LDS-DMA loads per wave per K or V tile
+  int ring_stages;        // bf16 context: K/V tiles in the LDS ring (2..4)
   float scale;            // 1/sqrt(d)
   float scale_log2e;      // log2(e)/sqrt(d)
 };
@@ -60,14 +64,19 @@ struct OutArgs {
 
 hipError_t launch_segmeans(bool bf16, int d, const void* q, const void* k, const SegArgs& a,
                            hipStream_t s);
+// Separate pseudo-inverse launch, used only when it is not fused (mp > 64).
 hipError_t launch_pinv(int d, const CtxArgs& a, hipStream_t s);
-hipError_t launch_flash(bool bf16, int d, const CtxArgs& a, hipStream_t s);
+hipError_t launch_context(bool bf16, int d, const CtxArgs& a, hipStream_t s);
 hipError_t launch_output(bool bf16, int d, int conv_ksteps, const OutArgs& a, hipStream_t s);
 
 // Dynamic LDS each launch needs (bytes), and one-time kernel attribute setup.
-size_t context_lds_bytes(bool bf16, int d, int mp, int LG, int TG);
+// pinv fused into the context launch?
+inline bool context_fuses_pinv(int mp) { return mp <= 64; }
+// LDS-DMA ring geometry of the bf16 context kernel (sets a.ring_ni, a.ring_stages).
+void context_ring_geometry(int d, CtxArgs& a);
+size_t context_lds_bytes(bool bf16, int d, const CtxArgs& a);
 size_t output_lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C);
-hipError_t configure_context(bool bf16, int d, size_t flash_lds);
+hipError_t configure_context(bool bf16, int d, int mp, size_t ctx_lds);
 hipError_t configure_output(bool bf16, int d, int conv_ksteps, size_t out_lds);
 
 }  // namespace nys

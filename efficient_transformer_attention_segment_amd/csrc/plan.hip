@@ -37,6 +37,7 @@ struct nys_attn_plan {
   int B, H, n, d, m, mp, W, half, iters, ks;
   nys_dtype dtype;
   int BH, chunk, C, LG, TG, tok_per_block, G;
+  bool fused;  // pseudo-inverse blocks ride in the context launch (mp <= 64)
   int device;
   char* ws;
   size_t ws_bytes;
@@ -96,8 +97,12 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   p->TG = p->LG >= 4 ? 1 : 4 / p->LG;
   const int step = 32 * p->TG;
   const long long work = (long long)p->BH * n;
-  // about 1024 context blocks, at most 16 chunks per head (bounds the merge)
-  p->chunk = (int)round_up(std::max<long long>({(long long)step, (work + 1023) / 1024,
+  p->fused = nys::context_fuses_pinv(p->mp);
+  // Context blocks: about one resident wave of them next to the fused pseudo-inverse
+  // blocks (two 4-wave blocks per CU), at most 16 chunks per head (bounds the merge).
+  const long long slots = 2LL * std::max(1, prop.multiProcessorCount);
+  const long long target = std::max<long long>(slots / 2, slots - (p->fused ? p->BH : 0));
+  p->chunk = (int)round_up(std::max<long long>({(long long)step, (work + target - 1) / target,
                                                  ((long long)n + 15) / 16}), step);
   p->chunk = (int)std::min<long long>(p->chunk, round_up(n, step));
   p->C = ceil_div(n, p->chunk);
@@ -107,14 +112,20 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   p->ks = (p->half == 0) ? 2 : (p->half <= 16 ? 4 : 6);
   const bool bf16 = dtype == NYS_BF16;
 
-  const size_t flash_lds = nys::context_lds_bytes(bf16, d, p->mp, p->LG, p->TG);
+  nys::CtxArgs& c = p->ctx;
+  std::memset(&c, 0, sizeof(c));
+  c.BH = p->BH; c.n = n; c.d = d; c.m = m; c.mp = p->mp; c.iters = pinv_iters;
+  c.chunk = p->chunk; c.C = p->C; c.LG = p->LG; c.TG = p->TG;
+  c.npinv = p->fused ? p->BH : 0;
+  nys::context_ring_geometry(d, c);
+  const size_t ctx_lds = nys::context_lds_bytes(bf16, d, c);
   const size_t out_lds = nys::output_lds_bytes(bf16, d, p->mp, p->ks, p->C);
   const size_t max_lds = (size_t)prop.sharedMemPerBlock;
-  if (flash_lds > max_lds || out_lds > max_lds || (size_t)12 * 64 * 72 * 2 > max_lds) {
+  if (ctx_lds > max_lds || out_lds > max_lds) {
     delete p;
     return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
   }
-  if (nys::configure_context(bf16, d, flash_lds) != hipSuccess ||
+  if (nys::configure_context(bf16, d, p->mp, ctx_lds) != hipSuccess ||
       nys::configure_output(bf16, d, p->ks, out_lds) != hipSuccess) {
     (void)hipGetLastError();
     delete p;
@@ -164,13 +175,9 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
 
   p->seg = nys::SegArgs{p->BH, n, m, p->mp, n / m, F(o_qt), F(o_kt), U(o_qhl), U(o_khl)};
 
-  nys::CtxArgs& c = p->ctx;
-  std::memset(&c, 0, sizeof(c));
   c.qt = F(o_qt); c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
   c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.z_hl = U(o_zhl);
   c.part_w = F(o_pw); c.part_ml = F(o_pml);
-  c.BH = p->BH; c.n = n; c.d = d; c.m = m; c.mp = p->mp; c.iters = pinv_iters;
-  c.chunk = p->chunk; c.C = p->C; c.LG = p->LG; c.TG = p->TG;
   c.scale = 1.0f / std::sqrt((float)d);
   c.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)d));
 
@@ -233,8 +240,8 @@ static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, c
   o.attn_tap = taps ? taps->attn : nullptr;
   if (!taps || (!taps->w && !taps->y)) o.w_tap = o.y_tap = nullptr;
   if (!mark(0) || !chk(nys::launch_segmeans(bf16, p->d, q, k, p->seg, s), "segment means launch") ||
-      !mark(1) || !chk(nys::launch_pinv(p->d, c, s), "pseudo-inverse launch") ||
-      !mark(2) || !chk(nys::launch_flash(bf16, p->d, c, s), "landmark context launch") ||
+      !mark(1) || (!p->fused && !chk(nys::launch_pinv(p->d, c, s), "pseudo-inverse launch")) ||
+      !mark(2) || !chk(nys::launch_context(bf16, p->d, c, s), "landmark context launch") ||
       !mark(3) || !chk(nys::launch_output(bf16, p->d, p->ks, o, s), "output launch") ||
       !mark(4))
     return NYS_E_LAUNCH;
