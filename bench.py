@@ -100,8 +100,10 @@ def cpu_baseline(cfg, x, budget_s: float = 12.0) -> dict:
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # a forward is ~0.13 ms: defaults give the GPU ~60 ms to reach steady clocks before
+    # ~0.25 s of timed work (short runs measure the clock ramp, not the kernels)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -149,11 +151,12 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     # per-stage kernel times: HIP events the library records on the forward's stream
-    att.profile_enable(args.steps)
-    for i in range(args.steps):
+    nprof = min(args.steps, 200)
+    att.profile_enable(nprof)
+    for i in range(nprof):
         step(i)
     torch.cuda.synchronize()
-    prof = np.array(att.profile_read(args.steps), dtype=np.float64)
+    prof = np.array(att.profile_read(nprof), dtype=np.float64)
     stage_ms = {s: float(prof[:, j].mean()) for j, s in enumerate(STAGES)}
 
     if args.copy_calibration:

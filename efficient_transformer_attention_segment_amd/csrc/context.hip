@@ -275,22 +275,34 @@ __device__ __forceinline__ int row_tile_col(int col0, int rr, int lane) {
   return col0 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
 }
 
-// C[row0:+32, col0:+32] of C = A B for MP x MP planes, row-per-lane layout: lane l holds
-// row row0 + l % 32, register rr column row_tile_col(col0, rr, l).
+// MFMA B operand of C = A B from rows row0..row0+31 of A: lane l holds row row0 + l % 32,
+// k-slots 16 s + 8 (l / 32) + e of k-step s.
 template <int MP>
-__device__ __forceinline__ f32x16 prod_rows(const uint16_t* ahi, const uint16_t* alo,
-                                            const uint16_t* bhi, const uint16_t* blo,
-                                            int row0, int col0, int lane) {
-  constexpr int KS = MP / 16;
+__device__ __forceinline__ void load_row_operand(const uint16_t* ahi, const uint16_t* alo,
+                                                 int row0, int lane, Pair8* bo) {
   const int r = lane & 31, h = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < MP / 16; ++s) {
+    const int k0 = 16 * s + 8 * h;
+    bo[s] = Pair8{ld8(ahi + swz<MP>(row0 + r, k0)), ld8(alo + swz<MP>(row0 + r, k0))};
+  }
+}
+
+// C[row0:+32, col0:+32] of C = A B for MP x MP planes, row-per-lane layout: lane l holds
+// row row0 + l % 32, register rr column row_tile_col(col0, rr, l). bo: rows of A from
+// load_row_operand.
+template <int MP>
+__device__ __forceinline__ f32x16 prod_rows_op(const Pair8* bo, const uint16_t* bhi,
+                                               const uint16_t* blo, int col0, int lane) {
+  constexpr int KS = MP / 16;
+  const int h = lane >> 5;
   // transposed reads: lane 4j + q of each 16-lane group addresses row k0 + j, column
   // col0 + 16 * (group & 1) + 4q; the result lane then holds column col0 + lane % 32
   const int trj = (lane & 15) >> 2, trc = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  Pair8 ao[KS], bo[KS];
+  Pair8 ao[KS];
 #pragma unroll
   for (int s = 0; s < KS; ++s) {
     const int k0 = 16 * s + 8 * h;
-    bo[s] = Pair8{ld8(ahi + swz<MP>(row0 + r, k0)), ld8(alo + swz<MP>(row0 + r, k0))};
     ao[s].hi = lds_tr16x2(bhi + swz<MP>(k0 + trj, trc), bhi + swz<MP>(k0 + 4 + trj, trc));
     ao[s].lo = lds_tr16x2(blo + swz<MP>(k0 + trj, trc), blo + swz<MP>(k0 + 4 + trj, trc));
   }
@@ -298,6 +310,15 @@ __device__ __forceinline__ f32x16 prod_rows(const uint16_t* ahi, const uint16_t*
 #pragma unroll
   for (int s = 0; s < KS; ++s) acc = mfma_pair<true, true>(ao[s], bo[s], acc);
   return acc;
+}
+
+template <int MP>
+__device__ __forceinline__ f32x16 prod_rows(const uint16_t* ahi, const uint16_t* alo,
+                                            const uint16_t* bhi, const uint16_t* blo,
+                                            int row0, int col0, int lane) {
+  Pair8 bo[MP / 16];
+  load_row_operand<MP>(ahi, alo, row0, lane, bo);
+  return prod_rows_op<MP>(bo, bhi, blo, col0, lane);
 }
 
 // Store a row-per-lane tile into swizzled hi/lo planes (four 8-byte runs per plane).
@@ -328,7 +349,9 @@ __device__ __forceinline__ void store_row_tile_f32(float* p, int row0, int col0,
     *reinterpret_cast<f32x4*>(q + 8 * g) = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
 }
 
-enum { kQA = 0, kQZ = 2, kQX = 4, kQT = 6, kQPlanes = 8 };
+// LDS planes (hi, lo pairs): Z, X, T (= X^2, then 13I - 15X + 7X^2 - X^3). A_S passes
+// through the T pair once on its way into registers.
+enum { kQZ = 0, kQX = 2, kQT = 4, kQPlanes = 6 };
 
 template <int MP>
 constexpr size_t pinv_lds_planes_bytes() { return (size_t)kQPlanes * MP * MP * 2; }
@@ -422,7 +445,7 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
   // 3. A_S (fp32 copy and operand planes), Z_0 = alpha A_S^T
   if (mine) {
     store_row_tile_f32<MP>(a.a_s + (size_t)bh * P, row0, col0, at, lane);
-    store_row_tile<MP>(plane(kQA), plane(kQA + 1), row0, col0, at, lane);
+    store_row_tile<MP>(plane(kQT), plane(kQT + 1), row0, col0, at, lane);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {  // element (i, j) of A goes to Z_0[j][i]
       const int j = row_tile_col(col0, rr, lane);
@@ -435,11 +458,16 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
     }
   }
   __syncthreads();
+  // the wave's rows of A_S stay in registers for every X = A Z (the T planes that held
+  // them are first rewritten after the barrier that follows the first X)
+  constexpr int KM = MP / 16;
+  Pair8 abo[KM];
+  if (mine) load_row_operand<MP>(plane(kQT), plane(kQT + 1), row0, lane, abo);
   // 4. iterations Z <- 1/4 Z (13I - 15X + 7X^2 - X^3), X = A Z
   for (int it = 0; it < a.iters; ++it) {
     f32x16 x, x2, acc;
     if (mine) {  // X = A Z
-      x = prod_rows<MP>(plane(kQA), plane(kQA + 1), plane(kQZ), plane(kQZ + 1), row0, col0, lane);
+      x = prod_rows_op<MP>(abo, plane(kQZ), plane(kQZ + 1), col0, lane);
       store_row_tile<MP>(plane(kQX), plane(kQX + 1), row0, col0, x, lane);
     }
     __syncthreads();
@@ -850,8 +878,16 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
 // ------------------------------------------------------------------ context launch
 // MP > 0: blocks [0, BH) run the pseudo-inverse of their head (mp = MP), the rest the
 // landmark context; MP == 0: context blocks only. NCH applies to fp32 inputs.
+// Occupancy target: three 4-wave blocks per CU for bf16 with d <= 64 (their LDS is 48 KiB),
+// else two (fused) or one 8-wave block.
+template <typename Tin, int D>
+constexpr int context_min_blocks(int mp) {
+  return mp == 0 ? 1 : (!Input<Tin>::kSplit && D <= 64) ? 3 : 2;
+}
+
 template <typename Tin, int D, int MP, int NCH>
-__global__ __launch_bounds__(MP > 0 ? 256 : 512, MP > 0 ? 2 : 1) void context_kernel(CtxArgs a) {
+__global__ __launch_bounds__(MP > 0 ? 256 : 512, (context_min_blocks<Tin, D>(MP)))
+void context_kernel(CtxArgs a) {
   extern __shared__ __align__(16) char lds[];
   int blk = blockIdx.x;
   if constexpr (MP > 0) {
@@ -879,8 +915,8 @@ void context_ring_geometry(int d, CtxArgs& a) {
   const int nw = a.LG * a.TG, step = 32 * a.TG, chunks = step * (d / 8);
   a.ring_ni = (chunks + 64 * nw - 1) / (64 * nw);
   const size_t stage = (size_t)2 * nw * a.ring_ni * 1024;
-  // 64 KiB keeps two blocks per CU next to the fused pseudo-inverse's planes
-  const size_t budget = std::max<size_t>(64 * 1024, pinv_lds_bytes(a.mp));
+  // 48 KiB (the fused pseudo-inverse's planes at m = 64) keeps three blocks per CU
+  const size_t budget = std::max<size_t>(48 * 1024, pinv_lds_bytes(a.mp));
   a.ring_stages = (int)std::min<size_t>(4, std::max<size_t>(2, budget / stage));
 }
 

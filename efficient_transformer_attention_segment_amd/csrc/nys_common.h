@@ -56,16 +56,28 @@ __device__ __forceinline__ bf16x8 zero8() {
   return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 }
 
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+
 // Round-to-nearest-even fp32 -> bf16 (hardware v_cvt_pk_bf16_f32).
 __device__ __forceinline__ __bf16 bf16_rne(float x) { return (__bf16)x; }
+
+// Two values per conversion instruction (v_cvt_pk_bf16_f32 takes a pair).
+__device__ __forceinline__ bf16x2 bf16_rne2(float a, float b) {
+  return __builtin_convertvector(f32x2{a, b}, bf16x2);
+}
 
 __device__ __forceinline__ Pair8 split8(const float* x) {
   Pair8 p;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    __bf16 h = bf16_rne(x[e]);
-    p.hi[e] = h;
-    p.lo[e] = bf16_rne(x[e] - (float)h);
+  for (int e = 0; e < 8; e += 2) {
+    const bf16x2 h = bf16_rne2(x[e], x[e + 1]);
+    const f32x2 hf = __builtin_convertvector(h, f32x2);
+    const bf16x2 l = bf16_rne2(x[e] - hf[0], x[e + 1] - hf[1]);
+    p.hi[e] = h[0];
+    p.hi[e + 1] = h[1];
+    p.lo[e] = l[0];
+    p.lo[e + 1] = l[1];
   }
   return p;
 }

@@ -8,7 +8,9 @@
 // landmark context (per landmark, weights exp2(M_c - M*) / sum_c exp2(M_c - M*) L_c,
 // fixed chunk order) into W^T in LDS, form Y = Z W on MFMA and keep Y^T (hi/lo bf16,
 // landmark index permuted to match the score registers) in LDS; stage Kt (hi/lo, with
-// s*log2(e) folded in) and the conv filter's MFMA operand in LDS.
+// s*log2(e) folded in) and the conv filter's MFMA operand in LDS. All of its global
+// loads (chunk states, partials, Z, Kt, the first V rows and Q) are issued before any
+// is used, so the set-up costs about one memory round trip.
 //
 // The block then walks a contiguous token range of its head in steps of 128 tokens;
 // each wave owns 32 tokens per step. Per wave and step:
@@ -68,137 +70,16 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
 
   uint16_t* yl = reinterpret_cast<uint16_t*>(lds);     // [2][D][YS]  Y^T hi, lo
   uint16_t* wl = yl + (size_t)2 * D * YS;              // [KS][2][64][8] conv B operand
-  // region used first by the prologue (W^T planes, chunk weights), then by the main
-  // loop (Kt planes when kKtLds, V rows)
-  uint16_t* un = wl + (size_t)KS * 2 * 64 * 8;
+  uint16_t* kl = wl + (size_t)KS * 2 * 64 * 8;         // [2][mp][KR] Kt hi, lo (kKtLds)
+  // region used first by the prologue (W^T planes, chunk weights), then by the V rows
+  uint16_t* un = kl + (kKtLds ? (size_t)2 * mp * KR : 0);
   uint16_t* wtl = un;                                  // [2][D][YS]  W^T hi, lo
   float* wgt = reinterpret_cast<float*>(un + (size_t)2 * D * YS);  // [C][mp]
-  uint16_t* kl = un;                                   // [2][mp][KR] Kt hi, lo
-  uint16_t* vt = kl + (kKtLds ? (size_t)2 * mp * KR : 0);  // [EXT][VR] V rows (hi)
+  uint16_t* vt = un;                                   // [EXT][VR] V rows (hi)
   uint16_t* vt_lo = vt + (size_t)EXT * VR;             // V rows lo (fp32 input only)
   const bool taps = grp == 0;
+  const int C = a.C;
 
-  {
-    // chunk weights per landmark
-    const int C = a.C;
-    const float* pml = a.part_ml + (size_t)bh * C * 2 * mp;
-    for (int j = tid; j < mp; j += 256) {
-      if (j >= a.m) {
-        for (int c = 0; c < C; ++c) wgt[c * mp + j] = 0.f;
-        continue;
-      }
-      float ms = kNegBig;
-      for (int c0 = 0; c0 < C; c0 += 8) {
-        float mv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) mv[u] = (c0 + u < C) ? pml[(size_t)(2 * (c0 + u)) * mp + j] : kNegBig;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) ms = fmaxf(ms, mv[u]);
-      }
-      float den = 0.f;
-      for (int c0 = 0; c0 < C; c0 += 8) {
-        float ev[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const bool ok = c0 + u < C;
-          ev[u] = ok ? fast_exp2(pml[(size_t)(2 * (c0 + u)) * mp + j] - ms) : 0.f;
-          if (ok) wgt[(c0 + u) * mp + j] = ev[u];
-          den += ev[u] * (ok ? pml[(size_t)(2 * (c0 + u) + 1) * mp + j] : 0.f);
-        }
-      }
-      const float inv = 1.f / den;
-      for (int c = 0; c < C; ++c) wgt[c * mp + j] *= inv;
-    }
-    // conv filter as the B operand of the banded product (identical for every wave)
-    if (tid < 64) {
-      const float* w = a.conv_w + (size_t)head * a.W;
-#pragma unroll
-      for (int s = 0; s < KS; ++s) {
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int k = 16 * s + 8 * h + e - r32;
-          x[e] = (k >= 0 && k < a.W) ? w[k] : 0.f;
-        }
-        const Pair8 p = split8(x);
-        st8(wl + ((size_t)(2 * s) * 64 + lane) * 8, p.hi);
-        st8(wl + ((size_t)(2 * s + 1) * 64 + lane) * 8, p.lo);
-      }
-    }
-    __syncthreads();
-    // W^T[f][j] = sum_c wgt[c][j] * partial_c^T[f][j], four landmarks per thread
-    const float* pw = a.part_w + (size_t)bh * C * D * mp;
-    for (int e = tid; e < D * mp / 4; e += 256) {
-      const int f = e / (mp / 4), j = (e % (mp / 4)) * 4;
-      f32x4 acc{0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < C; c0 += 8) {
-        f32x4 pv[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          pv[u] = (c0 + u < C) ? *reinterpret_cast<const f32x4*>(pw + ((size_t)(c0 + u) * D + f) * mp + j)
-                               : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 8; ++u)
-          if (c0 + u < C) acc += *reinterpret_cast<const f32x4*>(wgt + (c0 + u) * mp + j) * pv[u];
-      }
-      uint16_t hb[4], lb[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) split1(acc[q], hb[q], lb[q]);
-      *reinterpret_cast<u32x2*>(wtl + (size_t)f * YS + j) =
-          u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
-      *reinterpret_cast<u32x2*>(wtl + (size_t)D * YS + (size_t)f * YS + j) =
-          u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
-      if (taps && a.w_tap != nullptr)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) a.w_tap[((size_t)bh * mp + j + q) * D + f] = acc[q];
-    }
-    __syncthreads();
-    // Y = Z W: A operand Z rows (global hi/lo), B operand W read along landmarks (W^T)
-    const size_t P = (size_t)mp * mp;
-    const uint16_t* zr = a.z_hl + (size_t)bh * 2 * P;
-    const int ntj = D / 32, ntiles = (mp / 32) * ntj;
-    for (int t = wave; t < ntiles; t += 4) {
-      const int row0 = 32 * (t / ntj), col0 = 32 * (t % ntj);
-      const f32x16 yv = gemm_tile(zr, zr + P, mp, wtl, wtl + (size_t)D * YS, YS, row0, col0, mp, lane);
-      const int f = col0 + r32;
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int i = acc_row(row0, rr, lane);
-        const int ip = (i & ~15) | kslot_perm(i & 15);
-        uint16_t hb, lb;
-        split1(yv[rr], hb, lb);
-        yl[(size_t)f * YS + ip] = hb;
-        yl[(size_t)D * YS + (size_t)f * YS + ip] = lb;
-        if (taps && a.y_tap != nullptr) a.y_tap[((size_t)bh * mp + i) * D + f] = yv[rr];
-      }
-    }
-    __syncthreads();
-    if constexpr (kKtLds) {
-      if constexpr (NT > 0) {  // from the fp32 landmarks, scaled to log2 units, then split
-        const float* ksrc = a.kt + (size_t)bh * mp * D;
-        for (int e = tid; e < mp * (D / 8); e += 256) {
-          const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
-          const f32x4 u0 = *reinterpret_cast<const f32x4*>(ksrc + (size_t)row * D + c8);
-          const f32x4 u1 = *reinterpret_cast<const f32x4*>(ksrc + (size_t)row * D + c8 + 4);
-          float x[8];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            x[q] = u0[q] * a.scale_log2e;
-            x[4 + q] = u1[q] * a.scale_log2e;
-          }
-          const Pair8 p = split8(x);
-          st8(kl + (size_t)row * KR + c8, p.hi);
-          st8(kl + (size_t)mp * KR + (size_t)row * KR + c8, p.lo);
-        }
-      } else {
-        const uint16_t* ksrc = a.kt_hl + (size_t)bh * 2 * mp * D;
-        for (int e = tid; e < 2 * mp * (D / 8); e += 256) {
-          const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
-          st8(kl + (size_t)row * KR + c8, ld8(ksrc + (size_t)row * D + c8));
-        }
-      }
-    }
-  }
   const uint16_t* khl = a.kt_hl + (size_t)bh * 2 * mp * D;
   const Tin* Q = static_cast<const Tin*>(a.q) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
@@ -263,11 +144,225 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     }
   };
 
+  // ---- prologue. Every global load is issued before any of it is used, so the whole
+  // set-up costs about one memory round trip; the first V rows and Q are in flight too.
   Chunk<Tin> vc[NCH];
   Pair8 qb[KD];
   load_v(t_begin, vc);
   load_q(t_begin, qb);
-  __syncthreads();  // prologue done with the region the V tile reuses
+  constexpr int kCB = 4;  // chunk states per load batch
+  const float* pml = a.part_ml + (size_t)bh * C * 2 * mp;
+  const float* pw = a.part_w + (size_t)bh * C * D * mp;
+  const uint16_t* zr = a.z_hl + (size_t)bh * 2 * mp * mp;
+  const size_t P = (size_t)mp * mp;
+  const int ntj = D / 32, ntiles = (mp / 32) * ntj;
+  // running max / sum of landmark tid in the first kCB chunks
+  float cm[kCB], cl[kCB];
+  if (tid < mp) {
+#pragma unroll
+    for (int c = 0; c < kCB; ++c) {
+      cm[c] = c < C ? pml[(size_t)(2 * c) * mp + tid] : kNegBig;
+      cl[c] = c < C ? pml[(size_t)(2 * c + 1) * mp + tid] : 0.f;
+    }
+  }
+  // register-resident softmax shapes (mp = 32 NT): partial W^T of the first kCB chunks
+  // (UP float4 outputs per thread), Z rows of the wave's Y tiles, the thread's Kt share
+  constexpr int UP = NT > 0 ? (D * 8 * NT + 255) / 256 : 1;
+  constexpr int TPY = NT > 0 ? (NT * (D / 32) + 3) / 4 : 1;
+  constexpr int KM = NT > 0 ? 2 * NT : 1;
+  constexpr int KU = NT > 0 ? (4 * NT * D + 255) / 256 : 1;
+  f32x4 pv[UP][kCB];
+  Pair8 za[TPY][KM];
+  f32x4 kx[KU][2];
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      const int e = tid + 256 * u, f = e / (mp / 4), j = (e % (mp / 4)) * 4;
+#pragma unroll
+      for (int c = 0; c < kCB; ++c)
+        pv[u][c] = (e < D * mp / 4 && c < C)
+                       ? *reinterpret_cast<const f32x4*>(pw + ((size_t)c * D + f) * mp + j)
+                       : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < TPY; ++u) {
+      const int t = wave + 4 * u;
+      const int row0 = 32 * (t / ntj);
+#pragma unroll
+      for (int s = 0; s < KM; ++s) {
+        const size_t o = (size_t)(row0 + r32) * mp + 16 * s + 8 * h;
+        za[u][s] = t < ntiles ? Pair8{ld8(zr + o), ld8(zr + P + o)} : Pair8{zero8(), zero8()};
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < KU; ++u) {
+      const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      const float* ks = a.kt + ((size_t)bh * mp + row) * D + c8;
+      const bool ok = e < mp * (D / 8);
+      kx[u][0] = ok ? *reinterpret_cast<const f32x4*>(ks) : f32x4{0.f, 0.f, 0.f, 0.f};
+      kx[u][1] = ok ? *reinterpret_cast<const f32x4*>(ks + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+
+  // chunk weights per landmark: exp2(M_c - M*) / sum_c exp2(M_c - M*) L_c
+  if (tid < mp) {
+    const int j = tid;
+    if (j >= a.m) {
+      for (int c = 0; c < C; ++c) wgt[c * mp + j] = 0.f;
+    } else if (C <= kCB) {
+      float ms = kNegBig;
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) ms = fmaxf(ms, cm[c]);
+      float den = 0.f;
+#pragma unroll
+      for (int c = 0; c < kCB; ++c) {
+        cm[c] = c < C ? fast_exp2(cm[c] - ms) : 0.f;
+        den += cm[c] * cl[c];
+      }
+      const float inv = 1.f / den;
+#pragma unroll
+      for (int c = 0; c < kCB; ++c)
+        if (c < C) wgt[c * mp + j] = cm[c] * inv;
+    } else {
+      float ms = kNegBig;
+      for (int c = 0; c < C; ++c) ms = fmaxf(ms, pml[(size_t)(2 * c) * mp + j]);
+      float den = 0.f;
+      for (int c = 0; c < C; ++c) {
+        const float ev = fast_exp2(pml[(size_t)(2 * c) * mp + j] - ms);
+        wgt[c * mp + j] = ev;
+        den += ev * pml[(size_t)(2 * c + 1) * mp + j];
+      }
+      const float inv = 1.f / den;
+      for (int c = 0; c < C; ++c) wgt[c * mp + j] *= inv;
+    }
+  }
+  // conv filter as the B operand of the banded product (identical for every wave)
+  if (tid < 64) {
+    const float* w = a.conv_w + (size_t)head * a.W;
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int k = 16 * s + 8 * h + e - r32;
+        x[e] = (k >= 0 && k < a.W) ? w[k] : 0.f;
+      }
+      const Pair8 p = split8(x);
+      st8(wl + ((size_t)(2 * s) * 64 + lane) * 8, p.hi);
+      st8(wl + ((size_t)(2 * s + 1) * 64 + lane) * 8, p.lo);
+    }
+  }
+  // Kt planes: from the fp32 landmarks scaled to log2 units (NT > 0), else the hi/lo copy
+  if constexpr (kKtLds) {
+    if constexpr (NT > 0) {
+#pragma unroll
+      for (int u = 0; u < KU; ++u) {
+        const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+        if (e < mp * (D / 8)) {
+          float x[8];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            x[q] = kx[u][0][q] * a.scale_log2e;
+            x[4 + q] = kx[u][1][q] * a.scale_log2e;
+          }
+          const Pair8 p = split8(x);
+          st8(kl + (size_t)row * KR + c8, p.hi);
+          st8(kl + (size_t)mp * KR + (size_t)row * KR + c8, p.lo);
+        }
+      }
+    } else {
+      const uint16_t* ksrc = a.kt_hl + (size_t)bh * 2 * mp * D;
+      for (int e = tid; e < 2 * mp * (D / 8); e += 256) {
+        const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+        st8(kl + (size_t)row * KR + c8, ld8(ksrc + (size_t)row * D + c8));
+      }
+    }
+  }
+  __syncthreads();
+  // W^T[f][j] = sum_c wgt[c][j] * partial_c^T[f][j], four landmarks per thread
+  auto put_w = [&](int f, int j, const f32x4& acc) {
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split1(acc[q], hb[q], lb[q]);
+    *reinterpret_cast<u32x2*>(wtl + (size_t)f * YS + j) =
+        u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    *reinterpret_cast<u32x2*>(wtl + (size_t)D * YS + (size_t)f * YS + j) =
+        u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+    if (taps && a.w_tap != nullptr)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a.w_tap[((size_t)bh * mp + j + q) * D + f] = acc[q];
+  };
+  auto merge_rest = [&](int f, int j, f32x4 acc, int cfrom) {  // chunks cfrom.. C-1
+    for (int c0 = cfrom; c0 < C; c0 += kCB) {
+      f32x4 v[kCB];
+#pragma unroll
+      for (int u = 0; u < kCB; ++u)
+        v[u] = c0 + u < C ? *reinterpret_cast<const f32x4*>(pw + ((size_t)(c0 + u) * D + f) * mp + j)
+                          : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < kCB; ++u)
+        if (c0 + u < C) acc += *reinterpret_cast<const f32x4*>(wgt + (c0 + u) * mp + j) * v[u];
+    }
+    return acc;
+  };
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int u = 0; u < UP; ++u) {
+      const int e = tid + 256 * u, f = e / (mp / 4), j = (e % (mp / 4)) * 4;
+      if (e < D * mp / 4) {
+        f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < kCB; ++c)
+          if (c < C) acc += *reinterpret_cast<const f32x4*>(wgt + c * mp + j) * pv[u][c];
+        if (C > kCB) acc = merge_rest(f, j, acc, kCB);
+        put_w(f, j, acc);
+      }
+    }
+  } else {
+    for (int e = tid; e < D * mp / 4; e += 256) {
+      const int f = e / (mp / 4), j = (e % (mp / 4)) * 4;
+      put_w(f, j, merge_rest(f, j, f32x4{0.f, 0.f, 0.f, 0.f}, 0));
+    }
+  }
+  __syncthreads();
+  // Y = Z W: A operand Z rows (global hi/lo), B operand W read along landmarks (W^T);
+  // stored as Y^T with landmark i at (i & ~15) | kslot_perm(i & 15)
+  auto put_y = [&](int row0, int col0, const f32x16& yv) {
+    const int f = col0 + r32;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int i = acc_row(row0, rr, lane);
+      const int ip = (i & ~15) | kslot_perm(i & 15);
+      uint16_t hb, lb;
+      split1(yv[rr], hb, lb);
+      yl[(size_t)f * YS + ip] = hb;
+      yl[(size_t)D * YS + (size_t)f * YS + ip] = lb;
+      if (taps && a.y_tap != nullptr) a.y_tap[((size_t)bh * mp + i) * D + f] = yv[rr];
+    }
+  };
+  if constexpr (NT > 0) {
+#pragma unroll
+    for (int u = 0; u < TPY; ++u) {
+      const int t = wave + 4 * u;
+      if (t < ntiles) {
+        const int row0 = 32 * (t / ntj), col0 = 32 * (t % ntj);
+        const size_t ob = (size_t)(col0 + r32) * YS + 8 * h;
+        f32x16 yv = zero16();
+#pragma unroll
+        for (int s = 0; s < KM; ++s) {
+          const Pair8 b{ld8(wtl + ob + 16 * s), ld8(wtl + (size_t)D * YS + ob + 16 * s)};
+          yv = mfma_pair<true, true>(za[u][s], b, yv);
+        }
+        put_y(row0, col0, yv);
+      }
+    }
+  } else {
+    for (int t = wave; t < ntiles; t += 4) {
+      const int row0 = 32 * (t / ntj), col0 = 32 * (t % ntj);
+      put_y(row0, col0, gemm_tile(zr, zr + P, mp, wtl, wtl + (size_t)D * YS, YS, row0, col0, mp, lane));
+    }
+  }
+  __syncthreads();  // the V rows take over the W^T region
   store_v(vc);
   __syncthreads();
 
@@ -390,9 +485,13 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
         for (int f = 0; f < FT; ++f) {
           bf16x8 lo8, hi8;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            lo8[e] = bf16_rne(oacc[f][e]);
-            hi8[e] = bf16_rne(oacc[f][8 + e]);
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 a2 = bf16_rne2(oacc[f][e], oacc[f][e + 1]);
+            const bf16x2 b2 = bf16_rne2(oacc[f][8 + e], oacc[f][9 + e]);
+            lo8[e] = a2[0];
+            lo8[e + 1] = a2[1];
+            hi8[e] = b2[0];
+            hi8[e + 1] = b2[1];
           }
           st8(op + 16 * f, lo8);
           st8(op + 16 * f + 8, hi8);
@@ -417,10 +516,10 @@ static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, bool k
   const size_t ext = 96 + 16 * (size_t)conv_ksteps;
   const size_t yl = (size_t)2 * d * (mp + 8) * 2;
   const size_t wl = (size_t)conv_ksteps * 2 * 64 * 8 * 2;
-  const size_t prologue = yl + (size_t)C * mp * 4;
-  const size_t main = ((kt_lds ? (size_t)2 * mp * (d + 8) : 0) +
-                       (bf16 ? 1 : 2) * ext * (size_t)(d + 8)) * 2;
-  return yl + wl + (prologue > main ? prologue : main);
+  const size_t kl = kt_lds ? (size_t)2 * mp * (d + 8) * 2 : 0;
+  const size_t wtl = (size_t)2 * d * (mp + 8) * 2 + (size_t)C * mp * 4;  // W^T + chunk weights
+  const size_t vt = (bf16 ? 1 : 2) * ext * (size_t)(d + 8) * 2;        // shares wtl's region
+  return yl + wl + kl + (wtl > vt ? wtl : vt);
 }
 
 static bool kt_in_lds(bool bf16, int d, int mp, int conv_ksteps, int C) {

@@ -99,11 +99,15 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   const long long work = (long long)p->BH * n;
   p->fused = nys::context_fuses_pinv(p->mp);
   // Context blocks: about one resident wave of them next to the fused pseudo-inverse
-  // blocks (two 4-wave blocks per CU), at most 16 chunks per head (bounds the merge).
-  const long long slots = 2LL * std::max(1, prop.multiProcessorCount);
+  // blocks (three 4-wave blocks per CU), at most 16 chunks per head (bounds the merge),
+  // and at most 4 when that still fills half the slots: the output prologue loads the
+  // chunk states of four chunks in one batch.
+  const long long slots = 3LL * std::max(1, prop.multiProcessorCount);
   const long long target = std::max<long long>(slots / 2, slots - (p->fused ? p->BH : 0));
-  p->chunk = (int)round_up(std::max<long long>({(long long)step, (work + target - 1) / target,
-                                                 ((long long)n + 15) / 16}), step);
+  const long long heads = std::max(1, p->BH);  // B*H == 0 is an empty problem
+  long long nc = std::min<long long>(16, std::max<long long>(1, (target + heads - 1) / heads));
+  if (nc > 4 && 4LL * heads >= target / 2) nc = 4;
+  p->chunk = (int)round_up(std::max<long long>(step, ((long long)n + nc - 1) / nc), step);
   p->chunk = (int)std::min<long long>(p->chunk, round_up(n, step));
   p->C = ceil_div(n, p->chunk);
   p->tok_per_block = (int)round_up(std::max<long long>(128, (work + 511) / 512), 128);

@@ -1,10 +1,11 @@
 // Segment-means landmarks (Nystromformer review page, "Proposed method": landmarks are
 // the means of contiguous token segments, an O(n) step).
 //
-// One thread owns one (matrix in {Q, K}, head, segment j, 8-feature chunk) and sums the
-// l = n/m rows of its segment in fp32 with 16-byte loads. Consecutive threads take
-// consecutive chunks of a row, so each load instruction of a wave reads whole 128-byte
-// row pieces of several segments; there is no cross-thread reduction.
+// One wave owns one (matrix in {Q, K}, head, segment j) and streams the segment's l = n/m
+// contiguous rows: lane L reads 16-byte chunk L % CPR of row L / CPR + RPW * it, so each
+// load instruction covers RPW whole consecutive rows (1 KiB contiguous), and the loads of
+// eight iterations are in flight together. Each lane sums its rows in fp32; lanes that
+// share a chunk are then combined with a butterfly over the row bits of the lane index.
 //
 // Outputs per head: fp32 means [mp][d] (rows m..mp-1 are left untouched; the workspace
 // keeps them zero) and the same values as hi/lo bf16 planes [2][mp][d] for the MFMA
@@ -18,48 +19,73 @@ template <typename Tin, int D>
 __global__ __launch_bounds__(256) void segmeans_kernel(const Tin* __restrict__ q,
                                                        const Tin* __restrict__ k,
                                                        SegArgs a) {
-  constexpr int kChunks = D / 8;
-  const long long g = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  const long long total = 2LL * a.BH * a.m * kChunks;
-  if (g >= total) return;
-  const int c = (int)(g % kChunks);
-  long long rest = g / kChunks;
-  const int j = (int)(rest % a.m);
-  rest /= a.m;
-  const int bh = (int)(rest % a.BH);
-  const int which = (int)(rest / a.BH);
+  constexpr int EPC = 16 / sizeof(Tin);  // elements per 16-byte chunk
+  constexpr int CPR = D / EPC;           // chunks per row
+  constexpr int RPW = 64 / CPR;          // rows per wave load
+  static_assert(CPR >= 1 && CPR <= 64 && (64 % CPR) == 0, "row must tile a wave");
+  const int lane = threadIdx.x & 63;
+  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= 2LL * a.BH * a.m) return;  // whole waves only; the kernel has no barrier
+  const int j = (int)(task % a.m);
+  const int bh = (int)((task / a.m) % a.BH);
+  const int which = (int)(task / ((long long)a.m * a.BH));
+  const int c = lane % CPR, r0 = lane / CPR;
 
-  const Tin* src = (which ? k : q) + (size_t)bh * a.n * D + (size_t)j * a.l * D + c * 8;
-  float acc[8];
+  const Tin* src = (which ? k : q) + (size_t)bh * a.n * D + (size_t)j * a.l * D + c * EPC;
+  float acc[EPC];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  const int nit = (a.l + RPW - 1) / RPW;
 #pragma unroll 8
-  for (int r = 0; r < a.l; ++r) {
+  for (int it = 0; it < nit; ++it) {
+    const int r = r0 + RPW * it;
     float x[8];
-    Input<Tin>::load_raw(src + (size_t)r * D, true, x);
+    if constexpr (EPC == 8) {
+      Input<Tin>::load_raw(src + (size_t)r * D, r < a.l, x);
+    } else {
+      const f32x4 v = r < a.l ? *reinterpret_cast<const f32x4*>(src + (size_t)r * D)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += x[e];
+      for (int e = 0; e < 4; ++e) x[e] = v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += x[e];
   }
+  // lanes c, c + CPR, c + 2 CPR, ... hold partial sums of the same chunk
+#pragma unroll
+  for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+  if (lane >= CPR) return;
+
   const float inv_l = 1.0f / (float)a.l;
   float mean[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) mean[e] = acc[e] * inv_l;
-
-  float* dst = (which ? a.kt : a.qt) + ((size_t)bh * a.mp + j) * D + c * 8;
+  for (int e = 0; e < EPC; ++e) mean[e] = acc[e] * inv_l;
+  float* dst = (which ? a.kt : a.qt) + ((size_t)bh * a.mp + j) * D + c * EPC;
+  uint16_t* hl = (which ? a.kt_hl : a.qt_hl) + (size_t)bh * 2 * a.mp * D + (size_t)j * D + c * EPC;
   *reinterpret_cast<f32x4*>(dst) = f32x4{mean[0], mean[1], mean[2], mean[3]};
-  *reinterpret_cast<f32x4*>(dst + 4) = f32x4{mean[4], mean[5], mean[6], mean[7]};
-
-  Pair8 p = split8(mean);
-  uint16_t* hl = (which ? a.kt_hl : a.qt_hl) + (size_t)bh * 2 * a.mp * D + (size_t)j * D + c * 8;
-  st8(hl, p.hi);
-  st8(hl + (size_t)a.mp * D, p.lo);
+  if constexpr (EPC == 8) {
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{mean[4], mean[5], mean[6], mean[7]};
+    const Pair8 p = split8(mean);
+    st8(hl, p.hi);
+    st8(hl + (size_t)a.mp * D, p.lo);
+  } else {
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split1(mean[e], hb[e], lb[e]);
+    *reinterpret_cast<u32x2*>(hl) =
+        u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    *reinterpret_cast<u32x2*>(hl + (size_t)a.mp * D) =
+        u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+  }
 }
 
 template <typename Tin, int D>
 static hipError_t launch_segmeans_t(const void* q, const void* k, const SegArgs& a,
                                     hipStream_t s) {
-  const long long total = 2LL * a.BH * a.m * (D / 8);
-  const int blocks = (int)((total + 255) / 256);
+  const long long waves = 2LL * a.BH * a.m;  // one per (matrix, head, segment)
+  const int blocks = (int)((waves + 3) / 4);
   hipLaunchKernelGGL((segmeans_kernel<Tin, D>), dim3(blocks), dim3(256), 0, s,
                      static_cast<const Tin*>(q), static_cast<const Tin*>(k), a);
   return hipGetLastError();
