@@ -33,9 +33,10 @@ HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 CSRC = os.path.join(ROOT, "efficient_transformer_attention_segment_amd", "csrc")
 STAGES = ("segment_means", "pinv", "context", "output")
-# kernel name (as rocprofv3 reports it) of each stage
-STAGE_KERNEL = {"segment_means": "segmeans_kernel", "pinv": "pinv_kernel",
-                "context": "flash_kernel", "output": "output_kernel"}
+# kernel name (as rocprofv3 reports it) of each stage; for m <= 64 the pseudo-inverse
+# blocks run inside context_kernel and the "pinv" stage is empty
+STAGE_KERNEL = {"segment_means": "segmeans_kernel", "pinv": "pinv_global_kernel",
+                "context": "context_kernel", "output": "output_kernel"}
 
 
 def stage_bytes(cfg) -> dict:
@@ -51,7 +52,8 @@ def stage_bytes(cfg) -> dict:
 
 def source_hash(stage: str) -> str:
     files = {"segment_means": ["segmeans.hip"], "pinv": ["context.hip"],
-             "context": ["context.hip"], "output": ["output.hip"]}[stage] + ["nys_common.h"]
+             "context": ["context.hip"], "output": ["output.hip"]}[stage]
+    files += ["nys_common.h", "nys_kernels.h"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -97,6 +99,86 @@ def cpu_baseline(cfg, x, budget_s: float = 12.0) -> dict:
                       f"{dt:.1f} s, numpy fp64, BLAS threads={cores}"}
 
 
+# ------------------------------------------------------------------ profile summaries
+# rocprofv3 output -> short text summaries under profiles/ (no GPU needed)
+
+def _short(name: str) -> str:
+    name = name.replace("void ", "")
+    return name.split("(")[0].replace("nys::", "")
+
+
+def summarize_trace(trace_dir: str, cfg_name: str, command: str) -> str:
+    """Per-kernel dispatch count and mean duration from a rocprofv3 --kernel-trace
+    --stats database: over all dispatches (what --stats reports) and over the last 200
+    (the event-profiled forwards that bench.py's stage times come from)."""
+    import glob
+    import sqlite3
+    db = sorted(glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True))[0]
+    con = sqlite3.connect(db)
+    rows = con.execute("select name, total_calls, average from top_kernels").fetchall()
+    per = {}
+    for name, dur in con.execute("select name, duration from kernels order by start"):
+        per.setdefault(name, []).append(dur)
+    lines = [f"Kernel trace of the Nystrom attention forward, workload {cfg_name} "
+             f"({CONFIG_TEXT[cfg_name]}), one MI355X.", "",
+             "Command (repository root; rocprofv3 wants the program right after --):",
+             f"  {command}", "",
+             f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'last200_us':>11s}"]
+    for name, calls, avg in rows:
+        d = per.get(name, [])
+        tail = sum(d[-200:]) / max(1, len(d[-200:])) / 1e3
+        lines.append(f"{_short(name)[:64]:64s} {calls:6d} {avg:9.3f} {tail:11.3f}")
+    return "\n".join(lines) + "\n"
+
+
+def _read_counters(d: str):
+    import csv
+    import glob
+    out = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                out.append((int(r["Dispatch_Id"]), r["Kernel_Name"], r["Counter_Name"],
+                            float(r["Counter_Value"])))
+    return out
+
+
+def summarize_counters(fetch_dir: str, write_dir: str, cfg_name: str, commands) -> dict:
+    """HBM traffic per launch of each kernel from a FETCH_SIZE run and a WRITE_SIZE run
+    (KiB per dispatch), each scaled by what the counter reads for the 256 MiB device
+    copies of --copy-calibration (known to read and write 256 MiB)."""
+    fetch = _read_counters(fetch_dir)
+    write = _read_counters(write_dir)
+    cal_kib = 256 * 1024
+    cal_ids = [i for i, n, c, v in write
+               if "copyBuffer" in n and c == "WRITE_SIZE" and abs(v - cal_kib) < 0.1 * cal_kib]
+    cw = [v for i, n, c, v in write if i in cal_ids and c == "WRITE_SIZE"]
+    cf = [v for i, n, c, v in fetch if i in cal_ids and c == "FETCH_SIZE"]
+    if not cw or not cf:
+        raise SystemExit("no calibration copies found (run with --copy-calibration)")
+    wscale, fscale = cal_kib / (sum(cw) / len(cw)), cal_kib / (sum(cf) / len(cf))
+    res = {}
+    for stage, kern in STAGE_KERNEL.items():
+        fv = [v for i, n, c, v in fetch if _short(n).startswith(kern + "<") and c == "FETCH_SIZE"]
+        wv = [v for i, n, c, v in write if _short(n).startswith(kern + "<") and c == "WRITE_SIZE"]
+        if not fv or not wv:
+            continue
+        f_kib, w_kib = sum(fv) / len(fv), sum(wv) / len(wv)
+        res[kern] = {
+            "kernel": kern, "workload": cfg_name, "source_hash": source_hash(stage),
+            "fetch_kib_per_dispatch": f_kib, "write_kib_per_dispatch": w_kib,
+            "fetch_scale": fscale, "write_scale": wscale,
+            "calibration": "256 MiB device copies (hipMemcpy D2D kernel): counter KiB "
+                           "-> true KiB",
+            "traffic_bytes_per_launch": (f_kib * fscale + w_kib * wscale) * 1024,
+            "commands": list(commands)}
+    return res
+
+
+CONFIG_TEXT = {"long": "B=16 H=8 n=4096 d=64 m=64, conv width 33, 6 pseudo-inverse "
+                       "iterations, bf16 I/O"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -108,7 +190,31 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="write profiles/nystrom_forward_<config>_kernel_trace.txt from a "
+                         "rocprofv3 --kernel-trace --stats output directory and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/<kernel>_<config>_counters.json from rocprofv3 "
+                         "--pmc FETCH_SIZE and --pmc WRITE_SIZE output directories and exit")
+    ap.add_argument("--command", action="append", default=[],
+                    help="command line(s) that produced the summarized output")
     args = ap.parse_args()
+    if args.summarize_trace:
+        os.makedirs(PROFILES, exist_ok=True)
+        path = os.path.join(PROFILES, f"nystrom_forward_{args.config}_kernel_trace.txt")
+        with open(path, "w") as fh:
+            fh.write(summarize_trace(args.summarize_trace, args.config, " && ".join(args.command)))
+        print(f"wrote {path}")
+        return
+    if args.summarize_counters:
+        os.makedirs(PROFILES, exist_ok=True)
+        for kern, rec in summarize_counters(*args.summarize_counters, args.config,
+                                            args.command).items():
+            path = os.path.join(PROFILES, f"{kern}_{args.config}_counters.json")
+            with open(path, "w") as fh:
+                json.dump(rec, fh, indent=1)
+            print(f"wrote {path}")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               "(the forward shards over (batch, head) without communication; see the "
