@@ -10,6 +10,7 @@ from .nystrom import (  # noqa: F401
     nystrom_forward,
     nystrom_head,
     pinv_scaling,
+    segment_boundaries,
     segment_means,
     softmax_rows,
 )

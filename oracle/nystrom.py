@@ -18,7 +18,13 @@ silent (each one listed in the repository's design notes):
 * softmax is row-wise over the last axis, no mask, no causality;
 * the 1/sqrt(d) scale is applied inside all three softmaxes (M1, M3 show it; M2 omits
   it, read as shorthand);
-* segments are m contiguous, equal-length blocks of tokens; n % m == 0 is required;
+* segments are m contiguous blocks of tokens: token t of a length-L sequence belongs to
+  segment floor(t m / L), i.e. segment j is rows [ceil(j L / m), ceil((j+1) L / m)) of
+  floor(L/m) or ceil(L/m) tokens (all equal when m divides L), with 1 <= m <= L;
+* padding masks / ragged batches: batch element b has a valid length L_b (m <= L_b <= n).
+  Rows [0, L_b) of its output are the forward of the unpadded length-L_b sequence
+  (padding tokens are neither keys, values, landmark members nor conv inputs) and rows
+  [L_b, n) are zero;
 * the pseudo-inverse iteration (M5 names an iterative method and about six iterations,
   but gives no formula) is the third-order Newton-type scheme
   Z <- 1/4 Z (13I - X(15I - X(7I - X))), X = A Z, started from
@@ -39,16 +45,23 @@ def softmax_rows(x: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def segment_boundaries(n: int, m: int) -> list:
+    """Start rows of the m contiguous segments of n tokens, plus n: segment j is rows
+    [ceil(j n / m), ceil((j+1) n / m)) (l = n/m rows each when m divides n)."""
+    if m < 1 or m > n:
+        raise ValueError("segment means need 1 <= m <= n")
+    return [(j * n + m - 1) // m for j in range(m + 1)]
+
+
 def segment_means(x: np.ndarray, m: int) -> np.ndarray:
-    """M4: landmarks as segment means. x is (n, d); segment j is rows [j*l, (j+1)*l)
-    with l = n/m; returns the (m, d) matrix of per-segment means."""
+    """M4: landmarks as segment means. x is (n, d); returns the (m, d) matrix of the
+    means of the m contiguous segments given by segment_boundaries."""
     n, d = x.shape
-    if m < 1 or n % m != 0:
-        raise ValueError("segment means need n % m == 0")
-    l = n // m
+    bnd = segment_boundaries(n, m)
     out = np.empty((m, d), dtype=np.float64)
     for j in range(m):
-        out[j] = x[j * l:(j + 1) * l].astype(np.float64).sum(axis=0) / l
+        rows = x[bnd[j]:bnd[j + 1]].astype(np.float64)
+        out[j] = rows.sum(axis=0) / rows.shape[0]
     return out
 
 
@@ -122,22 +135,32 @@ def nystrom_head(q: np.ndarray, k: np.ndarray, v: np.ndarray, m: int, iters: int
 
 
 def nystrom_forward(q, k, v, conv_w, m: int, iters: int = 6, heads=None,
-                    return_stages: bool = False):
+                    return_stages: bool = False, lengths=None):
     """Full forward over [B, H, n, d] inputs: attention part plus the depthwise-conv
     skip on V. ``conv_w`` is [H, W]. ``heads`` optionally restricts the computation
     to a list of (b, h) pairs (their outputs are returned in that order, stacked as
-    [len(heads), n, d]); otherwise the result is [B, H, n, d].
+    [len(heads), n, d]); otherwise the result is [B, H, n, d]. ``lengths`` (B ints,
+    default all n) are the valid lengths of a padded batch: each (b, h) is computed on
+    its first lengths[b] tokens and the remaining output rows are zero.
     """
     q = np.asarray(q)
     B, H, n, d = q.shape
+    lens = [n] * B if lengths is None else [int(x) for x in lengths]
+    if len(lens) != B or any(not (m <= x <= n) for x in lens):
+        raise ValueError("lengths must hold B values in [m, n]")
     pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
     outs, attns, stages = [], [], []
     for (b, h) in pairs:
-        st = nystrom_head(q[b, h], k[b, h], v[b, h], m, iters)
-        conv = depthwise_conv_seq(np.asarray(v[b, h], dtype=np.float64),
+        L = lens[b]
+        st = nystrom_head(q[b, h, :L], k[b, h, :L], v[b, h, :L], m, iters)
+        conv = depthwise_conv_seq(np.asarray(v[b, h, :L], dtype=np.float64),
                                   np.asarray(conv_w[h], dtype=np.float64))
-        outs.append(st["attn"] + conv)
-        attns.append(st["attn"])
+        full = np.zeros((n, d))
+        full[:L] = st["attn"] + conv
+        attn = np.zeros((n, d))
+        attn[:L] = st["attn"]
+        outs.append(full)
+        attns.append(attn)
         if return_stages:
             stages.append(st)
     out = np.stack(outs)

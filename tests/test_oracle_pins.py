@@ -27,6 +27,7 @@ def _ns(**over):
         pinv_scaling=orc.pinv_scaling,
         depthwise_conv_seq=orc.depthwise_conv_seq,
         nystrom_head=orc.nystrom_head,
+        nystrom_forward=orc.nystrom_forward,
     )
     for k, v in over.items():
         setattr(ns, k, v)
@@ -47,6 +48,33 @@ def pin_segment_means_bruteforce(ns) -> float:
             for t in range(j * l, j * l + l):
                 acc += float(x[t, c])
             worst = max(worst, abs(acc / l - got[j, c]))
+    return worst
+
+
+def pin_segment_means_uneven_bruteforce(ns) -> float:
+    """n % m != 0: token t belongs to segment floor(t m / n) (written here as integer
+    comparisons t m >= j n, independently of the oracle's boundary list); each landmark
+    is the mean over its tokens, accumulated one token at a time."""
+    rng = np.random.default_rng(19)
+    worst = 0.0
+    for n, m in ((23, 5), (64, 7), (10, 10), (9, 1), (100, 33), (31, 30)):
+        d = 3
+        x = rng.standard_normal((n, d))
+        got = ns.segment_means(x, m)
+        sums = [[0.0] * d for _ in range(m)]
+        cnt = [0] * m
+        for t in range(n):
+            j = 0
+            while j + 1 < m and t * m >= (j + 1) * n:
+                j += 1
+            cnt[j] += 1
+            for c in range(d):
+                sums[j][c] += float(x[t, c])
+        for j in range(m):
+            if cnt[j] == 0:
+                return np.inf
+            for c in range(d):
+                worst = max(worst, abs(sums[j][c] / cnt[j] - got[j, c]))
     return worst
 
 
@@ -164,6 +192,50 @@ def pin_block_separated(ns) -> float:
     return float(np.abs(st["attn"] - ref).max())
 
 
+def pin_ragged_exact(ns) -> float:
+    """A padded sequence of valid length L with m = L landmarks and a converged
+    pseudo-inverse: rows [0, L) are dense softmax attention over the first L tokens
+    plus the conv of the first L rows of V (torch SDPA, numpy correlate), rows [L, n)
+    are zero, and whatever sits in the padding rows does not matter."""
+    worst = 0.0
+    for n, L, d, seed in ((24, 16, 4, 4), (40, 29, 8, 5)):
+        x = gen.make_well_conditioned_square(L, d, seed, scale=0.5)
+        rng = np.random.default_rng(seed)
+        pad = lambda a: np.concatenate([a[0, 0], 50.0 * rng.standard_normal((n - L, d))])[None, None]
+        q, k, v = pad(x.q), pad(x.k), pad(x.v)
+        w = rng.standard_normal((1, 5))
+        out, attn = ns.nystrom_forward(q, k, v, w, L, 60, lengths=[L])
+        ref = _sdpa(q[0, 0, :L], k[0, 0, :L], v[0, 0, :L])
+        conv = np.stack([np.correlate(np.concatenate([np.zeros(2), v[0, 0, :L, c], np.zeros(2)]),
+                                      w[0], mode="valid") for c in range(d)], axis=1)
+        sc = np.sqrt(np.mean(ref ** 2))
+        worst = max(worst, np.abs(attn[0, 0, :L] - ref).max() / sc,
+                    np.abs(out[0, 0, :L] - ref - conv).max() / sc,
+                    np.abs(out[0, 0, L:]).max(), np.abs(attn[0, 0, L:]).max())
+    return worst
+
+
+def pin_ragged_block_separated(ns) -> float:
+    """Uneven segments at scale: valid length L = 997 (m = 64 does not divide it), Q = K
+    with every token of segment j = floor(t m / L) equal to r e_j, r^2/sqrt(d) = 30, and
+    random padding rows. The landmark kernel is the identity up to e^-30, six
+    iterations give Z = I, so each valid row is the mean of V over its segment."""
+    n, L, d, m = 1024, 997, 64, 64
+    rng = np.random.default_rng(31)
+    r = np.sqrt(30.0 * np.sqrt(d))
+    seg = np.array([t * m // L for t in range(L)])
+    q = np.zeros((n, d))
+    q[np.arange(L), seg] = r
+    q[L:] = rng.standard_normal((n - L, d)) * 3.0
+    v = rng.standard_normal((n, d))
+    ref = np.zeros((L, d))
+    for j in range(m):
+        ref[seg == j] = v[:L][seg == j].mean(axis=0)
+    out, attn = ns.nystrom_forward(q[None, None], q[None, None], v[None, None],
+                                   np.zeros((1, 1)), m, 6, lengths=[L])
+    return float(max(np.abs(attn[0, 0, :L] - ref).max(), np.abs(out[0, 0, L:]).max()))
+
+
 def pin_single_landmark(ns) -> float:
     """m = 1: A_S = [1], alpha = 1 and 1 is a fixed point of the iteration, so every
     output row equals softmax(q_bar K^T / sqrt(d)) V with q_bar the mean query."""
@@ -215,6 +287,9 @@ def pin_softmax_factors(ns) -> float:
 
 PINS = {
     "segment_means_bruteforce": (pin_segment_means_bruteforce, 1e-13),
+    "segment_means_uneven_bruteforce": (pin_segment_means_uneven_bruteforce, 1e-13),
+    "ragged_exact": (pin_ragged_exact, 1e-9),
+    "ragged_block_separated": (pin_ragged_block_separated, 1e-8),
     "softmax_library": (pin_softmax_library, 1e-14),
     "pinv_closed_form": (pin_pinv_closed_form, 1e-9),
     "pinv_symmetry": (pin_pinv_symmetry, 1e-12),
@@ -272,6 +347,34 @@ def _segmeans_strided(x, m):
     return np.stack([x[j::m].mean(axis=0) for j in range(m)])
 
 
+def _segmeans_floor_boundaries(x, m):
+    n, d = x.shape
+    b = [j * n // m for j in range(m + 1)]
+    return np.stack([x[b[j]:b[j + 1]].mean(axis=0) for j in range(m)])
+
+
+def _forward_ignores_lengths(q, k, v, w, m, iters=6, heads=None, return_stages=False,
+                             lengths=None):
+    return orc.nystrom_forward(q, k, v, w, m, iters, heads, return_stages)
+
+
+def _forward_keeps_padding(q, k, v, w, m, iters=6, heads=None, return_stages=False,
+                           lengths=None):
+    out, attn = orc.nystrom_forward(q, k, v, w, m, iters, heads, return_stages, lengths)
+    full, full_attn = orc.nystrom_forward(q, k, v, w, m, iters, heads, return_stages)
+    L = np.asarray(q).shape[2] if lengths is None else lengths[0]
+    out[..., L:, :] = full[..., L:, :]
+    attn[..., L:, :] = full_attn[..., L:, :]
+    return out, attn
+
+
+def _forward_length_plus_one(q, k, v, w, m, iters=6, heads=None, return_stages=False,
+                             lengths=None):
+    n = np.asarray(q).shape[2]
+    lens = None if lengths is None else [min(n, x + 1) for x in lengths]
+    return orc.nystrom_forward(q, k, v, w, m, iters, heads, return_stages, lens)
+
+
 def _conv_flipped(v, w):
     return orc.depthwise_conv_seq(v, np.asarray(w)[::-1])
 
@@ -304,6 +407,10 @@ MUTANTS = {
     "pinv_dropped_term": dict(iterative_pinv=_pinv_dropped_term),
     "pinv_row_norm_twice": dict(iterative_pinv=_pinv_row_norm_twice),
     "segmeans_strided": dict(segment_means=_segmeans_strided),
+    "segmeans_floor_boundaries": dict(segment_means=_segmeans_floor_boundaries),
+    "forward_ignores_lengths": dict(nystrom_forward=_forward_ignores_lengths),
+    "forward_keeps_padding": dict(nystrom_forward=_forward_keeps_padding),
+    "forward_length_plus_one": dict(nystrom_forward=_forward_length_plus_one),
     "conv_flipped": dict(depthwise_conv_seq=_conv_flipped),
     "softmax_cols": dict(softmax_rows=_softmax_cols),
     "head_wrong_scale": dict(nystrom_head=_head_wrong_scale),
