@@ -39,15 +39,18 @@ STAGE_KERNEL = {"segment_means": "segmeans_kernel", "pinv": "pinv_global_kernel"
                 "context": "context_kernel", "output": "output_kernel"}
 
 
-def stage_bytes(cfg) -> dict:
+def stage_bytes(cfg, lengths=None) -> dict:
     """Algorithmic HBM bytes per launch of each stage (inputs read once, output written
-    once; the small landmark-sized workspace traffic is not counted)."""
+    once; the small landmark-sized workspace traffic is not counted). With padded
+    lengths only valid rows are read; every output row is written (zeros on padding)."""
     e = 2 if cfg.dtype == "bf16" else 4
-    tok = cfg.bh * cfg.n * cfg.d * e
+    valid = cfg.n * cfg.B if lengths is None else sum(lengths)
+    tok = cfg.H * valid * cfg.d * e
+    full = cfg.bh * cfg.n * cfg.d * e
     return {"segment_means": 2 * tok,      # read Q, K
             "pinv": 0,                     # landmark-sized only (compute/latency bound)
             "context": 2 * tok,            # read K, V
-            "output": 3 * tok}             # read Q, V; write out
+            "output": 2 * tok + full}      # read Q, V; write out
 
 
 def source_hash(stage: str) -> str:
@@ -74,7 +77,7 @@ def measured_traffic(stage: str, cfg_name: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(cfg, x, budget_s: float = 12.0) -> dict:
+def cpu_baseline(cfg, x, budget_s: float = 12.0, lengths=None) -> dict:
     """Time the fp64 oracle (untuned) on the host: whole forwards of the workload,
     repeated until about budget_s seconds have passed."""
     import oracle
@@ -88,12 +91,14 @@ def cpu_baseline(cfg, x, budget_s: float = 12.0) -> dict:
     t0 = time.perf_counter()
     passes = 0
     while True:
-        oracle.nystrom_forward(x.q, x.k, x.v, x.w, cfg.m, cfg.pinv_iters, heads=heads)
+        oracle.nystrom_forward(x.q, x.k, x.v, x.w, cfg.m, cfg.pinv_iters, heads=heads,
+                               lengths=lengths)
         passes += 1
         if time.perf_counter() - t0 >= budget_s:
             break
     dt = time.perf_counter() - t0
-    return {"value": passes * cfg.tokens / dt, "unit": "tokens/s", "cores": int(cores),
+    tokens = cfg.tokens if lengths is None else sum(lengths)
+    return {"value": passes * tokens / dt, "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
             "sample": f"{passes} full forward(s) of the workload ({cfg.bh} heads) in "
                       f"{dt:.1f} s, numpy fp64, BLAS threads={cores}"}
@@ -188,6 +193,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=500)
     ap.add_argument("--config", default="long")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--ragged", action="store_true",
+                    help="padded batch: seeded valid lengths in [n/2, n] per batch element "
+                         "(tokens/s then counts valid tokens)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -241,9 +249,12 @@ def main():
     att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, cfg.conv_width,
                            cfg.pinv_iters, cfg.dtype)
 
+    lengths = gen.ragged_lengths(cfg, cfg.seed) if args.ragged else None
+    lens_dev = torch.tensor(lengths, dtype=torch.int32, device="cuda") if lengths else None
+
     def step(i):
         q, k, v, w = dev_sets[i % 2]
-        att.forward(q, k, v, w, out=outs[i % 2])
+        att.forward(q, k, v, w, out=outs[i % 2], lengths=lens_dev)
 
     for i in range(args.warmup):
         step(i)
@@ -272,12 +283,13 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
 
-    tokens = cfg.tokens
+    tokens = cfg.tokens if lengths is None else sum(lengths)
     value = tokens / (ms * 1e-3)
-    sbytes = stage_bytes(cfg)
+    sbytes = stage_bytes(cfg, lengths)
     dom = max((s for s in STAGES if sbytes[s] > 0), key=lambda s: stage_ms[s])
     achieved = sbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    path_bytes = 4 * cfg.bh * cfg.n * cfg.d * (2 if cfg.dtype == "bf16" else 4)
+    path_bytes = (sbytes["context"] * 3 // 2 + cfg.bh * cfg.n * cfg.d
+                  * (2 if cfg.dtype == "bf16" else 4))  # Q, K, V valid rows once + out
     path_roof_ms = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
     rec = {
         "metric": METRIC,
@@ -293,20 +305,22 @@ def main():
         "dtype": cfg.dtype,
         "data": "synthetic",
         "config": {"workload": f"nystrom_attention_forward_B{cfg.B}_H{cfg.H}_n{cfg.n}_"
-                               f"d{cfg.d}_m{cfg.m}_conv{cfg.conv_width}_iters{cfg.pinv_iters}",
+                               f"d{cfg.d}_m{cfg.m}_conv{cfg.conv_width}_iters{cfg.pinv_iters}"
+                               + ("_ragged" if lengths else ""),
                    "B": cfg.B, "H": cfg.H, "n": cfg.n, "d": cfg.d, "m": cfg.m,
                    "conv_width": cfg.conv_width, "pinv_iters": cfg.pinv_iters,
-                   "inputs": "two alternating seeded N(0,1) sets"},
+                   "inputs": "two alternating seeded N(0,1) sets",
+                   **({"lengths": lengths} if lengths else {})},
         "roofline": {"kernel": STAGE_KERNEL[dom], "bound": "hbm", "achieved": achieved,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic(dom, args.config)},
+                     "traffic": None if lengths else measured_traffic(dom, args.config)},
         "stages_ms": stage_ms,
         "stage_algorithmic_bytes": sbytes,
         "path_roofline": {"bound": "hbm", "compulsory_bytes": path_bytes,
                           "roofline_ms": path_roof_ms, "frac": path_roof_ms / ms},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, sets[0])
+        rec["cpu_baseline"] = cpu_baseline(cfg, sets[0], lengths=lengths)
     att.close()
     print(json.dumps(rec), flush=True)
 

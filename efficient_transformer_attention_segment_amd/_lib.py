@@ -38,6 +38,7 @@ SIGNATURES = {
                                  _c_int, _c_int, _c_int, _c_int]),
     "nys_attn_forward": (_c_int, [_c_void_p] * 7),
     "nys_attn_forward_debug": (_c_int, [_c_void_p] * 7 + [ctypes.POINTER(Taps)]),
+    "nys_attn_forward_varlen": (_c_int, [_c_void_p] * 8 + [ctypes.POINTER(Taps)]),
     "nys_attn_workspace_bytes": (_c_size_t, [_c_void_p]),
     "nys_attn_profile_enable": (_c_int, [_c_void_p, _c_int]),
     "nys_attn_profile_read": (_c_int, [_c_void_p, ctypes.POINTER(ctypes.c_float), _c_int,
@@ -98,6 +99,13 @@ def nys_attn_forward_debug(plan, q, k, v, conv_w, out, stream, taps: Taps | None
     _check(_LIB.nys_attn_forward_debug(plan, q, k, v, conv_w, out, stream,
                                        ctypes.byref(taps) if taps is not None else None),
            "nys_attn_forward_debug")
+
+
+def nys_attn_forward_varlen(plan, q, k, v, conv_w, lengths, out, stream,
+                            taps: Taps | None = None) -> None:
+    _check(_LIB.nys_attn_forward_varlen(plan, q, k, v, conv_w, lengths, out, stream,
+                                        ctypes.byref(taps) if taps is not None else None),
+           "nys_attn_forward_varlen")
 
 
 def nys_attn_workspace_bytes(plan) -> int:
@@ -172,7 +180,10 @@ class NystromAttention:
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
 
-    def forward(self, q, k, v, conv_w, out=None, taps: dict | None = None):
+    def forward(self, q, k, v, conv_w, out=None, taps: dict | None = None, lengths=None):
+        """``lengths``: valid length per batch element of a padded batch, as an int32
+        device tensor [B] (passed through) or a host sequence / CPU tensor (checked to
+        lie in [m, n], then copied to the device); None means all n."""
         import torch
         dt = self._torch_dtype()
         for name, t in (("q", q), ("k", k), ("v", v)):
@@ -183,18 +194,33 @@ class NystromAttention:
         else:
             self._check("out", out, self.shape, dt)
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        args = (self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), conv_w.data_ptr(),
-                out.data_ptr(), stream)
-        if taps is None:
-            nys_attn_forward(*args)
-        else:
+        lens = None
+        if lengths is not None:
+            if isinstance(lengths, torch.Tensor) and lengths.device.type == "cuda":
+                self._check("lengths", lengths, (self.shape[0],), torch.int32)
+                lens = lengths
+            else:
+                vals = [int(x) for x in lengths]
+                if len(vals) != self.shape[0] or any(not (self.m <= x <= self.shape[2])
+                                                    for x in vals):
+                    raise ValueError(f"lengths must hold {self.shape[0]} values in "
+                                     f"[{self.m}, {self.shape[2]}]")
+                lens = torch.tensor(vals, dtype=torch.int32).to(q.device)
+        t = None
+        if taps is not None:
             t = Taps()
             for key, val in taps.items():
                 if val is not None:
                     if val.dtype != torch.float32 or not val.is_contiguous():
                         raise ValueError(f"tap {key} must be contiguous fp32")
                     setattr(t, key, val.data_ptr())
-            nys_attn_forward_debug(*args, t)
+        args = (self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(), conv_w.data_ptr())
+        if lens is not None:
+            nys_attn_forward_varlen(*args, lens.data_ptr(), out.data_ptr(), stream, t)
+        elif t is None:
+            nys_attn_forward(*args, out.data_ptr(), stream)
+        else:
+            nys_attn_forward_debug(*args, out.data_ptr(), stream, t)
         return out
 
     __call__ = forward

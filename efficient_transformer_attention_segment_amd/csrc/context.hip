@@ -582,7 +582,9 @@ __device__ __forceinline__ void flash_reg_body(const CtxArgs& a, int blk, char* 
   const int mp = a.mp;
   int bh, c;
   xcd_map(blk, a.BH, a.C, bh, c);
-  const int c0 = c * a.chunk, c1 = min(a.n, c0 + a.chunk);
+  // the chunk, cut at the head's valid length (an empty chunk leaves M = -inf, L = 0)
+  const int c0 = c * a.chunk;
+  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), c0 + a.chunk);
   const Tin* K = static_cast<const Tin*>(a.k) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
 
@@ -622,7 +624,7 @@ __device__ __forceinline__ void flash_reg_body(const CtxArgs& a, int blk, char* 
     for (int u = 0; u < NCH; ++u) {
       const int qi = tid + nthreads * u;
       const int row = qi / (D / 8), cf = qi % (D / 8), tok = base + row;
-      vc[u].load(V + (size_t)tok * D + cf * 8, qi < nchunks && tok < a.n);
+      vc[u].load(V + (size_t)tok * D + cf * 8, qi < nchunks && tok < c1);
     }
   };
   auto store_v = [&](const Chunk<Tin>* vc) {
@@ -639,7 +641,7 @@ __device__ __forceinline__ void flash_reg_body(const CtxArgs& a, int blk, char* 
     const int tok = base + 32 * tg + r32;
 #pragma unroll
     for (int s = 0; s < KD; ++s)
-      ka[s] = Input<Tin>::load8(K + (size_t)tok * D + 16 * s + 8 * h, tok < a.n);
+      ka[s] = Input<Tin>::load8(K + (size_t)tok * D + 16 * s + 8 * h, tok < c1);
   };
 
   Chunk<Tin> vc[NCH];
@@ -746,7 +748,9 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
   const int mp = a.mp;
   int bh, c;
   xcd_map(blk, a.BH, a.C, bh, c);
-  const int c0 = c * a.chunk, c1 = min(a.n, c0 + a.chunk);
+  // the chunk, cut at the head's valid length (an empty chunk leaves M = -inf, L = 0)
+  const int c0 = c * a.chunk;
+  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), c0 + a.chunk);
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)bh * a.n * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)bh * a.n * D;
 
@@ -754,7 +758,7 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
   const int NI = a.ring_ni, S = a.ring_stages;
   const int tile_elems = nw * NI * 512;  // 1 KiB (512 bf16) per wave instruction
   const int real = step * CPR;
-  const int nsteps = (c1 - c0 + step - 1) / step;
+  const int nsteps = c1 > c0 ? (c1 - c0 + step - 1) / step : 0;
   uint16_t* ring = reinterpret_cast<uint16_t*>(lds);
   auto issue = [&](int t) {
     const int base = c0 + t * step;

@@ -8,7 +8,8 @@ namespace nys {
 
 // Stage 1: segment means of Q and K.
 struct SegArgs {
-  int BH, n, m, mp, l;
+  const int* lengths;  // [B] valid lengths, or nullptr (all n)
+  int BH, H, n, m, mp;
   float* qt;       // [BH][mp][d]
   float* kt;       // [BH][mp][d]
   uint16_t* qt_hl; // [BH][2][mp][d] hi plane then lo plane
@@ -21,6 +22,7 @@ struct SegArgs {
 struct CtxArgs {
   const void* k;
   const void* v;
+  const int* lengths;     // [B] valid lengths, or nullptr (all n)
   const float* qt;        // [BH][mp][d]  landmarks Qt (fp32)
   const uint16_t* qt_hl;  // [BH][2][mp][d]
   const uint16_t* kt_hl;  // [BH][2][mp][d]
@@ -31,13 +33,20 @@ struct CtxArgs {
   uint16_t* z_hl;         // [BH][2][mp][mp]  final Z, row-major hi/lo
   float* part_w;          // [BH][C][d][mp]   per-chunk unnormalised (Bbar V)^T
   float* part_ml;         // [BH][C][2][mp]   per-chunk running max (log2 units), sum
-  int BH, n, d, m, mp, iters, chunk, C, LG, TG;
+  int BH, H, n, d, m, mp, iters, chunk, C, LG, TG;
   int npinv;              // pseudo-inverse blocks at the front of the context grid (0 or BH)
   int ring_ni;            // bf16 context: 1 KiB LDS-DMA loads per wave per K or V tile
   int ring_stages;        // bf16 context: K/V tiles in the LDS ring (2..4)
   float scale;            // 1/sqrt(d)
   float scale_log2e;      // log2(e)/sqrt(d)
 };
+
+// Valid length of head bh: lengths[bh / H] clamped into [m, n], or n.
+__device__ __forceinline__ int valid_length(const int* lengths, int bh, int H, int n, int m) {
+  if (lengths == nullptr) return n;
+  const int L = lengths[bh / H];
+  return L < m ? m : (L > n ? n : L);
+}
 
 // Number of hi/lo bf16 mp x mp planes per head in CtxArgs::planes.
 constexpr int kPlanes = 18;
@@ -48,6 +57,7 @@ constexpr int kPlanes = 18;
 struct OutArgs {
   const void* q;
   const void* v;
+  const int* lengths;     // [B] valid lengths, or nullptr (all n)
   const float* conv_w;    // [H][W]
   void* out;              // [BH][n][d]
   float* attn_tap;        // [BH][n][d] or nullptr

@@ -65,6 +65,22 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   const int head = bh % a.H;
   const int t_begin = grp * a.tok_per_block;
   const int t_end = min(a.n, t_begin + a.tok_per_block);
+  // tokens at or past the head's valid length are padding: not read (the conv sees
+  // zeros there), written as zeros
+  const int t_valid_v = valid_length(a.lengths, bh, a.H, a.n, a.m);
+  const int t_valid = min(t_end, t_valid_v);
+  if (t_begin >= t_valid) {
+    constexpr int EPV = 16 / sizeof(Tin);  // elements per 16-byte store
+    Tin* o = static_cast<Tin*>(a.out) + ((size_t)bh * a.n + t_begin) * D;
+    for (int e = threadIdx.x; e < (t_end - t_begin) * (D / EPV); e += 256)
+      *reinterpret_cast<u32x4*>(o + (size_t)e * EPV) = u32x4{0u, 0u, 0u, 0u};
+    if (a.attn_tap != nullptr) {
+      float* tp = a.attn_tap + ((size_t)bh * a.n + t_begin) * D;
+      for (int e = threadIdx.x; e < (t_end - t_begin) * (D / 4); e += 256)
+        *reinterpret_cast<f32x4*>(tp + (size_t)e * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    return;
+  }
   // scores in log2 units: folded into Kt when it is staged (NT > 0), else applied here
   const float score_scale = NT > 0 ? 1.f : a.scale_log2e;
 
@@ -94,7 +110,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     for (int u = 0; u < NCH; ++u) {
       const int qi = tid + 256 * u;
       const int row = qi / (D / 8), cf = qi % (D / 8), tok = e0 + row;
-      vc[u].load(V + (size_t)tok * D + cf * 8, qi < EXT * (D / 8) && tok >= 0 && tok < a.n);
+      vc[u].load(V + (size_t)tok * D + cf * 8, qi < EXT * (D / 8) && tok >= 0 && tok < t_valid_v);
     }
   };
   auto store_v = [&](const Chunk<Tin>* vc) {
@@ -111,7 +127,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     const int tq = T0 + 32 * wave + r32;
 #pragma unroll
     for (int s = 0; s < KD; ++s)
-      qb[s] = Input<Tin>::load8(Q + (size_t)tq * D + 16 * s + 8 * h, tq < t_end);
+      qb[s] = Input<Tin>::load8(Q + (size_t)tq * D + 16 * s + 8 * h, tq < t_valid);
   };
   // scores of landmark tile lt (landmarks x tokens)
   auto scores = [&](int lt, const Pair8* qb) -> f32x16 {
@@ -375,6 +391,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     }
     const int tq = T0 + 32 * wave + r32;
     const bool qok = tq < t_end;
+    const bool qpad = t_valid < t_end && tq >= t_valid;  // padding row of a cut block
 
     f32x16 oacc[FT];
 #pragma unroll
@@ -445,6 +462,9 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
       for (int f = 0; f < FT; ++f) oacc[f] *= inv;
     }
 
+    if (qpad)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) oacc[f] = zero16();
     if (a.attn_tap != nullptr && qok) {
       float* tp = a.attn_tap + ((size_t)bh * a.n + tq) * D + (D / 2) * h;
 #pragma unroll
@@ -470,6 +490,9 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
       }
     }
 
+    if (qpad)
+#pragma unroll
+      for (int f = 0; f < FT; ++f) oacc[f] = zero16();
     if (qok) {
       if constexpr (kS) {
         float* op = static_cast<float*>(a.out) + ((size_t)bh * a.n + tq) * D + (D / 2) * h;

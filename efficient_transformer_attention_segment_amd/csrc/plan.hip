@@ -54,7 +54,6 @@ static nys_status validate_shape(int B, int H, int n, int d, int m, int W, int i
   if (n < 1) return fail(NYS_E_ARG, "n must be >= 1");
   if (m < 1 || m > n) return fail(NYS_E_ARG, "need 1 <= m <= n");
   if (m > 256) return fail(NYS_E_UNSUPPORTED, "m > 256 is not built");
-  if (n % m != 0) return fail(NYS_E_UNSUPPORTED, "n must be a multiple of m (equal segments)");
   if (d < 1) return fail(NYS_E_ARG, "d must be >= 1");
   if (d != 32 && d != 64 && d != 128) return fail(NYS_E_UNSUPPORTED, "d must be 32, 64 or 128");
   if (W < 1 || (W % 2) == 0) return fail(NYS_E_ARG, "conv_width must be odd and >= 1");
@@ -118,7 +117,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
 
   nys::CtxArgs& c = p->ctx;
   std::memset(&c, 0, sizeof(c));
-  c.BH = p->BH; c.n = n; c.d = d; c.m = m; c.mp = p->mp; c.iters = pinv_iters;
+  c.BH = p->BH; c.H = H; c.n = n; c.d = d; c.m = m; c.mp = p->mp; c.iters = pinv_iters;
   c.chunk = p->chunk; c.C = p->C; c.LG = p->LG; c.TG = p->TG;
   c.npinv = p->fused ? p->BH : 0;
   nys::context_ring_geometry(d, c);
@@ -177,7 +176,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
   auto U = [&](size_t o) { return reinterpret_cast<uint16_t*>(ws + o); };
 
-  p->seg = nys::SegArgs{p->BH, n, m, p->mp, n / m, F(o_qt), F(o_kt), U(o_qhl), U(o_khl)};
+  p->seg = nys::SegArgs{nullptr, p->BH, H, n, m, p->mp, F(o_qt), F(o_kt), U(o_qhl), U(o_khl)};
 
   c.qt = F(o_qt); c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
   c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.z_hl = U(o_zhl);
@@ -206,7 +205,7 @@ static bool ranges_overlap(const void* a, size_t na, const void* b, size_t nb) {
 }
 
 static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, const void* v,
-                               const float* conv_w, void* out, void* stream,
+                               const float* conv_w, const int* lengths, void* out, void* stream,
                                const nys_attn_taps* taps) {
   if (p == nullptr) return fail(NYS_E_ARG, "plan is NULL");
   if (p->BH == 0) return NYS_OK;
@@ -233,17 +232,21 @@ static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, c
     return true;
   };
   auto mark = [&](int i) { return !prof || chk(hipEventRecord(ev[i], s), "event record"); };
+  nys::SegArgs sg = p->seg;
+  sg.lengths = lengths;
   nys::CtxArgs c = p->ctx;
   c.k = k;
   c.v = v;
+  c.lengths = lengths;
   nys::OutArgs o = p->out;
   o.q = q;
   o.v = v;
   o.conv_w = conv_w;
+  o.lengths = lengths;
   o.out = out;
   o.attn_tap = taps ? taps->attn : nullptr;
   if (!taps || (!taps->w && !taps->y)) o.w_tap = o.y_tap = nullptr;
-  if (!mark(0) || !chk(nys::launch_segmeans(bf16, p->d, q, k, p->seg, s), "segment means launch") ||
+  if (!mark(0) || !chk(nys::launch_segmeans(bf16, p->d, q, k, sg, s), "segment means launch") ||
       !mark(1) || (!p->fused && !chk(nys::launch_pinv(p->d, c, s), "pseudo-inverse launch")) ||
       !mark(2) || !chk(nys::launch_context(bf16, p->d, c, s), "landmark context launch") ||
       !mark(3) || !chk(nys::launch_output(bf16, p->d, p->ks, o, s), "output launch") ||
@@ -279,13 +282,20 @@ static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, c
 extern "C" nys_status nys_attn_forward(nys_attn_plan* plan, const void* q, const void* k,
                                        const void* v, const float* conv_w, void* out,
                                        void* stream) {
-  return forward_impl(plan, q, k, v, conv_w, out, stream, nullptr);
+  return forward_impl(plan, q, k, v, conv_w, nullptr, out, stream, nullptr);
 }
 
 extern "C" nys_status nys_attn_forward_debug(nys_attn_plan* plan, const void* q, const void* k,
                                              const void* v, const float* conv_w, void* out,
                                              void* stream, const nys_attn_taps* taps) {
-  return forward_impl(plan, q, k, v, conv_w, out, stream, taps);
+  return forward_impl(plan, q, k, v, conv_w, nullptr, out, stream, taps);
+}
+
+extern "C" nys_status nys_attn_forward_varlen(nys_attn_plan* plan, const void* q, const void* k,
+                                              const void* v, const float* conv_w,
+                                              const int* lengths, void* out, void* stream,
+                                              const nys_attn_taps* taps) {
+  return forward_impl(plan, q, k, v, conv_w, lengths, out, stream, taps);
 }
 
 extern "C" size_t nys_attn_workspace_bytes(const nys_attn_plan* plan) {

@@ -1,7 +1,10 @@
 // Segment-means landmarks (Nystromformer review page, "Proposed method": landmarks are
 // the means of contiguous token segments, an O(n) step).
 //
-// One wave owns one (matrix in {Q, K}, head, segment j) and streams the segment's l = n/m
+// Segment j of a head with valid length L (n, or the padded batch's length) is rows
+// [ceil(j L / m), ceil((j+1) L / m)): token t belongs to segment floor(t m / L).
+//
+// One wave owns one (matrix in {Q, K}, head, segment j) and streams the segment's
 // contiguous rows: lane L reads 16-byte chunk L % CPR of row L / CPR + RPW * it, so each
 // load instruction covers RPW whole consecutive rows (1 KiB contiguous), and the loads of
 // eight iterations are in flight together. Each lane sums its rows in fp32; lanes that
@@ -30,20 +33,23 @@ __global__ __launch_bounds__(256) void segmeans_kernel(const Tin* __restrict__ q
   const int bh = (int)((task / a.m) % a.BH);
   const int which = (int)(task / ((long long)a.m * a.BH));
   const int c = lane % CPR, r0 = lane / CPR;
+  const int L = valid_length(a.lengths, bh, a.H, a.n, a.m);
+  const int start = (int)(((long long)j * L + a.m - 1) / a.m);
+  const int rows = (int)(((long long)(j + 1) * L + a.m - 1) / a.m) - start;
 
-  const Tin* src = (which ? k : q) + (size_t)bh * a.n * D + (size_t)j * a.l * D + c * EPC;
+  const Tin* src = (which ? k : q) + ((size_t)bh * a.n + start) * D + c * EPC;
   float acc[EPC];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
-  const int nit = (a.l + RPW - 1) / RPW;
+  const int nit = (rows + RPW - 1) / RPW;
 #pragma unroll 8
   for (int it = 0; it < nit; ++it) {
     const int r = r0 + RPW * it;
     float x[8];
     if constexpr (EPC == 8) {
-      Input<Tin>::load_raw(src + (size_t)r * D, r < a.l, x);
+      Input<Tin>::load_raw(src + (size_t)r * D, r < rows, x);
     } else {
-      const f32x4 v = r < a.l ? *reinterpret_cast<const f32x4*>(src + (size_t)r * D)
+      const f32x4 v = r < rows ? *reinterpret_cast<const f32x4*>(src + (size_t)r * D)
                               : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int e = 0; e < 4; ++e) x[e] = v[e];
@@ -58,7 +64,7 @@ __global__ __launch_bounds__(256) void segmeans_kernel(const Tin* __restrict__ q
     for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
   if (lane >= CPR) return;
 
-  const float inv_l = 1.0f / (float)a.l;
+  const float inv_l = 1.0f / (float)rows;
   float mean[8];
 #pragma unroll
   for (int e = 0; e < EPC; ++e) mean[e] = acc[e] * inv_l;

@@ -181,3 +181,14 @@ def make_well_conditioned_square(n: int, d: int, seed: int, scale: float = 0.5,
     v = rng.standard_normal(shape, dtype=np.float32)
     w = conv_weights(rng, H, conv_width)
     return _assemble(cfg, q, k, v, w)
+
+
+def ragged_lengths(cfg: Config, seed: int) -> list:
+    """Valid lengths of a padded batch: one seeded uniform draw per batch element in
+    [max(m, n // 2), n] (a length mix like a bucketed batch of real sequences), with
+    the first element at full length."""
+    rng = np.random.default_rng(seed + 7919)
+    lo = max(cfg.m, cfg.n // 2)
+    lens = [int(x) for x in rng.integers(lo, cfg.n + 1, size=cfg.B)]
+    lens[0] = cfg.n
+    return lens

@@ -5,7 +5,8 @@
  * Self-Attention", section "Proposed method"): for every (batch b, head h) with
  * Q, K, V in R^{n x d} and s = 1/sqrt(d),
  *
- *   Qt, Kt  = segment means of Q, K over m contiguous segments of l = n/m tokens
+ *   Qt, Kt  = segment means of Q, K over m contiguous segments (token t in segment
+ *             floor(t m / n): rows [ceil(j n / m), ceil((j+1) n / m)) form segment j)
  *   F       = softmax_row(s Q Kt^T)          (n x m)
  *   A_S     = softmax_row(s Qt Kt^T)         (m x m)
  *   Bbar    = softmax_row(s Qt K^T)          (m x n)
@@ -63,7 +64,7 @@ typedef struct {
 /* Create a plan for one problem size and allocate its device workspace on the current
  * device.
  *   B, H >= 0 (B*H == 0 is an empty problem: forward does nothing);
- *   n >= 1; 1 <= m <= 256, m <= n, n % m == 0 (else NYS_E_UNSUPPORTED);
+ *   n >= 1; 1 <= m <= 256, m <= n (m need not divide n);
  *   d in {32, 64, 128} (other positive d: NYS_E_UNSUPPORTED);
  *   conv_width odd, 1 <= conv_width <= 65;
  *   0 <= pinv_iters <= 100;  dtype NYS_F32 or NYS_BF16; n*d < 2^31.
@@ -89,6 +90,23 @@ nys_status nys_attn_forward(nys_attn_plan *plan, const void *q, const void *k,
 nys_status nys_attn_forward_debug(nys_attn_plan *plan, const void *q, const void *k,
                                   const void *v, const float *conv_w, void *out,
                                   void *stream, const nys_attn_taps *taps);
+
+/* Forward of a padded batch with per-element valid lengths (padding masks / ragged
+ * batches; the page does not define masking, this entry point takes the reading that a
+ * padded element is the unpadded sequence):
+ *   lengths : device, int32 [B], or NULL for all n. Entry b is the valid length L_b of
+ *             batch element b, m <= L_b <= n; tokens [L_b, n) are padding.
+ * For every head of element b, rows [0, L_b) of out are the forward of the unpadded
+ * length-L_b sequence (segments by floor(t m / L_b); padding tokens are neither keys,
+ * values, landmark members nor conv inputs, and their q, k, v rows are not read) and
+ * rows [L_b, n) are written as zeros. Entries outside [m, n] are clamped into it on the
+ * device so that no access leaves the tensors; their results are unspecified.
+ * taps: as for nys_attn_forward_debug (may be NULL; rows past L_b of taps->attn are
+ * zero, the landmark-sized taps are those of the unpadded sequence).
+ * Other arguments and errors as nys_attn_forward. */
+nys_status nys_attn_forward_varlen(nys_attn_plan *plan, const void *q, const void *k,
+                                   const void *v, const float *conv_w, const int *lengths,
+                                   void *out, void *stream, const nys_attn_taps *taps);
 
 /* Bytes of device workspace the plan owns (0 for a NULL plan). */
 size_t nys_attn_workspace_bytes(const nys_attn_plan *plan);

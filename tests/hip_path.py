@@ -37,8 +37,9 @@ def make_taps(cfg):
                 w=f(BH, m, d), y=f(BH, m, d), attn=f(BH, n, d))
 
 
-def run_hip(x, taps: bool = False, iters: int | None = None, att=None):
-    """Forward on the GPU. Returns (out fp64 [B,H,n,d], taps dict of fp64 arrays)."""
+def run_hip(x, taps: bool = False, iters: int | None = None, att=None, lengths=None):
+    """Forward on the GPU (``lengths``: valid length per batch element, or None).
+    Returns (out fp64 [B,H,n,d], taps dict of fp64 arrays)."""
     import torch
     from efficient_transformer_attention_segment_amd import NystromAttention
     cfg = x.cfg
@@ -48,7 +49,7 @@ def run_hip(x, taps: bool = False, iters: int | None = None, att=None):
         att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, cfg.conv_width, it, cfg.dtype)
     q, k, v, w = upload(x)
     tp = make_taps(cfg) if taps else None
-    out = att.forward(q, k, v, w, taps=tp)
+    out = att.forward(q, k, v, w, taps=tp, lengths=lengths)
     torch.cuda.synchronize()
     o = out.float().cpu().numpy().astype(np.float64)
     t = {key: val.cpu().numpy().astype(np.float64) for key, val in (tp or {}).items()}

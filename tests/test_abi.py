@@ -21,8 +21,8 @@ def declared_functions():
 def test_header_declares_the_api():
     names = declared_functions()
     assert {"nys_attn_create", "nys_attn_forward", "nys_attn_destroy",
-            "nys_attn_forward_debug", "nys_attn_workspace_bytes",
-            "nys_attn_last_error"} <= set(names)
+            "nys_attn_forward_debug", "nys_attn_forward_varlen",
+            "nys_attn_workspace_bytes", "nys_attn_last_error"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -49,7 +49,6 @@ def _create(*args):
     ((1, 1, 64, 32, 8, 33, -1, 1), _lib.NYS_E_ARG),          # iterations < 0
     ((1, 1, 64, 32, 8, 33, 101, 1), _lib.NYS_E_ARG),         # iterations > 100
     ((1, 1, 64, 0, 8, 33, 6, 1), _lib.NYS_E_ARG),            # d = 0
-    ((1, 1, 60, 32, 8, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),   # n % m != 0
     ((1, 1, 64, 48, 8, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),   # d not built
     ((1, 1, 1024, 32, 512, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),  # m > 256
     ((1, 1, 64, 32, 8, 67, 6, 1), _lib.NYS_E_UNSUPPORTED),   # conv width > 65
@@ -72,15 +71,19 @@ def test_null_safe_entry_points():
     assert L.nys_attn_forward(None, None, None, None, None, None, None) == _lib.NYS_E_ARG
     assert L.nys_attn_forward_debug(None, None, None, None, None, None, None,
                                     None) == _lib.NYS_E_ARG
+    assert L.nys_attn_forward_varlen(None, None, None, None, None, None, None, None,
+                                     None) == _lib.NYS_E_ARG
     assert L.nys_attn_profile_enable(None, 4) == _lib.NYS_E_ARG
     n = ctypes.c_int(0)
     assert L.nys_attn_profile_read(None, None, 0, ctypes.byref(n)) == _lib.NYS_E_ARG
 
 
-def test_valid_shape_without_gpu_reports_device():
+@pytest.mark.parametrize("args", [(1, 1, 64, 32, 8, 33, 6, 1),
+                                  (1, 1, 60, 32, 8, 33, 6, 1)])  # m need not divide n
+def test_valid_shape_without_gpu_reports_device(args):
     import torch
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
-    st, plan = _create(1, 1, 64, 32, 8, 33, 6, 1)
+    st, plan = _create(*args)
     assert st == _lib.NYS_E_DEVICE and plan is None
     assert "device" in _lib.nys_attn_last_error()
