@@ -14,3 +14,4 @@ from .nystrom import (  # noqa: F401
     segment_means,
     softmax_rows,
 )
+from .projections import nystrom_layer, out_project, qkv_project  # noqa: F401
