@@ -196,6 +196,9 @@ def main():
     ap.add_argument("--ragged", action="store_true",
                     help="padded batch: seeded valid lengths in [n/2, n] per batch element "
                          "(tokens/s then counts valid tokens)")
+    ap.add_argument("--layer", type=int, metavar="D", default=0,
+                    help="time the projected layer instead: Q/K/V projection from model "
+                         "width D, the forward, and the output projection back to D")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -234,8 +237,10 @@ def main():
     from efficient_transformer_attention_segment_amd import inputs as gen
 
     cfg = gen.CONFIGS[args.config]
-    sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
     torch.cuda.set_device(0)
+    if args.layer:
+        return layer_bench(args, cfg)
+    sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
 
     def dev(a):
         if cfg.dtype == gen.BF16:
@@ -322,6 +327,111 @@ def main():
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, sets[0], lengths=lengths)
     att.close()
+    print(json.dumps(rec), flush=True)
+
+
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def proj_roofline(flops: float, nbytes: float, ms: float) -> dict:
+    """Roofline of one projection GEMM: whichever of dense bf16 MFMA and HBM takes
+    longer at peak binds."""
+    t_mfma = flops / (MFMA_BF16_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBS * 1e9)
+    if t_mfma >= t_hbm:
+        a = flops / (ms * 1e-3) / 1e12
+        return {"bound": "mfma", "achieved": a, "peak": MFMA_BF16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": a / MFMA_BF16_PEAK_TFLOPS}
+    a = nbytes / (ms * 1e-3) / 1e9
+    return {"bound": "hbm", "achieved": a, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": a / HBM_PEAK_GBS}
+
+
+def layer_bench(args, cfg):
+    """Steps of the projected layer: x [B n][D] -> Q, K, V (bf16 GEMM) -> Nystrom
+    forward -> output projection -> y [B n][D]. Per-kernel times come from torch events
+    on the stream the projections are launched on (torch's current stream) and from the
+    library's own stage events for the core."""
+    import torch
+    from efficient_transformer_attention_segment_amd import NystromLayer, nys_proj_out, nys_proj_qkv
+    from efficient_transformer_attention_segment_amd import inputs as gen
+    D = args.layer
+    sets = [gen.make_layer_inputs(cfg, D), gen.make_layer_inputs(cfg, D, seed=cfg.seed + 1000)]
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    dev_sets = [(dev(s.x_dev), dev(s.w_qkv_dev), dev(s.w_o_dev), torch.from_numpy(s.w).cuda())
+                for s in sets]
+    ys = [torch.empty(cfg.B, cfg.n, D, dtype=torch.bfloat16, device="cuda") for _ in sets]
+    layer = NystromLayer(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, D, cfg.conv_width, cfg.pinv_iters)
+
+    def step(i):
+        x, wq, wo, w = dev_sets[i % 2]
+        layer.forward(x, wq, wo, w, y=ys[i % 2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(args.steps):
+        step(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+
+    # per-kernel times: the projections bracketed by events on their own stream, the core
+    # by the library's stage events, over a shorter profiled pass
+    nprof = min(args.steps, 200)
+    B, H, n, d = cfg.B, cfg.H, cfg.n, cfg.d
+    stream = torch.cuda.current_stream().cuda_stream
+    buf = layer._buffers(torch.device("cuda", 0))
+    q, k, v, o = buf[0], buf[1], buf[2], buf[3]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(nprof)]
+    layer.attn.profile_enable(nprof)
+    for i in range(nprof):
+        x, wq, wo, w = dev_sets[i % 2]
+        e = marks[i]
+        e[0].record()
+        nys_proj_qkv(x.data_ptr(), wq.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     B, H, n, d, D, stream)
+        e[1].record()
+        layer.attn.forward(q, k, v, w, out=o)
+        e[2].record()
+        nys_proj_out(o.data_ptr(), wo.data_ptr(), ys[i % 2].data_ptr(), B, H, n, d, D, stream)
+        e[3].record()
+    torch.cuda.synchronize()
+    qkv_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in marks]))
+    out_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in marks]))
+    prof = np.array(layer.attn.profile_read(nprof), dtype=np.float64)
+    stage_ms = {s: float(prof[:, j].mean()) for j, s in enumerate(STAGES)}
+    stage_ms["qkv_proj"], stage_ms["out_proj"] = qkv_ms, out_ms
+
+    M, HD = B * n, H * d
+    qkv_flops, out_flops = 2.0 * M * 3 * HD * D, 2.0 * M * D * HD
+    qkv_bytes = 2.0 * (M * D + 3 * HD * D + 3 * M * HD)   # read x, w_qkv; write q, k, v
+    out_bytes = 2.0 * (M * HD + D * HD + M * D)           # read o, w_o; write y
+    qkv_roof = proj_roofline(qkv_flops, qkv_bytes, qkv_ms)
+    out_roof = proj_roofline(out_flops, out_bytes, out_ms)
+    value = cfg.tokens / (ms * 1e-3)
+    rec = {
+        "metric": "Nystrom layer (projections + attention) fwd tokens/s",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"nystrom_layer_B{B}_H{H}_n{n}_d{d}_m{cfg.m}_D{D}_"
+                               f"conv{cfg.conv_width}_iters{cfg.pinv_iters}",
+                   "B": B, "H": H, "n": n, "d": d, "m": cfg.m, "d_model": D,
+                   "inputs": "two alternating seeded sets: x ~ N(0,1), weights ~ "
+                             "N(0, 1/fan_in)"},
+        "roofline": {"kernel": "qkv_proj_kernel", **qkv_roof,
+                     "flops": qkv_flops, "algorithmic_bytes": qkv_bytes, "traffic": None},
+        "out_proj_roofline": {"kernel": "out_proj_kernel", **out_roof,
+                              "flops": out_flops, "algorithmic_bytes": out_bytes},
+        "stages_ms": stage_ms,
+    }
+    layer.close()
     print(json.dumps(rec), flush=True)
 
 

@@ -43,6 +43,8 @@ SIGNATURES = {
     "nys_attn_profile_enable": (_c_int, [_c_void_p, _c_int]),
     "nys_attn_profile_read": (_c_int, [_c_void_p, ctypes.POINTER(ctypes.c_float), _c_int,
                                        ctypes.POINTER(_c_int)]),
+    "nys_proj_qkv": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 + [_c_void_p]),
+    "nys_proj_out": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p]),
     "nys_attn_destroy": (None, [_c_void_p]),
     "nys_attn_last_error": (ctypes.c_char_p, []),
 }
@@ -130,6 +132,14 @@ def nys_attn_profile_read(plan, max_calls: int):
 
 def nys_attn_destroy(plan) -> None:
     _LIB.nys_attn_destroy(plan)
+
+
+def nys_proj_qkv(x, w_qkv, q, k, v, B, H, n, d, d_model, stream) -> None:
+    _check(_LIB.nys_proj_qkv(x, w_qkv, q, k, v, B, H, n, d, d_model, stream), "nys_proj_qkv")
+
+
+def nys_proj_out(o, w_o, y, B, H, n, d, d_model, stream) -> None:
+    _check(_LIB.nys_proj_out(o, w_o, y, B, H, n, d, d_model, stream), "nys_proj_out")
 
 
 # ------------------------------------------------------------------ torch wrapper
@@ -230,3 +240,50 @@ class NystromAttention:
 
     def profile_read(self, max_calls: int):
         return nys_attn_profile_read(self.plan, max_calls)
+
+
+class NystromLayer:
+    """Projections around the core: ``y = out_proj(attention(qkv_proj(x)))`` with
+    x, y [B, n, D] bf16, w_qkv [3 H d, D], w_o [D, H d] bf16 and conv weights [H, W]
+    fp32. Three calls of the C ABI on torch's current stream; q, k, v and the heads'
+    output live in buffers this object owns (4 B H n d bf16 elements)."""
+
+    def __init__(self, B, H, n, d, m, d_model, conv_width=33, pinv_iters=6):
+        import torch
+        self.attn = NystromAttention(B, H, n, d, m, conv_width, pinv_iters, "bf16")
+        self.B, self.H, self.n, self.d, self.D = B, H, n, d, d_model
+        self._buf = None
+        self._torch = torch
+
+    def close(self):
+        self.attn.close()
+        self._buf = None
+
+    def _buffers(self, device):
+        torch = self._torch
+        if self._buf is None or self._buf.device != device:
+            self._buf = torch.empty((4, self.B, self.H, self.n, self.d), dtype=torch.bfloat16,
+                                    device=device)
+        return self._buf
+
+    def forward(self, x, w_qkv, w_o, conv_w, y=None, lengths=None):
+        torch = self._torch
+        B, H, n, d, D = self.B, self.H, self.n, self.d, self.D
+        chk = self.attn._check
+        chk("x", x, (B, n, D), torch.bfloat16)
+        chk("w_qkv", w_qkv, (3 * H * d, D), torch.bfloat16)
+        chk("w_o", w_o, (D, H * d), torch.bfloat16)
+        if y is None:
+            y = torch.empty((B, n, D), dtype=torch.bfloat16, device=x.device)
+        else:
+            chk("y", y, (B, n, D), torch.bfloat16)
+        buf = self._buffers(x.device)
+        q, k, v, o = buf[0], buf[1], buf[2], buf[3]
+        stream = torch.cuda.current_stream(x.device).cuda_stream
+        nys_proj_qkv(x.data_ptr(), w_qkv.data_ptr(), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                     B, H, n, d, D, stream)
+        self.attn.forward(q, k, v, conv_w, out=o, lengths=lengths)
+        nys_proj_out(o.data_ptr(), w_o.data_ptr(), y.data_ptr(), B, H, n, d, D, stream)
+        return y
+
+    __call__ = forward

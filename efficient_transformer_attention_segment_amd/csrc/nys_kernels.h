@@ -72,6 +72,22 @@ struct OutArgs {
   float scale_log2e;
 };
 
+// Projections around the core (bf16): q, k, v = split_heads(x w_qkv^T) and
+// y = concat_heads(o) w_o^T.
+struct ProjArgs {
+  const void* a;     // x [B n][D] (qkv) or o [B][H][n][d] (out)
+  const void* w;     // w_qkv [3 H d][D] or w_o [D][H d]
+  void* q;           // qkv outputs [B][H][n][d]
+  void* k;
+  void* v;
+  void* y;           // out output [B n][D]
+  int B, H, n, d, D;
+};
+hipError_t launch_qkv_proj(const ProjArgs& a, hipStream_t s);
+hipError_t launch_out_proj(const ProjArgs& a, hipStream_t s);
+size_t proj_lds_bytes();
+hipError_t configure_proj();
+
 hipError_t launch_segmeans(bool bf16, int d, const void* q, const void* k, const SegArgs& a,
                            hipStream_t s);
 // Separate pseudo-inverse launch, used only when it is not fused (mp > 64).

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <mutex>
 #include <cmath>
 #include <cstdint>
 #include <cstdlib>
@@ -345,6 +346,85 @@ extern "C" void nys_attn_destroy(nys_attn_plan* p) {
   for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
   if (p->ws) (void)hipFree(p->ws);
   delete p;
+}
+
+// ------------------------------------------------------------------ projections
+static nys_status proj_checks(int B, int H, int n, int d, int d_model) {
+  if (B < 1 || H < 1 || n < 1) return fail(NYS_E_ARG, "B, H and n must be >= 1");
+  if (d < 1 || d_model < 1) return fail(NYS_E_ARG, "d and d_model must be >= 1");
+  if (d != 32 && d != 64 && d != 128) return fail(NYS_E_UNSUPPORTED, "d must be 32, 64 or 128");
+  if (d_model % 64 != 0) return fail(NYS_E_UNSUPPORTED, "d_model must be a multiple of 64");
+  if ((H * d) % 64 != 0) return fail(NYS_E_UNSUPPORTED, "H*d must be a multiple of 64");
+  const long long wide = std::max<long long>(d_model, 3LL * H * d);
+  if ((long long)B * n * wide >= (1LL << 31)) return fail(NYS_E_UNSUPPORTED, "tensor too large");
+  return NYS_OK;
+}
+
+static nys_status proj_device() {
+  static std::once_flag once;
+  static nys_status status = NYS_OK;
+  static std::string why;
+  std::call_once(once, [] {
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+      (void)hipGetLastError();
+      status = NYS_E_DEVICE;
+      why = "no HIP device available";
+      return;
+    }
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      status = NYS_E_DEVICE;
+      why = "device is not gfx950";
+      return;
+    }
+    if (nys::configure_proj() != hipSuccess) {
+      (void)hipGetLastError();
+      status = NYS_E_LAUNCH;
+      why = "could not set projection kernel LDS limits";
+    }
+  });
+  return status == NYS_OK ? NYS_OK : fail(status, why);
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+extern "C" nys_status nys_proj_qkv(const void* x, const void* w_qkv, void* q, void* k, void* v,
+                                   int B, int H, int n, int d, int d_model, void* stream) {
+  nys_status st = proj_checks(B, H, n, d, d_model);
+  if (st != NYS_OK) return st;
+  if (!x || !w_qkv || !q || !k || !v) return fail(NYS_E_ARG, "NULL tensor pointer");
+  if (!aligned16(x) || !aligned16(w_qkv) || !aligned16(q) || !aligned16(k) || !aligned16(v))
+    return fail(NYS_E_ARG, "tensors must be 16-byte aligned");
+  const size_t xb = (size_t)B * n * d_model * 2, hb = (size_t)B * H * n * d * 2;
+  for (const void* o : {q, k, v})
+    if (ranges_overlap(o, hb, x, xb) || ranges_overlap(o, hb, w_qkv, (size_t)3 * H * d * d_model * 2))
+      return fail(NYS_E_ARG, "q, k, v must not overlap x or w_qkv");
+  if ((st = proj_device()) != NYS_OK) return st;
+  const nys::ProjArgs a{x, w_qkv, q, k, v, nullptr, B, H, n, d, d_model};
+  const hipError_t e = nys::launch_qkv_proj(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NYS_E_LAUNCH, std::string("qkv projection launch: ") + hipGetErrorString(e));
+  return NYS_OK;
+}
+
+extern "C" nys_status nys_proj_out(const void* o, const void* w_o, void* y, int B, int H, int n,
+                                   int d, int d_model, void* stream) {
+  nys_status st = proj_checks(B, H, n, d, d_model);
+  if (st != NYS_OK) return st;
+  if (!o || !w_o || !y) return fail(NYS_E_ARG, "NULL tensor pointer");
+  if (!aligned16(o) || !aligned16(w_o) || !aligned16(y))
+    return fail(NYS_E_ARG, "tensors must be 16-byte aligned");
+  const size_t yb = (size_t)B * n * d_model * 2;
+  if (ranges_overlap(y, yb, o, (size_t)B * H * n * d * 2) ||
+      ranges_overlap(y, yb, w_o, (size_t)d_model * H * d * 2))
+    return fail(NYS_E_ARG, "y must not overlap o or w_o");
+  if ((st = proj_device()) != NYS_OK) return st;
+  const nys::ProjArgs a{o, w_o, nullptr, nullptr, nullptr, y, B, H, n, d, d_model};
+  const hipError_t e = nys::launch_out_proj(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return fail(NYS_E_LAUNCH, std::string("output projection launch: ") + hipGetErrorString(e));
+  return NYS_OK;
 }
 
 extern "C" const char* nys_attn_last_error(void) { return g_err.c_str(); }

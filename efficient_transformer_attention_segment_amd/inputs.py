@@ -192,3 +192,35 @@ def ragged_lengths(cfg: Config, seed: int) -> list:
     lens = [int(x) for x in rng.integers(lo, cfg.n + 1, size=cfg.B)]
     lens[0] = cfg.n
     return lens
+
+
+@dataclass
+class LayerInputs:
+    """Seeded inputs of the projected layer: x [B, n, D], w_qkv [3 H d, D], w_o [D, H d]
+    as bf16 bit patterns (``*_dev``) and their exact float64 values, plus conv weights
+    [H, W] fp32."""
+    cfg: Config
+    D: int
+    x: np.ndarray
+    w_qkv: np.ndarray
+    w_o: np.ndarray
+    w: np.ndarray
+    x_dev: np.ndarray
+    w_qkv_dev: np.ndarray
+    w_o_dev: np.ndarray
+
+
+def make_layer_inputs(cfg: Config, D: int | None = None, seed: int | None = None) -> LayerInputs:
+    """x ~ N(0, 1); weights ~ N(0, 1/fan_in) (Q, K, V and the output then have unit
+    variance per feature, like the core's own iid inputs); conv weights as
+    ``conv_weights``. D defaults to H d. Draw order: x, w_qkv, w_o, conv weights;
+    generator ``numpy.random.default_rng(seed + 104729)``."""
+    D = cfg.H * cfg.d if D is None else D
+    HD = cfg.H * cfg.d
+    rng = np.random.default_rng((cfg.seed if seed is None else seed) + 104729)
+    x = rng.standard_normal((cfg.B, cfg.n, D), dtype=np.float32)
+    wq = rng.standard_normal((3 * HD, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(D))
+    wo = rng.standard_normal((D, HD), dtype=np.float32) * np.float32(1.0 / np.sqrt(HD))
+    w = conv_weights(rng, cfg.H, cfg.conv_width)
+    (xd, x64), (wqd, wq64), (wod, wo64) = (_quantize(a, BF16) for a in (x, wq, wo))
+    return LayerInputs(cfg, D, x64, wq64, wo64, w, xd, wqd, wod)

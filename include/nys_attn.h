@@ -108,6 +108,29 @@ nys_status nys_attn_forward_varlen(nys_attn_plan *plan, const void *q, const voi
                                    const void *v, const float *conv_w, const int *lengths,
                                    void *out, void *stream, const nys_attn_taps *taps);
 
+/* Projections around the attention core (Fastformer review page, "Proposed method": the
+ * input embeddings become Q, K, V through linear projections per head), bf16 in and out,
+ * fp32 accumulation. No plan: these are plain products on the given stream.
+ *
+ * nys_proj_qkv: for each head h, q[b][h] = x[b] Wq_h^T, k[b][h] = x[b] Wk_h^T,
+ * v[b][h] = x[b] Wv_h^T, where Wq_h, Wk_h, Wv_h are the d rows of w_qkv starting at
+ * h*d, (H + h)*d and (2H + h)*d.
+ *   x     : device bf16 [B][n][d_model]
+ *   w_qkv : device bf16 [3*H*d][d_model] ([out_features][in_features])
+ *   q,k,v : device bf16 [B][H][n][d], written (the layout nys_attn_forward reads)
+ * nys_proj_out: y[b][t][:] = concat_h(o[b][h][t][:]) w_o^T (head h at features h*d..).
+ *   o     : device bf16 [B][H][n][d]
+ *   w_o   : device bf16 [d_model][H*d]
+ *   y     : device bf16 [B][n][d_model], written
+ * Preconditions: B, H, n >= 1; d in {32, 64, 128}; d_model >= 64 and a multiple of 64;
+ * H*d a multiple of 64; all pointers 16-byte aligned, outputs not overlapping inputs;
+ * B*n*max(d_model, 3*H*d) < 2^31. Asynchronous like nys_attn_forward.
+ * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED, NYS_E_DEVICE, NYS_E_LAUNCH. */
+nys_status nys_proj_qkv(const void *x, const void *w_qkv, void *q, void *k, void *v, int B,
+                        int H, int n, int d, int d_model, void *stream);
+nys_status nys_proj_out(const void *o, const void *w_o, void *y, int B, int H, int n, int d,
+                        int d_model, void *stream);
+
 /* Bytes of device workspace the plan owns (0 for a NULL plan). */
 size_t nys_attn_workspace_bytes(const nys_attn_plan *plan);
 

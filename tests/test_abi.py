@@ -15,14 +15,15 @@ HEADER = os.path.join(ROOT, "include", "nys_attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nys_attn_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(nys_(?:attn|proj)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_api():
     names = declared_functions()
     assert {"nys_attn_create", "nys_attn_forward", "nys_attn_destroy",
             "nys_attn_forward_debug", "nys_attn_forward_varlen",
-            "nys_attn_workspace_bytes", "nys_attn_last_error"} <= set(names)
+            "nys_attn_workspace_bytes", "nys_attn_last_error", "nys_proj_qkv",
+            "nys_proj_out"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -87,3 +88,44 @@ def test_valid_shape_without_gpu_reports_device(args):
     st, plan = _create(*args)
     assert st == _lib.NYS_E_DEVICE and plan is None
     assert "device" in _lib.nys_attn_last_error()
+
+
+# Fake, 16-byte aligned, non-overlapping addresses: the projection entry points validate
+# them on the host and never dereference them before the device check.
+_X, _W, _Q, _K, _V = (0x10000000 * (i + 1) for i in range(5))
+
+
+@pytest.mark.parametrize("dims,status", [
+    ((0, 2, 64, 64, 128), _lib.NYS_E_ARG),           # B = 0
+    ((1, 0, 64, 64, 128), _lib.NYS_E_ARG),           # H = 0
+    ((1, 2, 0, 64, 128), _lib.NYS_E_ARG),            # n = 0
+    ((1, 2, 64, 48, 128), _lib.NYS_E_UNSUPPORTED),   # d not built
+    ((1, 2, 64, 64, 96), _lib.NYS_E_UNSUPPORTED),    # d_model not a multiple of 64
+    ((1, 1, 64, 32, 128), _lib.NYS_E_UNSUPPORTED),   # H d = 32
+    ((4096, 64, 4096, 128, 128), _lib.NYS_E_UNSUPPORTED),  # index range
+])
+def test_projections_reject_bad_shapes(dims, status):
+    L = _lib.lib()
+    assert L.nys_proj_qkv(_X, _W, _Q, _K, _V, *dims, None) == status
+    assert L.nys_proj_out(_X, _W, _Q, *dims, None) == status
+    assert _lib.nys_attn_last_error() != ""
+
+
+def test_projections_reject_bad_pointers():
+    L = _lib.lib()
+    dims = (1, 2, 64, 64, 128)
+    assert L.nys_proj_qkv(None, _W, _Q, _K, _V, *dims, None) == _lib.NYS_E_ARG
+    assert L.nys_proj_qkv(_X, _W, _Q, _K, _V + 8, *dims, None) == _lib.NYS_E_ARG  # misaligned
+    assert L.nys_proj_qkv(_X, _W, _X + 64, _K, _V, *dims, None) == _lib.NYS_E_ARG  # overlap
+    assert L.nys_proj_out(_X, None, _Q, *dims, None) == _lib.NYS_E_ARG
+    assert L.nys_proj_out(_X, _W, _W + 16, *dims, None) == _lib.NYS_E_ARG  # y overlaps w_o
+
+
+def test_projections_valid_shape_without_gpu_reports_device():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    L = _lib.lib()
+    dims = (2, 2, 100, 64, 192)  # ragged M and N tiles
+    assert L.nys_proj_qkv(_X, _W, _Q, _K, _V, *dims, None) == _lib.NYS_E_DEVICE
+    assert L.nys_proj_out(_X, _W, _Q, *dims, None) == _lib.NYS_E_DEVICE
