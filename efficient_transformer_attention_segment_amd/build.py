@@ -30,11 +30,18 @@ FLAGS = [
     "-Wno-unused-command-line-argument",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# The projection GEMMs keep 256 accumulators per lane and only feed them to stores: they
+# belong in AGPRs, so those kernels are built without the VGPR-form setting.
+NO_VGPR_FORM = {"proj.hip"}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    flags = FLAGS
+    if src in NO_VGPR_FORM:
+        i = flags.index("-amdgpu-mfma-vgpr-form=1")
+        flags = flags[:i - 1] + flags[i + 1:]
+    cmd = [HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stdout}\n{r.stderr}")

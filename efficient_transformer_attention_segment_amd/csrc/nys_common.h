@@ -273,6 +273,22 @@ __device__ __forceinline__ void wait_dma_barrier(int n) {
   }
 }
 
+// As wait_dma_barrier, and also wait for this wave's outstanding LDS reads first, so
+// that after the barrier no wave still reads the stage a following DMA may overwrite.
+// n is 0, 8, 16 or 24.
+template <int N>
+__device__ __forceinline__ void wait_vm_lds_barrier_n() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lds_dma_barrier(int n) {
+  switch (n) {
+    case 8: wait_vm_lds_barrier_n<8>(); break;
+    case 16: wait_vm_lds_barrier_n<16>(); break;
+    case 24: wait_vm_lds_barrier_n<24>(); break;
+    default: wait_vm_lds_barrier_n<0>(); break;
+  }
+}
+
 // 16-byte chunk permutation of row-major bf16 tiles with cpr chunks per row (4, 8 or
 // 16): chunk c of row r is stored at chunk c ^ chunk_key(r). With it, eight consecutive
 // rows read at one chunk (16-byte operand fetches) hit eight distinct 16-byte bank
