@@ -15,3 +15,4 @@ from .nystrom import (  # noqa: F401
     softmax_rows,
 )
 from .projections import nystrom_layer, out_project, qkv_project  # noqa: F401
+from .backward import nystrom_backward  # noqa: F401
