@@ -9,7 +9,7 @@ _EXPORTS = {
     "nys_attn_forward_debug", "nys_attn_workspace_bytes", "nys_attn_profile_enable",
     "nys_attn_profile_read", "nys_attn_destroy", "nys_attn_last_error", "Taps",
     "NYS_F32", "NYS_BF16", "nys_attn_forward_varlen", "nys_proj_qkv", "nys_proj_out",
-    "NystromLayer",
+    "NystromLayer", "nys_attn_backward",
 }
 
 

@@ -43,6 +43,7 @@ SIGNATURES = {
     "nys_attn_profile_enable": (_c_int, [_c_void_p, _c_int]),
     "nys_attn_profile_read": (_c_int, [_c_void_p, ctypes.POINTER(ctypes.c_float), _c_int,
                                        ctypes.POINTER(_c_int)]),
+    "nys_attn_backward": (_c_int, [_c_void_p] * 12),
     "nys_proj_qkv": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 + [_c_void_p]),
     "nys_proj_out": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p]),
     "nys_attn_destroy": (None, [_c_void_p]),
@@ -132,6 +133,12 @@ def nys_attn_profile_read(plan, max_calls: int):
 
 def nys_attn_destroy(plan) -> None:
     _LIB.nys_attn_destroy(plan)
+
+
+def nys_attn_backward(plan, q, k, v, conv_w, lengths, dout, dq, dk, dv, dconv_w,
+                      stream) -> None:
+    _check(_LIB.nys_attn_backward(plan, q, k, v, conv_w, lengths, dout, dq, dk, dv, dconv_w,
+                                  stream), "nys_attn_backward")
 
 
 def nys_proj_qkv(x, w_qkv, q, k, v, B, H, n, d, d_model, stream) -> None:
@@ -234,6 +241,37 @@ class NystromAttention:
         return out
 
     __call__ = forward
+
+    def _lengths(self, lengths, device):
+        import torch
+        if lengths is None:
+            return None
+        if isinstance(lengths, torch.Tensor) and lengths.device.type == "cuda":
+            self._check("lengths", lengths, (self.shape[0],), torch.int32)
+            return lengths
+        vals = [int(x) for x in lengths]
+        if len(vals) != self.shape[0] or any(not (self.m <= x <= self.shape[2]) for x in vals):
+            raise ValueError(f"lengths must hold {self.shape[0]} values in "
+                             f"[{self.m}, {self.shape[2]}]")
+        return torch.tensor(vals, dtype=torch.int32).to(device)
+
+    def backward(self, q, k, v, conv_w, dout, lengths=None):
+        """Gradients of sum(out * dout): returns (dq, dk, dv, dconv_w) as new tensors
+        (bf16 [B, H, n, d] and fp32 [H, W]); enqueued on torch's current stream."""
+        import torch
+        dt = self._torch_dtype()
+        for name, t in (("q", q), ("k", k), ("v", v), ("dout", dout)):
+            self._check(name, t, self.shape, dt)
+        self._check("conv_w", conv_w, (self.shape[1], self.conv_width), torch.float32)
+        dq, dk, dv = (torch.empty(self.shape, dtype=dt, device=q.device) for _ in range(3))
+        dw = torch.empty((self.shape[1], self.conv_width), dtype=torch.float32, device=q.device)
+        lens = self._lengths(lengths, q.device)
+        stream = torch.cuda.current_stream(q.device).cuda_stream
+        nys_attn_backward(self.plan, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                          conv_w.data_ptr(), lens.data_ptr() if lens is not None else None,
+                          dout.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(),
+                          dw.data_ptr(), stream)
+        return dq, dk, dv, dw
 
     def profile_enable(self, max_calls: int):
         nys_attn_profile_enable(self.plan, max_calls)

@@ -1,0 +1,845 @@
+// Backward pass of the Nystrom self-attention forward (Nystromformer review page,
+// "Proposed method", bullets M1..M6): gradients of L = sum(out * dout) with respect to
+// Q, K, V and the depthwise conv weights, bf16 I/O, m <= 64 (mp <= 64).
+//
+// Per (batch, head), with s = 1/sqrt(d), F = softmax(s Q Kt^T) (n x m),
+// A = softmax(s Qt Kt^T) (m x m), B = softmax(s Qt K^T) (m x n), Z = the iterated
+// pseudo-inverse of A, W = B V, Y = Z W, out = F Y + conv(V):
+//
+//   dY = F^T dO                 dF = dO Y^T,  dSF = F o (dF - rowsum(F o dF))
+//   dQ += s dSF Kt              dKt += s dSF^T Q
+//   dZ = dY W^T                 dW = Z^T dY
+//   dA = reverse sweep of the iteration from dZ (plus the alpha term)
+//   dSA = A o (dA - rowsum(A o dA));  dQt += s dSA Kt;  dKt += s dSA^T Qt
+//   dB = dW V^T,  dSB = B o (dB - rowsum(B o dB)) with rowsum(B o dB) = rowsum(dW o W)
+//   dV = B^T dW + conv^T(dO)    dK += s dSB^T Qt    dQt += s dSB K
+//   dQ += dQt[seg(t)] / |seg|   dK += dKt[seg(t)] / |seg|  (segment means)
+//   dw[k] = sum_t dO[t] . V[t + k - (W-1)/2]
+//
+// Kernels, in stream order after the forward's segment-means and context kernels
+// (which leave Qt, Kt and the split-n partial states of B V in the workspace):
+//   bwd_land_fwd_kernel   one block per head: merge W and B's softmax statistics,
+//                         A, alpha, the iteration with every Z_k and X_k saved, Y = Z W
+//   bwd_pass1_kernel      over tokens (Q, dO): dQ's first term, partial dY and dKt
+//   bwd_land_bwd_kernel   one block per head: dZ, dW, the reverse sweep, dA, dSA, dQt,
+//                         dKt, rowsum(dW o W)
+//   bwd_pass2_kernel      over tokens (K, V): dK (complete), B^T dW, partial dQt
+//   bwd_final_kernel      over tokens (dO, V): dQ and dV complete, partial dw
+//   bwd_dw_kernel         dw summed over the batch and token chunks
+//
+// Token passes use v_mfma_f32_32x32x16_bf16 tiles whose operands are k-contiguous rows:
+// token rows straight from HBM (bf16, exact), landmark-sized operands as hi/lo bf16
+// planes (~17 significant bits), per-step transposed copies in LDS for the products
+// that contract over tokens. The m x m steps run in fp32 on the VALU out of LDS.
+#include "nys_common.h"
+#include "nys_kernels.h"
+
+namespace nys {
+
+constexpr int kBwdThreads = 256;  // landmark-sized kernels and the final pass
+
+// ------------------------------------------------------------------ fp32 block products
+// C[M][N] = alpha op(A) op(B) + beta C. op(A) is A stored [M][K] (lda) or, with TA, A
+// stored [K][M]; op(B) is B stored [K][N] (ldb) or, with TB, B stored [N][K]. Each
+// thread owns 4 x 4 outputs (M, N multiples of 4). C must not alias A or B; no barrier.
+template <bool TA, bool TB>
+__device__ void blk_mm(float* C, int ldc, const float* A, int lda, const float* B, int ldb,
+                       int M, int N, int K, float alpha, float beta) {
+  const int nb = N >> 2, total = (M >> 2) * nb;
+  for (int blk = threadIdx.x; blk < total; blk += blockDim.x) {
+    const int i0 = (blk / nb) * 4, j0 = (blk % nb) * 4;
+    float acc[4][4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+    for (int k = 0; k < K; ++k) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) av[r] = TA ? A[k * lda + i0 + r] : A[(i0 + r) * lda + k];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) bv[c] = TB ? B[(j0 + c) * ldb + k] : B[k * ldb + j0 + c];
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        float* p = C + (i0 + r) * ldc + j0 + c;
+        *p = beta != 0.f ? alpha * acc[r][c] + beta * *p : alpha * acc[r][c];
+      }
+  }
+}
+
+// C = b C + a I over the MP x MP block, identity only on the first m diagonal entries.
+__device__ void blk_eye(float* C, int ld, int MP, int m, float a, float b) {
+  for (int e = threadIdx.x; e < MP * MP; e += blockDim.x) {
+    const int i = e / MP, j = e % MP;
+    C[i * ld + j] = b * C[i * ld + j] + ((i == j && i < m) ? a : 0.f);
+  }
+}
+
+__device__ void blk_copy_out(float* dst, int ldd, const float* src, int lds_, int R, int Cc) {
+  for (int e = threadIdx.x; e < R * Cc; e += blockDim.x) {
+    const int i = e / Cc, j = e % Cc;
+    dst[(size_t)i * ldd + j] = src[i * lds_ + j];
+  }
+}
+
+__device__ void blk_copy_in(float* dst, int ldd, const float* src, int lds_, int R, int Cc) {
+  for (int e = threadIdx.x; e < R * Cc; e += blockDim.x) {
+    const int i = e / Cc, j = e % Cc;
+    dst[i * ldd + j] = src[(size_t)i * lds_ + j];
+  }
+}
+
+// hi/lo planes of an fp32 matrix src [R][Cc] (ld lds_): row-major [R][Cc] or transposed
+// [Cc][R] (plane stride R * Cc).
+template <bool kTrans>
+__device__ void blk_split_out(uint16_t* hl, const float* src, int lds_, int R, int Cc) {
+  for (int e = threadIdx.x; e < R * Cc; e += blockDim.x) {
+    const int i = kTrans ? e % R : e / Cc, j = kTrans ? e / R : e % Cc;
+    uint16_t hi, lo;
+    split1(src[(size_t)i * lds_ + j], hi, lo);
+    const size_t o = kTrans ? (size_t)j * R + i : (size_t)i * Cc + j;
+    hl[o] = hi;
+    hl[(size_t)R * Cc + o] = lo;
+  }
+}
+
+// ------------------------------------------------------------------ MFMA row tiles
+// acc += A[32 rows][0:K] B[0:K][32 cols]: lane (h, r32) passes the start of A row r32 and
+// of B^T row r32 (k contiguous); AL / BL say whether a lo plane is present (otherwise the
+// operand is exact bf16 and only the hi pointer is read).
+template <int K, bool AL, bool BL>
+__device__ __forceinline__ f32x16 mma_rows(f32x16 acc, const uint16_t* ahi, const uint16_t* alo,
+                                           const uint16_t* bhi, const uint16_t* blo, int h) {
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const Pair8 x{ld8(ahi + k0 + 8 * h), AL ? ld8(alo + k0 + 8 * h) : zero8()};
+    const Pair8 y{ld8(bhi + k0 + 8 * h), BL ? ld8(blo + k0 + 8 * h) : zero8()};
+    acc = mfma_pair<AL, BL>(x, y, acc);
+  }
+  return acc;
+}
+
+// Token row held by accumulator register rr of lane half h (within a 32-row tile).
+__device__ __forceinline__ int acc_r(int rr, int h) { return 8 * (rr >> 2) + 4 * h + (rr & 3); }
+
+__device__ __forceinline__ int seg_start(int j, int L, int m) {
+  return (int)(((long long)j * L + m - 1) / m);
+}
+
+// ======================================================================= L1
+template <int D, int MP>
+__global__ __launch_bounds__(kBwdThreads) void bwd_land_fwd_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) float smem[];
+  constexpr int LM = MP + 1, LD = D + 1;
+  float* Am = smem;               // [MP][LM]
+  float* Zb = Am + MP * LM;
+  float* Xb = Zb + MP * LM;
+  float* T1 = Xb + MP * LM;
+  float* T2 = T1 + MP * LM;
+  float* Wm = T2 + MP * LM;       // [MP][LD]
+  float* Yb = Wm + MP * LD;       // [MP][LD]
+  float* Qs = Wm;                 // Qt, Kt at the start (dead once A is formed)
+  float* Ks = Yb;
+  __shared__ float colsum[MP], rowsum[MP], sal;
+  const int bh = blockIdx.x, m = a.m, tid = threadIdx.x;
+  const float* qt = a.qt + (size_t)bh * MP * D;
+  const float* kt = a.kt + (size_t)bh * MP * D;
+
+  blk_split_out<true>(a.ktT_hl + (size_t)bh * 2 * D * MP, kt, D, MP, D);
+  blk_split_out<true>(a.qtT_hl + (size_t)bh * 2 * D * MP, qt, D, MP, D);
+  blk_copy_in(Qs, LD, qt, D, MP, D);
+  blk_copy_in(Ks, LD, kt, D, MP, D);
+  __syncthreads();
+  blk_mm<false, true>(Am, LM, Qs, LD, Ks, LD, MP, MP, D, a.scale, 0.f);
+  __syncthreads();
+  if (tid < MP) {  // row softmax over the m landmarks; padding rows and columns zero
+    const int i = tid;
+    float* row = Am + i * LM;
+    if (i < m) {
+      float mx = kNegBig;
+      for (int j = 0; j < m; ++j) mx = fmaxf(mx, row[j]);
+      float sum = 0.f;
+      for (int j = 0; j < m; ++j) {
+        const float e = expf(row[j] - mx);
+        row[j] = e;
+        sum += e;
+      }
+      const float inv = 1.f / sum;
+      for (int j = 0; j < m; ++j) row[j] *= inv;
+    }
+    for (int j = (i < m ? m : 0); j < MP; ++j) row[j] = 0.f;
+  }
+  __syncthreads();
+  if (tid < MP) {
+    float cs = 0.f, rs = 0.f;
+    for (int i = 0; i < MP; ++i) cs += fabsf(Am[i * LM + tid]);
+    for (int j = 0; j < MP; ++j) rs += fabsf(Am[tid * LM + j]);
+    colsum[tid] = cs;
+    rowsum[tid] = rs;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int jc = 0, ir = 0;
+    for (int j = 1; j < m; ++j)
+      if (colsum[j] > colsum[jc]) jc = j;
+    for (int i = 1; i < m; ++i)
+      if (rowsum[i] > rowsum[ir]) ir = i;
+    const float c = colsum[jc], r = rowsum[ir];
+    sal = 1.f / (c * r);
+    a.alpha[4 * bh + 0] = sal;
+    a.alpha[4 * bh + 1] = c;
+    a.alpha[4 * bh + 2] = r;
+    a.alpha[4 * bh + 3] = 0.f;
+    a.amax[2 * bh + 0] = jc;
+    a.amax[2 * bh + 1] = ir;
+  }
+  __syncthreads();
+  const float al = sal;
+  for (int e = tid; e < MP * MP; e += blockDim.x) {
+    const int i = e / MP, j = e % MP;
+    Zb[i * LM + j] = al * Am[j * LM + i];
+  }
+  __syncthreads();
+  const size_t mm2 = (size_t)MP * MP;
+  float* zs = a.zs + (size_t)bh * (a.iters + 1) * mm2;
+  float* xs = a.xs + (size_t)bh * a.iters * mm2;
+  blk_copy_out(zs, MP, Zb, LM, MP, MP);
+  float* Z = Zb;
+  float* Zn = T2;
+  for (int it = 0; it < a.iters; ++it) {
+    blk_mm<false, false>(Xb, LM, Am, LM, Z, LM, MP, MP, MP, 1.f, 0.f);
+    __syncthreads();
+    blk_copy_out(xs + it * mm2, MP, Xb, LM, MP, MP);
+    for (int e = tid; e < MP * MP; e += blockDim.x) {
+      const int i = e / MP, j = e % MP;
+      T1[i * LM + j] = ((i == j && i < m) ? 7.f : 0.f) - Xb[i * LM + j];  // 7I - X
+    }
+    __syncthreads();
+    blk_mm<false, false>(Zn, LM, Xb, LM, T1, LM, MP, MP, MP, -1.f, 0.f);  // -X(7I - X)
+    __syncthreads();
+    blk_eye(Zn, LM, MP, m, 15.f, 1.f);                        // 15I - X(7I - X)
+    __syncthreads();
+    blk_mm<false, false>(T1, LM, Xb, LM, Zn, LM, MP, MP, MP, -1.f, 0.f);
+    __syncthreads();
+    blk_eye(T1, LM, MP, m, 13.f, 1.f);                        // R = 13I - X(...)
+    __syncthreads();
+    blk_mm<false, false>(Zn, LM, Z, LM, T1, LM, MP, MP, MP, 0.25f, 0.f);
+    __syncthreads();
+    float* t = Z;
+    Z = Zn;
+    Zn = t;
+    blk_copy_out(zs + (it + 1) * mm2, MP, Z, LM, MP, MP);
+  }
+  // W = merge of the context partial states (rows >= m zero) and B's statistics
+  const float* pw = a.part_w + (size_t)bh * a.C * D * MP;
+  const float* pml = a.part_ml + (size_t)bh * a.C * 2 * MP;
+  float* stat = a.stat + (size_t)bh * 2 * MP;
+  for (int e = tid; e < MP * D; e += blockDim.x) {
+    const int j = e % MP, f = e / MP;
+    float val = 0.f;
+    if (j < m) {
+      float mx = kNegBig;
+      for (int c = 0; c < a.C; ++c) mx = fmaxf(mx, pml[c * 2 * MP + j]);
+      float ls = 0.f, acc = 0.f;
+      for (int c = 0; c < a.C; ++c) {
+        const float sc = fast_exp2(pml[c * 2 * MP + j] - mx);
+        ls += sc * pml[c * 2 * MP + MP + j];
+        acc += sc * pw[((size_t)c * D + f) * MP + j];
+      }
+      val = acc / ls;
+      if (f == 0) {
+        stat[j] = mx;
+        stat[MP + j] = ls;
+      }
+    } else if (f == 0) {
+      stat[j] = 0.f;
+      stat[MP + j] = 1.f;
+    }
+    Wm[j * LD + f] = val;
+  }
+  __syncthreads();
+  blk_copy_out(a.w + (size_t)bh * MP * D, D, Wm, LD, MP, D);
+  blk_mm<false, false>(Yb, LD, Z, LM, Wm, LD, MP, D, MP, 1.f, 0.f);
+  __syncthreads();
+  blk_split_out<false>(a.y_hl + (size_t)bh * 2 * MP * D, Yb, LD, MP, D);
+  blk_copy_out(a.a_s + (size_t)bh * mm2, MP, Am, LM, MP, MP);
+}
+
+// ======================================================================= pass 1
+template <int D, int MP, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
+  constexpr int T = 32 * NW, LT = MP / 32, FT = D / 32;
+  constexpr int NRED = 2 * LT * FT, RPW = (NRED + NW - 1) / NW;
+  extern __shared__ __align__(16) char lds[];
+  uint16_t* ft_hi = reinterpret_cast<uint16_t*>(lds);  // F^T   [MP][T]
+  uint16_t* ft_lo = ft_hi + MP * T;
+  uint16_t* st_hi = ft_lo + MP * T;                     // dSF^T [MP][T]
+  uint16_t* st_lo = st_hi + MP * T;
+  uint16_t* qT = st_lo + MP * T;                        // Q^T   [D][T]
+  uint16_t* oT = qT + D * T;                            // dO^T  [D][T]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
+  uint16_t* ds_hi = oT + D * T + wave * 2 * 32 * MP;    // dSF   [32][MP] per wave
+  uint16_t* ds_lo = ds_hi + 32 * MP;
+  int bh, c;
+  xcd_map(blockIdx.x, a.BH, a.C, bh, c);
+  const int m = a.m, L = valid_length(a.lengths, bh, a.H, a.n, a.m);
+  const int tb = c * a.chunk, te = min(tb + a.chunk, L);
+  const uint16_t* q = a.q + (size_t)bh * a.n * D;
+  const uint16_t* dO = a.dout + (size_t)bh * a.n * D;
+  const uint16_t* kt_hi = a.kt_hl + (size_t)bh * 2 * MP * D;
+  const uint16_t* kt_lo = kt_hi + MP * D;
+  const uint16_t* y_hi = a.y_hl + (size_t)bh * 2 * MP * D;
+  const uint16_t* y_lo = y_hi + MP * D;
+  const uint16_t* kT_hi = a.ktT_hl + (size_t)bh * 2 * D * MP;
+  const uint16_t* kT_lo = kT_hi + D * MP;
+  float* dqp = a.dq_part + (size_t)bh * a.n * D;
+  const float sl = a.scale_log2e;
+
+  f32x16 red[RPW];
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) red[u] = zero16();
+
+  for (int t0 = tb; t0 < te; t0 += T) {
+    const int tw = t0 + 32 * wave;
+    // transposed copies of this wave's Q and dO rows (zeros past the chunk's valid end)
+    for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
+      const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, tok = tw + i;
+      u32x4 qv{0u, 0u, 0u, 0u}, ov{0u, 0u, 0u, 0u};
+      if (tok < te) {
+        qv = *reinterpret_cast<const u32x4*>(q + (size_t)tok * D + f8);
+        ov = *reinterpret_cast<const u32x4*>(dO + (size_t)tok * D + f8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qT[(f8 + e) * T + 32 * wave + i] = (uint16_t)(qv[e >> 1] >> (16 * (e & 1)));
+        oT[(f8 + e) * T + 32 * wave + i] = (uint16_t)(ov[e >> 1] >> (16 * (e & 1)));
+      }
+    }
+    // S = Q Kt^T and dF = dO Y^T for 32 tokens: lane = landmark, registers = tokens
+    const int trow = min(tw + r32, L - 1);
+    f32x16 sc[LT], df[LT];
+#pragma unroll
+    for (int lt = 0; lt < LT; ++lt) {
+      const size_t kr = (size_t)(32 * lt + r32) * D;
+      sc[lt] = mma_rows<D, false, true>(zero16(), q + (size_t)trow * D, nullptr, kt_hi + kr,
+                                        kt_lo + kr, h);
+      df[lt] = mma_rows<D, false, true>(zero16(), dO + (size_t)trow * D, nullptr, y_hi + kr,
+                                        y_lo + kr, h);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const bool tv = tw + acc_r(rr, h) < te;
+      float x[LT], mx = kNegBig;
+#pragma unroll
+      for (int lt = 0; lt < LT; ++lt) {
+        x[lt] = (32 * lt + r32 < m) ? sc[lt][rr] * sl : kNegBig;
+        mx = fmaxf(mx, x[lt]);
+      }
+      mx = half_max(mx);
+      float sum = 0.f;
+#pragma unroll
+      for (int lt = 0; lt < LT; ++lt) {
+        x[lt] = (32 * lt + r32 < m) ? fast_exp2(x[lt] - mx) : 0.f;
+        sum += x[lt];
+      }
+      const float inv = 1.f / half_sum(sum);
+      float dsum = 0.f;
+#pragma unroll
+      for (int lt = 0; lt < LT; ++lt) {
+        x[lt] *= inv;
+        dsum += x[lt] * df[lt][rr];
+      }
+      dsum = half_sum(dsum);
+#pragma unroll
+      for (int lt = 0; lt < LT; ++lt) {
+        const float f = tv ? x[lt] : 0.f;
+        sc[lt][rr] = f;
+        df[lt][rr] = tv ? f * (df[lt][rr] - dsum) : 0.f;
+      }
+    }
+#pragma unroll
+    for (int lt = 0; lt < LT; ++lt) {
+      store_cols_hl(ft_hi, ft_lo, T, 32 * wave, 32 * lt, sc[lt], lane);
+      store_cols_hl(st_hi, st_lo, T, 32 * wave, 32 * lt, df[lt], lane);
+      store_rows_hl(ds_hi, ds_lo, MP, 0, 32 * lt, df[lt], lane);
+    }
+    // dQ (first term) = s dSF Kt for the wave's 32 tokens
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      const size_t br = (size_t)(32 * ft + r32) * MP;
+      const f32x16 acc = mma_rows<MP, true, true>(zero16(), ds_hi + r32 * MP, ds_lo + r32 * MP,
+                                                  kT_hi + br, kT_lo + br, h);
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int tok = tw + acc_r(rr, h);
+        if (tok < te) dqp[(size_t)tok * D + 32 * ft + r32] = a.scale * acc[rr];
+      }
+    }
+    __syncthreads();
+    // partial dY = F^T dO and dSF^T Q over the step's T tokens
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+      const int ti = wave + NW * u;
+      if (ti < NRED) {
+        const int which = ti / (LT * FT), rem = ti % (LT * FT), at = rem / FT, bt = rem % FT;
+        const uint16_t* ah = (which == 0 ? ft_hi : st_hi) + (32 * at + r32) * T;
+        const uint16_t* alo = (which == 0 ? ft_lo : st_lo) + (32 * at + r32) * T;
+        const uint16_t* bt_ = (which == 0 ? oT : qT) + (32 * bt + r32) * T;
+        red[u] = mma_rows<T, true, false>(red[u], ah, alo, bt_, nullptr, h);
+      }
+    }
+    __syncthreads();
+  }
+  float* part = a.part1 + ((size_t)bh * a.C + c) * 2 * MP * D;
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) {
+    const int ti = wave + NW * u;
+    if (ti < NRED) {
+      const int which = ti / (LT * FT), rem = ti % (LT * FT), at = rem / FT, bt = rem % FT;
+      store_rows_f32(part + (size_t)which * MP * D, D, 32 * at, 32 * bt, red[u], lane);
+    }
+  }
+}
+
+// ======================================================================= L2
+template <int D, int MP>
+__global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) float smem[];
+  constexpr int LM = MP + 1, LD = D + 1;
+  const int bh = blockIdx.x, m = a.m, tid = threadIdx.x;
+  const size_t mm2 = (size_t)MP * MP;
+  __shared__ float sred[kBwdThreads / 64];
+  // phase 1: dY, W, Z_T -> dZ = dY W^T, dW = Z_T^T dY
+  float* rdY = smem;                  // [MP][LD]
+  float* rW = rdY + MP * LD;          // [MP][LD]
+  float* rZ = rW + MP * LD;           // [MP][LM]
+  float* rdZ = rZ + MP * LM;          // [MP][LM]
+  float* rdW = rdZ + MP * LM;         // [MP][LD]
+  const float* p1 = a.part1 + (size_t)bh * a.C * 2 * MP * D;
+  for (int e = tid; e < MP * D; e += blockDim.x) {
+    const int j = e / D, f = e % D;
+    float acc = 0.f;
+    for (int c = 0; c < a.C; ++c) acc += p1[(size_t)c * 2 * MP * D + e];
+    rdY[j * LD + f] = acc;
+  }
+  const float* wg = a.w + (size_t)bh * MP * D;
+  blk_copy_in(rW, LD, wg, D, MP, D);
+  const float* zT = a.zs + ((size_t)bh * (a.iters + 1) + a.iters) * mm2;
+  blk_copy_in(rZ, LM, zT, MP, MP, MP);
+  __syncthreads();
+  blk_mm<false, true>(rdZ, LM, rdY, LD, rW, LD, MP, MP, D, 1.f, 0.f);
+  blk_mm<true, false>(rdW, LD, rZ, LM, rdY, LD, MP, D, MP, 1.f, 0.f);
+  __syncthreads();
+  if (tid < MP) {
+    float acc = 0.f;
+    for (int f = 0; f < D; ++f) acc += rdW[tid * LD + f] * rW[tid * LD + f];
+    a.db[(size_t)bh * MP + tid] = acc;
+  }
+  blk_split_out<false>(a.dw_hl + (size_t)bh * 2 * MP * D, rdW, LD, MP, D);
+  blk_split_out<true>(a.dwT_hl + (size_t)bh * 2 * D * MP, rdW, LD, MP, D);
+  // dZ into registers (the loop's buffers overlap phase 1)
+  constexpr int PER = (MP * MP + kBwdThreads - 1) / kBwdThreads;
+  float g0[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + kBwdThreads * u;
+    g0[u] = e < MP * MP ? rdZ[(e / MP) * LM + e % MP] : 0.f;
+  }
+  __syncthreads();
+  // phase 2: reverse sweep of the iteration
+  float* Am = smem;
+  float* dA = Am + MP * LM;
+  float* G = dA + MP * LM;
+  float* Xb = G + MP * LM;
+  float* Zb = Xb + MP * LM;
+  float* B1 = Zb + MP * LM;
+  float* B2 = B1 + MP * LM;
+  float* B3 = B2 + MP * LM;
+  float* B4 = B3 + MP * LM;
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = tid + kBwdThreads * u;
+    if (e < MP * MP) G[(e / MP) * LM + e % MP] = g0[u];
+  }
+  blk_copy_in(Am, LM, a.a_s + (size_t)bh * mm2, MP, MP, MP);
+  for (int e = tid; e < MP * LM; e += blockDim.x) dA[e] = 0.f;
+  const float* zs = a.zs + (size_t)bh * (a.iters + 1) * mm2;
+  const float* xs = a.xs + (size_t)bh * a.iters * mm2;
+  for (int it = a.iters - 1; it >= 0; --it) {
+    blk_copy_in(Xb, LM, xs + it * mm2, MP, MP, MP);
+    blk_copy_in(Zb, LM, zs + it * mm2, MP, MP, MP);
+    __syncthreads();
+    for (int e = tid; e < MP * MP; e += blockDim.x) {  // P = 7I - X
+      const int i = e / MP, j = e % MP;
+      B1[i * LM + j] = ((i == j && i < m) ? 7.f : 0.f) - Xb[i * LM + j];
+    }
+    __syncthreads();
+    blk_mm<false, false>(B2, LM, Xb, LM, B1, LM, MP, MP, MP, -1.f, 0.f);
+    __syncthreads();
+    blk_eye(B2, LM, MP, m, 15.f, 1.f);                          // Qm = 15I - X P
+    __syncthreads();
+    blk_mm<false, false>(B3, LM, Xb, LM, B2, LM, MP, MP, MP, -1.f, 0.f);
+    __syncthreads();
+    blk_eye(B3, LM, MP, m, 13.f, 1.f);                          // R = 13I - X Qm
+    __syncthreads();
+    blk_mm<false, true>(B4, LM, G, LM, B3, LM, MP, MP, MP, 0.25f, 0.f);   // G_new = G R^T / 4
+    __syncthreads();
+    blk_mm<true, false>(B3, LM, Zb, LM, G, LM, MP, MP, MP, 0.25f, 0.f);   // dR = Z^T G / 4
+    __syncthreads();
+    blk_mm<false, true>(G, LM, B3, LM, B2, LM, MP, MP, MP, -1.f, 0.f);    // dX = -dR Qm^T
+    __syncthreads();
+    blk_mm<true, false>(B2, LM, Xb, LM, B3, LM, MP, MP, MP, -1.f, 0.f);   // dQm = -X^T dR
+    __syncthreads();
+    blk_mm<false, true>(G, LM, B2, LM, B1, LM, MP, MP, MP, -1.f, 1.f);    // dX -= dQm P^T
+    blk_mm<true, false>(B3, LM, Xb, LM, B2, LM, MP, MP, MP, -1.f, 0.f);   // dP = -X^T dQm
+    __syncthreads();
+    for (int e = tid; e < MP * MP; e += blockDim.x) {             // dX -= dP
+      const int i = e / MP, j = e % MP;
+      G[i * LM + j] -= B3[i * LM + j];
+    }
+    __syncthreads();
+    blk_mm<false, true>(dA, LM, G, LM, Zb, LM, MP, MP, MP, 1.f, 1.f);     // dA += dX Z^T
+    blk_mm<true, false>(B4, LM, Am, LM, G, LM, MP, MP, MP, 1.f, 1.f);     // G_new += A^T dX
+    __syncthreads();
+    float* t = G;
+    G = B4;
+    B4 = t;
+  }
+  // Z_0 = alpha A^T: dA += alpha G^T, d alpha = <G, A^T>, alpha = 1 / (c r)
+  const float al = a.alpha[4 * bh], cmax = a.alpha[4 * bh + 1], rmax = a.alpha[4 * bh + 2];
+  const int jc = a.amax[2 * bh], ir = a.amax[2 * bh + 1];
+  float part = 0.f;
+  for (int e = tid; e < MP * MP; e += blockDim.x) {
+    const int i = e / MP, j = e % MP;
+    part += G[i * LM + j] * Am[j * LM + i];
+  }
+  part = wave_sum(part);
+  if ((tid & 63) == 0) sred[tid >> 6] = part;
+  __syncthreads();
+  float dal = 0.f;
+#pragma unroll
+  for (int w = 0; w < kBwdThreads / 64; ++w) dal += sred[w];
+  for (int e = tid; e < MP * MP; e += blockDim.x) {
+    const int i = e / MP, j = e % MP;
+    float v = dA[i * LM + j] + al * G[j * LM + i];
+    if (i < m && j < m) {
+      if (j == jc) v -= dal * al / cmax;
+      if (i == ir) v -= dal * al / rmax;
+    }
+    dA[i * LM + j] = v;
+  }
+  __syncthreads();
+  // dSA = A o (dA - rowsum(A o dA)) into Xb
+  if (tid < MP) {
+    const int i = tid;
+    float rs = 0.f;
+    for (int j = 0; j < MP; ++j) rs += Am[i * LM + j] * dA[i * LM + j];
+    for (int j = 0; j < MP; ++j)
+      Xb[i * LM + j] = (i < m && j < m) ? Am[i * LM + j] * (dA[i * LM + j] - rs) : 0.f;
+  }
+  __syncthreads();
+  // dQt (A_S path) = s dSA Kt -> global; dKt = s dSA^T Qt + s sum_c (dSF^T Q)_c
+  blk_mm<false, false>(a.dqt + (size_t)bh * MP * D, D, Xb, LM, a.kt + (size_t)bh * MP * D, D,
+                       MP, D, MP, a.scale, 0.f);
+  float* rK = B1;  // [MP][LD] over B1.. (dead)
+  for (int e = tid; e < MP * D; e += blockDim.x) {
+    const int j = e / D, f = e % D;
+    float acc = 0.f;
+    for (int c = 0; c < a.C; ++c) acc += p1[(size_t)c * 2 * MP * D + MP * D + e];
+    rK[j * LD + f] = a.scale * acc;
+  }
+  __syncthreads();
+  blk_mm<true, false>(rK, LD, Xb, LM, a.qt + (size_t)bh * MP * D, D, MP, D, MP, a.scale, 1.f);
+  __syncthreads();
+  blk_copy_out(a.dkt + (size_t)bh * MP * D, D, rK, LD, MP, D);
+}
+
+// ======================================================================= pass 2
+template <int D, int MP, int NW>
+__global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
+  constexpr int T = 32 * NW, LT = MP / 32, FT = D / 32;
+  constexpr int NRED = LT * FT, RPW = (NRED + NW - 1) / NW;
+  extern __shared__ __align__(16) char lds[];
+  uint16_t* sT_hi = reinterpret_cast<uint16_t*>(lds);  // dSB^T [MP][T] (landmark rows)
+  uint16_t* sT_lo = sT_hi + MP * T;
+  uint16_t* kT = sT_lo + MP * T;                        // K^T   [D][T]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
+  uint16_t* bm_hi = kT + D * T + wave * 4 * 32 * MP;    // B (token rows) [32][MP]
+  uint16_t* bm_lo = bm_hi + 32 * MP;
+  uint16_t* sb_hi = bm_lo + 32 * MP;                    // dSB (token rows) [32][MP]
+  uint16_t* sb_lo = sb_hi + 32 * MP;
+  int bh, c;
+  xcd_map(blockIdx.x, a.BH, a.C, bh, c);
+  const int m = a.m, L = valid_length(a.lengths, bh, a.H, a.n, a.m);
+  const int tb = c * a.chunk, te = min(tb + a.chunk, L);
+  const uint16_t* kk = a.k + (size_t)bh * a.n * D;
+  const uint16_t* vv = a.v + (size_t)bh * a.n * D;
+  const uint16_t* qt_hi = a.qt_hl + (size_t)bh * 2 * MP * D;
+  const uint16_t* qt_lo = qt_hi + MP * D;
+  const uint16_t* dw_hi = a.dw_hl + (size_t)bh * 2 * MP * D;
+  const uint16_t* dw_lo = dw_hi + MP * D;
+  const uint16_t* qT_hi = a.qtT_hl + (size_t)bh * 2 * D * MP;
+  const uint16_t* qT_lo = qT_hi + D * MP;
+  const uint16_t* wT_hi = a.dwT_hl + (size_t)bh * 2 * D * MP;
+  const uint16_t* wT_lo = wT_hi + D * MP;
+  const float* stat = a.stat + (size_t)bh * 2 * MP;
+  const float* dbv = a.db + (size_t)bh * MP;
+  const float* dkt = a.dkt + (size_t)bh * MP * D;
+  uint16_t* dk = a.dk + (size_t)bh * a.n * D;
+  float* dvp = a.dv_part + (size_t)bh * a.n * D;
+  const float sl = a.scale_log2e;
+  float smx[LT], sinv[LT], sdb[LT];
+#pragma unroll
+  for (int lt = 0; lt < LT; ++lt) {
+    const int j = 32 * lt + r32;
+    smx[lt] = stat[j];
+    sinv[lt] = 1.f / stat[MP + j];
+    sdb[lt] = dbv[j];
+  }
+  f32x16 red[RPW];
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) red[u] = zero16();
+
+  for (int t0 = tb; t0 < te; t0 += T) {
+    const int tw = t0 + 32 * wave;
+    for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
+      const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, tok = tw + i;
+      u32x4 kv{0u, 0u, 0u, 0u};
+      if (tok < te) kv = *reinterpret_cast<const u32x4*>(kk + (size_t)tok * D + f8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        kT[(f8 + e) * T + 32 * wave + i] = (uint16_t)(kv[e >> 1] >> (16 * (e & 1)));
+    }
+    const int trow = min(tw + r32, L - 1);
+    f32x16 sc[LT], db[LT];
+#pragma unroll
+    for (int lt = 0; lt < LT; ++lt) {
+      const size_t lr = (size_t)(32 * lt + r32) * D;
+      sc[lt] = mma_rows<D, false, true>(zero16(), kk + (size_t)trow * D, nullptr, qt_hi + lr,
+                                        qt_lo + lr, h);
+      db[lt] = mma_rows<D, false, true>(zero16(), vv + (size_t)trow * D, nullptr, dw_hi + lr,
+                                        dw_lo + lr, h);
+    }
+#pragma unroll
+    for (int lt = 0; lt < LT; ++lt) {
+      const bool jv = 32 * lt + r32 < m;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const bool v = jv && (tw + acc_r(rr, h) < te);
+        const float b = v ? fast_exp2(sc[lt][rr] * sl - smx[lt]) * sinv[lt] : 0.f;
+        sc[lt][rr] = b;
+        db[lt][rr] = v ? b * (db[lt][rr] - sdb[lt]) : 0.f;
+      }
+      store_rows_hl(bm_hi, bm_lo, MP, 0, 32 * lt, sc[lt], lane);
+      store_rows_hl(sb_hi, sb_lo, MP, 0, 32 * lt, db[lt], lane);
+      store_cols_hl(sT_hi, sT_lo, T, 32 * wave, 32 * lt, db[lt], lane);
+    }
+    // dK = s dSB Qt + dKt[seg] / |seg|  and  B^T dW  for the wave's 32 tokens
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      const size_t br = (size_t)(32 * ft + r32) * MP;
+      const f32x16 gk = mma_rows<MP, true, true>(zero16(), sb_hi + r32 * MP, sb_lo + r32 * MP,
+                                                 qT_hi + br, qT_lo + br, h);
+      const f32x16 gv = mma_rows<MP, true, true>(zero16(), bm_hi + r32 * MP, bm_lo + r32 * MP,
+                                                 wT_hi + br, wT_lo + br, h);
+      const int f = 32 * ft + r32;
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int tok = tw + acc_r(rr, h);
+        if (tok < te) {
+          const int j = (int)(((long long)tok * m) / L);
+          const float len = (float)(seg_start(j + 1, L, m) - seg_start(j, L, m));
+          const float val = a.scale * gk[rr] + dkt[(size_t)j * D + f] / len;
+          dk[(size_t)tok * D + f] = __builtin_bit_cast(uint16_t, bf16_rne(val));
+          dvp[(size_t)tok * D + f] = gv[rr];
+        }
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < RPW; ++u) {
+      const int ti = wave + NW * u;
+      if (ti < NRED) {
+        const int at = ti / FT, bt = ti % FT;
+        red[u] = mma_rows<T, true, false>(red[u], sT_hi + (32 * at + r32) * T,
+                                          sT_lo + (32 * at + r32) * T, kT + (32 * bt + r32) * T,
+                                          nullptr, h);
+      }
+    }
+    __syncthreads();
+  }
+  float* part = a.part2 + ((size_t)bh * a.C + c) * MP * D;
+#pragma unroll
+  for (int u = 0; u < RPW; ++u) {
+    const int ti = wave + NW * u;
+    if (ti < NRED) store_rows_f32(part, D, 32 * (ti / FT), 32 * (ti % FT), red[u], lane);
+  }
+  // padding rows of this chunk: dK = 0
+  const int zb = max(tb, L), ze = min(tb + a.chunk, a.n);
+  for (int e = threadIdx.x; e < (ze > zb ? (ze - zb) * D : 0); e += blockDim.x)
+    dk[(size_t)zb * D + e] = 0;
+}
+
+// ======================================================================= final pass
+constexpr int kFinTok = 128;  // tokens per block
+
+template <int D>
+__global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
+  extern __shared__ __align__(16) char lds[];
+  const int W = a.W, half = (W - 1) / 2, R = kFinTok + W - 1, MP = a.mp, m = a.m;
+  uint16_t* so = reinterpret_cast<uint16_t*>(lds);   // dO rows t0 - half .. [R][D]
+  uint16_t* sv = so + R * D;                         // V rows  t0 - half .. [R][D]
+  float* sq = reinterpret_cast<float*>(sv + R * D);  // dQt / |seg| for the block's segments
+  float* sw = sq + MP * D;                           // conv taps [W]
+  float* sdw = sw + 65;                              // [4][W] per-wave dw sums
+  int bh, c3;
+  xcd_map(blockIdx.x, a.BH, a.C3, bh, c3);
+  const int L = valid_length(a.lengths, bh, a.H, a.n, a.m), hh = bh % a.H;
+  const int t0 = c3 * kFinTok, t1 = min(t0 + kFinTok, a.n), tv = min(t1, L);
+  const uint16_t* dO = a.dout + (size_t)bh * a.n * D;
+  const uint16_t* vv = a.v + (size_t)bh * a.n * D;
+  for (int e = threadIdx.x; e < R * (D / 8); e += blockDim.x) {
+    const int r = e / (D / 8), f8 = (e % (D / 8)) * 8, tok = t0 - half + r;
+    u32x4 ov{0u, 0u, 0u, 0u}, vw{0u, 0u, 0u, 0u};
+    if (tok >= 0 && tok < L) {
+      ov = *reinterpret_cast<const u32x4*>(dO + (size_t)tok * D + f8);
+      vw = *reinterpret_cast<const u32x4*>(vv + (size_t)tok * D + f8);
+    }
+    *reinterpret_cast<u32x4*>(so + r * D + f8) = ov;
+    *reinterpret_cast<u32x4*>(sv + r * D + f8) = vw;
+  }
+  const int j0 = tv > t0 ? (int)(((long long)t0 * m) / L) : 0;
+  const int j1 = tv > t0 ? (int)(((long long)(tv - 1) * m) / L) : -1;
+  const float* dqt = a.dqt + (size_t)bh * MP * D;
+  const float* p2 = a.part2 + (size_t)bh * a.C * MP * D;
+  for (int e = threadIdx.x; e < (j1 - j0 + 1) * D; e += blockDim.x) {
+    const int j = j0 + e / D, f = e % D;
+    float acc = 0.f;
+    for (int c = 0; c < a.C; ++c) acc += p2[((size_t)c * MP + j) * D + f];
+    const float len = (float)(seg_start(j + 1, L, m) - seg_start(j, L, m));
+    sq[(j - j0) * D + f] = (dqt[(size_t)j * D + f] + a.scale * acc) / len;
+  }
+  for (int k = threadIdx.x; k < W; k += blockDim.x) sw[k] = a.conv_w[hh * W + k];
+  __syncthreads();
+  const float* dqp = a.dq_part + (size_t)bh * a.n * D;
+  const float* dvp = a.dv_part + (size_t)bh * a.n * D;
+  uint16_t* dq = a.dq + (size_t)bh * a.n * D;
+  uint16_t* dv = a.dv + (size_t)bh * a.n * D;
+  auto rd = [](const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); };
+  for (int e = threadIdx.x; e < (t1 - t0) * D; e += blockDim.x) {
+    const int i = e / D, f = e % D, t = t0 + i;
+    uint16_t oq = 0, ov = 0;
+    if (t < L) {
+      const int j = (int)(((long long)t * m) / L);
+      oq = __builtin_bit_cast(uint16_t, bf16_rne(dqp[(size_t)t * D + f] + sq[(j - j0) * D + f]));
+      // d out[t'] / d V[t] = w[k] for t' = t - k + half
+      float acc = dvp[(size_t)t * D + f];
+      for (int k = 0; k < W; ++k) acc += sw[k] * rd(so + (i + 2 * half - k) * D + f);
+      ov = __builtin_bit_cast(uint16_t, bf16_rne(acc));
+    }
+    dq[(size_t)t * D + f] = oq;
+    dv[(size_t)t * D + f] = ov;
+  }
+  // partial dw[k] = sum over the block's valid tokens t and features of dO[t] V[t + k - half]
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int k = 0; k < W; ++k) {
+    float p = 0.f;
+    for (int e = threadIdx.x; e < (tv > t0 ? (tv - t0) * D : 0); e += blockDim.x) {
+      const int i = e / D, f = e % D;
+      p += rd(so + (i + half) * D + f) * rd(sv + (i + k) * D + f);
+    }
+    p = wave_sum(p);
+    if (lane == 0) sdw[wave * W + k] = p;
+  }
+  __syncthreads();
+  for (int k = threadIdx.x; k < W; k += blockDim.x) {
+    float s = 0.f;
+    for (int w = 0; w < kBwdThreads / 64; ++w) s += sdw[w * W + k];
+    a.part_dw[((size_t)bh * a.C3 + c3) * W + k] = s;
+  }
+}
+
+__global__ void bwd_dw_kernel(BwdArgs a) {
+  const int hh = blockIdx.x;
+  for (int k = threadIdx.x; k < a.W; k += blockDim.x) {
+    float s = 0.f;
+    for (int b = 0; b < a.B; ++b)
+      for (int c = 0; c < a.C3; ++c) s += a.part_dw[(((size_t)b * a.H + hh) * a.C3 + c) * a.W + k];
+    a.dconv_w[hh * a.W + k] = s;
+  }
+}
+
+// ======================================================================= host side
+template <int D, int MP>
+struct BwdShape {
+  static constexpr int NW = D == 128 ? 2 : 4;
+  static constexpr int T = 32 * NW;
+  static constexpr size_t l1 = (5 * MP * (MP + 1) + 2 * MP * (D + 1)) * 4;
+  static constexpr size_t l2a = 9 * MP * (MP + 1), l2b = 3 * MP * (D + 1) + 2 * MP * (MP + 1);
+  static constexpr size_t l2 = (l2a > l2b ? l2a : l2b) * 4;
+  static constexpr size_t p1 = ((size_t)4 * MP * T + 2 * D * T + NW * 2 * 32 * MP) * 2;
+  static constexpr size_t p2 = ((size_t)2 * MP * T + D * T + NW * 4 * 32 * MP) * 2;
+  static constexpr size_t fin = (size_t)2 * (kFinTok + 64) * D * 2 + ((size_t)MP * D + 65 + 4 * 65) * 4;
+};
+
+template <int D, int MP>
+static hipError_t configure_bwd_t() {
+  using S = BwdShape<D, MP>;
+  const void* fns[] = {reinterpret_cast<const void*>(&bwd_land_fwd_kernel<D, MP>),
+                       reinterpret_cast<const void*>(&bwd_land_bwd_kernel<D, MP>),
+                       reinterpret_cast<const void*>(&bwd_pass1_kernel<D, MP, S::NW>),
+                       reinterpret_cast<const void*>(&bwd_pass2_kernel<D, MP, S::NW>),
+                       reinterpret_cast<const void*>(&bwd_final_kernel<D>)};
+  const size_t bytes[] = {S::l1, S::l2, S::p1, S::p2, S::fin};
+  for (int i = 0; i < 5; ++i) {
+    const hipError_t e = hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize,
+                                             (int)bytes[i]);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t configure_backward() {
+  hipError_t e;
+  if ((e = configure_bwd_t<32, 32>()) != hipSuccess) return e;
+  if ((e = configure_bwd_t<32, 64>()) != hipSuccess) return e;
+  if ((e = configure_bwd_t<64, 32>()) != hipSuccess) return e;
+  if ((e = configure_bwd_t<64, 64>()) != hipSuccess) return e;
+  if ((e = configure_bwd_t<128, 32>()) != hipSuccess) return e;
+  return configure_bwd_t<128, 64>();
+}
+
+template <int D, int MP>
+static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
+  using S = BwdShape<D, MP>;
+  const int BH = a.BH;
+  hipLaunchKernelGGL((bwd_land_fwd_kernel<D, MP>), dim3(BH), dim3(kBwdThreads), S::l1, s, a);
+  hipLaunchKernelGGL((bwd_pass1_kernel<D, MP, S::NW>), dim3(BH * a.C), dim3(64 * S::NW), S::p1,
+                     s, a);
+  hipLaunchKernelGGL((bwd_land_bwd_kernel<D, MP>), dim3(BH), dim3(kBwdThreads), S::l2, s, a);
+  hipLaunchKernelGGL((bwd_pass2_kernel<D, MP, S::NW>), dim3(BH * a.C), dim3(64 * S::NW), S::p2,
+                     s, a);
+  hipLaunchKernelGGL((bwd_final_kernel<D>), dim3(BH * a.C3), dim3(kBwdThreads), S::fin, s, a);
+  hipLaunchKernelGGL(bwd_dw_kernel, dim3(a.H), dim3(64), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s) {
+  if (a.mp == 32) {
+    if (a.d == 32) return launch_bwd_t<32, 32>(a, s);
+    if (a.d == 64) return launch_bwd_t<64, 32>(a, s);
+    return launch_bwd_t<128, 32>(a, s);
+  }
+  if (a.d == 32) return launch_bwd_t<32, 64>(a, s);
+  if (a.d == 64) return launch_bwd_t<64, 64>(a, s);
+  return launch_bwd_t<128, 64>(a, s);
+}
+
+}  // namespace nys

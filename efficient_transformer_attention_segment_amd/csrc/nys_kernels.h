@@ -72,6 +72,54 @@ struct OutArgs {
   float scale_log2e;
 };
 
+// Backward pass (bf16 I/O, mp <= 64): gradients of sum(out * dout) with respect to q, k,
+// v and the conv weights. The forward's segment-means and context kernels run first
+// (SegArgs / CtxArgs of the plan); these kernels then use their workspace outputs.
+struct BwdArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* dout;
+  const float* conv_w;      // [H][W]
+  const int* lengths;       // [B] or nullptr
+  uint16_t* dq;             // [BH][n][d] outputs
+  uint16_t* dk;
+  uint16_t* dv;
+  float* dconv_w;           // [H][W] output
+  // forward state
+  const float* qt;          // [BH][mp][d] landmarks (fp32), rows >= m zero
+  const float* kt;
+  const uint16_t* qt_hl;    // [BH][2][mp][d]
+  const uint16_t* kt_hl;
+  const float* part_w;      // [BH][C][d][mp] context partial (Bbar V)^T
+  const float* part_ml;     // [BH][C][2][mp] context partial max (log2 units), sum
+  // backward workspace
+  float* w;                 // [BH][mp][d]   W = B V (merged)
+  float* stat;              // [BH][2][mp]   B's reference max (log2 units) and sum
+  float* a_s;               // [BH][mp][mp]  A_S
+  float* alpha;             // [BH][4]       alpha, max column sum, max row sum, pad
+  int* amax;                // [BH][2]       argmax column, argmax row
+  float* zs;                // [BH][T+1][mp][mp] iterates Z_0..Z_T
+  float* xs;                // [BH][T][mp][mp]   X_k = A Z_k
+  uint16_t* y_hl;           // [BH][2][mp][d]  Y = Z W
+  uint16_t* ktT_hl;         // [BH][2][d][mp]  Kt^T
+  uint16_t* qtT_hl;         // [BH][2][d][mp]  Qt^T
+  float* part1;             // [BH][C][2][mp][d] pass-1 partials: F^T dO, dSF^T Q
+  uint16_t* dw_hl;          // [BH][2][mp][d]  dW
+  uint16_t* dwT_hl;         // [BH][2][d][mp]  dW^T
+  float* db;                // [BH][mp]        D_B = rowsum(dW o W)
+  float* dkt;               // [BH][mp][d]     dKt (complete)
+  float* dqt;               // [BH][mp][d]     dQt from the A_S path
+  float* part2;             // [BH][C][mp][d]  pass-2 partials: dSB K
+  float* dq_part;           // [BH][n][d]      s dSF Kt
+  float* dv_part;           // [BH][n][d]      B^T dW
+  float* part_dw;           // [BH][C3][W]
+  int B, H, BH, n, d, m, mp, W, iters, chunk, C, chunk3, C3;
+  float scale, scale_log2e;
+};
+hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
+hipError_t configure_backward();
+
 // Projections around the core (bf16): q, k, v = split_heads(x w_qkv^T) and
 // y = concat_heads(o) w_o^T.
 struct ProjArgs {

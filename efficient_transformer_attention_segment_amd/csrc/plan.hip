@@ -1,7 +1,7 @@
 // Host side of the C ABI declared in include/nys_attn.h: argument validation (before
 // any HIP call), device check, workspace sizing and carving, the launch sequence on the
-// caller's stream (segment means, pseudo-inverse, landmark context, output), debug taps
-// and stage timing.
+// caller's stream (segment means, pseudo-inverse, landmark context, output), debug taps,
+// stage timing, the backward pass and the projections.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -47,6 +47,9 @@ struct nys_attn_plan {
   nys::OutArgs out;
   int prof_max, prof_count;
   std::vector<hipEvent_t> prof_ev;  // kStages + 1 per recorded call
+  char* bws;                        // backward workspace (first backward call), or null
+  size_t bws_bytes;
+  nys::BwdArgs bwd;
 };
 
 static nys_status validate_shape(int B, int H, int n, int d, int m, int W, int iters,
@@ -195,6 +198,9 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
 
   p->prof_max = 0;
   p->prof_count = 0;
+  p->bws = nullptr;
+  p->bws_bytes = 0;
+  std::memset(&p->bwd, 0, sizeof(p->bwd));
   *plan = p;
   g_err.clear();
   return NYS_OK;
@@ -345,7 +351,134 @@ extern "C" void nys_attn_destroy(nys_attn_plan* p) {
   (void)hipDeviceSynchronize();
   for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
   if (p->ws) (void)hipFree(p->ws);
+  if (p->bws) (void)hipFree(p->bws);
   delete p;
+}
+
+// ------------------------------------------------------------------ backward
+static constexpr int kFinalTokens = 128;  // tokens per block of the final backward pass
+
+// Carves (or, with base == nullptr, sizes) the backward workspace into p->bwd.
+static size_t carve_backward(nys_attn_plan* p, char* base) {
+  const size_t BHs = (size_t)p->BH, mp = (size_t)p->mp, dd = (size_t)p->d;
+  const size_t P = mp * mp, T = (size_t)p->iters, C = (size_t)p->C;
+  const int C3 = ceil_div(p->n, kFinalTokens);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align256(off + bytes);
+    return base ? base + o : nullptr;
+  };
+  nys::BwdArgs& b = p->bwd;
+  b.w = reinterpret_cast<float*>(take(BHs * mp * dd * 4));
+  b.stat = reinterpret_cast<float*>(take(BHs * 2 * mp * 4));
+  b.a_s = reinterpret_cast<float*>(take(BHs * P * 4));
+  b.alpha = reinterpret_cast<float*>(take(BHs * 4 * 4));
+  b.amax = reinterpret_cast<int*>(take(BHs * 2 * 4));
+  b.zs = reinterpret_cast<float*>(take(BHs * (T + 1) * P * 4));
+  b.xs = reinterpret_cast<float*>(take(BHs * T * P * 4));
+  b.y_hl = reinterpret_cast<uint16_t*>(take(BHs * 2 * mp * dd * 2));
+  b.ktT_hl = reinterpret_cast<uint16_t*>(take(BHs * 2 * dd * mp * 2));
+  b.qtT_hl = reinterpret_cast<uint16_t*>(take(BHs * 2 * dd * mp * 2));
+  b.part1 = reinterpret_cast<float*>(take(BHs * C * 2 * mp * dd * 4));
+  b.dw_hl = reinterpret_cast<uint16_t*>(take(BHs * 2 * mp * dd * 2));
+  b.dwT_hl = reinterpret_cast<uint16_t*>(take(BHs * 2 * dd * mp * 2));
+  b.db = reinterpret_cast<float*>(take(BHs * mp * 4));
+  b.dkt = reinterpret_cast<float*>(take(BHs * mp * dd * 4));
+  b.dqt = reinterpret_cast<float*>(take(BHs * mp * dd * 4));
+  b.part2 = reinterpret_cast<float*>(take(BHs * C * mp * dd * 4));
+  b.dq_part = reinterpret_cast<float*>(take(BHs * p->n * dd * 4));
+  b.dv_part = reinterpret_cast<float*>(take(BHs * p->n * dd * 4));
+  b.part_dw = reinterpret_cast<float*>(take(BHs * C3 * p->W * 4));
+  b.B = p->B; b.H = p->H; b.BH = p->BH; b.n = p->n; b.d = p->d; b.m = p->m; b.mp = p->mp;
+  b.W = p->W; b.iters = p->iters; b.chunk = p->chunk; b.C = p->C;
+  b.chunk3 = kFinalTokens; b.C3 = C3;
+  b.scale = p->ctx.scale;
+  b.scale_log2e = p->ctx.scale_log2e;
+  return off;
+}
+
+static nys_status backward_setup(nys_attn_plan* p) {
+  static std::once_flag once;
+  static hipError_t cfg = hipSuccess;
+  std::call_once(once, [] { cfg = nys::configure_backward(); });
+  if (cfg != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(NYS_E_LAUNCH, "could not set backward kernel LDS limits");
+  }
+  if (p->bws) return NYS_OK;
+  const size_t bytes = carve_backward(p, nullptr);
+  if (hipMalloc(reinterpret_cast<void**>(&p->bws), bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    p->bws = nullptr;
+    return fail(NYS_E_NOMEM, "backward workspace allocation failed");
+  }
+  p->bws_bytes = bytes;
+  carve_backward(p, p->bws);
+  const nys::SegArgs& sg = p->seg;
+  nys::BwdArgs& b = p->bwd;
+  b.qt = sg.qt; b.kt = sg.kt; b.qt_hl = sg.qt_hl; b.kt_hl = sg.kt_hl;
+  b.part_w = p->ctx.part_w; b.part_ml = p->ctx.part_ml;
+  return NYS_OK;
+}
+
+extern "C" nys_status nys_attn_backward(nys_attn_plan* p, const void* q, const void* k,
+                                        const void* v, const float* conv_w, const int* lengths,
+                                        const void* dout, void* dq, void* dk, void* dv,
+                                        float* dconv_w, void* stream) {
+  if (p == nullptr) return fail(NYS_E_ARG, "plan is NULL");
+  if (p->dtype != NYS_BF16) return fail(NYS_E_UNSUPPORTED, "backward: bf16 plans only");
+  if (p->mp > 64) return fail(NYS_E_UNSUPPORTED, "backward: m <= 64 only");
+  if (!q || !k || !v || !conv_w || !dout || !dq || !dk || !dv || !dconv_w)
+    return fail(NYS_E_ARG, "NULL tensor pointer");
+  for (const void* t : {q, k, v, dout, (const void*)dq, (const void*)dk, (const void*)dv})
+    if ((reinterpret_cast<uintptr_t>(t) & 15u) != 0)
+      return fail(NYS_E_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
+  const size_t bytes = (size_t)p->BH * p->n * p->d * 2;
+  const void* outs[] = {dq, dk, dv};
+  const void* ins[] = {q, k, v, dout};
+  for (int i = 0; i < 3; ++i) {
+    for (const void* in : ins)
+      if (ranges_overlap(outs[i], bytes, in, bytes))
+        return fail(NYS_E_ARG, "dq, dk, dv must not overlap q, k, v or dout");
+    for (int j = 0; j < i; ++j)
+      if (ranges_overlap(outs[i], bytes, outs[j], bytes))
+        return fail(NYS_E_ARG, "dq, dk and dv must not overlap each other");
+  }
+  const size_t wbytes = (size_t)p->H * p->W * 4;
+  if (ranges_overlap(dconv_w, wbytes, conv_w, wbytes))
+    return fail(NYS_E_ARG, "dconv_w must not overlap conv_w");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p->BH == 0) {
+    if (hipMemsetAsync(dconv_w, 0, wbytes, s) != hipSuccess)
+      return fail(NYS_E_LAUNCH, "dconv_w clear failed");
+    return NYS_OK;
+  }
+  nys_status st = backward_setup(p);
+  if (st != NYS_OK) return st;
+  nys::SegArgs sg = p->seg;
+  sg.lengths = lengths;
+  nys::CtxArgs c = p->ctx;
+  c.k = k;
+  c.v = v;
+  c.lengths = lengths;
+  nys::BwdArgs b = p->bwd;
+  b.q = static_cast<const uint16_t*>(q);
+  b.k = static_cast<const uint16_t*>(k);
+  b.v = static_cast<const uint16_t*>(v);
+  b.dout = static_cast<const uint16_t*>(dout);
+  b.conv_w = conv_w;
+  b.lengths = lengths;
+  b.dq = static_cast<uint16_t*>(dq);
+  b.dk = static_cast<uint16_t*>(dk);
+  b.dv = static_cast<uint16_t*>(dv);
+  b.dconv_w = dconv_w;
+  hipError_t e = nys::launch_segmeans(true, p->d, q, k, sg, s);
+  if (e == hipSuccess && !p->fused) e = nys::launch_pinv(p->d, c, s);
+  if (e == hipSuccess) e = nys::launch_context(true, p->d, c, s);
+  if (e == hipSuccess) e = nys::launch_backward(b, s);
+  if (e != hipSuccess) return fail(NYS_E_LAUNCH, std::string("backward launch: ") + hipGetErrorString(e));
+  return NYS_OK;
 }
 
 // ------------------------------------------------------------------ projections

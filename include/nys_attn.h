@@ -108,6 +108,24 @@ nys_status nys_attn_forward_varlen(nys_attn_plan *plan, const void *q, const voi
                                    const void *v, const float *conv_w, const int *lengths,
                                    void *out, void *stream, const nys_attn_taps *taps);
 
+/* Backward pass: gradients of L = sum(out * dout) for the forward of this plan, i.e. the
+ * derivative of the method of the Nystromformer review page ("Proposed method", bullets
+ * M1..M6), including the alpha scaling of the pseudo-inverse start and the conv skip.
+ *   q, k, v, conv_w, lengths : as for nys_attn_forward_varlen (lengths may be NULL)
+ *   dout   : device bf16 [B][H][n][d], the upstream gradient of out
+ *   dq, dk, dv : device bf16 [B][H][n][d], written (rows >= lengths[b] are zero)
+ *   dconv_w: device fp32 [H][conv_width], written (summed over the batch)
+ * The forward's segment means and landmark context are recomputed on the stream first;
+ * the call does not need a preceding forward. Preconditions: a bf16 plan with m <= 64;
+ * 16-byte aligned tensors; dq, dk, dv distinct from each other and from q, k, v, dout;
+ * dconv_w distinct from conv_w. The first call on a plan allocates its backward workspace
+ * (about BH (2 n d + (2 iters + 1) mp^2 + 3 C mp d) * 4 bytes; freed by nys_attn_destroy).
+ * Shares the plan workspace with nys_attn_forward: one call at a time per plan.
+ * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED (fp32 plan, m > 64), NYS_E_NOMEM, NYS_E_LAUNCH. */
+nys_status nys_attn_backward(nys_attn_plan *plan, const void *q, const void *k, const void *v,
+                             const float *conv_w, const int *lengths, const void *dout,
+                             void *dq, void *dk, void *dv, float *dconv_w, void *stream);
+
 /* Projections around the attention core (Fastformer review page, "Proposed method": the
  * input embeddings become Q, K, V through linear projections per head), bf16 in and out,
  * fp32 accumulation. No plan: these are plain products on the given stream.

@@ -23,7 +23,7 @@ def test_header_declares_the_api():
     assert {"nys_attn_create", "nys_attn_forward", "nys_attn_destroy",
             "nys_attn_forward_debug", "nys_attn_forward_varlen",
             "nys_attn_workspace_bytes", "nys_attn_last_error", "nys_proj_qkv",
-            "nys_proj_out"} <= set(names)
+            "nys_proj_out", "nys_attn_backward"} <= set(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -75,6 +75,7 @@ def test_null_safe_entry_points():
     assert L.nys_attn_forward_varlen(None, None, None, None, None, None, None, None,
                                      None) == _lib.NYS_E_ARG
     assert L.nys_attn_profile_enable(None, 4) == _lib.NYS_E_ARG
+    assert L.nys_attn_backward(*([None] * 12)) == _lib.NYS_E_ARG
     n = ctypes.c_int(0)
     assert L.nys_attn_profile_read(None, None, 0, ctypes.byref(n)) == _lib.NYS_E_ARG
 

@@ -1,0 +1,115 @@
+"""GPU parity of the backward pass (nys_attn_backward) against the fp64 gradient oracle
+(oracle/backward.py), through the C ABI.
+
+Criterion (no tolerance is stated for gradients; this one follows from the arithmetic):
+the gradients are stored in bf16, so the best possible result is the exact gradient
+rounded to bf16, up to half a bf16 ulp per element, which relative to the RMS reaches
+~2.3e-2 on these heavy-tailed tensors. The computation itself (fp32 accumulation, bf16
+token operands, landmark operands as hi/lo bf16 pairs) must add at most 2e-3 * RMS on
+top, per (batch, head): |GPU - oracle| <= ulp/2 + 2e-3 * rms(oracle head) elementwise
+over the valid rows, with exact zeros on padding rows. dconv_w (fp32 output) must agree
+to 2e-3 * rms. Inputs are the exact bf16 values the device sees; dout is a seeded N(0, 1)
+draw rounded to bf16.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from efficient_transformer_attention_segment_amd import inputs as gen
+from hip_path import dev_tensor, excess_over_rounding, log, rel_max_err
+
+pytestmark = pytest.mark.gpu
+
+EXCESS = 2e-3   # beyond bf16 storage rounding, relative to the head's RMS
+DW_TOL = 2e-3
+
+CASES = {
+    "d64_m32": (gen.Config("b1", 1, 2, 256, 64, 32, seed=301), None),
+    "d32_m20_uneven": (gen.Config("b2", 2, 1, 300, 32, 20, seed=302), None),
+    "d128_m64": (gen.Config("b3", 1, 2, 512, 128, 64, seed=303), None),
+    "d64_m64_bert_like": (gen.Config("b4", 2, 2, 512, 64, 64, seed=304), None),
+    "ragged_m16": (gen.Config("b5", 3, 2, 400, 64, 16, seed=305), [400, 250, 16]),
+    "ragged_d128_m40": (gen.Config("b6", 2, 1, 700, 128, 40, seed=306), [333, 700]),
+    "conv_w1": (gen.Config("b7", 1, 2, 200, 64, 8, conv_width=1, seed=307), None),
+    "conv_w65": (gen.Config("b8", 1, 1, 300, 64, 32, conv_width=65, seed=308), None),
+    "iters0": (gen.Config("b9", 1, 2, 128, 32, 16, pinv_iters=0, seed=309), None),
+    "m1": (gen.Config("b10", 2, 1, 100, 64, 1, seed=310), [100, 37]),
+}
+
+
+def _dout(cfg, seed):
+    rng = np.random.default_rng(seed + 555)
+    bits = gen.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.H, cfg.n, cfg.d),
+                                                    dtype=np.float32))
+    return bits, gen.bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def run_backward(x, g_bits, lengths=None):
+    import torch
+    from efficient_transformer_attention_segment_amd import NystromAttention
+    cfg = x.cfg
+    att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, cfg.conv_width, cfg.pinv_iters,
+                           "bf16")
+    q, k, v = (dev_tensor(a, "bf16") for a in (x.q_dev, x.k_dev, x.v_dev))
+    w = torch.from_numpy(np.ascontiguousarray(x.w)).to("cuda")
+    g = dev_tensor(g_bits, "bf16")
+    dq, dk, dv, dw = att.backward(q, k, v, w, g, lengths=lengths)
+    torch.cuda.synchronize()
+    out = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv, dw)]
+    att.close()
+    return out
+
+
+def _check(cfg, lengths, heads=None):
+    x = gen.make_inputs(cfg)
+    g_bits, g = _dout(cfg, cfg.seed)
+    got = run_backward(x, g_bits, lengths)
+    pairs = heads or [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
+    rq, rk, rv, rw = oracle.nystrom_backward(x.q, x.k, x.v, x.w, g, cfg.m, cfg.pinv_iters,
+                                             lengths=lengths, heads=pairs)
+    lens = [cfg.n] * cfg.B if lengths is None else list(lengths)
+    worst = {"dq": [0.0, 0.0], "dk": [0.0, 0.0], "dv": [0.0, 0.0]}
+    pad = 0.0
+    for i, (b, h) in enumerate(pairs):
+        L = lens[b]
+        for name, gt, rf in (("dq", got[0], rq), ("dk", got[1], rk), ("dv", got[2], rv)):
+            gg, rr = gt[b, h, :L], rf[i, :L]
+            worst[name][0] = max(worst[name][0], rel_max_err(gg, rr))
+            worst[name][1] = max(worst[name][1], excess_over_rounding(gg, rr, "bf16"))
+            if L < cfg.n:
+                pad = max(pad, float(np.abs(gt[b, h, L:]).max()))
+    hs = sorted({h for _, h in pairs})
+    dw_err = rel_max_err(got[3][hs], rw[hs])
+    log("[gpu]   " + "  ".join(f"{k} full {f:.2e} excess {e:.2e}" for k, (f, e) in worst.items())
+        + f"  dw {dw_err:.2e}  padding {pad:g}")
+    for name, (_, e) in worst.items():
+        assert e <= EXCESS, (name, e)
+    assert dw_err <= DW_TOL
+    assert pad == 0.0
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_backward_parity(name):
+    cfg, lengths = CASES[name]
+    log(f"[gpu] backward case {name}: {cfg} lengths={lengths}")
+    _check(cfg, lengths)
+
+
+def test_backward_full_size_sampled():
+    """The long workload (B 16, H 8, n 4096, d 64, m 64) computed whole on the GPU; every
+    batch element of head 3 checked against the oracle (which also fixes dw[3])."""
+    cfg = gen.CONFIGS["long"]
+    log(f"[gpu] backward at full size {cfg}, checking head 3 of every batch element")
+    _check(cfg, None, heads=[(b, 3) for b in range(cfg.B)])
+
+
+def test_backward_repeatable():
+    """Two calls on one plan give identical bits (the workspace carries no state across
+    calls that changes the result)."""
+    cfg, lengths = CASES["ragged_m16"]
+    x = gen.make_inputs(cfg)
+    g_bits, _ = _dout(cfg, cfg.seed)
+    a = run_backward(x, g_bits, lengths)
+    b = run_backward(x, g_bits, lengths)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
