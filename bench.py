@@ -199,6 +199,9 @@ def main():
     ap.add_argument("--layer", type=int, metavar="D", default=0,
                     help="time the projected layer instead: Q/K/V projection from model "
                          "width D, the forward, and the output projection back to D")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the backward pass (gradients of sum(out * dout) for Q, K, V "
+                         "and the conv weights) instead of the forward")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -240,6 +243,8 @@ def main():
     torch.cuda.set_device(0)
     if args.layer:
         return layer_bench(args, cfg)
+    if args.backward:
+        return backward_bench(args, cfg)
     sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
 
     def dev(a):
@@ -326,6 +331,60 @@ def main():
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(cfg, sets[0], lengths=lengths)
+    att.close()
+    print(json.dumps(rec), flush=True)
+
+
+def backward_bench(args, cfg):
+    """Steps of the backward pass on the workload: one nys_attn_backward call per step
+    (it recomputes the landmarks and the context states, then the gradient kernels),
+    inputs and dout resident, two alternating seeded sets."""
+    import torch
+    from efficient_transformer_attention_segment_amd import NystromAttention
+    from efficient_transformer_attention_segment_amd import inputs as gen
+    sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    rng = np.random.default_rng(cfg.seed + 555)
+    gs = [dev(gen.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.H, cfg.n, cfg.d),
+                                                       dtype=np.float32))) for _ in sets]
+    dev_sets = [(dev(s.q_dev), dev(s.k_dev), dev(s.v_dev), torch.from_numpy(s.w).cuda())
+                for s in sets]
+    att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, cfg.conv_width,
+                           cfg.pinv_iters, cfg.dtype)
+
+    def step(i):
+        q, k, v, w = dev_sets[i % 2]
+        att.backward(q, k, v, w, gs[i % 2])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(args.steps):
+        step(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    e = 2
+    compulsory = 7 * cfg.bh * cfg.n * cfg.d * e   # read Q, K, V, dO; write dQ, dK, dV
+    roof_ms = compulsory / (HBM_PEAK_GBS * 1e9) * 1e3
+    rec = {
+        "metric": "Nystrom attn backward tokens/s",
+        "value": cfg.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": f"nystrom_attention_backward_B{cfg.B}_H{cfg.H}_n{cfg.n}_"
+                               f"d{cfg.d}_m{cfg.m}_conv{cfg.conv_width}_iters{cfg.pinv_iters}",
+                   "B": cfg.B, "H": cfg.H, "n": cfg.n, "d": cfg.d, "m": cfg.m,
+                   "inputs": "two alternating seeded N(0,1) sets, dout N(0,1)"},
+        "path_roofline": {"bound": "hbm", "compulsory_bytes": compulsory,
+                          "roofline_ms": roof_ms, "frac": roof_ms / ms},
+    }
     att.close()
     print(json.dumps(rec), flush=True)
 

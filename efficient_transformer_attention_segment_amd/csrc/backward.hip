@@ -129,8 +129,13 @@ __device__ __forceinline__ f32x16 mma_rows(f32x16 acc, const uint16_t* ahi, cons
 // Token row held by accumulator register rr of lane half h (within a 32-row tile).
 __device__ __forceinline__ int acc_r(int rr, int h) { return 8 * (rr >> 2) + 4 * h + (rr & 3); }
 
+// Segment bounds in 32-bit unsigned arithmetic: L * m < 2^32 because n * d < 2^31,
+// d >= 32 and m <= 64.
 __device__ __forceinline__ int seg_start(int j, int L, int m) {
-  return (int)(((long long)j * L + m - 1) / m);
+  return (int)(((unsigned)j * (unsigned)L + (unsigned)(m - 1)) / (unsigned)m);
+}
+__device__ __forceinline__ int seg_of(int t, int L, int m) {
+  return (int)(((unsigned)t * (unsigned)m) / (unsigned)L);
 }
 
 // ======================================================================= L1
@@ -642,6 +647,14 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
       store_cols_hl(sT_hi, sT_lo, T, 32 * wave, 32 * lt, db[lt], lane);
     }
     // dK = s dSB Qt + dKt[seg] / |seg|  and  B^T dW  for the wave's 32 tokens
+    int segj[16];
+    float seginv[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int tok = min(tw + acc_r(rr, h), L - 1);
+      segj[rr] = seg_of(tok, L, m);
+      seginv[rr] = 1.f / (float)(seg_start(segj[rr] + 1, L, m) - seg_start(segj[rr], L, m));
+    }
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const size_t br = (size_t)(32 * ft + r32) * MP;
@@ -654,9 +667,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
       for (int rr = 0; rr < 16; ++rr) {
         const int tok = tw + acc_r(rr, h);
         if (tok < te) {
-          const int j = (int)(((long long)tok * m) / L);
-          const float len = (float)(seg_start(j + 1, L, m) - seg_start(j, L, m));
-          const float val = a.scale * gk[rr] + dkt[(size_t)j * D + f] / len;
+          const float val = a.scale * gk[rr] + dkt[(size_t)segj[rr] * D + f] * seginv[rr];
           dk[(size_t)tok * D + f] = __builtin_bit_cast(uint16_t, bf16_rne(val));
           dvp[(size_t)tok * D + f] = gv[rr];
         }
@@ -689,6 +700,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
 
 // ======================================================================= final pass
 constexpr int kFinTok = 128;  // tokens per block
+constexpr int kMaxConv = 65;  // widest conv filter built
 
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
@@ -699,12 +711,14 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   float* sq = reinterpret_cast<float*>(sv + R * D);  // dQt / |seg| for the block's segments
   float* sw = sq + MP * D;                           // conv taps [W]
   float* sdw = sw + 65;                              // [4][W] per-wave dw sums
+  int* srow = reinterpret_cast<int*>(sdw + 4 * 65);  // per token: its dQt row offset
   int bh, c3;
   xcd_map(blockIdx.x, a.BH, a.C3, bh, c3);
   const int L = valid_length(a.lengths, bh, a.H, a.n, a.m), hh = bh % a.H;
   const int t0 = c3 * kFinTok, t1 = min(t0 + kFinTok, a.n), tv = min(t1, L);
   const uint16_t* dO = a.dout + (size_t)bh * a.n * D;
   const uint16_t* vv = a.v + (size_t)bh * a.n * D;
+#pragma unroll 4
   for (int e = threadIdx.x; e < R * (D / 8); e += blockDim.x) {
     const int r = e / (D / 8), f8 = (e % (D / 8)) * 8, tok = t0 - half + r;
     u32x4 ov{0u, 0u, 0u, 0u}, vw{0u, 0u, 0u, 0u};
@@ -715,8 +729,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
     *reinterpret_cast<u32x4*>(so + r * D + f8) = ov;
     *reinterpret_cast<u32x4*>(sv + r * D + f8) = vw;
   }
-  const int j0 = tv > t0 ? (int)(((long long)t0 * m) / L) : 0;
-  const int j1 = tv > t0 ? (int)(((long long)(tv - 1) * m) / L) : -1;
+  const int j0 = tv > t0 ? seg_of(t0, L, m) : 0;
+  const int j1 = tv > t0 ? seg_of(tv - 1, L, m) : -1;
   const float* dqt = a.dqt + (size_t)bh * MP * D;
   const float* p2 = a.part2 + (size_t)bh * a.C * MP * D;
   for (int e = threadIdx.x; e < (j1 - j0 + 1) * D; e += blockDim.x) {
@@ -727,37 +741,58 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
     sq[(j - j0) * D + f] = (dqt[(size_t)j * D + f] + a.scale * acc) / len;
   }
   for (int k = threadIdx.x; k < W; k += blockDim.x) sw[k] = a.conv_w[hh * W + k];
+  for (int i = threadIdx.x; i < kFinTok; i += blockDim.x)
+    srow[i] = t0 + i < tv ? (seg_of(t0 + i, L, m) - j0) * D : 0;
   __syncthreads();
   const float* dqp = a.dq_part + (size_t)bh * a.n * D;
   const float* dvp = a.dv_part + (size_t)bh * a.n * D;
   uint16_t* dq = a.dq + (size_t)bh * a.n * D;
   uint16_t* dv = a.dv + (size_t)bh * a.n * D;
   auto rd = [](const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); };
-  for (int e = threadIdx.x; e < (t1 - t0) * D; e += blockDim.x) {
-    const int i = e / D, f = e % D, t = t0 + i;
-    uint16_t oq = 0, ov = 0;
-    if (t < L) {
-      const int j = (int)(((long long)t * m) / L);
-      oq = __builtin_bit_cast(uint16_t, bf16_rne(dqp[(size_t)t * D + f] + sq[(j - j0) * D + f]));
-      // d out[t'] / d V[t] = w[k] for t' = t - k + half
-      float acc = dvp[(size_t)t * D + f];
-      for (int k = 0; k < W; ++k) acc += sw[k] * rd(so + (i + 2 * half - k) * D + f);
-      ov = __builtin_bit_cast(uint16_t, bf16_rne(acc));
+  // thread = (feature f, token i): dQ, dV, and dw[k] += dO[t] V[t + k - half] in registers
+  float dwacc[kMaxConv];
+#pragma unroll
+  for (int k = 0; k < kMaxConv; ++k) dwacc[k] = 0.f;
+  // elements e = tid + 256 u: the fp32 partials of a batch of eight are loaded together
+  constexpr int NE = kFinTok * D / kBwdThreads, NB = 8;
+  for (int u0 = 0; u0 < NE; u0 += NB) {
+    float pq[NB], pv[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int e = threadIdx.x + kBwdThreads * (u0 + u), i = e / D, f = e % D, t = t0 + i;
+      pq[u] = t < tv ? dqp[(size_t)t * D + f] : 0.f;
+      pv[u] = t < tv ? dvp[(size_t)t * D + f] : 0.f;
     }
-    dq[(size_t)t * D + f] = oq;
-    dv[(size_t)t * D + f] = ov;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int e = threadIdx.x + kBwdThreads * (u0 + u), i = e / D, f = e % D, t = t0 + i;
+      if (t >= t1) continue;
+      uint16_t oq = 0, ov = 0;
+      if (t < tv) {
+        oq = __builtin_bit_cast(uint16_t, bf16_rne(pq[u] + sq[srow[i] + f]));
+        // d out[t'] / d V[t] = w[k] for t' = t - k + half
+        float acc = pv[u];
+        const uint16_t* op = so + (i + 2 * half) * D + f;
+#pragma unroll 8
+        for (int k = 0; k < W; ++k) acc += sw[k] * rd(op - k * D);
+        ov = __builtin_bit_cast(uint16_t, bf16_rne(acc));
+        const float o = rd(so + (i + half) * D + f);
+        const uint16_t* vp = sv + i * D + f;
+#pragma unroll
+        for (int k = 0; k < kMaxConv; ++k)
+          if (k < W) dwacc[k] += o * rd(vp + k * D);
+      }
+      dq[(size_t)t * D + f] = oq;
+      dv[(size_t)t * D + f] = ov;
+    }
   }
-  // partial dw[k] = sum over the block's valid tokens t and features of dO[t] V[t + k - half]
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  for (int k = 0; k < W; ++k) {
-    float p = 0.f;
-    for (int e = threadIdx.x; e < (tv > t0 ? (tv - t0) * D : 0); e += blockDim.x) {
-      const int i = e / D, f = e % D;
-      p += rd(so + (i + half) * D + f) * rd(sv + (i + k) * D + f);
+#pragma unroll
+  for (int k = 0; k < kMaxConv; ++k)
+    if (k < W) {
+      const float p = wave_sum(dwacc[k]);
+      if (lane == 0) sdw[wave * W + k] = p;
     }
-    p = wave_sum(p);
-    if (lane == 0) sdw[wave * W + k] = p;
-  }
   __syncthreads();
   for (int k = threadIdx.x; k < W; k += blockDim.x) {
     float s = 0.f;
@@ -766,13 +801,22 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   }
 }
 
-__global__ void bwd_dw_kernel(BwdArgs a) {
-  const int hh = blockIdx.x;
-  for (int k = threadIdx.x; k < a.W; k += blockDim.x) {
-    float s = 0.f;
-    for (int b = 0; b < a.B; ++b)
-      for (int c = 0; c < a.C3; ++c) s += a.part_dw[(((size_t)b * a.H + hh) * a.C3 + c) * a.W + k];
-    a.dconv_w[hh * a.W + k] = s;
+// dw[h][k]: one block per (head, tap) sums the B * C3 partials.
+__global__ __launch_bounds__(kBwdThreads) void bwd_dw_kernel(BwdArgs a) {
+  __shared__ float sred[kBwdThreads / 64];
+  const int hh = blockIdx.x / a.W, k = blockIdx.x % a.W;
+  float s = 0.f;
+  for (int e = threadIdx.x; e < a.B * a.C3; e += blockDim.x) {
+    const int b = e / a.C3, c = e % a.C3;
+    s += a.part_dw[(((size_t)b * a.H + hh) * a.C3 + c) * a.W + k];
+  }
+  s = wave_sum(s);
+  if ((threadIdx.x & 63) == 0) sred[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float t = 0.f;
+    for (int w = 0; w < kBwdThreads / 64; ++w) t += sred[w];
+    a.dconv_w[hh * a.W + k] = t;
   }
 }
 
@@ -786,7 +830,8 @@ struct BwdShape {
   static constexpr size_t l2 = (l2a > l2b ? l2a : l2b) * 4;
   static constexpr size_t p1 = ((size_t)4 * MP * T + 2 * D * T + NW * 2 * 32 * MP) * 2;
   static constexpr size_t p2 = ((size_t)2 * MP * T + D * T + NW * 4 * 32 * MP) * 2;
-  static constexpr size_t fin = (size_t)2 * (kFinTok + 64) * D * 2 + ((size_t)MP * D + 65 + 4 * 65) * 4;
+  static constexpr size_t fin =
+      (size_t)2 * (kFinTok + 64) * D * 2 + ((size_t)MP * D + 65 + 4 * 65 + kFinTok) * 4;
 };
 
 template <int D, int MP>
@@ -827,7 +872,7 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_pass2_kernel<D, MP, S::NW>), dim3(BH * a.C), dim3(64 * S::NW), S::p2,
                      s, a);
   hipLaunchKernelGGL((bwd_final_kernel<D>), dim3(BH * a.C3), dim3(kBwdThreads), S::fin, s, a);
-  hipLaunchKernelGGL(bwd_dw_kernel, dim3(a.H), dim3(64), 0, s, a);
+  hipLaunchKernelGGL(bwd_dw_kernel, dim3(a.H * a.W), dim3(kBwdThreads), 0, s, a);
   return hipGetLastError();
 }
 
