@@ -16,3 +16,4 @@ from .nystrom import (  # noqa: F401
 )
 from .projections import nystrom_layer, out_project, qkv_project  # noqa: F401
 from .backward import nystrom_backward  # noqa: F401
+from .flash import mixed_chunk_attention  # noqa: F401
