@@ -202,6 +202,9 @@ def main():
     ap.add_argument("--backward", action="store_true",
                     help="time the backward pass (gradients of sum(out * dout) for Q, K, V "
                          "and the conv weights) instead of the forward")
+    ap.add_argument("--flash", type=int, metavar="CHUNK", default=0,
+                    help="time FLASH mixed-chunk attention with this chunk size instead")
+    ap.add_argument("--causal", action="store_true", help="with --flash: causal variant")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
     ap.add_argument("--summarize-trace", metavar="DIR",
@@ -245,6 +248,8 @@ def main():
         return layer_bench(args, cfg)
     if args.backward:
         return backward_bench(args, cfg)
+    if args.flash:
+        return flash_bench(args, cfg)
     sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
 
     def dev(a):
@@ -386,6 +391,100 @@ def backward_bench(args, cfg):
                           "roofline_ms": roof_ms, "frac": roof_ms / ms},
     }
     att.close()
+    print(json.dumps(rec), flush=True)
+
+
+def flash_bench(args, cfg):
+    """Steps of FLASH mixed-chunk attention on the workload's Q, K, V: the chunk-state
+    phase (K^T V per chunk, global sums) and the attention phase, each timed with events
+    on the stream they run on."""
+    import torch
+    from efficient_transformer_attention_segment_amd import (nys_flash_attend, nys_flash_states,
+                                                             nys_flash_workspace_bytes)
+    from efficient_transformer_attention_segment_amd import inputs as gen
+    c, causal = args.flash, args.causal
+    B, H, n, d = cfg.B, cfg.H, cfg.n, cfg.d
+    sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
+
+    def dev(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+    dev_sets = [(dev(s.q_dev), dev(s.k_dev), dev(s.v_dev)) for s in sets]
+    outs = [torch.empty_like(dev_sets[0][0]) for _ in sets]
+    nb = nys_flash_workspace_bytes(B, H, n, d, c, causal)
+    ws = torch.empty(nb, dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+
+    def states(i):
+        _, k, v = dev_sets[i % 2]
+        nys_flash_states(k.data_ptr(), v.data_ptr(), B, H, n, d, c, causal, ws.data_ptr(), nb,
+                         stream)
+
+    def attend(i):
+        q, k, v = dev_sets[i % 2]
+        nys_flash_attend(q.data_ptr(), k.data_ptr(), v.data_ptr(), outs[i % 2].data_ptr(), B, H,
+                         n, d, c, causal, ws.data_ptr(), nb, stream)
+
+    for i in range(args.warmup):
+        states(i)
+        attend(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record()
+    for i in range(args.steps):
+        states(i)
+        attend(i)
+    ev[1].record()
+    torch.cuda.synchronize()
+    ms = ev[0].elapsed_time(ev[1]) / args.steps
+    nprof = min(args.steps, 200)
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(nprof)]
+    for i in range(nprof):
+        marks[i][0].record()
+        states(i)
+        marks[i][1].record()
+        attend(i)
+        marks[i][2].record()
+    torch.cuda.synchronize()
+    st_ms = float(np.mean([m[0].elapsed_time(m[1]) for m in marks]))
+    at_ms = float(np.mean([m[1].elapsed_time(m[2]) for m in marks]))
+    e = 2
+    attend_bytes = 4 * cfg.bh * n * d * e            # read Q, K, V; write out
+    state_bytes = 2 * cfg.bh * n * d * e             # read K, V
+    achieved = attend_bytes / (at_ms * 1e-3) / 1e9
+    compulsory = 4 * cfg.bh * n * d * e
+    rec = {
+        "metric": "FLASH mixed-chunk attention fwd tokens/s",
+        "value": cfg.tokens / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"flash_mixed_chunk_B{B}_H{H}_n{n}_d{d}_chunk{c}_"
+                               + ("causal" if causal else "bidirectional"),
+                   "B": B, "H": H, "n": n, "d": d, "chunk": c, "causal": causal,
+                   "inputs": "two alternating seeded N(0,1) sets"},
+        "roofline": {"kernel": "flash_attend_kernel", "bound": "hbm", "achieved": achieved,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                     "algorithmic_bytes": attend_bytes, "traffic": None},
+        "stages_ms": {"states": st_ms, "attend": at_ms},
+        "state_roofline": {"bound": "hbm", "algorithmic_bytes": state_bytes,
+                           "achieved": state_bytes / (st_ms * 1e-3) / 1e9},
+        "path_roofline": {"bound": "hbm", "compulsory_bytes": compulsory,
+                          "roofline_ms": compulsory / (HBM_PEAK_GBS * 1e9) * 1e3,
+                          "frac": compulsory / (HBM_PEAK_GBS * 1e9) * 1e3 / ms},
+    }
+    if not args.no_cpu_baseline:
+        import time
+        import oracle
+        heads, t0 = [], time.perf_counter()
+        while time.perf_counter() - t0 < 10.0 and len(heads) < cfg.bh:
+            pair = (len(heads) // H, len(heads) % H)
+            oracle.mixed_chunk_attention(sets[0].q, sets[0].k, sets[0].v, c, causal, heads=[pair])
+            heads.append(pair)
+        dt = time.perf_counter() - t0
+        rec["cpu_baseline"] = {"value": len(heads) * n / dt, "unit": "tokens/s",
+                               "cores": os.cpu_count() or 1, "kind": "oracle",
+                               "sample": f"{len(heads)} of {cfg.bh} heads in {dt:.1f} s"}
     print(json.dumps(rec), flush=True)
 
 

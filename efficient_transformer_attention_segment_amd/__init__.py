@@ -9,7 +9,8 @@ _EXPORTS = {
     "nys_attn_forward_debug", "nys_attn_workspace_bytes", "nys_attn_profile_enable",
     "nys_attn_profile_read", "nys_attn_destroy", "nys_attn_last_error", "Taps",
     "NYS_F32", "NYS_BF16", "nys_attn_forward_varlen", "nys_proj_qkv", "nys_proj_out",
-    "NystromLayer", "nys_attn_backward",
+    "NystromLayer", "nys_attn_backward", "flash_mixed_chunk", "nys_flash_workspace_bytes",
+    "nys_flash_states", "nys_flash_attend", "nys_flash_attention",
 }
 
 

@@ -44,6 +44,13 @@ SIGNATURES = {
     "nys_attn_profile_read": (_c_int, [_c_void_p, ctypes.POINTER(ctypes.c_float), _c_int,
                                        ctypes.POINTER(_c_int)]),
     "nys_attn_backward": (_c_int, [_c_void_p] * 12),
+    "nys_flash_workspace_bytes": (_c_size_t, [_c_int] * 6),
+    "nys_flash_states": (_c_int, [_c_void_p] * 2 + [_c_int] * 6 + [_c_void_p, _c_size_t,
+                                                                   _c_void_p]),
+    "nys_flash_attend": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_void_p, _c_size_t,
+                                                                   _c_void_p]),
+    "nys_flash_attention": (_c_int, [_c_void_p] * 4 + [_c_int] * 6 + [_c_void_p, _c_size_t,
+                                                                      _c_void_p]),
     "nys_proj_qkv": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 + [_c_void_p]),
     "nys_proj_out": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p]),
     "nys_attn_destroy": (None, [_c_void_p]),
@@ -139,6 +146,47 @@ def nys_attn_backward(plan, q, k, v, conv_w, lengths, dout, dq, dk, dv, dconv_w,
                       stream) -> None:
     _check(_LIB.nys_attn_backward(plan, q, k, v, conv_w, lengths, dout, dq, dk, dv, dconv_w,
                                   stream), "nys_attn_backward")
+
+
+def nys_flash_workspace_bytes(B, H, n, d, chunk, causal) -> int:
+    return int(_LIB.nys_flash_workspace_bytes(B, H, n, d, chunk, int(causal)))
+
+
+def nys_flash_states(k, v, B, H, n, d, chunk, causal, ws, ws_bytes, stream) -> None:
+    _check(_LIB.nys_flash_states(k, v, B, H, n, d, chunk, int(causal), ws, ws_bytes, stream),
+           "nys_flash_states")
+
+
+def nys_flash_attend(q, k, v, out, B, H, n, d, chunk, causal, ws, ws_bytes, stream) -> None:
+    _check(_LIB.nys_flash_attend(q, k, v, out, B, H, n, d, chunk, int(causal), ws, ws_bytes,
+                                 stream), "nys_flash_attend")
+
+
+def nys_flash_attention(q, k, v, out, B, H, n, d, chunk, causal, ws, ws_bytes, stream) -> None:
+    _check(_LIB.nys_flash_attention(q, k, v, out, B, H, n, d, chunk, int(causal), ws,
+                                    ws_bytes, stream), "nys_flash_attention")
+
+
+def flash_mixed_chunk(q, k, v, chunk: int, causal: bool = False, out=None, workspace=None):
+    """Mixed-chunk attention of torch bf16 device tensors [B, H, n, d] on torch's current
+    stream; allocates the workspace (and out) unless given."""
+    import torch
+    B, H, n, d = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.device.type != "cuda" or not t.is_contiguous() \
+                or tuple(t.shape) != (B, H, n, d):
+            raise ValueError(f"{name} must be a contiguous bf16 device tensor [B, H, n, d]")
+    nb = nys_flash_workspace_bytes(B, H, n, d, chunk, causal)
+    if nb == 0:
+        raise NysError(NYS_E_UNSUPPORTED, "nys_flash_workspace_bytes", "unsupported shape")
+    if workspace is None:
+        workspace = torch.empty(nb, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    nys_flash_attention(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, n, d,
+                        chunk, causal, workspace.data_ptr(), workspace.numel(), stream)
+    return out
 
 
 def nys_proj_qkv(x, w_qkv, q, k, v, B, H, n, d, d_model, stream) -> None:

@@ -1,0 +1,280 @@
+// FLASH mixed-chunk attention (review page "Transformer Quality in Linear Time",
+// "Proposed method", third bullet): the sequence is cut into non-overlapping chunks of
+// c tokens; inside a chunk, softmax attention (quadratic in c); across chunks, a linear
+// attention with identity features, averaged over the keys it covers; the two summed.
+// Per (batch, head), s = 1/sqrt(d), chunk g = tokens [g c, min((g+1) c, n)):
+//
+//   out[t] = softmax_{t' in chunk(t), t' <= t if causal}(s Q_t . K_t') V_t'
+//          + s Q_t M_g / n_g,   M_g = sum over covered chunks of S_j,  S_j = K_j^T V_j
+//
+// covered = every chunk (non-causal) or the chunks before g (causal; n_g = g c, and
+// chunk 0 has no global term).
+//
+//   flash_state_kernel   one block per (head, chunk): S_g = K_g^T V_g (d x d, fp32) on
+//                        MFMA from transposed bf16 copies of the chunk in LDS
+//   flash_scan_kernel    one block per head: the global sums, scaled by s / n_g and
+//                        stored as hi/lo bf16 planes of M^T (one per head, or one per
+//                        chunk when causal)
+//   flash_attend_kernel  one block per (head, chunk), one wave per 32 queries: local
+//                        attention with an online softmax over 32-key tiles (scores on
+//                        MFMA with keys across lanes, half-wave reductions, P as hi/lo
+//                        bf16 through LDS, V^T staged in LDS), then + Q M_g, bf16 store
+#include "nys_common.h"
+#include "nys_kernels.h"
+
+namespace nys {
+
+template <int K, bool AL, bool BL>
+__device__ __forceinline__ f32x16 fl_mma(f32x16 acc, const uint16_t* ahi, const uint16_t* alo,
+                                         const uint16_t* bhi, const uint16_t* blo, int h) {
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const Pair8 x{ld8(ahi + k0 + 8 * h), AL ? ld8(alo + k0 + 8 * h) : zero8()};
+    const Pair8 y{ld8(bhi + k0 + 8 * h), BL ? ld8(blo + k0 + 8 * h) : zero8()};
+    acc = mfma_pair<AL, BL>(x, y, acc);
+  }
+  return acc;
+}
+
+__device__ __forceinline__ int fl_row(int rr, int h) { return 8 * (rr >> 2) + 4 * h + (rr & 3); }
+
+// ------------------------------------------------------------------ chunk states
+template <int D, int C>
+__global__ __launch_bounds__(256) void flash_state_kernel(FlashArgs a) {
+  constexpr int LT = C + 8;  // padded row of the transposed copies
+  extern __shared__ __align__(16) char lds[];
+  uint16_t* kT = reinterpret_cast<uint16_t*>(lds);  // K^T [D][LT]
+  uint16_t* vT = kT + D * LT;                         // V^T [D][LT]
+  int bh, g;
+  xcd_map(blockIdx.x, a.BH, a.G, bh, g);
+  const int t0 = g * C, t1 = min(t0 + C, a.n);
+  const uint16_t* k = a.k + (size_t)bh * a.n * D;
+  const uint16_t* v = a.v + (size_t)bh * a.n * D;
+  for (int e = threadIdx.x; e < C * (D / 8); e += blockDim.x) {
+    const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = t0 + i;
+    u32x4 kv{0u, 0u, 0u, 0u}, vv{0u, 0u, 0u, 0u};
+    if (t < t1) {
+      kv = *reinterpret_cast<const u32x4*>(k + (size_t)t * D + f8);
+      vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      kT[(f8 + q) * LT + i] = (uint16_t)(kv[q >> 1] >> (16 * (q & 1)));
+      vT[(f8 + q) * LT + i] = (uint16_t)(vv[q >> 1] >> (16 * (q & 1)));
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
+  constexpr int FT = D / 32;
+  float* st = a.states + ((size_t)bh * a.G + g) * D * D;
+  for (int tile = wave; tile < FT * FT; tile += 4) {
+    const int ti = tile / FT, tj = tile % FT;
+    const f32x16 acc = fl_mma<C, false, false>(zero16(), kT + (32 * ti + r32) * LT, nullptr,
+                                               vT + (32 * tj + r32) * LT, nullptr, h);
+    store_rows_f32(st, D, 32 * ti, 32 * tj, acc, lane);
+  }
+}
+
+// ------------------------------------------------------------------ global sums
+template <int D>
+__global__ __launch_bounds__(256) void flash_scan_kernel(FlashArgs a) {
+  const int bh = blockIdx.x;
+  const float* st = a.states + (size_t)bh * a.G * D * D;
+  constexpr int PER = D * D / 256;
+  float run[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) run[u] = 0.f;
+  if (!a.causal) {
+    for (int g = 0; g < a.G; ++g)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) run[u] += st[(size_t)g * D * D + threadIdx.x + 256 * u];
+  }
+  const int nplanes = a.causal ? a.G : 1;
+  for (int g = 0; g < nplanes; ++g) {
+    const int ncov = a.causal ? g * a.chunk : a.n;
+    const float sc = ncov > 0 ? a.scale / (float)ncov : 0.f;
+    uint16_t* pl = a.mplanes + ((size_t)bh * nplanes + g) * 2 * D * D;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = threadIdx.x + 256 * u, i = e / D, j = e % D;  // M[i][j] -> M^T[j][i]
+      uint16_t hi, lo;
+      split1(run[u] * sc, hi, lo);
+      pl[j * D + i] = hi;
+      pl[D * D + j * D + i] = lo;
+    }
+    if (a.causal)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) run[u] += st[(size_t)g * D * D + threadIdx.x + 256 * u];
+  }
+}
+
+// ------------------------------------------------------------------ local + global
+template <int D, int C>
+__global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
+  constexpr int NW = C / 32, LT = C + 8, LP = 40, FT = D / 32;
+  extern __shared__ __align__(16) char lds[];
+  uint16_t* vT = reinterpret_cast<uint16_t*>(lds);   // V^T [D][LT]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
+  uint16_t* p_hi = vT + D * LT + wave * 2 * 32 * LP;  // P [32][LP] per wave
+  uint16_t* p_lo = p_hi + 32 * LP;
+  int bh, g;
+  xcd_map(blockIdx.x, a.BH, a.G, bh, g);
+  const int t0 = g * C, t1 = min(t0 + C, a.n);
+  const uint16_t* q = a.q + (size_t)bh * a.n * D;
+  const uint16_t* k = a.k + (size_t)bh * a.n * D;
+  const uint16_t* v = a.v + (size_t)bh * a.n * D;
+  for (int e = threadIdx.x; e < C * (D / 8); e += blockDim.x) {
+    const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = t0 + i;
+    u32x4 vv{0u, 0u, 0u, 0u};
+    if (t < t1) vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) vT[(f8 + u) * LT + i] = (uint16_t)(vv[u >> 1] >> (16 * (u & 1)));
+  }
+  __syncthreads();
+  const int q0 = t0 + 32 * wave;  // this wave's first query
+  if (q0 >= t1) return;           // no barrier follows
+  const int qrow = min(q0 + r32, t1 - 1);
+  bf16x8 qa[D / 16];
+#pragma unroll
+  for (int s = 0; s < D / 16; ++s) qa[s] = ld8(q + (size_t)qrow * D + 16 * s + 8 * h);
+  f32x16 o[FT];
+#pragma unroll
+  for (int f = 0; f < FT; ++f) o[f] = zero16();
+  float mrow[16], lrow[16];
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    mrow[rr] = kNegBig;
+    lrow[rr] = 0.f;
+  }
+  const float sl = a.scale_log2e;
+  const int ntile = a.causal ? wave + 1 : (t1 - t0 + 31) / 32;
+  for (int kt = 0; kt < ntile; ++kt) {
+    const int k0 = t0 + 32 * kt, key = k0 + r32;  // lane's key
+    const int krow = min(key, t1 - 1);
+    f32x16 sc = zero16();
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s)
+      sc = mfma(qa[s], ld8(k + (size_t)krow * D + 16 * s + 8 * h), sc);
+    f32x16 p;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int qi = q0 + fl_row(rr, h);
+      const bool ok = key < t1 && (!a.causal || key <= qi);
+      const float x = ok ? sc[rr] * sl : kNegBig;
+      const float mn = fmaxf(mrow[rr], half_max(x));
+      const float corr = fast_exp2(mrow[rr] - mn);
+      const float e = ok ? fast_exp2(x - mn) : 0.f;
+      lrow[rr] = lrow[rr] * corr + half_sum(e);
+      mrow[rr] = mn;
+      p[rr] = e;
+#pragma unroll
+      for (int f = 0; f < FT; ++f) o[f][rr] *= corr;
+    }
+    store_rows_hl(p_hi, p_lo, LP, 0, 0, p, lane);
+#pragma unroll
+    for (int f = 0; f < FT; ++f)
+      o[f] = fl_mma<32, true, false>(o[f], p_hi + r32 * LP, p_lo + r32 * LP,
+                                     vT + (32 * f + r32) * LT + 32 * kt, nullptr, h);
+  }
+  // + Q M_g (planes already scaled by s / n_g), then the bf16 store
+  const uint16_t* pl = a.mplanes + ((size_t)bh * (a.causal ? a.G : 1) + (a.causal ? g : 0)) *
+                                       2 * D * D;
+  uint16_t* out = a.out + (size_t)bh * a.n * D;
+#pragma unroll
+  for (int f = 0; f < FT; ++f) {
+    f32x16 gl = zero16();
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const uint16_t* row = pl + (size_t)(32 * f + r32) * D + 16 * s + 8 * h;
+      const Pair8 x{qa[s], zero8()};
+      const Pair8 y{ld8(row), ld8(row + D * D)};
+      gl = mfma_pair<false, true>(x, y, gl);
+    }
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const int qi = q0 + fl_row(rr, h);
+      if (qi < t1) {
+        const float val = o[f][rr] / lrow[rr] + gl[rr];
+        out[(size_t)qi * D + 32 * f + r32] = __builtin_bit_cast(uint16_t, bf16_rne(val));
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ host side
+template <int D, int C>
+struct FlashShape {
+  static constexpr size_t state_lds = (size_t)2 * D * (C + 8) * 2;
+  static constexpr size_t attend_lds = (size_t)D * (C + 8) * 2 + (size_t)(C / 32) * 2 * 32 * 40 * 2;
+};
+
+template <int D, int C>
+static hipError_t flash_cfg_t() {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&flash_state_kernel<D, C>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     (int)FlashShape<D, C>::state_lds);
+  if (e != hipSuccess) return e;
+  return hipFuncSetAttribute(reinterpret_cast<const void*>(&flash_attend_kernel<D, C>),
+                             hipFuncAttributeMaxDynamicSharedMemorySize,
+                             (int)FlashShape<D, C>::attend_lds);
+}
+
+hipError_t configure_flash() {
+  hipError_t e = hipSuccess;
+#define NYS_FLASH_CFG(D, C) \
+  if ((e = flash_cfg_t<D, C>()) != hipSuccess) return e;
+  NYS_FLASH_CFG(32, 64) NYS_FLASH_CFG(32, 128) NYS_FLASH_CFG(32, 256)
+  NYS_FLASH_CFG(64, 64) NYS_FLASH_CFG(64, 128) NYS_FLASH_CFG(64, 256)
+  NYS_FLASH_CFG(128, 64) NYS_FLASH_CFG(128, 128) NYS_FLASH_CFG(128, 256)
+#undef NYS_FLASH_CFG
+  return e;
+}
+
+template <int D, int C>
+static hipError_t flash_states_t(const FlashArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((flash_state_kernel<D, C>), dim3(a.BH * a.G), dim3(256),
+                     (FlashShape<D, C>::state_lds), s, a);
+  hipLaunchKernelGGL((flash_scan_kernel<D>), dim3(a.BH), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int C>
+static hipError_t flash_attend_t(const FlashArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((flash_attend_kernel<D, C>), dim3(a.BH * a.G), dim3(2 * C),
+                     (FlashShape<D, C>::attend_lds), s, a);
+  return hipGetLastError();
+}
+
+template <template <int, int> class Op>
+static hipError_t flash_dispatch(const FlashArgs& a, hipStream_t s) {
+  switch (a.d * 1000 + a.chunk) {
+    case 32064: return Op<32, 64>::run(a, s);
+    case 32128: return Op<32, 128>::run(a, s);
+    case 32256: return Op<32, 256>::run(a, s);
+    case 64064: return Op<64, 64>::run(a, s);
+    case 64128: return Op<64, 128>::run(a, s);
+    case 64256: return Op<64, 256>::run(a, s);
+    case 128064: return Op<128, 64>::run(a, s);
+    case 128128: return Op<128, 128>::run(a, s);
+    case 128256: return Op<128, 256>::run(a, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+template <int D, int C>
+struct FlashStatesOp {
+  static hipError_t run(const FlashArgs& a, hipStream_t s) { return flash_states_t<D, C>(a, s); }
+};
+template <int D, int C>
+struct FlashAttendOp {
+  static hipError_t run(const FlashArgs& a, hipStream_t s) { return flash_attend_t<D, C>(a, s); }
+};
+
+hipError_t launch_flash_states(const FlashArgs& a, hipStream_t s) {
+  return flash_dispatch<FlashStatesOp>(a, s);
+}
+hipError_t launch_flash_attend(const FlashArgs& a, hipStream_t s) {
+  return flash_dispatch<FlashAttendOp>(a, s);
+}
+
+}  // namespace nys

@@ -120,6 +120,21 @@ struct BwdArgs {
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 hipError_t configure_backward();
 
+// FLASH mixed-chunk attention (bf16 I/O): chunk states, global sums, local + global.
+struct FlashArgs {
+  const uint16_t* q;        // [BH][n][d]
+  const uint16_t* k;
+  const uint16_t* v;
+  uint16_t* out;            // [BH][n][d]
+  float* states;            // [BH][G][d][d]  K_g^T V_g
+  uint16_t* mplanes;        // [BH][causal ? G : 1][2][d][d]  hi/lo of (s / n_g) M_g^T
+  int BH, n, d, chunk, G, causal;
+  float scale, scale_log2e;
+};
+hipError_t launch_flash_states(const FlashArgs& a, hipStream_t s);
+hipError_t launch_flash_attend(const FlashArgs& a, hipStream_t s);
+hipError_t configure_flash();
+
 // Projections around the core (bf16): q, k, v = split_heads(x w_qkv^T) and
 // y = concat_heads(o) w_o^T.
 struct ProjArgs {

@@ -560,4 +560,118 @@ extern "C" nys_status nys_proj_out(const void* o, const void* w_o, void* y, int 
   return NYS_OK;
 }
 
+// ------------------------------------------------------------------ FLASH mixed chunks
+static size_t flash_layout(int B, int H, int n, int d, int chunk, int causal, size_t* planes_off) {
+  const size_t BH = (size_t)B * H, G = (size_t)ceil_div(n, chunk);
+  const size_t states = align256(BH * G * d * d * 4);
+  if (planes_off) *planes_off = states;
+  return states + align256(BH * (causal ? G : 1) * 2 * d * d * 2);
+}
+
+static nys_status flash_checks(int B, int H, int n, int d, int chunk, int causal) {
+  if (B < 1 || H < 1 || n < 1) return fail(NYS_E_ARG, "B, H and n must be >= 1");
+  if (causal != 0 && causal != 1) return fail(NYS_E_ARG, "causal must be 0 or 1");
+  if (chunk < 1) return fail(NYS_E_ARG, "chunk must be >= 1");
+  if (d != 32 && d != 64 && d != 128) return fail(NYS_E_UNSUPPORTED, "d must be 32, 64 or 128");
+  if (chunk != 64 && chunk != 128 && chunk != 256)
+    return fail(NYS_E_UNSUPPORTED, "chunk must be 64, 128 or 256");
+  if ((long long)B * H * n * d >= (1LL << 31)) return fail(NYS_E_UNSUPPORTED, "tensor too large");
+  return NYS_OK;
+}
+
+static nys_status flash_device() {
+  static std::once_flag once;
+  static nys_status status = NYS_OK;
+  static std::string why;
+  std::call_once(once, [] {
+    int ndev = 0;
+    if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+      (void)hipGetLastError();
+      status = NYS_E_DEVICE;
+      why = "no HIP device available";
+      return;
+    }
+    int dev = 0;
+    hipDeviceProp_t prop;
+    if (hipGetDevice(&dev) != hipSuccess || hipGetDeviceProperties(&prop, dev) != hipSuccess ||
+        std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+      status = NYS_E_DEVICE;
+      why = "device is not gfx950";
+      return;
+    }
+    if (nys::configure_flash() != hipSuccess) {
+      (void)hipGetLastError();
+      status = NYS_E_LAUNCH;
+      why = "could not set mixed-chunk kernel LDS limits";
+    }
+  });
+  return status == NYS_OK ? NYS_OK : fail(status, why);
+}
+
+extern "C" size_t nys_flash_workspace_bytes(int B, int H, int n, int d, int chunk, int causal) {
+  if (flash_checks(B, H, n, d, chunk, causal) != NYS_OK) return 0;
+  return flash_layout(B, H, n, d, chunk, causal, nullptr);
+}
+
+// phase: 1 = chunk states and global sums, 2 = attention, 3 = both
+static nys_status flash_run(int phase, const void* q, const void* k, const void* v, void* out,
+                            int B, int H, int n, int d, int chunk, int causal, void* ws,
+                            size_t ws_bytes, void* stream) {
+  nys_status st = flash_checks(B, H, n, d, chunk, causal);
+  if (st != NYS_OK) return st;
+  if (!k || !v || !ws || ((phase & 2) && (!q || !out))) return fail(NYS_E_ARG, "NULL pointer");
+  for (const void* t : {q, k, v, (const void*)out, (const void*)ws})
+    if (t && (reinterpret_cast<uintptr_t>(t) & 15u) != 0)
+      return fail(NYS_E_ARG, "tensors and workspace must be 16-byte aligned");
+  size_t poff = 0;
+  const size_t need = flash_layout(B, H, n, d, chunk, causal, &poff);
+  if (ws_bytes < need) return fail(NYS_E_ARG, "workspace too small");
+  const size_t bytes = (size_t)B * H * n * d * 2;
+  if (phase & 2)
+    for (const void* in : {q, k, v})
+      if (ranges_overlap(out, bytes, in, bytes) || ranges_overlap(out, bytes, ws, need))
+        return fail(NYS_E_ARG, "out must not overlap q, k, v or the workspace");
+  for (const void* in : {q, k, v})
+    if (in && ranges_overlap(ws, need, in, bytes))
+      return fail(NYS_E_ARG, "workspace must not overlap q, k or v");
+  if ((st = flash_device()) != NYS_OK) return st;
+  nys::FlashArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.out = static_cast<uint16_t*>(out);
+  a.states = reinterpret_cast<float*>(ws);
+  a.mplanes = reinterpret_cast<uint16_t*>(static_cast<char*>(ws) + poff);
+  a.BH = B * H; a.n = n; a.d = d; a.chunk = chunk; a.G = ceil_div(n, chunk); a.causal = causal;
+  a.scale = 1.0f / std::sqrt((float)d);
+  a.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)d));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (phase & 1) e = nys::launch_flash_states(a, s);
+  if (e == hipSuccess && (phase & 2)) e = nys::launch_flash_attend(a, s);
+  if (e != hipSuccess) return fail(NYS_E_LAUNCH, std::string("mixed-chunk launch: ") + hipGetErrorString(e));
+  return NYS_OK;
+}
+
+extern "C" nys_status nys_flash_states(const void* k, const void* v, int B, int H, int n, int d,
+                                       int chunk, int causal, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+  return flash_run(1, nullptr, k, v, nullptr, B, H, n, d, chunk, causal, workspace,
+                   workspace_bytes, stream);
+}
+
+extern "C" nys_status nys_flash_attend(const void* q, const void* k, const void* v, void* out,
+                                       int B, int H, int n, int d, int chunk, int causal,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  return flash_run(2, q, k, v, out, B, H, n, d, chunk, causal, workspace, workspace_bytes,
+                   stream);
+}
+
+extern "C" nys_status nys_flash_attention(const void* q, const void* k, const void* v, void* out,
+                                          int B, int H, int n, int d, int chunk, int causal,
+                                          void* workspace, size_t workspace_bytes, void* stream) {
+  return flash_run(3, q, k, v, out, B, H, n, d, chunk, causal, workspace, workspace_bytes,
+                   stream);
+}
+
 extern "C" const char* nys_attn_last_error(void) { return g_err.c_str(); }

@@ -149,6 +149,31 @@ nys_status nys_proj_qkv(const void *x, const void *w_qkv, void *q, void *k, void
 nys_status nys_proj_out(const void *o, const void *w_o, void *y, int B, int H, int n, int d,
                         int d_model, void *stream);
 
+/* FLASH mixed-chunk attention (review page "Transformer Quality in Linear Time", "Proposed
+ * method", third bullet), bf16 in and out, one output per head:
+ *   out[t] = softmax over t' in chunk(t) (t' <= t if causal) of (s q_t . k_t') v_t'
+ *          + s q_t (sum over covered keys u of k_u^T v_u) / (number of covered keys)
+ * with s = 1/sqrt(d), chunk g = tokens [g*chunk, min((g+1)*chunk, n)), covered = all
+ * tokens (causal = 0) or the tokens of the chunks before t's chunk (causal = 1; none for
+ * the first chunk, whose global term is zero).
+ *   q, k, v, out : device bf16 [B][H][n][d]; out written
+ *   workspace    : device memory of at least nys_flash_workspace_bytes(...) bytes, owned
+ *                  by the caller, 16-byte aligned, not overlapping the tensors
+ * nys_flash_states fills the workspace from k and v (chunk sums K_g^T V_g, then the
+ * scaled global sums); nys_flash_attend reads it and writes out; nys_flash_attention does
+ * both. Preconditions: B, H, n >= 1; d in {32, 64, 128}; chunk in {64, 128, 256}; causal
+ * in {0, 1}; B*H*n*d < 2^31. Asynchronous on the given stream.
+ * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED, NYS_E_DEVICE, NYS_E_LAUNCH. */
+size_t nys_flash_workspace_bytes(int B, int H, int n, int d, int chunk, int causal);
+nys_status nys_flash_states(const void *k, const void *v, int B, int H, int n, int d, int chunk,
+                            int causal, void *workspace, size_t workspace_bytes, void *stream);
+nys_status nys_flash_attend(const void *q, const void *k, const void *v, void *out, int B, int H,
+                            int n, int d, int chunk, int causal, void *workspace,
+                            size_t workspace_bytes, void *stream);
+nys_status nys_flash_attention(const void *q, const void *k, const void *v, void *out, int B,
+                               int H, int n, int d, int chunk, int causal, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Bytes of device workspace the plan owns (0 for a NULL plan). */
 size_t nys_attn_workspace_bytes(const nys_attn_plan *plan);
 

@@ -15,7 +15,7 @@ HEADER = os.path.join(ROOT, "include", "nys_attn.h")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(nys_(?:attn|proj)_\w+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(nys_(?:attn|proj|flash)_\w+)\s*\(", text)))
 
 
 def test_header_declares_the_api():
@@ -130,3 +130,20 @@ def test_projections_valid_shape_without_gpu_reports_device():
     dims = (2, 2, 100, 64, 192)  # ragged M and N tiles
     assert L.nys_proj_qkv(_X, _W, _Q, _K, _V, *dims, None) == _lib.NYS_E_DEVICE
     assert L.nys_proj_out(_X, _W, _Q, *dims, None) == _lib.NYS_E_DEVICE
+
+
+def test_flash_validation_without_gpu():
+    L = _lib.lib()
+    ws = 0x50000000
+    assert L.nys_flash_workspace_bytes(1, 1, 100, 48, 64, 0) == 0            # d not built
+    assert L.nys_flash_workspace_bytes(1, 1, 100, 64, 96, 0) == 0            # chunk not built
+    nb = L.nys_flash_workspace_bytes(2, 2, 1000, 64, 128, 1)
+    assert nb >= 2 * 2 * 8 * 64 * 64 * 4
+    args = (_X, _W, _Q, _K, 2, 2, 1000, 64, 128, 1, ws, nb, None)
+    assert L.nys_flash_attention(*args[:10], ws, nb - 1, None) == _lib.NYS_E_ARG  # too small
+    assert L.nys_flash_attention(None, *args[1:]) == _lib.NYS_E_ARG
+    assert L.nys_flash_attention(*args[:9], 2, ws, nb, None) == _lib.NYS_E_ARG   # causal = 2
+    assert L.nys_flash_attention(*args[:8], 96, 1, ws, nb, None) == _lib.NYS_E_UNSUPPORTED
+    import torch
+    if not torch.cuda.is_available():
+        assert L.nys_flash_attention(*args) == _lib.NYS_E_DEVICE
