@@ -112,7 +112,8 @@ def _short(name: str) -> str:
     return name.split("(")[0].replace("nys::", "")
 
 
-def summarize_trace(trace_dir: str, cfg_name: str, command: str) -> str:
+def summarize_trace(trace_dir: str, cfg_name: str, command: str,
+                    title: str = "the Nystrom attention forward") -> str:
     """Per-kernel dispatch count and mean duration from a rocprofv3 --kernel-trace
     --stats database: over all dispatches (what --stats reports) and over the last 200
     (the event-profiled forwards that bench.py's stage times come from)."""
@@ -124,7 +125,7 @@ def summarize_trace(trace_dir: str, cfg_name: str, command: str) -> str:
     per = {}
     for name, dur in con.execute("select name, duration from kernels order by start"):
         per.setdefault(name, []).append(dur)
-    lines = [f"Kernel trace of the Nystrom attention forward, workload {cfg_name} "
+    lines = [f"Kernel trace of {title}, workload {cfg_name} "
              f"({CONFIG_TEXT[cfg_name]}), one MI355X.", "",
              "Command (repository root; rocprofv3 wants the program right after --):",
              f"  {command}", "",
@@ -213,14 +214,19 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/<kernel>_<config>_counters.json from rocprofv3 "
                          "--pmc FETCH_SIZE and --pmc WRITE_SIZE output directories and exit")
+    ap.add_argument("--trace-name", default="nystrom_forward",
+                    help="with --summarize-trace: file name stem of the summary")
+    ap.add_argument("--trace-title", default="the Nystrom attention forward",
+                    help="with --summarize-trace: what the trace covers")
     ap.add_argument("--command", action="append", default=[],
                     help="command line(s) that produced the summarized output")
     args = ap.parse_args()
     if args.summarize_trace:
         os.makedirs(PROFILES, exist_ok=True)
-        path = os.path.join(PROFILES, f"nystrom_forward_{args.config}_kernel_trace.txt")
+        path = os.path.join(PROFILES, f"{args.trace_name}_{args.config}_kernel_trace.txt")
         with open(path, "w") as fh:
-            fh.write(summarize_trace(args.summarize_trace, args.config, " && ".join(args.command)))
+            fh.write(summarize_trace(args.summarize_trace, args.config, " && ".join(args.command),
+                                     args.trace_title))
         print(f"wrote {path}")
         return
     if args.summarize_counters:
