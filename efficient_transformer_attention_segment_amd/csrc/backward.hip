@@ -700,17 +700,18 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
 
 // ======================================================================= final pass
 constexpr int kFinTok = 128;  // tokens per block
-constexpr int kMaxConv = 65;  // widest conv filter built
+constexpr int kFinRows = kFinTok + 64;  // staged rows: the tile, its halo and the
+                                        // dw band's last column tile (zero past the halo)
 
 template <int D>
 __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   extern __shared__ __align__(16) char lds[];
   const int W = a.W, half = (W - 1) / 2, R = kFinTok + W - 1, MP = a.mp, m = a.m;
-  uint16_t* so = reinterpret_cast<uint16_t*>(lds);   // dO rows t0 - half .. [R][D]
-  uint16_t* sv = so + R * D;                         // V rows  t0 - half .. [R][D]
-  float* sq = reinterpret_cast<float*>(sv + R * D);  // dQt / |seg| for the block's segments
+  uint16_t* so = reinterpret_cast<uint16_t*>(lds);   // dO rows t0 - half .. [kFinRows][D]
+  uint16_t* sv = so + kFinRows * D;                  // V rows  t0 - half .. [kFinRows][D]
+  float* sq = reinterpret_cast<float*>(sv + kFinRows * D);  // dQt / |seg| per segment
   float* sw = sq + MP * D;                           // conv taps [W]
-  float* sdw = sw + 65;                              // [4][W] per-wave dw sums
+  float* sdw = sw + 65;                              // dw sums [W]
   int* srow = reinterpret_cast<int*>(sdw + 4 * 65);  // per token: its dQt row offset
   int bh, c3;
   xcd_map(blockIdx.x, a.BH, a.C3, bh, c3);
@@ -719,10 +720,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   const uint16_t* dO = a.dout + (size_t)bh * a.n * D;
   const uint16_t* vv = a.v + (size_t)bh * a.n * D;
 #pragma unroll 4
-  for (int e = threadIdx.x; e < R * (D / 8); e += blockDim.x) {
+  for (int e = threadIdx.x; e < kFinRows * (D / 8); e += blockDim.x) {
     const int r = e / (D / 8), f8 = (e % (D / 8)) * 8, tok = t0 - half + r;
     u32x4 ov{0u, 0u, 0u, 0u}, vw{0u, 0u, 0u, 0u};
-    if (tok >= 0 && tok < L) {
+    if (r < R && tok >= 0 && tok < L) {
       ov = *reinterpret_cast<const u32x4*>(dO + (size_t)tok * D + f8);
       vw = *reinterpret_cast<const u32x4*>(vv + (size_t)tok * D + f8);
     }
@@ -740,7 +741,10 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
     const float len = (float)(seg_start(j + 1, L, m) - seg_start(j, L, m));
     sq[(j - j0) * D + f] = (dqt[(size_t)j * D + f] + a.scale * acc) / len;
   }
-  for (int k = threadIdx.x; k < W; k += blockDim.x) sw[k] = a.conv_w[hh * W + k];
+  for (int k = threadIdx.x; k < W; k += blockDim.x) {
+    sw[k] = a.conv_w[hh * W + k];
+    sdw[k] = 0.f;
+  }
   for (int i = threadIdx.x; i < kFinTok; i += blockDim.x)
     srow[i] = t0 + i < tv ? (seg_of(t0 + i, L, m) - j0) * D : 0;
   __syncthreads();
@@ -749,11 +753,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   uint16_t* dq = a.dq + (size_t)bh * a.n * D;
   uint16_t* dv = a.dv + (size_t)bh * a.n * D;
   auto rd = [](const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); };
-  // thread = (feature f, token i): dQ, dV, and dw[k] += dO[t] V[t + k - half] in registers
-  float dwacc[kMaxConv];
-#pragma unroll
-  for (int k = 0; k < kMaxConv; ++k) dwacc[k] = 0.f;
-  // elements e = tid + 256 u: the fp32 partials of a batch of eight are loaded together
+  // thread = (feature f, token i): dQ and dV
   constexpr int NE = kFinTok * D / kBwdThreads, NB = 8;
   for (int u0 = 0; u0 < NE; u0 += NB) {
     float pq[NB], pv[NB];
@@ -770,38 +770,45 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
       uint16_t oq = 0, ov = 0;
       if (t < tv) {
         oq = __builtin_bit_cast(uint16_t, bf16_rne(pq[u] + sq[srow[i] + f]));
-        // d out[t'] / d V[t] = w[k] for t' = t - k + half
-        float acc = pv[u];
+        // d out[t'] / d V[t] = w[k] for t' = t - k + half; eight independent partial sums
         const uint16_t* op = so + (i + 2 * half) * D + f;
-#pragma unroll 8
-        for (int k = 0; k < W; ++k) acc += sw[k] * rd(op - k * D);
-        ov = __builtin_bit_cast(uint16_t, bf16_rne(acc));
-        const float o = rd(so + (i + half) * D + f);
-        const uint16_t* vp = sv + i * D + f;
+        float ps[8] = {pv[u], 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int k = 0;
+        for (; k + 8 <= W; k += 8)
 #pragma unroll
-        for (int k = 0; k < kMaxConv; ++k)
-          if (k < W) dwacc[k] += o * rd(vp + k * D);
+          for (int j = 0; j < 8; ++j) ps[j] += sw[k + j] * rd(op - (k + j) * D);
+        for (; k < W; ++k) ps[0] += sw[k] * rd(op - k * D);
+        const float acc = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+        ov = __builtin_bit_cast(uint16_t, bf16_rne(acc));
       }
       dq[(size_t)t * D + f] = oq;
       dv[(size_t)t * D + f] = ov;
     }
   }
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // dw[k] = sum over rows i < tv - t0 of G[i][i + k], G = dO_tile V_ext^T on MFMA (wave w:
+  // rows 32 w .. 32 w + 31, the column tiles that meet the band 0 <= j - i < W)
+  {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, h = lane >> 5, r32 = lane & 31;
+    const int nvalid = tv - t0;
+    if (32 * wave < nvalid) {
+      const int tj1 = wave + (30 + W) / 32;
+      for (int tj = wave; tj <= tj1; ++tj) {
+        f32x16 g = zero16();
+        g = mma_rows<D, false, false>(g, so + (32 * wave + r32 + half) * D, nullptr,
+                                      sv + (32 * tj + r32) * D, nullptr, h);
 #pragma unroll
-  for (int k = 0; k < kMaxConv; ++k)
-    if (k < W) {
-      const float p = wave_sum(dwacc[k]);
-      if (lane == 0) sdw[wave * W + k] = p;
+        for (int rr = 0; rr < 16; ++rr) {
+          const int i = 32 * wave + acc_r(rr, h), k = 32 * tj + r32 - i;
+          if (k >= 0 && k < W && i < nvalid) atomicAdd(&sdw[k], g[rr]);
+        }
+      }
     }
-  __syncthreads();
-  for (int k = threadIdx.x; k < W; k += blockDim.x) {
-    float s = 0.f;
-    for (int w = 0; w < kBwdThreads / 64; ++w) s += sdw[w * W + k];
-    a.part_dw[((size_t)bh * a.C3 + c3) * W + k] = s;
   }
+  __syncthreads();
+  for (int k = threadIdx.x; k < W; k += blockDim.x)
+    a.part_dw[((size_t)bh * a.C3 + c3) * W + k] = sdw[k];
 }
 
-// dw[h][k]: one block per (head, tap) sums the B * C3 partials.
 __global__ __launch_bounds__(kBwdThreads) void bwd_dw_kernel(BwdArgs a) {
   __shared__ float sred[kBwdThreads / 64];
   const int hh = blockIdx.x / a.W, k = blockIdx.x % a.W;
@@ -831,7 +838,7 @@ struct BwdShape {
   static constexpr size_t p1 = ((size_t)4 * MP * T + 2 * D * T + NW * 2 * 32 * MP) * 2;
   static constexpr size_t p2 = ((size_t)2 * MP * T + D * T + NW * 4 * 32 * MP) * 2;
   static constexpr size_t fin =
-      (size_t)2 * (kFinTok + 64) * D * 2 + ((size_t)MP * D + 65 + 4 * 65 + kFinTok) * 4;
+      (size_t)2 * kFinRows * D * 2 + ((size_t)MP * D + 65 + 4 * 65 + kFinTok) * 4;
 };
 
 template <int D, int MP>

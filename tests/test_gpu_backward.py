@@ -104,12 +104,14 @@ def test_backward_full_size_sampled():
 
 
 def test_backward_repeatable():
-    """Two calls on one plan give identical bits (the workspace carries no state across
-    calls that changes the result)."""
+    """Two calls on one plan give identical dq, dk, dv bits (the workspace carries no
+    state across calls that changes the result); dw, summed with LDS atomics inside a
+    block, may differ in the order of its fp32 additions only."""
     cfg, lengths = CASES["ragged_m16"]
     x = gen.make_inputs(cfg)
     g_bits, _ = _dout(cfg, cfg.seed)
     a = run_backward(x, g_bits, lengths)
     b = run_backward(x, g_bits, lengths)
-    for u, v in zip(a, b):
+    for u, v in zip(a[:3], b[:3]):
         assert np.array_equal(u, v)
+    np.testing.assert_allclose(a[3], b[3], rtol=1e-5, atol=1e-6 * np.abs(a[3]).max())
