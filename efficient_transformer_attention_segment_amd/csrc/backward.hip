@@ -41,7 +41,9 @@ constexpr int kBwdThreads = 256;  // landmark-sized kernels and the final pass
 // ------------------------------------------------------------------ fp32 block products
 // C[M][N] = alpha op(A) op(B) + beta C. op(A) is A stored [M][K] (lda) or, with TA, A
 // stored [K][M]; op(B) is B stored [K][N] (ldb) or, with TB, B stored [N][K]. Each
-// thread owns 4 x 4 outputs (M, N multiples of 4). C must not alias A or B; no barrier.
+// thread owns 4 x 4 outputs and reads its operands as 16-byte runs, four k at a time:
+// M, N, K multiples of 4, lda and ldb multiples of 4, A and B 16-byte aligned. C must
+// not alias A or B; no barrier inside.
 template <bool TA, bool TB>
 __device__ void blk_mm(float* C, int ldc, const float* A, int lda, const float* B, int ldb,
                        int M, int N, int K, float alpha, float beta) {
@@ -53,16 +55,26 @@ __device__ void blk_mm(float* C, int ldc, const float* A, int lda, const float* 
     for (int r = 0; r < 4; ++r)
 #pragma unroll
       for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-    for (int k = 0; k < K; ++k) {
-      float av[4], bv[4];
+    for (int k = 0; k < K; k += 4) {
+      float av[4][4], bv[4][4];  // av[r][kk] = op(A)[i0 + r][k + kk], bv[kk][c] = op(B)[k + kk][j0 + c]
 #pragma unroll
-      for (int r = 0; r < 4; ++r) av[r] = TA ? A[k * lda + i0 + r] : A[(i0 + r) * lda + k];
+      for (int x = 0; x < 4; ++x) {
+        const f32x4 ra = TA ? *reinterpret_cast<const f32x4*>(A + (k + x) * lda + i0)
+                            : *reinterpret_cast<const f32x4*>(A + (i0 + x) * lda + k);
+        const f32x4 rb = TB ? *reinterpret_cast<const f32x4*>(B + (j0 + x) * ldb + k)
+                            : *reinterpret_cast<const f32x4*>(B + (k + x) * ldb + j0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) bv[c] = TB ? B[(j0 + c) * ldb + k] : B[k * ldb + j0 + c];
+        for (int y = 0; y < 4; ++y) {
+          if (TA) av[y][x] = ra[y]; else av[x][y] = ra[y];
+          if (TB) bv[y][x] = rb[y]; else bv[x][y] = rb[y];
+        }
+      }
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
+      for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int c = 0; c < 4; ++c) acc[r][c] += av[r][kk] * bv[kk][c];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -93,6 +105,49 @@ __device__ void blk_copy_in(float* dst, int ldd, const float* src, int lds_, int
   for (int e = threadIdx.x; e < R * Cc; e += blockDim.x) {
     const int i = e / Cc, j = e % Cc;
     dst[i * ldd + j] = src[(size_t)i * lds_ + j];
+  }
+}
+
+// dst[R][Cc] (ld ldd) = src[R][Cc] (ld lds_) as 16-byte pieces, every load of the copy
+// issued before the first store (one memory latency per copy). R, Cc, ldd, lds_ multiples
+// of 4 where needed, both pointers 16-byte aligned.
+template <int R, int Cc>
+__device__ __forceinline__ void blk_load4(float* dst, int ldd, const float* src, int lds_) {
+  constexpr int N4 = R * Cc / 4, PER = (N4 + kBwdThreads - 1) / kBwdThreads;
+  f32x4 v[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = threadIdx.x + kBwdThreads * u;
+    if (e < N4)
+      v[u] = *reinterpret_cast<const f32x4*>(src + (size_t)(e / (Cc / 4)) * lds_ + 4 * (e % (Cc / 4)));
+  }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = threadIdx.x + kBwdThreads * u;
+    if (e < N4) *reinterpret_cast<f32x4*>(dst + (e / (Cc / 4)) * ldd + 4 * (e % (Cc / 4))) = v[u];
+  }
+}
+
+// dst[R][Cc] = scale * sum over nc slabs (stride elements apart) of src[R][Cc] (ld Cc);
+// the loads of one slab are issued together.
+template <int R, int Cc>
+__device__ __forceinline__ void blk_sum4(float* dst, int ldd, const float* src, size_t stride,
+                                         int nc, float scale) {
+  constexpr int N4 = R * Cc / 4, PER = (N4 + kBwdThreads - 1) / kBwdThreads;
+  f32x4 acc[PER];
+#pragma unroll
+  for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < nc; ++c)
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = threadIdx.x + kBwdThreads * u;
+      if (e < N4) acc[u] += *reinterpret_cast<const f32x4*>(src + c * stride + 4 * (size_t)e);
+    }
+#pragma unroll
+  for (int u = 0; u < PER; ++u) {
+    const int e = threadIdx.x + kBwdThreads * u;
+    if (e < N4)
+      *reinterpret_cast<f32x4*>(dst + (e / (Cc / 4)) * ldd + 4 * (e % (Cc / 4))) = acc[u] * scale;
   }
 }
 
@@ -142,7 +197,7 @@ __device__ __forceinline__ int seg_of(int t, int L, int m) {
 template <int D, int MP>
 __global__ __launch_bounds__(kBwdThreads) void bwd_land_fwd_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float smem[];
-  constexpr int LM = MP + 1, LD = D + 1;
+  constexpr int LM = MP + 4, LD = D + 4;  // 16-byte rows
   float* Am = smem;               // [MP][LM]
   float* Zb = Am + MP * LM;
   float* Xb = Zb + MP * LM;
@@ -159,8 +214,8 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_fwd_kernel(BwdArgs a) {
 
   blk_split_out<true>(a.ktT_hl + (size_t)bh * 2 * D * MP, kt, D, MP, D);
   blk_split_out<true>(a.qtT_hl + (size_t)bh * 2 * D * MP, qt, D, MP, D);
-  blk_copy_in(Qs, LD, qt, D, MP, D);
-  blk_copy_in(Ks, LD, kt, D, MP, D);
+  blk_load4<MP, D>(Qs, LD, qt, D);
+  blk_load4<MP, D>(Ks, LD, kt, D);
   __syncthreads();
   blk_mm<false, true>(Am, LM, Qs, LD, Ks, LD, MP, MP, D, a.scale, 0.f);
   __syncthreads();
@@ -242,32 +297,50 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_fwd_kernel(BwdArgs a) {
     Zn = t;
     blk_copy_out(zs + (it + 1) * mm2, MP, Z, LM, MP, MP);
   }
-  // W = merge of the context partial states (rows >= m zero) and B's statistics
+  // W = merge of the context partial states (rows >= m zero) and B's statistics:
+  // per landmark the merged reference max and sum, then W^T in 16-byte pieces
   const float* pw = a.part_w + (size_t)bh * a.C * D * MP;
   const float* pml = a.part_ml + (size_t)bh * a.C * 2 * MP;
   float* stat = a.stat + (size_t)bh * 2 * MP;
-  for (int e = tid; e < MP * D; e += blockDim.x) {
-    const int j = e % MP, f = e / MP;
-    float val = 0.f;
+  float* cscale = T1;  // [C][MP] per-chunk weight exp2(ml_c - mx) / ls (T1 is free here)
+  if (tid < MP) {
+    const int j = tid;
+    float mx = kNegBig, ls = 0.f;
     if (j < m) {
-      float mx = kNegBig;
       for (int c = 0; c < a.C; ++c) mx = fmaxf(mx, pml[c * 2 * MP + j]);
-      float ls = 0.f, acc = 0.f;
-      for (int c = 0; c < a.C; ++c) {
-        const float sc = fast_exp2(pml[c * 2 * MP + j] - mx);
-        ls += sc * pml[c * 2 * MP + MP + j];
-        acc += sc * pw[((size_t)c * D + f) * MP + j];
-      }
-      val = acc / ls;
-      if (f == 0) {
-        stat[j] = mx;
-        stat[MP + j] = ls;
-      }
-    } else if (f == 0) {
-      stat[j] = 0.f;
-      stat[MP + j] = 1.f;
+      for (int c = 0; c < a.C; ++c) ls += fast_exp2(pml[c * 2 * MP + j] - mx) * pml[c * 2 * MP + MP + j];
+      for (int c = 0; c < a.C; ++c) cscale[c * MP + j] = fast_exp2(pml[c * 2 * MP + j] - mx) / ls;
+    } else {
+      for (int c = 0; c < a.C; ++c) cscale[c * MP + j] = 0.f;
     }
-    Wm[j * LD + f] = val;
+    stat[j] = j < m ? mx : 0.f;
+    stat[MP + j] = j < m ? ls : 1.f;
+  }
+  __syncthreads();
+  {
+    constexpr int N4 = D * MP / 4, PER = (N4 + kBwdThreads - 1) / kBwdThreads;
+    f32x4 acc[PER];
+#pragma unroll
+    for (int u = 0; u < PER; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int c = 0; c < a.C; ++c)
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int e = tid + kBwdThreads * u;  // feature e / (MP/4), landmarks 4 (e % (MP/4)) ..
+        if (e < N4) {
+          const f32x4 w4 = *reinterpret_cast<const f32x4*>(pw + (size_t)c * D * MP + 4 * (size_t)e);
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(cscale + c * MP + 4 * (e % (MP / 4)));
+          acc[u] += w4 * s4;
+        }
+      }
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int e = tid + kBwdThreads * u;
+      if (e < N4) {
+        const int f = e / (MP / 4), j0 = 4 * (e % (MP / 4));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) Wm[(j0 + q) * LD + f] = acc[u][q];
+      }
+    }
   }
   __syncthreads();
   blk_copy_out(a.w + (size_t)bh * MP * D, D, Wm, LD, MP, D);
@@ -417,7 +490,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
 template <int D, int MP>
 __global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
   extern __shared__ __align__(16) float smem[];
-  constexpr int LM = MP + 1, LD = D + 1;
+  constexpr int LM = MP + 4, LD = D + 4;  // 16-byte rows
   const int bh = blockIdx.x, m = a.m, tid = threadIdx.x;
   const size_t mm2 = (size_t)MP * MP;
   __shared__ float sred[kBwdThreads / 64];
@@ -428,16 +501,11 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
   float* rdZ = rZ + MP * LM;          // [MP][LM]
   float* rdW = rdZ + MP * LM;         // [MP][LD]
   const float* p1 = a.part1 + (size_t)bh * a.C * 2 * MP * D;
-  for (int e = tid; e < MP * D; e += blockDim.x) {
-    const int j = e / D, f = e % D;
-    float acc = 0.f;
-    for (int c = 0; c < a.C; ++c) acc += p1[(size_t)c * 2 * MP * D + e];
-    rdY[j * LD + f] = acc;
-  }
+  blk_sum4<MP, D>(rdY, LD, p1, (size_t)2 * MP * D, a.C, 1.f);
   const float* wg = a.w + (size_t)bh * MP * D;
-  blk_copy_in(rW, LD, wg, D, MP, D);
+  blk_load4<MP, D>(rW, LD, wg, D);
   const float* zT = a.zs + ((size_t)bh * (a.iters + 1) + a.iters) * mm2;
-  blk_copy_in(rZ, LM, zT, MP, MP, MP);
+  blk_load4<MP, MP>(rZ, LM, zT, MP);
   __syncthreads();
   blk_mm<false, true>(rdZ, LM, rdY, LD, rW, LD, MP, MP, D, 1.f, 0.f);
   blk_mm<true, false>(rdW, LD, rZ, LM, rdY, LD, MP, D, MP, 1.f, 0.f);
@@ -473,13 +541,13 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
     const int e = tid + kBwdThreads * u;
     if (e < MP * MP) G[(e / MP) * LM + e % MP] = g0[u];
   }
-  blk_copy_in(Am, LM, a.a_s + (size_t)bh * mm2, MP, MP, MP);
+  blk_load4<MP, MP>(Am, LM, a.a_s + (size_t)bh * mm2, MP);
   for (int e = tid; e < MP * LM; e += blockDim.x) dA[e] = 0.f;
   const float* zs = a.zs + (size_t)bh * (a.iters + 1) * mm2;
   const float* xs = a.xs + (size_t)bh * a.iters * mm2;
   for (int it = a.iters - 1; it >= 0; --it) {
-    blk_copy_in(Xb, LM, xs + it * mm2, MP, MP, MP);
-    blk_copy_in(Zb, LM, zs + it * mm2, MP, MP, MP);
+    blk_load4<MP, MP>(Xb, LM, xs + it * mm2, MP);
+    blk_load4<MP, MP>(Zb, LM, zs + it * mm2, MP);
     __syncthreads();
     for (int e = tid; e < MP * MP; e += blockDim.x) {  // P = 7I - X
       const int i = e / MP, j = e % MP;
@@ -554,12 +622,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
   blk_mm<false, false>(a.dqt + (size_t)bh * MP * D, D, Xb, LM, a.kt + (size_t)bh * MP * D, D,
                        MP, D, MP, a.scale, 0.f);
   float* rK = B1;  // [MP][LD] over B1.. (dead)
-  for (int e = tid; e < MP * D; e += blockDim.x) {
-    const int j = e / D, f = e % D;
-    float acc = 0.f;
-    for (int c = 0; c < a.C; ++c) acc += p1[(size_t)c * 2 * MP * D + MP * D + e];
-    rK[j * LD + f] = a.scale * acc;
-  }
+  blk_sum4<MP, D>(rK, LD, p1 + (size_t)MP * D, (size_t)2 * MP * D, a.C, a.scale);
   __syncthreads();
   blk_mm<true, false>(rK, LD, Xb, LM, a.qt + (size_t)bh * MP * D, D, MP, D, MP, a.scale, 1.f);
   __syncthreads();
@@ -832,8 +895,8 @@ template <int D, int MP>
 struct BwdShape {
   static constexpr int NW = D == 128 ? 2 : 4;
   static constexpr int T = 32 * NW;
-  static constexpr size_t l1 = (5 * MP * (MP + 1) + 2 * MP * (D + 1)) * 4;
-  static constexpr size_t l2a = 9 * MP * (MP + 1), l2b = 3 * MP * (D + 1) + 2 * MP * (MP + 1);
+  static constexpr size_t l1 = (5 * MP * (MP + 4) + 2 * MP * (D + 4)) * 4;
+  static constexpr size_t l2a = 9 * MP * (MP + 4), l2b = 3 * MP * (D + 4) + 2 * MP * (MP + 4);
   static constexpr size_t l2 = (l2a > l2b ? l2a : l2b) * 4;
   static constexpr size_t p1 = ((size_t)4 * MP * T + 2 * D * T + NW * 2 * 32 * MP) * 2;
   static constexpr size_t p2 = ((size_t)2 * MP * T + D * T + NW * 4 * 32 * MP) * 2;
