@@ -181,6 +181,27 @@ __device__ __forceinline__ f32x16 mma_rows(f32x16 acc, const uint16_t* ahi, cons
   return acc;
 }
 
+// Same product with B given as a row-major tile bt[K][ldb] (k rows, output columns
+// col0.. across), read with LDS transpose reads: lane 4j + q of each 16-lane group
+// addresses row k + j, column col0 + 16 (group & 1) + 4q, and receives column
+// col0 + lane % 32 at k-slots 8h .. 8h + 7. B is exact bf16.
+template <int K, bool AL>
+__device__ __forceinline__ f32x16 mma_rows_btr(f32x16 acc, const uint16_t* ahi,
+                                               const uint16_t* alo, const uint16_t* bt, int ldb,
+                                               int col0, int lane) {
+  const int h = lane >> 5, trj = (lane & 15) >> 2;
+  const int trc = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+#pragma unroll
+  for (int k0 = 0; k0 < K; k0 += 16) {
+    const int kk = k0 + 8 * h;
+    const Pair8 x{ld8(ahi + kk), AL ? ld8(alo + kk) : zero8()};
+    const Pair8 y{lds_tr16x2(bt + (kk + trj) * ldb + trc, bt + (kk + 4 + trj) * ldb + trc),
+                  zero8()};
+    acc = mfma_pair<AL, false>(x, y, acc);
+  }
+  return acc;
+}
+
 // Token row held by accumulator register rr of lane half h (within a 32-row tile).
 __device__ __forceinline__ int acc_r(int rr, int h) { return 8 * (rr >> 2) + 4 * h + (rr & 3); }
 
@@ -360,10 +381,10 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
   uint16_t* ft_lo = ft_hi + MP * T;
   uint16_t* st_hi = ft_lo + MP * T;                     // dSF^T [MP][T]
   uint16_t* st_lo = st_hi + MP * T;
-  uint16_t* qT = st_lo + MP * T;                        // Q^T   [D][T]
-  uint16_t* oT = qT + D * T;                            // dO^T  [D][T]
+  uint16_t* qR = st_lo + MP * T;                        // Q     [T][D] (step's tokens)
+  uint16_t* oR = qR + T * D;                            // dO    [T][D]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
-  uint16_t* ds_hi = oT + D * T + wave * 2 * 32 * MP;    // dSF   [32][MP] per wave
+  uint16_t* ds_hi = oR + T * D + wave * 2 * 32 * MP;    // dSF   [32][MP] per wave
   uint16_t* ds_lo = ds_hi + 32 * MP;
   int bh, c;
   xcd_map(blockIdx.x, a.BH, a.C, bh, c);
@@ -386,7 +407,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
 
   for (int t0 = tb; t0 < te; t0 += T) {
     const int tw = t0 + 32 * wave;
-    // transposed copies of this wave's Q and dO rows (zeros past the chunk's valid end)
+    // this wave's Q and dO rows, row-major (zeros past the chunk's valid end)
+#pragma unroll
     for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
       const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, tok = tw + i;
       u32x4 qv{0u, 0u, 0u, 0u}, ov{0u, 0u, 0u, 0u};
@@ -394,11 +416,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
         qv = *reinterpret_cast<const u32x4*>(q + (size_t)tok * D + f8);
         ov = *reinterpret_cast<const u32x4*>(dO + (size_t)tok * D + f8);
       }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        qT[(f8 + e) * T + 32 * wave + i] = (uint16_t)(qv[e >> 1] >> (16 * (e & 1)));
-        oT[(f8 + e) * T + 32 * wave + i] = (uint16_t)(ov[e >> 1] >> (16 * (e & 1)));
-      }
+      *reinterpret_cast<u32x4*>(qR + (32 * wave + i) * D + f8) = qv;
+      *reinterpret_cast<u32x4*>(oR + (32 * wave + i) * D + f8) = ov;
     }
     // S = Q Kt^T and dF = dO Y^T for 32 tokens: lane = landmark, registers = tokens
     const int trow = min(tw + r32, L - 1);
@@ -469,8 +488,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
         const int which = ti / (LT * FT), rem = ti % (LT * FT), at = rem / FT, bt = rem % FT;
         const uint16_t* ah = (which == 0 ? ft_hi : st_hi) + (32 * at + r32) * T;
         const uint16_t* alo = (which == 0 ? ft_lo : st_lo) + (32 * at + r32) * T;
-        const uint16_t* bt_ = (which == 0 ? oT : qT) + (32 * bt + r32) * T;
-        red[u] = mma_rows<T, true, false>(red[u], ah, alo, bt_, nullptr, h);
+        red[u] = mma_rows_btr<T, true>(red[u], ah, alo, which == 0 ? oR : qR, D, 32 * bt, lane);
       }
     }
     __syncthreads();
@@ -637,9 +655,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
   extern __shared__ __align__(16) char lds[];
   uint16_t* sT_hi = reinterpret_cast<uint16_t*>(lds);  // dSB^T [MP][T] (landmark rows)
   uint16_t* sT_lo = sT_hi + MP * T;
-  uint16_t* kT = sT_lo + MP * T;                        // K^T   [D][T]
+  uint16_t* kR = sT_lo + MP * T;                        // K     [T][D] (step's tokens)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
-  uint16_t* bm_hi = kT + D * T + wave * 4 * 32 * MP;    // B (token rows) [32][MP]
+  uint16_t* bm_hi = kR + T * D + wave * 4 * 32 * MP;    // B (token rows) [32][MP]
   uint16_t* bm_lo = bm_hi + 32 * MP;
   uint16_t* sb_hi = bm_lo + 32 * MP;                    // dSB (token rows) [32][MP]
   uint16_t* sb_lo = sb_hi + 32 * MP;
@@ -677,13 +695,12 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
 
   for (int t0 = tb; t0 < te; t0 += T) {
     const int tw = t0 + 32 * wave;
+#pragma unroll
     for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
       const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, tok = tw + i;
       u32x4 kv{0u, 0u, 0u, 0u};
       if (tok < te) kv = *reinterpret_cast<const u32x4*>(kk + (size_t)tok * D + f8);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        kT[(f8 + e) * T + 32 * wave + i] = (uint16_t)(kv[e >> 1] >> (16 * (e & 1)));
+      *reinterpret_cast<u32x4*>(kR + (32 * wave + i) * D + f8) = kv;
     }
     const int trow = min(tw + r32, L - 1);
     f32x16 sc[LT], db[LT];
@@ -742,9 +759,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
       const int ti = wave + NW * u;
       if (ti < NRED) {
         const int at = ti / FT, bt = ti % FT;
-        red[u] = mma_rows<T, true, false>(red[u], sT_hi + (32 * at + r32) * T,
-                                          sT_lo + (32 * at + r32) * T, kT + (32 * bt + r32) * T,
-                                          nullptr, h);
+        red[u] = mma_rows_btr<T, true>(red[u], sT_hi + (32 * at + r32) * T,
+                                       sT_lo + (32 * at + r32) * T, kR, D, 32 * bt, lane);
       }
     }
     __syncthreads();
