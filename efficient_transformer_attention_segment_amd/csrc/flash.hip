@@ -17,8 +17,9 @@
 //                        chunk when causal)
 //   flash_attend_kernel  one block per (head, chunk), one wave per 32 queries: local
 //                        attention with an online softmax over 32-key tiles (scores on
-//                        MFMA with keys across lanes, half-wave reductions, P as hi/lo
-//                        bf16 through LDS, V^T staged in LDS), then + Q M_g, bf16 store
+//                        MFMA with queries across lanes and keys in registers, P kept in
+//                        registers as hi/lo bf16, V row-major in LDS read transposed),
+//                        then + Q M_g, bf16 store
 #include "nys_common.h"
 #include "nys_kernels.h"
 
@@ -109,93 +110,111 @@ __global__ __launch_bounds__(256) void flash_scan_kernel(FlashArgs a) {
 }
 
 // ------------------------------------------------------------------ local + global
+// One wave per 32 queries, in the transposed orientation: S^T = K Q^T puts each query on
+// a lane and its keys in the accumulator registers (key 8 (r/4) + 4 h + r % 4 of the
+// tile in register r of lane half h), so the online max and sum need one exchange with
+// the other half per tile. P stays in registers and is the B operand of
+// O^T += V^T P^T directly: for k-step s, registers 8 s .. 8 s + 7 hold keys
+// 16 s + 4 h + (0..3) and 16 s + 8 + 4 h + (0..3), so the A operand reads V^T in that key
+// order -- two 4-row transpose reads of the row-major V tile at rows 16 s + 4 h and
+// 16 s + 8 + 4 h.
 template <int D, int C>
 __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
-  constexpr int NW = C / 32, LT = C + 8, LP = 40, FT = D / 32;
+  constexpr int FT = D / 32;
   extern __shared__ __align__(16) char lds[];
-  uint16_t* vT = reinterpret_cast<uint16_t*>(lds);   // V^T [D][LT]
+  uint16_t* vS = reinterpret_cast<uint16_t*>(lds);   // V [C][D] (row-major)
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
-  uint16_t* p_hi = vT + D * LT + wave * 2 * 32 * LP;  // P [32][LP] per wave
-  uint16_t* p_lo = p_hi + 32 * LP;
   int bh, g;
   xcd_map(blockIdx.x, a.BH, a.G, bh, g);
   const int t0 = g * C, t1 = min(t0 + C, a.n);
   const uint16_t* q = a.q + (size_t)bh * a.n * D;
   const uint16_t* k = a.k + (size_t)bh * a.n * D;
   const uint16_t* v = a.v + (size_t)bh * a.n * D;
+#pragma unroll 4
   for (int e = threadIdx.x; e < C * (D / 8); e += blockDim.x) {
     const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = t0 + i;
     u32x4 vv{0u, 0u, 0u, 0u};
     if (t < t1) vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) vT[(f8 + u) * LT + i] = (uint16_t)(vv[u >> 1] >> (16 * (u & 1)));
+    *reinterpret_cast<u32x4*>(vS + i * D + f8) = vv;
   }
   __syncthreads();
   const int q0 = t0 + 32 * wave;  // this wave's first query
   if (q0 >= t1) return;           // no barrier follows
-  const int qrow = min(q0 + r32, t1 - 1);
-  bf16x8 qa[D / 16];
+  const int qi = q0 + r32;        // the lane's query
+  const int qrow = min(qi, t1 - 1);
+  bf16x8 qb[D / 16];              // B operand: query qrow, features 16 s + 8 h ..
 #pragma unroll
-  for (int s = 0; s < D / 16; ++s) qa[s] = ld8(q + (size_t)qrow * D + 16 * s + 8 * h);
-  f32x16 o[FT];
+  for (int s = 0; s < D / 16; ++s) qb[s] = ld8(q + (size_t)qrow * D + 16 * s + 8 * h);
+  f32x16 o[FT];                   // O^T: features 32 f + row, this lane's query
 #pragma unroll
   for (int f = 0; f < FT; ++f) o[f] = zero16();
-  float mrow[16], lrow[16];
-#pragma unroll
-  for (int rr = 0; rr < 16; ++rr) {
-    mrow[rr] = kNegBig;
-    lrow[rr] = 0.f;
-  }
+  float mrow = kNegBig, lrow = 0.f;
   const float sl = a.scale_log2e;
+  const int trj = (lane & 15) >> 2, trc = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int ntile = a.causal ? wave + 1 : (t1 - t0 + 31) / 32;
   for (int kt = 0; kt < ntile; ++kt) {
-    const int k0 = t0 + 32 * kt, key = k0 + r32;  // lane's key
-    const int krow = min(key, t1 - 1);
+    const int k0 = t0 + 32 * kt;
+    const uint16_t* krow = k + (size_t)min(k0 + r32, t1 - 1) * D;  // A operand: key rows
     f32x16 sc = zero16();
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      sc = mfma(qa[s], ld8(k + (size_t)krow * D + 16 * s + 8 * h), sc);
-    f32x16 p;
+    for (int s = 0; s < D / 16; ++s) sc = mfma(ld8(krow + 16 * s + 8 * h), qb[s], sc);
+    float mx = kNegBig;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const int qi = q0 + fl_row(rr, h);
+      const int key = k0 + fl_row(rr, h);
       const bool ok = key < t1 && (!a.causal || key <= qi);
-      const float x = ok ? sc[rr] * sl : kNegBig;
-      const float mn = fmaxf(mrow[rr], half_max(x));
-      const float corr = fast_exp2(mrow[rr] - mn);
-      const float e = ok ? fast_exp2(x - mn) : 0.f;
-      lrow[rr] = lrow[rr] * corr + half_sum(e);
-      mrow[rr] = mn;
-      p[rr] = e;
-#pragma unroll
-      for (int f = 0; f < FT; ++f) o[f][rr] *= corr;
+      sc[rr] = ok ? sc[rr] * sl : kNegBig;
+      mx = fmaxf(mx, sc[rr]);
     }
-    store_rows_hl(p_hi, p_lo, LP, 0, 0, p, lane);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mn = fmaxf(mrow, mx), corr = fast_exp2(mrow - mn);
+    float ps = 0.f, pe[16];
 #pragma unroll
-    for (int f = 0; f < FT; ++f)
-      o[f] = fl_mma<32, true, false>(o[f], p_hi + r32 * LP, p_lo + r32 * LP,
-                                     vT + (32 * f + r32) * LT + 32 * kt, nullptr, h);
+    for (int rr = 0; rr < 16; ++rr) {
+      pe[rr] = sc[rr] > 0.5f * kNegBig ? fast_exp2(sc[rr] - mn) : 0.f;
+      ps += pe[rr];
+    }
+    Pair8 pb[2];
+#pragma unroll
+    for (int s2 = 0; s2 < 2; ++s2) pb[s2] = split8(pe + 8 * s2);
+    ps += __shfl_xor(ps, 32);
+    lrow = lrow * corr + ps;
+    mrow = mn;
+#pragma unroll
+    for (int f = 0; f < FT; ++f) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) o[f][rr] *= corr;
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const uint16_t* base = vS + 32 * f + trc;
+        const int r0 = 32 * kt + 16 * s2 + 4 * h + trj;
+        const bf16x8 va = lds_tr16x2(base + r0 * D, base + (r0 + 8) * D);
+        o[f] = mfma_pair<false, true>(Pair8{va, zero8()}, pb[s2], o[f]);
+      }
+    }
   }
-  // + Q M_g (planes already scaled by s / n_g), then the bf16 store
+  // + (M^T Q^T) from the planes (already scaled by s / n_g), then the bf16 store
   const uint16_t* pl = a.mplanes + ((size_t)bh * (a.causal ? a.G : 1) + (a.causal ? g : 0)) *
                                        2 * D * D;
   uint16_t* out = a.out + (size_t)bh * a.n * D;
+  const float inv = 1.f / lrow;
 #pragma unroll
   for (int f = 0; f < FT; ++f) {
     f32x16 gl = zero16();
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) {
       const uint16_t* row = pl + (size_t)(32 * f + r32) * D + 16 * s + 8 * h;
-      const Pair8 x{qa[s], zero8()};
-      const Pair8 y{ld8(row), ld8(row + D * D)};
-      gl = mfma_pair<false, true>(x, y, gl);
+      gl = mfma_pair<true, false>(Pair8{ld8(row), ld8(row + D * D)}, Pair8{qb[s], zero8()}, gl);
     }
+    if (qi < t1) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int qi = q0 + fl_row(rr, h);
-      if (qi < t1) {
-        const float val = o[f][rr] / lrow[rr] + gl[rr];
-        out[(size_t)qi * D + 32 * f + r32] = __builtin_bit_cast(uint16_t, bf16_rne(val));
+      for (int g4 = 0; g4 < 4; ++g4) {
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = o[f][4 * g4 + e] * inv + gl[4 * g4 + e];
+        const bf16x2 lo2 = bf16_rne2(x[0], x[1]), hi2 = bf16_rne2(x[2], x[3]);
+        *reinterpret_cast<u32x2*>(out + (size_t)qi * D + 32 * f + 8 * g4 + 4 * h) =
+            u32x2{__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2)};
       }
     }
   }
@@ -205,7 +224,7 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
 template <int D, int C>
 struct FlashShape {
   static constexpr size_t state_lds = (size_t)2 * D * (C + 8) * 2;
-  static constexpr size_t attend_lds = (size_t)D * (C + 8) * 2 + (size_t)(C / 32) * 2 * 32 * 40 * 2;
+  static constexpr size_t attend_lds = (size_t)C * D * 2;
 };
 
 template <int D, int C>
