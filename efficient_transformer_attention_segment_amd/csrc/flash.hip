@@ -10,7 +10,7 @@
 // covered = every chunk (non-causal) or the chunks before g (causal; n_g = g c, and
 // chunk 0 has no global term).
 //
-//   flash_state_kernel   one block per (head, chunk): S_g = K_g^T V_g (d x d, fp32) on
+//   flash_state_kernel   one block per (head, chunk): S_g^T = V_g^T K_g (d x d, fp32) on
 //                        MFMA from transposed bf16 copies of the chunk in LDS
 //   flash_scan_kernel    one block per head: the global sums, scaled by s / n_g and
 //                        stored as hi/lo bf16 planes of M^T (one per head, or one per
@@ -68,10 +68,12 @@ __global__ __launch_bounds__(256) void flash_state_kernel(FlashArgs a) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
   constexpr int FT = D / 32;
   float* st = a.states + ((size_t)bh * a.G + g) * D * D;
+  // S_g^T = V^T K (row j, column i = sum_t V[t][j] K[t][i]), stored row-major so the
+  // global sums read and write M^T rows contiguously
   for (int tile = wave; tile < FT * FT; tile += 4) {
     const int ti = tile / FT, tj = tile % FT;
-    const f32x16 acc = fl_mma<C, false, false>(zero16(), kT + (32 * ti + r32) * LT, nullptr,
-                                               vT + (32 * tj + r32) * LT, nullptr, h);
+    const f32x16 acc = fl_mma<C, false, false>(zero16(), vT + (32 * ti + r32) * LT, nullptr,
+                                               kT + (32 * tj + r32) * LT, nullptr, h);
     store_rows_f32(st, D, 32 * ti, 32 * tj, acc, lane);
   }
 }
@@ -96,12 +98,12 @@ __global__ __launch_bounds__(256) void flash_scan_kernel(FlashArgs a) {
     const float sc = ncov > 0 ? a.scale / (float)ncov : 0.f;
     uint16_t* pl = a.mplanes + ((size_t)bh * nplanes + g) * 2 * D * D;
 #pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int e = threadIdx.x + 256 * u, i = e / D, j = e % D;  // M[i][j] -> M^T[j][i]
+    for (int u = 0; u < PER; ++u) {  // run holds M^T row-major (the states are S_g^T)
+      const int e = threadIdx.x + 256 * u;
       uint16_t hi, lo;
       split1(run[u] * sc, hi, lo);
-      pl[j * D + i] = hi;
-      pl[D * D + j * D + i] = lo;
+      pl[e] = hi;
+      pl[D * D + e] = lo;
     }
     if (a.causal)
 #pragma unroll

@@ -126,7 +126,7 @@ struct FlashArgs {
   const uint16_t* k;
   const uint16_t* v;
   uint16_t* out;            // [BH][n][d]
-  float* states;            // [BH][G][d][d]  K_g^T V_g
+  float* states;            // [BH][G][d][d]  (K_g^T V_g)^T
   uint16_t* mplanes;        // [BH][causal ? G : 1][2][d][d]  hi/lo of (s / n_g) M_g^T
   int BH, n, d, chunk, G, causal;
   float scale, scale_log2e;
