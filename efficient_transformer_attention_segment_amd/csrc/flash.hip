@@ -11,7 +11,7 @@
 // chunk 0 has no global term).
 //
 //   flash_state_kernel   one block per (head, chunk): S_g^T = V_g^T K_g (d x d, fp32) on
-//                        MFMA from transposed bf16 copies of the chunk in LDS
+//                        MFMA, the chunk staged row-major in LDS and read transposed
 //   flash_scan_kernel    one block per head: the global sums, scaled by s / n_g and
 //                        stored as hi/lo bf16 planes of M^T (one per head, or one per
 //                        chunk when causal)
@@ -25,32 +25,30 @@
 
 namespace nys {
 
-template <int K, bool AL, bool BL>
-__device__ __forceinline__ f32x16 fl_mma(f32x16 acc, const uint16_t* ahi, const uint16_t* alo,
-                                         const uint16_t* bhi, const uint16_t* blo, int h) {
-#pragma unroll
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    const Pair8 x{ld8(ahi + k0 + 8 * h), AL ? ld8(alo + k0 + 8 * h) : zero8()};
-    const Pair8 y{ld8(bhi + k0 + 8 * h), BL ? ld8(blo + k0 + 8 * h) : zero8()};
-    acc = mfma_pair<AL, BL>(x, y, acc);
-  }
-  return acc;
-}
-
 __device__ __forceinline__ int fl_row(int rr, int h) { return 8 * (rr >> 2) + 4 * h + (rr & 3); }
 
+// Eight k values (rows k .. k + 7 of a row-major bf16 tile with row stride ld) of column
+// col0 + lane % 32, as an MFMA operand: LDS transpose reads, lane 4j + q of each 16-lane
+// group addressing row k + j, column col0 + 16 (group & 1) + 4q.
+__device__ __forceinline__ bf16x8 fl_tr8(const uint16_t* tile, int ld, int k, int col0, int lane) {
+  const int trj = (lane & 15) >> 2, trc = col0 + 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
+  return lds_tr16x2(tile + (k + trj) * ld + trc, tile + (k + 4 + trj) * ld + trc);
+}
+
 // ------------------------------------------------------------------ chunk states
+// S_g^T = V_g^T K_g: the chunk's K and V rows are staged row-major (16-byte writes) and
+// both operands, which contract over tokens, come from LDS transpose reads.
 template <int D, int C>
 __global__ __launch_bounds__(256) void flash_state_kernel(FlashArgs a) {
-  constexpr int LT = C + 8;  // padded row of the transposed copies
   extern __shared__ __align__(16) char lds[];
-  uint16_t* kT = reinterpret_cast<uint16_t*>(lds);  // K^T [D][LT]
-  uint16_t* vT = kT + D * LT;                         // V^T [D][LT]
+  uint16_t* kS = reinterpret_cast<uint16_t*>(lds);  // K [C][D]
+  uint16_t* vS = kS + C * D;                          // V [C][D]
   int bh, g;
   xcd_map(blockIdx.x, a.BH, a.G, bh, g);
   const int t0 = g * C, t1 = min(t0 + C, a.n);
   const uint16_t* k = a.k + (size_t)bh * a.n * D;
   const uint16_t* v = a.v + (size_t)bh * a.n * D;
+#pragma unroll 4
   for (int e = threadIdx.x; e < C * (D / 8); e += blockDim.x) {
     const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = t0 + i;
     u32x4 kv{0u, 0u, 0u, 0u}, vv{0u, 0u, 0u, 0u};
@@ -58,22 +56,21 @@ __global__ __launch_bounds__(256) void flash_state_kernel(FlashArgs a) {
       kv = *reinterpret_cast<const u32x4*>(k + (size_t)t * D + f8);
       vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      kT[(f8 + q) * LT + i] = (uint16_t)(kv[q >> 1] >> (16 * (q & 1)));
-      vT[(f8 + q) * LT + i] = (uint16_t)(vv[q >> 1] >> (16 * (q & 1)));
-    }
+    *reinterpret_cast<u32x4*>(kS + i * D + f8) = kv;
+    *reinterpret_cast<u32x4*>(vS + i * D + f8) = vv;
   }
   __syncthreads();
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
   constexpr int FT = D / 32;
   float* st = a.states + ((size_t)bh * a.G + g) * D * D;
-  // S_g^T = V^T K (row j, column i = sum_t V[t][j] K[t][i]), stored row-major so the
-  // global sums read and write M^T rows contiguously
   for (int tile = wave; tile < FT * FT; tile += 4) {
     const int ti = tile / FT, tj = tile % FT;
-    const f32x16 acc = fl_mma<C, false, false>(zero16(), vT + (32 * ti + r32) * LT, nullptr,
-                                               kT + (32 * tj + r32) * LT, nullptr, h);
+    f32x16 acc = zero16();
+#pragma unroll 4
+    for (int k0 = 0; k0 < C; k0 += 16) {
+      const int kk = k0 + 8 * h;
+      acc = mfma(fl_tr8(vS, D, kk, 32 * ti, lane), fl_tr8(kS, D, kk, 32 * tj, lane), acc);
+    }
     store_rows_f32(st, D, 32 * ti, 32 * tj, acc, lane);
   }
 }
@@ -225,7 +222,7 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
 // ------------------------------------------------------------------ host side
 template <int D, int C>
 struct FlashShape {
-  static constexpr size_t state_lds = (size_t)2 * D * (C + 8) * 2;
+  static constexpr size_t state_lds = (size_t)2 * C * D * 2;
   static constexpr size_t attend_lds = (size_t)C * D * 2;
 };
 
