@@ -153,13 +153,16 @@ __device__ __forceinline__ void blk_sum4(float* dst, int ldd, const float* src, 
 
 // hi/lo planes of an fp32 matrix src [R][Cc] (ld lds_): row-major [R][Cc] or transposed
 // [Cc][R] (plane stride R * Cc).
-template <bool kTrans>
+// With kPerm (transposed only), row i of src lands at column (i & ~15) | kslot_perm(i & 15):
+// the k order in which accumulator registers feed the next product as its B operand.
+template <bool kTrans, bool kPerm = false>
 __device__ void blk_split_out(uint16_t* hl, const float* src, int lds_, int R, int Cc) {
   for (int e = threadIdx.x; e < R * Cc; e += blockDim.x) {
     const int i = kTrans ? e % R : e / Cc, j = kTrans ? e / R : e % Cc;
     uint16_t hi, lo;
     split1(src[(size_t)i * lds_ + j], hi, lo);
-    const size_t o = kTrans ? (size_t)j * R + i : (size_t)i * Cc + j;
+    const int ip = kPerm ? ((i & ~15) | kslot_perm(i & 15)) : i;
+    const size_t o = kTrans ? (size_t)j * R + ip : (size_t)i * Cc + j;
     hl[o] = hi;
     hl[(size_t)R * Cc + o] = lo;
   }
@@ -234,7 +237,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_fwd_kernel(BwdArgs a) {
   const float* kt = a.kt + (size_t)bh * MP * D;
 
   blk_split_out<true>(a.ktT_hl + (size_t)bh * 2 * D * MP, kt, D, MP, D);
-  blk_split_out<true>(a.qtT_hl + (size_t)bh * 2 * D * MP, qt, D, MP, D);
+  blk_split_out<true, true>(a.qtT_hl + (size_t)bh * 2 * D * MP, qt, D, MP, D);
   blk_load4<MP, D>(Qs, LD, qt, D);
   blk_load4<MP, D>(Ks, LD, kt, D);
   __syncthreads();
@@ -534,7 +537,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
     a.db[(size_t)bh * MP + tid] = acc;
   }
   blk_split_out<false>(a.dw_hl + (size_t)bh * 2 * MP * D, rdW, LD, MP, D);
-  blk_split_out<true>(a.dwT_hl + (size_t)bh * 2 * D * MP, rdW, LD, MP, D);
+  blk_split_out<true, true>(a.dwT_hl + (size_t)bh * 2 * D * MP, rdW, LD, MP, D);
   // dZ into registers (the loop's buffers overlap phase 1)
   constexpr int PER = (MP * MP + kBwdThreads - 1) / kBwdThreads;
   float g0[PER];
@@ -648,19 +651,24 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
 }
 
 // ======================================================================= pass 2
+// Transposed orientation: S^T = Qt K^T and dB^T = dW V^T put each token on a lane and its
+// landmarks in the accumulator registers (landmark 32 lt + 8 (r/4) + 4 h + r % 4 in
+// register r of lane half h). B and dSB then feed dK^T = Qt^T dSB and dV^T = dW^T B as
+// B operands straight from the registers; Qt^T and dW^T are stored with each group of 16
+// landmarks in that register order (kslot_perm). Only dSB^T goes through LDS, for the
+// reduction over tokens.
 template <int D, int MP, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
   constexpr int T = 32 * NW, LT = MP / 32, FT = D / 32;
   constexpr int NRED = LT * FT, RPW = (NRED + NW - 1) / NW;
   extern __shared__ __align__(16) char lds[];
-  uint16_t* sT_hi = reinterpret_cast<uint16_t*>(lds);  // dSB^T [MP][T] (landmark rows)
+  uint16_t* sT_hi = reinterpret_cast<uint16_t*>(lds);  // dSB [MP][T] (landmark rows)
   uint16_t* sT_lo = sT_hi + MP * T;
-  uint16_t* kR = sT_lo + MP * T;                        // K     [T][D] (step's tokens)
+  uint16_t* kR = sT_lo + MP * T;                        // K   [T][D] (step's tokens)
+  float* smx = reinterpret_cast<float*>(kR + T * D);   // per landmark: max, 1/sum, D_B
+  float* sinv = smx + MP;
+  float* sdb = sinv + MP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
-  uint16_t* bm_hi = kR + T * D + wave * 4 * 32 * MP;    // B (token rows) [32][MP]
-  uint16_t* bm_lo = bm_hi + 32 * MP;
-  uint16_t* sb_hi = bm_lo + 32 * MP;                    // dSB (token rows) [32][MP]
-  uint16_t* sb_lo = sb_hi + 32 * MP;
   int bh, c;
   xcd_map(blockIdx.x, a.BH, a.C, bh, c);
   const int m = a.m, L = valid_length(a.lengths, bh, a.H, a.n, a.m);
@@ -675,81 +683,91 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
   const uint16_t* qT_lo = qT_hi + D * MP;
   const uint16_t* wT_hi = a.dwT_hl + (size_t)bh * 2 * D * MP;
   const uint16_t* wT_lo = wT_hi + D * MP;
-  const float* stat = a.stat + (size_t)bh * 2 * MP;
-  const float* dbv = a.db + (size_t)bh * MP;
   const float* dkt = a.dkt + (size_t)bh * MP * D;
   uint16_t* dk = a.dk + (size_t)bh * a.n * D;
   float* dvp = a.dv_part + (size_t)bh * a.n * D;
   const float sl = a.scale_log2e;
-  float smx[LT], sinv[LT], sdb[LT];
-#pragma unroll
-  for (int lt = 0; lt < LT; ++lt) {
-    const int j = 32 * lt + r32;
-    smx[lt] = stat[j];
-    sinv[lt] = 1.f / stat[MP + j];
-    sdb[lt] = dbv[j];
+  for (int j = threadIdx.x; j < MP; j += blockDim.x) {
+    const float* stat = a.stat + (size_t)bh * 2 * MP;
+    smx[j] = stat[j];
+    sinv[j] = 1.f / stat[MP + j];
+    sdb[j] = a.db[(size_t)bh * MP + j];
   }
+  __syncthreads();
   f32x16 red[RPW];
 #pragma unroll
   for (int u = 0; u < RPW; ++u) red[u] = zero16();
 
   for (int t0 = tb; t0 < te; t0 += T) {
-    const int tw = t0 + 32 * wave;
+    const int tw = t0 + 32 * wave, tok = tw + r32;  // the lane's token
+    const bool tv = tok < te;
 #pragma unroll
     for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
-      const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, tok = tw + i;
+      const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, t = tw + i;
       u32x4 kv{0u, 0u, 0u, 0u};
-      if (tok < te) kv = *reinterpret_cast<const u32x4*>(kk + (size_t)tok * D + f8);
+      if (t < te) kv = *reinterpret_cast<const u32x4*>(kk + (size_t)t * D + f8);
       *reinterpret_cast<u32x4*>(kR + (32 * wave + i) * D + f8) = kv;
     }
-    const int trow = min(tw + r32, L - 1);
-    f32x16 sc[LT], db[LT];
+    const int trow = min(tok, L - 1);
+    f32x16 sb[LT], db[LT];  // B and dSB: landmark rows, this lane's token
 #pragma unroll
     for (int lt = 0; lt < LT; ++lt) {
       const size_t lr = (size_t)(32 * lt + r32) * D;
-      sc[lt] = mma_rows<D, false, true>(zero16(), kk + (size_t)trow * D, nullptr, qt_hi + lr,
-                                        qt_lo + lr, h);
-      db[lt] = mma_rows<D, false, true>(zero16(), vv + (size_t)trow * D, nullptr, dw_hi + lr,
-                                        dw_lo + lr, h);
+      sb[lt] = mma_rows<D, true, false>(zero16(), qt_hi + lr, qt_lo + lr, kk + (size_t)trow * D,
+                                        nullptr, h);
+      db[lt] = mma_rows<D, true, false>(zero16(), dw_hi + lr, dw_lo + lr, vv + (size_t)trow * D,
+                                        nullptr, h);
     }
 #pragma unroll
     for (int lt = 0; lt < LT; ++lt) {
-      const bool jv = 32 * lt + r32 < m;
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
-        const bool v = jv && (tw + acc_r(rr, h) < te);
-        const float b = v ? fast_exp2(sc[lt][rr] * sl - smx[lt]) * sinv[lt] : 0.f;
-        sc[lt][rr] = b;
-        db[lt][rr] = v ? b * (db[lt][rr] - sdb[lt]) : 0.f;
+        const int j = 32 * lt + acc_r(rr, h);
+        const bool v = tv && j < m;
+        const float b = v ? fast_exp2(sb[lt][rr] * sl - smx[j]) * sinv[j] : 0.f;
+        sb[lt][rr] = b;
+        db[lt][rr] = v ? b * (db[lt][rr] - sdb[j]) : 0.f;
       }
-      store_rows_hl(bm_hi, bm_lo, MP, 0, 32 * lt, sc[lt], lane);
-      store_rows_hl(sb_hi, sb_lo, MP, 0, 32 * lt, db[lt], lane);
-      store_cols_hl(sT_hi, sT_lo, T, 32 * wave, 32 * lt, db[lt], lane);
+      store_rows_hl(sT_hi, sT_lo, T, 32 * lt, 32 * wave, db[lt], lane);
     }
-    // dK = s dSB Qt + dKt[seg] / |seg|  and  B^T dW  for the wave's 32 tokens
-    int segj[16];
-    float seginv[16];
+    // B operands from the registers: k-step s covers landmarks 16 s .. 16 s + 15, held in
+    // registers 8 (s % 2) .. 8 (s % 2) + 7 of tile s / 2
+    Pair8 pb[2 * LT], pd[2 * LT];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int tok = min(tw + acc_r(rr, h), L - 1);
-      segj[rr] = seg_of(tok, L, m);
-      seginv[rr] = 1.f / (float)(seg_start(segj[rr] + 1, L, m) - seg_start(segj[rr], L, m));
+    for (int s = 0; s < 2 * LT; ++s) {
+      float x[8], y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = sb[s / 2][8 * (s % 2) + e];
+        y[e] = db[s / 2][8 * (s % 2) + e];
+      }
+      pb[s] = split8(x);
+      pd[s] = split8(y);
     }
+    const int segj = seg_of(min(tok, L - 1), L, m);
+    const float seginv = 1.f / (float)(seg_start(segj + 1, L, m) - seg_start(segj, L, m));
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      const size_t br = (size_t)(32 * ft + r32) * MP;
-      const f32x16 gk = mma_rows<MP, true, true>(zero16(), sb_hi + r32 * MP, sb_lo + r32 * MP,
-                                                 qT_hi + br, qT_lo + br, h);
-      const f32x16 gv = mma_rows<MP, true, true>(zero16(), bm_hi + r32 * MP, bm_lo + r32 * MP,
-                                                 wT_hi + br, wT_lo + br, h);
-      const int f = 32 * ft + r32;
+      f32x16 gk = zero16(), gv = zero16();
 #pragma unroll
-      for (int rr = 0; rr < 16; ++rr) {
-        const int tok = tw + acc_r(rr, h);
-        if (tok < te) {
-          const float val = a.scale * gk[rr] + dkt[(size_t)segj[rr] * D + f] * seginv[rr];
-          dk[(size_t)tok * D + f] = __builtin_bit_cast(uint16_t, bf16_rne(val));
-          dvp[(size_t)tok * D + f] = gv[rr];
+      for (int s = 0; s < 2 * LT; ++s) {
+        const size_t ar = (size_t)(32 * ft + r32) * MP + 16 * s + 8 * h;
+        gk = mfma_pair<true, true>(Pair8{ld8(qT_hi + ar), ld8(qT_lo + ar)}, pd[s], gk);
+        gv = mfma_pair<true, true>(Pair8{ld8(wT_hi + ar), ld8(wT_lo + ar)}, pb[s], gv);
+      }
+      if (tv) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const int f0 = 32 * ft + 8 * g4 + 4 * h;
+          const f32x4 kt4 = *reinterpret_cast<const f32x4*>(dkt + (size_t)segj * D + f0);
+          float x[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = a.scale * gk[4 * g4 + e] + kt4[e] * seginv;
+          const bf16x2 lo2 = bf16_rne2(x[0], x[1]), hi2 = bf16_rne2(x[2], x[3]);
+          *reinterpret_cast<u32x2*>(dk + (size_t)tok * D + f0) =
+              u32x2{__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2)};
+          *reinterpret_cast<f32x4*>(dvp + (size_t)tok * D + f0) =
+              f32x4{gv[4 * g4], gv[4 * g4 + 1], gv[4 * g4 + 2], gv[4 * g4 + 3]};
         }
       }
     }
@@ -915,7 +933,7 @@ struct BwdShape {
   static constexpr size_t l2a = 9 * MP * (MP + 4), l2b = 3 * MP * (D + 4) + 2 * MP * (MP + 4);
   static constexpr size_t l2 = (l2a > l2b ? l2a : l2b) * 4;
   static constexpr size_t p1 = ((size_t)4 * MP * T + 2 * D * T + NW * 2 * 32 * MP) * 2;
-  static constexpr size_t p2 = ((size_t)2 * MP * T + D * T + NW * 4 * 32 * MP) * 2;
+  static constexpr size_t p2 = ((size_t)2 * MP * T + (size_t)T * D) * 2 + 3 * MP * 4;
   static constexpr size_t fin =
       (size_t)2 * kFinRows * D * 2 + ((size_t)MP * D + 65 + 4 * 65 + kFinTok) * 4;
 };
