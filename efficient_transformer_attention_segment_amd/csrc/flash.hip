@@ -117,11 +117,22 @@ __global__ __launch_bounds__(256) void flash_scan_kernel(FlashArgs a) {
 // 16 s + 4 h + (0..3) and 16 s + 8 + 4 h + (0..3), so the A operand reads V^T in that key
 // order -- two 4-row transpose reads of the row-major V tile at rows 16 s + 4 h and
 // 16 s + 8 + 4 h.
+// K rows go through LDS too when the block then still fits twice per CU (80 KiB);
+// otherwise every wave reads its keys from L2.
+template <int D, int C>
+struct FlashAttendLds {
+  static constexpr int LK = D + 8;  // padded K rows: 16-byte reads of 8 rows spread banks
+  static constexpr bool k_in_lds = (size_t)C * D * 2 + (size_t)C * LK * 2 <= 80 * 1024;
+  static constexpr size_t bytes = (size_t)C * D * 2 + (k_in_lds ? (size_t)C * LK * 2 : 0);
+};
+
 template <int D, int C>
 __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
-  constexpr int FT = D / 32;
+  constexpr int FT = D / 32, LK = FlashAttendLds<D, C>::LK;
+  constexpr bool kKL = FlashAttendLds<D, C>::k_in_lds;
   extern __shared__ __align__(16) char lds[];
   uint16_t* vS = reinterpret_cast<uint16_t*>(lds);   // V [C][D] (row-major)
+  uint16_t* kS = vS + C * D;                          // K [C][LK] when kKL
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
   int bh, g;
   xcd_map(blockIdx.x, a.BH, a.G, bh, g);
@@ -132,9 +143,13 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
 #pragma unroll 4
   for (int e = threadIdx.x; e < C * (D / 8); e += blockDim.x) {
     const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = t0 + i;
-    u32x4 vv{0u, 0u, 0u, 0u};
-    if (t < t1) vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
+    u32x4 vv{0u, 0u, 0u, 0u}, kv{0u, 0u, 0u, 0u};
+    if (t < t1) {
+      vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
+      if constexpr (kKL) kv = *reinterpret_cast<const u32x4*>(k + (size_t)t * D + f8);
+    }
     *reinterpret_cast<u32x4*>(vS + i * D + f8) = vv;
+    if constexpr (kKL) *reinterpret_cast<u32x4*>(kS + i * LK + f8) = kv;
   }
   __syncthreads();
   const int q0 = t0 + 32 * wave;  // this wave's first query
@@ -153,7 +168,8 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
   const int ntile = a.causal ? wave + 1 : (t1 - t0 + 31) / 32;
   for (int kt = 0; kt < ntile; ++kt) {
     const int k0 = t0 + 32 * kt;
-    const uint16_t* krow = k + (size_t)min(k0 + r32, t1 - 1) * D;  // A operand: key rows
+    const uint16_t* krow = kKL ? kS + (32 * kt + r32) * LK           // A operand: key rows
+                               : k + (size_t)min(k0 + r32, t1 - 1) * D;
     f32x16 sc = zero16();
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) sc = mfma(ld8(krow + 16 * s + 8 * h), qb[s], sc);
@@ -223,7 +239,7 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
 template <int D, int C>
 struct FlashShape {
   static constexpr size_t state_lds = (size_t)2 * C * D * 2;
-  static constexpr size_t attend_lds = (size_t)C * D * 2;
+  static constexpr size_t attend_lds = FlashAttendLds<D, C>::bytes;
 };
 
 template <int D, int C>
