@@ -493,8 +493,8 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     if (qpad)
 #pragma unroll
       for (int f = 0; f < FT; ++f) oacc[f] = zero16();
-    if (qok) {
-      if constexpr (kS) {
+    if constexpr (kS) {
+      if (qok) {
         float* op = static_cast<float*>(a.out) + ((size_t)bh * a.n + tq) * D + (D / 2) * h;
 #pragma unroll
         for (int f = 0; f < FT; ++f)
@@ -502,23 +502,37 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
           for (int q4 = 0; q4 < 4; ++q4)
             *reinterpret_cast<f32x4*>(op + 16 * f + 4 * q4) = f32x4{
                 oacc[f][4 * q4], oacc[f][4 * q4 + 1], oacc[f][4 * q4 + 2], oacc[f][4 * q4 + 3]};
-      } else {
-        uint16_t* op = static_cast<uint16_t*>(a.out) + ((size_t)bh * a.n + tq) * D + (D / 2) * h;
+      }
+    } else {
+      // bf16: a lane holds half a row, so direct stores would fill each 128-byte line a
+      // quarter per instruction. The wave's 32 rows are staged in its own slice of the V
+      // tile (free once every wave's conv reads are done; 16-byte chunk c of row r sits
+      // at chunk c ^ (r % CPR)) and written back as whole consecutive rows.
+      constexpr int CPR = D / 8;
+      __syncthreads();  // every wave has finished its conv reads of the V tile
+      uint16_t* ow = vt + (size_t)wave * 32 * D;
 #pragma unroll
-        for (int f = 0; f < FT; ++f) {
-          bf16x8 lo8, hi8;
+      for (int f = 0; f < FT; ++f) {
+        bf16x8 lo8, hi8;
 #pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 a2 = bf16_rne2(oacc[f][e], oacc[f][e + 1]);
-            const bf16x2 b2 = bf16_rne2(oacc[f][8 + e], oacc[f][9 + e]);
-            lo8[e] = a2[0];
-            lo8[e + 1] = a2[1];
-            hi8[e] = b2[0];
-            hi8[e + 1] = b2[1];
-          }
-          st8(op + 16 * f, lo8);
-          st8(op + 16 * f + 8, hi8);
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 a2 = bf16_rne2(oacc[f][e], oacc[f][e + 1]);
+          const bf16x2 b2 = bf16_rne2(oacc[f][8 + e], oacc[f][9 + e]);
+          lo8[e] = a2[0];
+          lo8[e + 1] = a2[1];
+          hi8[e] = b2[0];
+          hi8[e + 1] = b2[1];
         }
+        const int c0 = (CPR / 2) * h + 2 * f;  // chunk of features (D/2) h + 16 f
+        st8(ow + r32 * D + 8 * (c0 ^ (r32 % CPR)), lo8);
+        st8(ow + r32 * D + 8 * ((c0 + 1) ^ (r32 % CPR)), hi8);
+      }
+      uint16_t* ob = static_cast<uint16_t*>(a.out) + ((size_t)bh * a.n + T0 + 32 * wave) * D;
+#pragma unroll
+      for (int i = 0; i < CPR / 2; ++i) {
+        const int row = i * (64 / CPR) + lane / CPR, c = lane % CPR;
+        const bf16x8 v = ld8(ow + row * D + 8 * (c ^ (row % CPR)));
+        if (T0 + 32 * wave + row < t_end) st8(ob + (size_t)row * D + 8 * c, v);
       }
     }
     if (more) {
