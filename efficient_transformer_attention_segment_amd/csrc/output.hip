@@ -26,7 +26,9 @@
 //    expanded per lane into the B operand once per block; V is staged row-major in LDS
 //    with its halo (16-byte writes) and read feature-major with LDS transpose reads;
 //    the next step's V rows and Q are loaded into registers while this step computes;
-//  * bf16 (RNE) or fp32 store: each lane writes d/2 contiguous features of its token.
+//  * store: fp32 lanes write d/2 contiguous features of their token; bf16 (RNE) rows
+//    pass through the wave's slice of the V tile and leave as whole 128-byte lines,
+//    with non-temporal stores.
 #include "nys_common.h"
 #include "nys_kernels.h"
 
@@ -527,12 +529,17 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
         st8(ow + r32 * D + 8 * (c0 ^ (r32 % CPR)), lo8);
         st8(ow + r32 * D + 8 * ((c0 + 1) ^ (r32 % CPR)), hi8);
       }
+      // The output is not read again by this forward: non-temporal stores keep it from
+      // displacing Q, K and V in the memory-side cache, whose dirty lines would otherwise
+      // be written back during the next kernels' reads.
       uint16_t* ob = static_cast<uint16_t*>(a.out) + ((size_t)bh * a.n + T0 + 32 * wave) * D;
 #pragma unroll
       for (int i = 0; i < CPR / 2; ++i) {
         const int row = i * (64 / CPR) + lane / CPR, c = lane % CPR;
         const bf16x8 v = ld8(ow + row * D + 8 * (c ^ (row % CPR)));
-        if (T0 + 32 * wave + row < t_end) st8(ob + (size_t)row * D + 8 * c, v);
+        if (T0 + 32 * wave + row < t_end)
+          __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v),
+                                      reinterpret_cast<u32x4*>(ob + (size_t)row * D + 8 * c));
       }
     }
     if (more) {
