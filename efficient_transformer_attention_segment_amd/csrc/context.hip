@@ -349,8 +349,8 @@ __device__ __forceinline__ void store_row_tile_f32(float* p, int row0, int col0,
     *reinterpret_cast<f32x4*>(q + 8 * g) = f32x4{v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]};
 }
 
-// LDS planes (hi, lo pairs): Z, X, T (= X^2, then 13I - 15X + 7X^2 - X^3). A_S passes
-// through the T pair once on its way into registers.
+// LDS planes (hi, lo pairs) for Z, X and X^2 / T; the iteration rotates their roles.
+// A_S passes through the third pair once on its way into registers.
 enum { kQZ = 0, kQX = 2, kQT = 4, kQPlanes = 6 };
 
 template <int MP>
@@ -463,47 +463,53 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
   constexpr int KM = MP / 16;
   Pair8 abo[KM];
   if (mine) load_row_operand<MP>(plane(kQT), plane(kQT + 1), row0, lane, abo);
-  // 4. iterations Z <- 1/4 Z (13I - 15X + 7X^2 - X^3), X = A Z
+  // 4. iterations Z <- 1/4 Z (13I - 15X + 7X^2 - X^3), X = A Z. The three plane pairs
+  // rotate roles (pz holds Z, px receives X, pt X^2): once X = A Z is formed, each wave's
+  // rows of Z sit in registers, so T = 13I - 15X + 7X^2 - X^3 can overwrite the Z planes
+  // and the new Z the X planes, four barriers per iteration.
+  int pz = kQZ, px = kQX, pt = kQT;
   for (int it = 0; it < a.iters; ++it) {
-    f32x16 x, x2, acc;
-    if (mine) {  // X = A Z
-      x = prod_rows_op<MP>(abo, plane(kQZ), plane(kQZ + 1), col0, lane);
-      store_row_tile<MP>(plane(kQX), plane(kQX + 1), row0, col0, x, lane);
+    f32x16 u;  // 13I - 15X + 7X^2, formed once X^2 is known
+    Pair8 zrows[KM];
+    if (mine) {  // X = A Z; this wave's rows of Z kept for Z T
+      load_row_operand<MP>(plane(pz), plane(pz + 1), row0, lane, zrows);
+      u = prod_rows_op<MP>(abo, plane(pz), plane(pz + 1), col0, lane);
+      store_row_tile<MP>(plane(px), plane(px + 1), row0, col0, u, lane);
     }
     __syncthreads();
-    if (mine) {  // X^2 = X X, parked in the T planes
-      x2 = prod_rows<MP>(plane(kQX), plane(kQX + 1), plane(kQX), plane(kQX + 1), row0, col0, lane);
-      store_row_tile<MP>(plane(kQT), plane(kQT + 1), row0, col0, x2, lane);
-    }
-    __syncthreads();
-    if (mine)  // X^3 = X X^2
-      acc = prod_rows<MP>(plane(kQX), plane(kQX + 1), plane(kQT), plane(kQT + 1), row0, col0, lane);
-    __syncthreads();
-    if (mine) {  // T = 13I - 15X + 7X^2 - X^3  (= 13I - X(15I - X(7I - X)))
-      f32x16 tv;
+    if (mine) {  // X^2 = X X
+      const f32x16 x2 =
+          prod_rows<MP>(plane(px), plane(px + 1), plane(px), plane(px + 1), row0, col0, lane);
+      store_row_tile<MP>(plane(pt), plane(pt + 1), row0, col0, x2, lane);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
         const float diag = (irow == row_tile_col(col0, rr, lane)) ? 13.f : 0.f;
-        tv[rr] = diag - 15.f * x[rr] + 7.f * x2[rr] - acc[rr];
+        u[rr] = diag - 15.f * u[rr] + 7.f * x2[rr];
       }
-      store_row_tile<MP>(plane(kQT), plane(kQT + 1), row0, col0, tv, lane);
     }
     __syncthreads();
-    if (mine)  // Z T
-      acc = prod_rows<MP>(plane(kQZ), plane(kQZ + 1), plane(kQT), plane(kQT + 1), row0, col0, lane);
+    if (mine) {  // X^3 = X X^2, then T = 13I - 15X + 7X^2 - X^3 into the Z planes
+      const f32x16 x3 =
+          prod_rows<MP>(plane(px), plane(px + 1), plane(pt), plane(pt + 1), row0, col0, lane);
+      store_row_tile<MP>(plane(pz), plane(pz + 1), row0, col0, u - x3, lane);
+    }
     __syncthreads();
-    if (mine) {  // Z <- Z T / 4
-      const f32x16 zv = acc * 0.25f;
-      store_row_tile<MP>(plane(kQZ), plane(kQZ + 1), row0, col0, zv, lane);
+    if (mine) {  // Z <- Z T / 4, into the X planes
+      const f32x16 zv = prod_rows_op<MP>(zrows, plane(pz), plane(pz + 1), col0, lane) * 0.25f;
+      store_row_tile<MP>(plane(px), plane(px + 1), row0, col0, zv, lane);
       if (it == a.iters - 1) store_row_tile_f32<MP>(a.z + (size_t)bh * P, row0, col0, zv, lane);
     }
     __syncthreads();
+    const int nz = px;
+    px = pt;
+    pt = pz;
+    pz = nz;
   }
   // 5. Z (row-major hi/lo, unpermuted) for the output stage
   uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
   for (int e = tid; e < 2 * P / 8; e += blockDim.x) {
     const int which = e / (P / 8), r = (e % (P / 8)) / (MP / 8), c8 = (e % (MP / 8)) * 8;
-    st8(dst + (size_t)which * P + r * MP + c8, ld8(plane(kQZ + which) + swz<MP>(r, c8)));
+    st8(dst + (size_t)which * P + r * MP + c8, ld8(plane(pz + which) + swz<MP>(r, c8)));
   }
 }
 
