@@ -5,8 +5,9 @@
 //                     steps of Z <- 1/4 Z (13I - X(15I - X(7I - X))), X = A_S Z, every
 //                     m x m product on MFMA. For mp <= 64 the operand planes live in LDS
 //                     (4 waves) and these blocks ride at the front of the context launch;
-//                     larger mp keeps them in global memory (pinv_global_kernel, 16
-//                     waves, its own launch).
+//                     larger mp keeps them in global memory: pinv_global_kernel (16
+//                     waves per head) forms A_S and Z_0, then every product of the
+//                     iteration is its own launch over all heads (pinv_phase_kernel).
 //  * landmark context BH * C blocks: the right factor softmax_row(s Qt K^T) V, computed
 //                     without forming the m x n matrix: each block streams one chunk of
 //                     K/V tiles, keeps a running max / sum per landmark (online softmax
@@ -63,7 +64,6 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
   const size_t P = (size_t)mp * mp;
   const int dd = a.d;
   float* A = a.a_s + (size_t)bh * P;
-  float* own = a.own + (size_t)bh * 2 * P;  // fp32 X, X^2 (global variant only)
   auto plane = [&](int idx) { return pl + (size_t)idx * P; };
 
   // 1. logits Qt Kt^T (both landmark sets as hi/lo planes, K = d), scaled to log2
@@ -189,69 +189,74 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
   }
   __syncthreads();
 
-  // 5. iterations. Each wave owns tiles t = wave + nw*u.
-  {
-    // mp > 64: planes in global memory; Z and T get separate (ping-pong) planes so every
-    // product is written as soon as it is formed. fp32 X, X^2 of the own tiles go to
-    // per-head scratch and are read back by the same wave.
-    for (int it = 0; it < a.iters; ++it) {
-      const int zr = (it & 1) ? kGZr1 : kPZr, zc = (it & 1) ? kGZc1 : kPZc;
-      const int zr_n = (it & 1) ? kPZr : kGZr1, zc_n = (it & 1) ? kPZc : kGZc1;
-#pragma unroll 1
-      for (int t = wave; t < ntiles; t += nw) {  // X = A Z
-        const int row0 = 32 * (t / nt), col0 = 32 * (t % nt);
-        const f32x16 x = gemm_tile(plane(kPA), plane(kPA + 1), mp, plane(zc), plane(zc + 1), mp,
-                                   row0, col0, mp, lane);
-        store_rows_hl(plane(kPXr), plane(kPXr + 1), mp, row0, col0, x, lane);
-        store_cols_hl(plane(kPXc), plane(kPXc + 1), mp, row0, col0, x, lane);
-        store_rows_f32(own, mp, row0, col0, x, lane);
-      }
-      __syncthreads();
-#pragma unroll 1
-      for (int t = wave; t < ntiles; t += nw) {  // X^2 = X X
-        const int row0 = 32 * (t / nt), col0 = 32 * (t % nt);
-        const f32x16 x2 = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPXc),
-                                    plane(kPXc + 1), mp, row0, col0, mp, lane);
-        store_cols_hl(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, x2, lane);
-        store_rows_f32(own + P, mp, row0, col0, x2, lane);
-      }
-      __syncthreads();
-#pragma unroll 1
-      for (int t = wave; t < ntiles; t += nw) {  // T = 13I - 15X + 7X^2 - X X^2
-        const int row0 = 32 * (t / nt), col0 = 32 * (t % nt);
-        const int j = col0 + (lane & 31);
-        const f32x16 x3 = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPX2T),
-                                    plane(kPX2T + 1), mp, row0, col0, mp, lane);
-        f32x16 tv;
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          const size_t o = (size_t)acc_row(row0, rr, lane) * mp + j;
-          const float diag = (acc_row(row0, rr, lane) == j) ? 13.f : 0.f;
-          tv[rr] = diag - 15.f * own[o] + 7.f * own[P + o] - x3[rr];
-        }
-        store_cols_hl(plane(kGT), plane(kGT + 1), mp, row0, col0, tv, lane);
-      }
-      __syncthreads();
-#pragma unroll 1
-      for (int t = wave; t < ntiles; t += nw) {  // Z <- Z T / 4
-        const int row0 = 32 * (t / nt), col0 = 32 * (t % nt);
-        const f32x16 zv = gemm_tile(plane(zr), plane(zr + 1), mp, plane(kGT), plane(kGT + 1), mp,
-                                    row0, col0, mp, lane) * 0.25f;
-        store_rows_hl(plane(zr_n), plane(zr_n + 1), mp, row0, col0, zv, lane);
-        store_cols_hl(plane(zc_n), plane(zc_n + 1), mp, row0, col0, zv, lane);
-        if (it == a.iters - 1) store_rows_f32(a.z + (size_t)bh * P, mp, row0, col0, zv, lane);
-      }
-      __syncthreads();
-    }
-    }
-  // 6. hand Z (row-major hi/lo) to the Y = Z W product of the output stage
-  {
-    const int zfin = (a.iters & 1) ? kGZr1 : kPZr;
+  // 5. the iterations run as separate launches (pinv_phase_kernel); with none, hand Z_0
+  //    (row-major hi/lo) to the output stage here
+  if (a.iters == 0) {
     uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
     const int n8 = (int)(P / 8);
     for (int e = tid; e < 2 * n8; e += nthreads) {
       const int which = e / n8, off = (e % n8) * 8;
-      st8(dst + (size_t)which * P + off, ld8(plane(zfin + which) + off));
+      st8(dst + (size_t)which * P + off, ld8(plane(kPZr + which) + off));
+    }
+  }
+}
+
+// One product of an iteration for every head at once (mp > 64): one wave per 32 x 32
+// output tile, operands read from the head's planes in global memory (they stay in the
+// XCD's L2: a head's tiles run on one XCD). Successive phases are ordered by the launch
+// boundaries, so the m x m products of a head spread over many CUs instead of one.
+//   PH 0: X = A Z        -> X rows and columns (hi/lo), fp32 X
+//   PH 1: X^2 = X X      -> X^2 columns (hi/lo), fp32 X^2
+//   PH 2: T = 13I - 15X + 7X^2 - X X^2 -> T columns (hi/lo)
+//   PH 3: Z <- Z T / 4   -> Z rows and columns of the other Z pair; after the last
+//                           iteration fp32 Z and the row-major hi/lo copy for the output
+template <int PH>
+__global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
+  const int lane = threadIdx.x;
+  const int mp = a.mp, nt = mp / 32;
+  int bh, t;
+  xcd_map(blockIdx.x, a.BH, nt * nt, bh, t);
+  const size_t P = (size_t)mp * mp;
+  const int row0 = 32 * (t / nt), col0 = 32 * (t % nt);
+  uint16_t* pl = a.planes + (size_t)bh * kPlanes * P;
+  auto plane = [&](int idx) { return pl + (size_t)idx * P; };
+  float* own = a.own + (size_t)bh * 2 * P;
+  if constexpr (PH == 0) {
+    const int zc = (it & 1) ? kGZc1 : kPZc;
+    const f32x16 x = gemm_tile(plane(kPA), plane(kPA + 1), mp, plane(zc), plane(zc + 1), mp,
+                               row0, col0, mp, lane);
+    store_rows_hl(plane(kPXr), plane(kPXr + 1), mp, row0, col0, x, lane);
+    store_cols_hl(plane(kPXc), plane(kPXc + 1), mp, row0, col0, x, lane);
+    store_rows_f32(own, mp, row0, col0, x, lane);
+  } else if constexpr (PH == 1) {
+    const f32x16 x2 = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPXc), plane(kPXc + 1),
+                                mp, row0, col0, mp, lane);
+    store_cols_hl(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, x2, lane);
+    store_rows_f32(own + P, mp, row0, col0, x2, lane);
+  } else if constexpr (PH == 2) {
+    const int j = col0 + (lane & 31);
+    const f32x16 x3 = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPX2T),
+                                plane(kPX2T + 1), mp, row0, col0, mp, lane);
+    f32x16 tv;
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      const size_t o = (size_t)acc_row(row0, rr, lane) * mp + j;
+      const float diag = (acc_row(row0, rr, lane) == j) ? 13.f : 0.f;
+      tv[rr] = diag - 15.f * own[o] + 7.f * own[P + o] - x3[rr];
+    }
+    store_cols_hl(plane(kGT), plane(kGT + 1), mp, row0, col0, tv, lane);
+  } else {
+    const int zr = (it & 1) ? kGZr1 : kPZr;
+    const int zr_n = (it & 1) ? kPZr : kGZr1, zc_n = (it & 1) ? kPZc : kGZc1;
+    const f32x16 zv = gemm_tile(plane(zr), plane(zr + 1), mp, plane(kGT), plane(kGT + 1), mp,
+                                row0, col0, mp, lane) * 0.25f;
+    if (it == a.iters - 1) {
+      uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
+      store_rows_hl(dst, dst + P, mp, row0, col0, zv, lane);
+      store_rows_f32(a.z + (size_t)bh * P, mp, row0, col0, zv, lane);
+    } else {
+      store_rows_hl(plane(zr_n), plane(zr_n + 1), mp, row0, col0, zv, lane);
+      store_cols_hl(plane(zc_n), plane(zc_n + 1), mp, row0, col0, zv, lane);
     }
   }
 }
@@ -946,7 +951,17 @@ size_t context_lds_bytes(bool bf16, int d, const CtxArgs& a) {
 template <int D>
 static hipError_t launch_pinv_t(const CtxArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((pinv_global_kernel<D>), dim3(a.BH), dim3(1024), 0, s, a);
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  const int tiles = (a.mp / 32) * (a.mp / 32);
+  const dim3 grid(a.BH * tiles), block(64);
+  for (int it = 0; it < a.iters && e == hipSuccess; ++it) {
+    hipLaunchKernelGGL((pinv_phase_kernel<0>), grid, block, 0, s, a, it);
+    hipLaunchKernelGGL((pinv_phase_kernel<1>), grid, block, 0, s, a, it);
+    hipLaunchKernelGGL((pinv_phase_kernel<2>), grid, block, 0, s, a, it);
+    hipLaunchKernelGGL((pinv_phase_kernel<3>), grid, block, 0, s, a, it);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 hipError_t launch_pinv(int d, const CtxArgs& a, hipStream_t s) {
