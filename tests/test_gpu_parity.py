@@ -61,6 +61,11 @@ SMALL = {
     "tail8": gen.Config("tail8", 1, 2, 136, 64, 8, seed=36),
     "m40_pad": gen.Config("m40", 1, 2, 200, 64, 40, seed=37),
     "m64_d32": gen.Config("m64d32", 2, 2, 1024, 32, 64, seed=38),
+    # m > 64: the iteration runs as one launch per product; cover no and one iteration
+    # (the hand-off of Z then happens in the first kernel / in the only last phase)
+    "m128_iters0": gen.Config("m128i0", 1, 2, 1024, 64, 128, pinv_iters=0, seed=39),
+    "m128_iters1": gen.Config("m128i1", 1, 2, 1024, 64, 128, pinv_iters=1, seed=40),
+    "m160_iters3": gen.Config("m160i3", 1, 3, 960, 32, 160, pinv_iters=3, seed=41),
 }
 
 
