@@ -163,11 +163,17 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   };
 
   // ---- prologue. Every global load is issued before any of it is used, so the whole
-  // set-up costs about one memory round trip; the first V rows and Q are in flight too.
+  // set-up costs about one memory round trip. The landmark operands go first and the
+  // first V rows and Q after them: loads retire in order, so the merge below waits only
+  // for the landmark data while the token rows are still arriving.
   Chunk<Tin> vc[NCH];
   Pair8 qb[KD];
-  load_v(t_begin, vc);
-  load_q(t_begin, qb);
+  float wt0 = 0.f, wt1 = 0.f;  // conv taps `lane` and `lane + 64` of this head (wave 0)
+  if (tid < 64) {
+    const float* w = a.conv_w + (size_t)head * a.W;
+    wt0 = lane < a.W ? w[lane] : 0.f;
+    wt1 = lane + 64 < a.W ? w[lane + 64] : 0.f;
+  }
   constexpr int kCB = 4;  // chunk states per load batch
   const float* pml = a.part_ml + (size_t)bh * C * 2 * mp;
   const float* pw = a.part_w + (size_t)bh * C * D * mp;
@@ -222,6 +228,9 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     }
   }
 
+  load_v(t_begin, vc);
+  load_q(t_begin, qb);
+
   // chunk weights per landmark: exp2(M_c - M*) / sum_c exp2(M_c - M*) L_c
   if (tid < mp) {
     const int j = tid;
@@ -256,14 +265,14 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   }
   // conv filter as the B operand of the banded product (identical for every wave)
   if (tid < 64) {
-    const float* w = a.conv_w + (size_t)head * a.W;
 #pragma unroll
     for (int s = 0; s < KS; ++s) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
+      for (int e = 0; e < 8; ++e) {  // tap k from the lane that loaded it
         const int k = 16 * s + 8 * h + e - r32;
-        x[e] = (k >= 0 && k < a.W) ? w[k] : 0.f;
+        const float v0 = __shfl(wt0, k & 63), v1 = __shfl(wt1, k & 63);
+        x[e] = (k >= 0 && k < a.W) ? (k < 64 ? v0 : v1) : 0.f;
       }
       const Pair8 p = split8(x);
       st8(wl + ((size_t)(2 * s) * 64 + lane) * 8, p.hi);
