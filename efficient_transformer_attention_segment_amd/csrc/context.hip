@@ -592,10 +592,16 @@ __device__ __forceinline__ void flash_reg_body(const CtxArgs& a, int blk, char* 
   const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
   const int mp = a.mp;
   int bh, c;
-  xcd_map(blk, a.BH, a.C, bh, c);
+  if (a.chunk_tab != nullptr) {  // chunk-major blocks (the chunk table's order)
+    bh = blk % a.BH;
+    c = blk / a.BH;
+  } else {
+    xcd_map(blk, a.BH, a.C, bh, c);
+  }
   // the chunk, cut at the head's valid length (an empty chunk leaves M = -inf, L = 0)
-  const int c0 = c * a.chunk;
-  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), c0 + a.chunk);
+  const int* ct = a.chunk_tab != nullptr ? a.chunk_tab + 2 * ((size_t)bh * a.C + c) : nullptr;
+  const int c0 = ct != nullptr ? ct[0] : c * a.chunk;
+  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), ct != nullptr ? ct[1] : c0 + a.chunk);
   const Tin* K = static_cast<const Tin*>(a.k) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
 
@@ -758,10 +764,16 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
   const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
   const int mp = a.mp;
   int bh, c;
-  xcd_map(blk, a.BH, a.C, bh, c);
+  if (a.chunk_tab != nullptr) {  // chunk-major blocks (the chunk table's order)
+    bh = blk % a.BH;
+    c = blk / a.BH;
+  } else {
+    xcd_map(blk, a.BH, a.C, bh, c);
+  }
   // the chunk, cut at the head's valid length (an empty chunk leaves M = -inf, L = 0)
-  const int c0 = c * a.chunk;
-  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), c0 + a.chunk);
+  const int* ct = a.chunk_tab != nullptr ? a.chunk_tab + 2 * ((size_t)bh * a.C + c) : nullptr;
+  const int c0 = ct != nullptr ? ct[0] : c * a.chunk;
+  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), ct != nullptr ? ct[1] : c0 + a.chunk);
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)bh * a.n * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)bh * a.n * D;
 
@@ -1014,6 +1026,17 @@ hipError_t launch_context(bool bf16, int d, const CtxArgs& a, hipStream_t s) {
   const dim3 grid(a.npinv + a.BH * a.C), block(64 * a.LG * a.TG);
   void* args[] = {const_cast<CtxArgs*>(&a)};
   return hipLaunchKernel(fn, grid, block, args, context_lds_bytes(bf16, d, a), s);
+}
+
+int context_blocks_per_cu(bool bf16, int d, int mp, size_t ctx_lds) {
+  const int LG = mp / 32, TG = LG >= 4 ? 1 : 4 / LG;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, context_fn(bf16, d, mp, LG), 64 * LG * TG,
+                                                   ctx_lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return nb;
 }
 
 hipError_t configure_context(bool bf16, int d, int mp, size_t ctx_lds) {

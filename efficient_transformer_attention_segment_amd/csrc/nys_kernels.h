@@ -33,6 +33,8 @@ struct CtxArgs {
   uint16_t* z_hl;         // [BH][2][mp][mp]  final Z, row-major hi/lo
   float* part_w;          // [BH][C][d][mp]   per-chunk unnormalised (Bbar V)^T
   float* part_ml;         // [BH][C][2][mp]   per-chunk running max (log2 units), sum
+  const int* chunk_tab;   // [BH][C][2] token range [c0, c1) of each context chunk, or
+                          // nullptr: chunk c is [c * chunk, (c + 1) * chunk)
   int BH, H, n, d, m, mp, iters, chunk, C, LG, TG;
   int npinv;              // pseudo-inverse blocks at the front of the context grid (0 or BH)
   int ring_ni;            // bf16 context: 1 KiB LDS-DMA loads per wave per K or V tile
@@ -166,6 +168,8 @@ void context_ring_geometry(int d, CtxArgs& a);
 size_t context_lds_bytes(bool bf16, int d, const CtxArgs& a);
 size_t output_lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C);
 hipError_t configure_context(bool bf16, int d, int mp, size_t ctx_lds);
+// Context blocks resident per CU at this LDS size (0 if the runtime cannot tell).
+int context_blocks_per_cu(bool bf16, int d, int mp, size_t ctx_lds);
 hipError_t configure_output(bool bf16, int d, int conv_ksteps, size_t out_lds);
 
 }  // namespace nys

@@ -32,6 +32,53 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 long long round_up(long long a, long long b) { return ((a + b - 1) / b) * b; }
 
+// Token ranges of the context chunks when the fused pseudo-inverse blocks share CUs with
+// context blocks. Workgroups of one launch are placed round-robin over the CUs (block b
+// on CU b mod ncu while they all fit at once: measured with per-block clocks), so a
+// context block b >= ncu with b mod ncu < npinv runs next to a pseudo-inverse block and
+// progresses at about 0.7 of the speed of the others. With the table the context blocks
+// are taken chunk-major (block npinv + c * BH + bh holds chunk c of head bh; with BH a
+// multiple of 8 a head's blocks still share one XCD), so every head has chunks on both
+// kinds of CU, and each head's tokens are split in proportion to those speeds, in whole
+// steps. Returns false (uniform chunks, head-major blocks) when the launch does not fit
+// in one round of resident blocks or no context block shares a CU.
+bool uneven_chunks(int BH, int C, int n, int step, int npinv, int ncu, int slots_per_cu,
+                   std::vector<int>& tab) {
+  const long long blocks = (long long)npinv + (long long)BH * C;
+  if (npinv <= 0 || npinv >= ncu || C < 2 || (BH & 7) != 0 ||
+      blocks > (long long)slots_per_cu * ncu || blocks <= ncu)
+    return false;
+  constexpr double kShared = 0.7;
+  std::vector<double> w((size_t)BH * C, 1.0);
+  bool any = false;
+  for (int blk = 0; blk < BH * C; ++blk) {
+    const int bh = blk % BH, c = blk / BH;
+    const long long b = npinv + blk;
+    if (b >= ncu && (int)(b % ncu) < npinv) {
+      w[(size_t)bh * C + c] = kShared;
+      any = true;
+    }
+  }
+  if (!any) return false;
+  tab.assign((size_t)BH * C * 2, 0);
+  const int nsteps = ceil_div(n, step);
+  for (int bh = 0; bh < BH; ++bh) {
+    double total = 0.0;
+    for (int c = 0; c < C; ++c) total += w[(size_t)bh * C + c];
+    double cum = 0.0;
+    int start = 0;
+    for (int c = 0; c < C; ++c) {
+      cum += w[(size_t)bh * C + c];
+      const int end = c == C - 1 ? n
+                                 : std::min(n, step * (int)std::lround(nsteps * cum / total));
+      tab[2 * ((size_t)bh * C + c)] = std::min(start, end);
+      tab[2 * ((size_t)bh * C + c) + 1] = end;
+      start = std::max(start, end);
+    }
+  }
+  return true;
+}
+
 }  // namespace
 
 struct nys_attn_plan {
@@ -156,6 +203,12 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   const size_t o_zhl = take(BHs * 2 * P * 2);
   const size_t o_pw = take(BHs * p->C * mp * dd * 4), o_pml = take(BHs * p->C * 2 * mp * 4);
   const size_t o_w = take(BHs * mp * dd * 4), o_y = take(BHs * mp * dd * 4);
+  std::vector<int> chunk_tab;
+  const bool uneven = p->fused &&
+                      uneven_chunks(p->BH, p->C, n, step, p->BH, prop.multiProcessorCount,
+                                    nys::context_blocks_per_cu(bf16, d, p->mp, ctx_lds),
+                                    chunk_tab);
+  const size_t o_ct = take(uneven ? chunk_tab.size() * sizeof(int) : 0);
   p->ws_bytes = off;
   p->ws = nullptr;
 
@@ -170,10 +223,12 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
       delete p;
       return fail(NYS_E_NOMEM, "workspace allocation failed");
     }
-    if (hipMemset(p->ws, 0, p->ws_bytes) != hipSuccess) {
+    if (hipMemset(p->ws, 0, p->ws_bytes) != hipSuccess ||
+        (uneven && hipMemcpy(p->ws + o_ct, chunk_tab.data(), chunk_tab.size() * sizeof(int),
+                             hipMemcpyHostToDevice) != hipSuccess)) {
       (void)hipFree(p->ws);
       delete p;
-      return fail(NYS_E_LAUNCH, "workspace clear failed");
+      return fail(NYS_E_LAUNCH, "workspace set-up failed");
     }
   }
   char* ws = p->ws;
@@ -185,6 +240,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   c.qt = F(o_qt); c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
   c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.z_hl = U(o_zhl);
   c.part_w = F(o_pw); c.part_ml = F(o_pml);
+  c.chunk_tab = uneven ? reinterpret_cast<const int*>(ws + o_ct) : nullptr;
   c.scale = 1.0f / std::sqrt((float)d);
   c.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)d));
 
