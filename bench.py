@@ -182,7 +182,13 @@ def summarize_counters(fetch_dir: str, write_dir: str, cfg_name: str, commands) 
 
 
 CONFIG_TEXT = {"long": "B=16 H=8 n=4096 d=64 m=64, conv width 33, 6 pseudo-inverse "
-                       "iterations, bf16 I/O"}
+                       "iterations, bf16 I/O",
+               "bert": "B=32 H=12 n=512 d=64 m=64, conv width 33, 6 pseudo-inverse "
+                       "iterations, bf16 I/O",
+               "large_m": "B=4 H=8 n=16384 d=64 m=256, conv width 33, 6 pseudo-inverse "
+                          "iterations, bf16 I/O",
+               "very_long": "B=2 H=16 n=65536 d=128 m=128, conv width 33, 6 pseudo-inverse "
+                            "iterations, bf16 I/O, Q and K of variance 2"}
 
 
 def main():
