@@ -201,6 +201,101 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
   }
 }
 
+// First step for mp > 64 when the iteration runs (iters > 0), one block per 32-row strip
+// of A_S (nt = mp / 32 waves, wave w forms the tile in column strip w): the scaled logits,
+// the row softmax, A_S in fp32 (for the taps) and as hi/lo row planes, and the unscaled
+// row and column planes of A_S that Z_0 = alpha A_S^T is built from. alpha needs every
+// strip's column sums, so each strip stores its partial column abs-sums and its largest
+// row abs-sum; the first iteration's X = A Z_0 and Z_1 = Z_0 T / 4 apply alpha to their
+// products (pinv_alpha).
+__global__ __launch_bounds__(512) void pinv_strip_kernel(CtxArgs a) {
+  __shared__ float red_part[32 * 8];  // [row of the strip][column tile]
+  __shared__ float red_rows[8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31;
+  const int mp = a.mp, m = a.m, nt = mp / 32, dd = a.d;
+  int bh, strip;
+  xcd_map(blockIdx.x, a.BH, nt, bh, strip);
+  const size_t P = (size_t)mp * mp;
+  const int row0 = 32 * strip, col0 = 32 * wave, j = col0 + r32;
+  uint16_t* pl = a.planes + (size_t)bh * kPlanes * P;
+  auto plane = [&](int idx) { return pl + (size_t)idx * P; };
+  const uint16_t* qh = a.qt_hl + (size_t)bh * 2 * mp * dd;
+  const uint16_t* kh = a.kt_hl + (size_t)bh * 2 * mp * dd;
+  f32x16 at = gemm_tile(qh, qh + (size_t)mp * dd, dd, kh, kh + (size_t)mp * dd, dd, row0, col0,
+                        dd, lane) * a.scale_log2e;
+  auto lrow = [&](int rr) { return acc_row(0, rr, lane); };  // row within the strip
+  // row maxima over the m real columns: half-wave, then across the column tiles
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const float mx = half_max(j < m ? at[rr] : kNegBig);
+    if (r32 == 0) red_part[lrow(rr) * nt + wave] = mx;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int i = row0 + lrow(rr);
+    float mx = kNegBig;
+    for (int c = 0; c < nt; ++c) mx = fmaxf(mx, red_part[lrow(rr) * nt + c]);
+    at[rr] = (i < m && j < m) ? fast_exp2(at[rr] - mx) : 0.f;
+  }
+  __syncthreads();  // every wave has read the maxima before the sums overwrite them
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const float sm = half_sum(at[rr]);
+    if (r32 == 0) red_part[lrow(rr) * nt + wave] = sm;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    float sum = 0.f;
+    for (int c = 0; c < nt; ++c) sum += red_part[lrow(rr) * nt + c];
+    at[rr] = row0 + lrow(rr) < m ? at[rr] / sum : 0.f;
+  }
+  __syncthreads();
+  // abs row sums (partials per column tile) and this strip's abs column sums
+  float cs = 0.f;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const float rs = half_sum(fabsf(at[rr]));
+    if (r32 == 0) red_part[lrow(rr) * nt + wave] = rs;
+    cs += fabsf(at[rr]);
+  }
+  cs += __shfl_xor(cs, 32);
+  float* part = a.alpha_part + ((size_t)bh * nt + strip) * (mp + 1);
+  if (lane < 32) part[j] = cs;
+  __syncthreads();
+  if (wave == 0) {
+    float rmax = 0.f;
+    if (lane < 32 && row0 + lane < m) {
+      float rs = 0.f;
+      for (int c = 0; c < nt; ++c) rs += red_part[lane * nt + c];
+      rmax = rs;
+    }
+    rmax = wave_max(rmax);
+    if (lane == 0) part[mp] = rmax;
+  }
+  // A_S (fp32 copy for inspection, hi/lo rows) and the unscaled Z_0 planes
+  store_rows_f32(a.a_s + (size_t)bh * P, mp, row0, col0, at, lane);
+  store_rows_hl(plane(kPA), plane(kPA + 1), mp, row0, col0, at, lane);
+  store_rows_hl(plane(kPZc), plane(kPZc + 1), mp, row0, col0, at, lane);
+  store_cols_hl(plane(kPZr), plane(kPZr + 1), mp, row0, col0, at, lane);
+}
+
+// alpha = 1 / (max column abs-sum * max row abs-sum) of head bh's A_S, from the partial
+// sums pinv_strip_kernel left (one wave, every lane gets the value).
+__device__ __forceinline__ float pinv_alpha(const CtxArgs& a, int bh, int lane) {
+  const int mp = a.mp, nt = mp / 32;
+  const float* part = a.alpha_part + (size_t)bh * nt * (mp + 1);
+  float cmax = 0.f, rmax = 0.f;
+  for (int j = lane; j < a.m; j += 64) {
+    float cs = 0.f;
+    for (int s = 0; s < nt; ++s) cs += part[(size_t)s * (mp + 1) + j];
+    cmax = fmaxf(cmax, cs);
+  }
+  if (lane < nt) rmax = part[(size_t)lane * (mp + 1) + mp];
+  return 1.0f / (wave_max(cmax) * wave_max(rmax));
+}
+
 // One product of an iteration for every head at once (mp > 64): one wave per 32 x 32
 // output tile, operands read from the head's planes in global memory (they stay in the
 // XCD's L2: a head's tiles run on one XCD). Successive phases are ordered by the launch
@@ -223,8 +318,9 @@ __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
   float* own = a.own + (size_t)bh * 2 * P;
   if constexpr (PH == 0) {
     const int zc = (it & 1) ? kGZc1 : kPZc;
-    const f32x16 x = gemm_tile(plane(kPA), plane(kPA + 1), mp, plane(zc), plane(zc + 1), mp,
-                               row0, col0, mp, lane);
+    f32x16 x = gemm_tile(plane(kPA), plane(kPA + 1), mp, plane(zc), plane(zc + 1), mp, row0,
+                         col0, mp, lane);
+    if (it == 0) x *= pinv_alpha(a, bh, lane);  // the Z_0 planes are unscaled
     store_rows_hl(plane(kPXr), plane(kPXr + 1), mp, row0, col0, x, lane);
     store_cols_hl(plane(kPXc), plane(kPXc + 1), mp, row0, col0, x, lane);
     store_rows_f32(own, mp, row0, col0, x, lane);
@@ -249,7 +345,8 @@ __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
     const int zr = (it & 1) ? kGZr1 : kPZr;
     const int zr_n = (it & 1) ? kPZr : kGZr1, zc_n = (it & 1) ? kPZc : kGZc1;
     const f32x16 zv = gemm_tile(plane(zr), plane(zr + 1), mp, plane(kGT), plane(kGT + 1), mp,
-                                row0, col0, mp, lane) * 0.25f;
+                                row0, col0, mp, lane) *
+                      (it == 0 ? 0.25f * pinv_alpha(a, bh, lane) : 0.25f);
     if (it == a.iters - 1) {
       uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
       store_rows_hl(dst, dst + P, mp, row0, col0, zv, lane);
@@ -962,7 +1059,12 @@ size_t context_lds_bytes(bool bf16, int d, const CtxArgs& a) {
 
 template <int D>
 static hipError_t launch_pinv_t(const CtxArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((pinv_global_kernel<D>), dim3(a.BH), dim3(1024), 0, s, a);
+  if (a.iters == 0) {  // no iteration: the per-head kernel also hands Z_0 over
+    hipLaunchKernelGGL((pinv_global_kernel<D>), dim3(a.BH), dim3(1024), 0, s, a);
+    return hipGetLastError();
+  }
+  const int nt = a.mp / 32;
+  hipLaunchKernelGGL(pinv_strip_kernel, dim3(a.BH * nt), dim3(64 * nt), 0, s, a);
   hipError_t e = hipGetLastError();
   const int tiles = (a.mp / 32) * (a.mp / 32);
   const dim3 grid(a.BH * tiles), block(64);

@@ -30,6 +30,7 @@ struct CtxArgs {
   float* z;               // [BH][mp][mp]  final Z (fp32)
   uint16_t* planes;       // [BH][kPlanes][mp][mp]  hi/lo bf16 operand planes
   float* own;             // [BH][2][mp][mp]  fp32 X, X^2 (global-memory pinv variant)
+  float* alpha_part;      // [BH][mp/32][mp+1] per-strip column abs-sums, row max (mp > 64)
   uint16_t* z_hl;         // [BH][2][mp][mp]  final Z, row-major hi/lo
   float* part_w;          // [BH][C][d][mp]   per-chunk unnormalised (Bbar V)^T
   float* part_ml;         // [BH][C][2][mp]   per-chunk running max (log2 units), sum

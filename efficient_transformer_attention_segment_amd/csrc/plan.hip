@@ -200,6 +200,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   const size_t o_as = take(BHs * P * 4), o_z = take(BHs * P * 4);
   const size_t o_pl = take(p->mp > 64 ? BHs * nys::kPlanes * P * 2 : 0);
   const size_t o_own = take(p->mp > 64 ? BHs * 2 * P * 4 : 0);
+  const size_t o_apart = take(p->mp > 64 ? BHs * (mp / 32) * (mp + 1) * 4 : 0);
   const size_t o_zhl = take(BHs * 2 * P * 2);
   const size_t o_pw = take(BHs * p->C * mp * dd * 4), o_pml = take(BHs * p->C * 2 * mp * 4);
   const size_t o_w = take(BHs * mp * dd * 4), o_y = take(BHs * mp * dd * 4);
@@ -238,7 +239,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   p->seg = nys::SegArgs{nullptr, p->BH, H, n, m, p->mp, F(o_qt), F(o_kt), U(o_qhl), U(o_khl)};
 
   c.qt = F(o_qt); c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
-  c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.z_hl = U(o_zhl);
+  c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.alpha_part = F(o_apart); c.z_hl = U(o_zhl);
   c.part_w = F(o_pw); c.part_ml = F(o_pml);
   c.chunk_tab = uneven ? reinterpret_cast<const int*>(ws + o_ct) : nullptr;
   c.scale = 1.0f / std::sqrt((float)d);
