@@ -602,6 +602,40 @@ static const void* pick_kernel(const OutArgs& a, bool kt_lds) {
 }
 
 template <typename Tin, int D, int KS>
+static int blocks_per_cu_t(int mp, int m, int C, size_t lds) {
+  constexpr bool kBf16 = !Input<Tin>::kSplit;
+  OutArgs a{};
+  a.mp = mp;
+  a.m = m;
+  a.C = C;
+  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, mp, KS, C));
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, lds) != hipSuccess) {
+    (void)hipGetLastError();
+    return 0;
+  }
+  return nb;
+}
+
+template <typename Tin, int D>
+static int blocks_per_cu_ks(int ks, int mp, int m, int C, size_t lds) {
+  if (ks == 2) return blocks_per_cu_t<Tin, D, 2>(mp, m, C, lds);
+  if (ks == 4) return blocks_per_cu_t<Tin, D, 4>(mp, m, C, lds);
+  return blocks_per_cu_t<Tin, D, 6>(mp, m, C, lds);
+}
+
+int output_blocks_per_cu(bool bf16, int d, int ks, int mp, int m, int C, size_t lds) {
+  if (bf16) {
+    if (d == 32) return blocks_per_cu_ks<uint16_t, 32>(ks, mp, m, C, lds);
+    if (d == 64) return blocks_per_cu_ks<uint16_t, 64>(ks, mp, m, C, lds);
+    return blocks_per_cu_ks<uint16_t, 128>(ks, mp, m, C, lds);
+  }
+  if (d == 32) return blocks_per_cu_ks<float, 32>(ks, mp, m, C, lds);
+  if (d == 64) return blocks_per_cu_ks<float, 64>(ks, mp, m, C, lds);
+  return blocks_per_cu_ks<float, 128>(ks, mp, m, C, lds);
+}
+
+template <typename Tin, int D, int KS>
 static hipError_t launch_t(const OutArgs& a, hipStream_t s) {
   constexpr bool kBf16 = !Input<Tin>::kSplit;
   const size_t lds = output_lds_bytes(kBf16, D, a.mp, KS, a.C);

@@ -185,6 +185,17 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
     delete p;
     return fail(NYS_E_LAUNCH, "could not set kernel LDS limits");
   }
+  // Output blocks: one resident round of them (the prologue of every block merges the
+  // context states and forms Y, so a second round repeats it); 512 slots when the
+  // runtime cannot tell the occupancy.
+  {
+    const int per_cu = nys::output_blocks_per_cu(bf16, d, p->ks, p->mp, m, p->C, out_lds);
+    const long long slots =
+        per_cu > 0 ? (long long)per_cu * std::max(1, prop.multiProcessorCount) : 512;
+    p->tok_per_block = (int)round_up(std::max<long long>(128, (work + slots - 1) / slots), 128);
+    p->tok_per_block = (int)std::min<long long>(p->tok_per_block, round_up(n, 128));
+    p->G = ceil_div(n, p->tok_per_block);
+  }
 
   // workspace carve
   const size_t BHs = (size_t)p->BH, mp = (size_t)p->mp, dd = (size_t)d;
