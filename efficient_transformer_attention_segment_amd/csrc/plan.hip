@@ -148,39 +148,48 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   const int step = 32 * p->TG;
   const long long work = (long long)p->BH * n;
   p->fused = nys::context_fuses_pinv(p->mp);
-  // Context blocks: about one resident wave of them next to the fused pseudo-inverse
-  // blocks (three 4-wave blocks per CU), at most 16 chunks per head (bounds the merge),
-  // and at most 4 when that still fills half the slots: the output prologue loads the
-  // chunk states of four chunks in one batch.
-  const long long slots = 3LL * std::max(1, prop.multiProcessorCount);
-  const long long target = std::max<long long>(slots / 2, slots - (p->fused ? p->BH : 0));
-  const long long heads = std::max(1, p->BH);  // B*H == 0 is an empty problem
-  long long nc = std::min<long long>(16, std::max<long long>(1, (target + heads - 1) / heads));
-  if (nc > 4 && 4LL * heads >= target / 2) nc = 4;
-  p->chunk = (int)round_up(std::max<long long>(step, ((long long)n + nc - 1) / nc), step);
-  p->chunk = (int)std::min<long long>(p->chunk, round_up(n, step));
-  p->C = ceil_div(n, p->chunk);
-  p->tok_per_block = (int)round_up(std::max<long long>(128, (work + 511) / 512), 128);
-  p->tok_per_block = (int)std::min<long long>(p->tok_per_block, round_up(n, 128));
-  p->G = ceil_div(n, p->tok_per_block);
   p->ks = (p->half == 0) ? 2 : (p->half <= 16 ? 4 : 6);
   const bool bf16 = dtype == NYS_BF16;
 
   nys::CtxArgs& c = p->ctx;
   std::memset(&c, 0, sizeof(c));
   c.BH = p->BH; c.H = H; c.n = n; c.d = d; c.m = m; c.mp = p->mp; c.iters = pinv_iters;
-  c.chunk = p->chunk; c.C = p->C; c.LG = p->LG; c.TG = p->TG;
+  c.LG = p->LG; c.TG = p->TG;
   c.npinv = p->fused ? p->BH : 0;
   nys::context_ring_geometry(d, c);
   const size_t ctx_lds = nys::context_lds_bytes(bf16, d, c);
-  const size_t out_lds = nys::output_lds_bytes(bf16, d, p->mp, p->ks, p->C);
   const size_t max_lds = (size_t)prop.sharedMemPerBlock;
-  if (ctx_lds > max_lds || out_lds > max_lds) {
+  if (ctx_lds > max_lds) {
     delete p;
     return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
   }
-  if (nys::configure_context(bf16, d, p->mp, ctx_lds) != hipSuccess ||
-      nys::configure_output(bf16, d, p->ks, out_lds) != hipSuccess) {
+  if (nys::configure_context(bf16, d, p->mp, ctx_lds) != hipSuccess) {
+    (void)hipGetLastError();
+    delete p;
+    return fail(NYS_E_LAUNCH, "could not set kernel LDS limits");
+  }
+  // Context blocks: about one resident round of them next to the fused pseudo-inverse
+  // blocks (the runtime's occupancy figure; three per CU if it cannot tell), at most 16
+  // chunks per head (bounds the merge), and, with the fused pseudo-inverse, at most 4
+  // when that still fills half the slots: the output prologue loads the chunk states of
+  // four chunks in one batch.
+  const int ctx_per_cu = nys::context_blocks_per_cu(bf16, d, p->mp, ctx_lds);
+  const long long slots =
+      (long long)(ctx_per_cu > 0 ? ctx_per_cu : 3) * std::max(1, prop.multiProcessorCount);
+  const long long target = std::max<long long>(slots / 2, slots - (p->fused ? p->BH : 0));
+  const long long heads = std::max(1, p->BH);  // B*H == 0 is an empty problem
+  long long nc = std::min<long long>(16, std::max<long long>(1, (target + heads - 1) / heads));
+  if (p->fused && nc > 4 && 4LL * heads >= target / 2) nc = 4;
+  p->chunk = (int)round_up(std::max<long long>(step, ((long long)n + nc - 1) / nc), step);
+  p->chunk = (int)std::min<long long>(p->chunk, round_up(n, step));
+  p->C = ceil_div(n, p->chunk);
+  c.chunk = p->chunk; c.C = p->C;
+  const size_t out_lds = nys::output_lds_bytes(bf16, d, p->mp, p->ks, p->C);
+  if (out_lds > max_lds) {
+    delete p;
+    return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
+  }
+  if (nys::configure_output(bf16, d, p->ks, out_lds) != hipSuccess) {
     (void)hipGetLastError();
     delete p;
     return fail(NYS_E_LAUNCH, "could not set kernel LDS limits");
@@ -218,7 +227,7 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   std::vector<int> chunk_tab;
   const bool uneven = p->fused &&
                       uneven_chunks(p->BH, p->C, n, step, p->BH, prop.multiProcessorCount,
-                                    nys::context_blocks_per_cu(bf16, d, p->mp, ctx_lds),
+                                    ctx_per_cu,
                                     chunk_tab);
   const size_t o_ct = take(uneven ? chunk_tab.size() * sizeof(int) : 0);
   p->ws_bytes = off;
