@@ -87,9 +87,100 @@ __global__ __launch_bounds__(256) void segmeans_kernel(const Tin* __restrict__ q
   }
 }
 
+// Long segments (more than 64 rows): one block of WPS (2, 4 or 8) waves per (matrix, head,
+// segment).
+// Wave w streams rows w, w + WPS, ... in whole-row loads as above (so every wave moves about
+// 64 rows, not one wave the whole segment), and the waves' chunk sums are added through LDS.
+template <typename Tin, int D, int WPS>
+__global__ __launch_bounds__(64 * WPS) void segmeans_split_kernel(const Tin* __restrict__ q,
+                                                                  const Tin* __restrict__ k,
+                                                                  SegArgs a) {
+  constexpr int EPC = 16 / sizeof(Tin), CPR = D / EPC, RPW = 64 / CPR;
+  __shared__ float part[WPS][CPR][EPC];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const long long task = blockIdx.x;  // (matrix, head, segment)
+  const int j = (int)(task % a.m);
+  const int bh = (int)((task / a.m) % a.BH);
+  const int which = (int)(task / ((long long)a.m * a.BH));
+  const int c = lane % CPR, r0 = lane / CPR;
+  const int L = valid_length(a.lengths, bh, a.H, a.n, a.m);
+  const int start = (int)(((long long)j * L + a.m - 1) / a.m);
+  const int rows = (int)(((long long)(j + 1) * L + a.m - 1) / a.m) - start;
+  const Tin* src = (which ? k : q) + ((size_t)bh * a.n + start) * D + c * EPC;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+  const int nit = (rows + RPW * WPS - 1) / (RPW * WPS);
+#pragma unroll 8
+  for (int it = 0; it < nit; ++it) {
+    const int r = r0 + RPW * (wave + WPS * it);
+    float x[8];
+    if constexpr (EPC == 8) {
+      Input<Tin>::load_raw(src + (size_t)r * D, r < rows, x);
+    } else {
+      const f32x4 v = r < rows ? *reinterpret_cast<const f32x4*>(src + (size_t)r * D)
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[e] = v[e];
+    }
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += x[e];
+  }
+#pragma unroll
+  for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+  if (lane < CPR)
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) part[wave][lane][e] = acc[e];
+  __syncthreads();
+  if (wave != 0 || lane >= CPR) return;
+  float mean[8];
+#pragma unroll
+  for (int e = 0; e < EPC; ++e) {
+    float sum = 0.f;
+#pragma unroll
+    for (int w = 0; w < WPS; ++w) sum += part[w][lane][e];  // fixed order
+    mean[e] = sum / (float)rows;
+  }
+  float* dst = (which ? a.kt : a.qt) + ((size_t)bh * a.mp + j) * D + c * EPC;
+  uint16_t* hl = (which ? a.kt_hl : a.qt_hl) + (size_t)bh * 2 * a.mp * D + (size_t)j * D + c * EPC;
+  *reinterpret_cast<f32x4*>(dst) = f32x4{mean[0], mean[1], mean[2], mean[3]};
+  if constexpr (EPC == 8) {
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{mean[4], mean[5], mean[6], mean[7]};
+    const Pair8 p = split8(mean);
+    st8(hl, p.hi);
+    st8(hl + (size_t)a.mp * D, p.lo);
+  } else {
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split1(mean[e], hb[e], lb[e]);
+    *reinterpret_cast<u32x2*>(hl) =
+        u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    *reinterpret_cast<u32x2*>(hl + (size_t)a.mp * D) =
+        u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+  }
+}
+
 template <typename Tin, int D>
 static hipError_t launch_segmeans_t(const void* q, const void* k, const SegArgs& a,
                                     hipStream_t s) {
+  const int lmax = (a.n + a.m - 1) / a.m;  // longest segment
+  if (lmax > 256) {
+    hipLaunchKernelGGL((segmeans_split_kernel<Tin, D, 8>), dim3((unsigned)(2LL * a.BH * a.m)),
+                       dim3(512), 0, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), a);
+    return hipGetLastError();
+  }
+  if (lmax > 128) {
+    hipLaunchKernelGGL((segmeans_split_kernel<Tin, D, 4>), dim3((unsigned)(2LL * a.BH * a.m)),
+                       dim3(256), 0, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), a);
+    return hipGetLastError();
+  }
+  if (lmax > 64) {
+    hipLaunchKernelGGL((segmeans_split_kernel<Tin, D, 2>), dim3((unsigned)(2LL * a.BH * a.m)),
+                       dim3(128), 0, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), a);
+    return hipGetLastError();
+  }
   const long long waves = 2LL * a.BH * a.m;  // one per (matrix, head, segment)
   const int blocks = (int)((waves + 3) / 4);
   hipLaunchKernelGGL((segmeans_kernel<Tin, D>), dim3(blocks), dim3(256), 0, s,
