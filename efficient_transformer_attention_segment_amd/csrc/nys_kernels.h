@@ -173,6 +173,8 @@ hipError_t configure_context(bool bf16, int d, int mp, size_t ctx_lds);
 int context_blocks_per_cu(bool bf16, int d, int mp, size_t ctx_lds);
 // Output blocks resident per CU at this LDS size (0 if the runtime cannot tell).
 int output_blocks_per_cu(bool bf16, int d, int ks, int mp, int m, int C, size_t lds);
+// Tokens per step of one output block (32 per wave).
+int output_step_tokens(bool bf16, int d, int mp, int conv_ksteps, int C);
 hipError_t configure_output(bool bf16, int d, int conv_ksteps, size_t out_lds);
 
 }  // namespace nys

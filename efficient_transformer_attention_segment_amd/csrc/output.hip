@@ -12,8 +12,9 @@
 // loads (chunk states, partials, Z, Kt, the first V rows and Q) are issued before any
 // is used, so the set-up costs about one memory round trip.
 //
-// The block then walks a contiguous token range of its head in steps of 128 tokens;
-// each wave owns 32 tokens per step. Per wave and step:
+// The block then walks a contiguous token range of its head in steps of 32 tokens per
+// wave (4 waves, or 8 for the online-softmax shapes where one block fills the LDS).
+// Per wave and step:
 //  * scores S^T = Kt Q^T (landmarks x tokens) on MFMA, Q read straight into the B
 //    operand;
 //  * softmax over the landmarks. Each lane holds one token, so the normaliser is
@@ -48,15 +49,19 @@ __device__ __forceinline__ int score_landmark(int lt, int rr, int h) {
 
 // NT: landmark tiles handled with all scores in registers (1 or 2), or 0 for the
 // online softmax over a runtime number of tiles. kFull: m == 32 * NT (no masking).
-template <typename Tin, int D, int KS, bool kKtLds, int NT, bool kFull>
-__global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
+// NW: waves per block (4, or 8 where one block fills a CU's LDS); a step covers 32 NW
+// tokens.
+template <typename Tin, int D, int KS, bool kKtLds, int NT, bool kFull, int NW>
+__global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   extern __shared__ __align__(16) char lds[];
   constexpr bool kS = Input<Tin>::kSplit;
   constexpr int KD = D / 16, FT = D / 32;
-  constexpr int EXT = 96 + 16 * KS;  // staged V rows per 128-token step (with halo)
+  constexpr int NTH = 64 * NW, STEP = 32 * NW;
+  constexpr int EXT = STEP - 32 + 16 * KS;  // staged V rows per step (with halo)
   constexpr int VR = D + 8;          // LDS row stride (elements) of the row-major V tile
   constexpr int KR = D + 8;          // LDS row stride of the Kt planes
-  constexpr int NCH = (EXT * (D / 8) + 255) / 256;  // 8-element V chunks per thread
+  constexpr int NCH = (EXT * (D / 8) + NTH - 1) / NTH;  // 8-element V chunks per thread
+  static_assert(32 * NW * D <= EXT * VR, "output rows are staged in the V tile");
   static_assert(NT == 0 || kKtLds, "register-resident softmax expects Kt in LDS");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, h = lane >> 5;
@@ -74,11 +79,11 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   if (t_begin >= t_valid) {
     constexpr int EPV = 16 / sizeof(Tin);  // elements per 16-byte store
     Tin* o = static_cast<Tin*>(a.out) + ((size_t)bh * a.n + t_begin) * D;
-    for (int e = threadIdx.x; e < (t_end - t_begin) * (D / EPV); e += 256)
+    for (int e = threadIdx.x; e < (t_end - t_begin) * (D / EPV); e += NTH)
       *reinterpret_cast<u32x4*>(o + (size_t)e * EPV) = u32x4{0u, 0u, 0u, 0u};
     if (a.attn_tap != nullptr) {
       float* tp = a.attn_tap + ((size_t)bh * a.n + t_begin) * D;
-      for (int e = threadIdx.x; e < (t_end - t_begin) * (D / 4); e += 256)
+      for (int e = threadIdx.x; e < (t_end - t_begin) * (D / 4); e += NTH)
         *reinterpret_cast<f32x4*>(tp + (size_t)e * 4) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
     return;
@@ -110,7 +115,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     const int e0 = T0 - a.half;
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int qi = tid + 256 * u;
+      const int qi = tid + NTH * u;
       const int row = qi / (D / 8), cf = qi % (D / 8), tok = e0 + row;
       vc[u].load(V + (size_t)tok * D + cf * 8, qi < EXT * (D / 8) && tok >= 0 && tok < t_valid_v);
     }
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   auto store_v = [&](const Chunk<Tin>* vc) {
 #pragma unroll
     for (int u = 0; u < NCH; ++u) {
-      const int qi = tid + 256 * u;
+      const int qi = tid + NTH * u;
       if (qi < EXT * (D / 8)) {
         const int row = qi / (D / 8), cf = qi % (D / 8);
         vc[u].store(vt + (size_t)row * VR + cf * 8, vt_lo + (size_t)row * VR + cf * 8);
@@ -191,17 +196,17 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   }
   // register-resident softmax shapes (mp = 32 NT): partial W^T of the first kCB chunks
   // (UP float4 outputs per thread), Z rows of the wave's Y tiles, the thread's Kt share
-  constexpr int UP = NT > 0 ? (D * 8 * NT + 255) / 256 : 1;
-  constexpr int TPY = NT > 0 ? (NT * (D / 32) + 3) / 4 : 1;
+  constexpr int UP = NT > 0 ? (D * 8 * NT + NTH - 1) / NTH : 1;
+  constexpr int TPY = NT > 0 ? (NT * (D / 32) + NW - 1) / NW : 1;
   constexpr int KM = NT > 0 ? 2 * NT : 1;
-  constexpr int KU = NT > 0 ? (4 * NT * D + 255) / 256 : 1;
+  constexpr int KU = NT > 0 ? (4 * NT * D + NTH - 1) / NTH : 1;
   f32x4 pv[UP][kCB];
   Pair8 za[TPY][KM];
   f32x4 kx[KU][2];
   if constexpr (NT > 0) {
 #pragma unroll
     for (int u = 0; u < UP; ++u) {
-      const int e = tid + 256 * u, f = e / (mp / 4), j = (e % (mp / 4)) * 4;
+      const int e = tid + NTH * u, f = e / (mp / 4), j = (e % (mp / 4)) * 4;
 #pragma unroll
       for (int c = 0; c < kCB; ++c)
         pv[u][c] = (e < D * mp / 4 && c < C)
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < TPY; ++u) {
-      const int t = wave + 4 * u;
+      const int t = wave + NW * u;
       const int row0 = 32 * (t / ntj);
 #pragma unroll
       for (int s = 0; s < KM; ++s) {
@@ -220,7 +225,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     }
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      const int e = tid + NTH * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
       const float* ks = a.kt + ((size_t)bh * mp + row) * D + c8;
       const bool ok = e < mp * (D / 8);
       kx[u][0] = ok ? *reinterpret_cast<const f32x4*>(ks) : f32x4{0.f, 0.f, 0.f, 0.f};
@@ -284,7 +289,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
     if constexpr (NT > 0) {
 #pragma unroll
       for (int u = 0; u < KU; ++u) {
-        const int e = tid + 256 * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+        const int e = tid + NTH * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
         if (e < mp * (D / 8)) {
           float x[8];
 #pragma unroll
@@ -299,7 +304,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
       }
     } else {
       const uint16_t* ksrc = a.kt_hl + (size_t)bh * 2 * mp * D;
-      for (int e = tid; e < 2 * mp * (D / 8); e += 256) {
+      for (int e = tid; e < 2 * mp * (D / 8); e += NTH) {
         const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
         st8(kl + (size_t)row * KR + c8, ld8(ksrc + (size_t)row * D + c8));
       }
@@ -335,7 +340,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   if constexpr (NT > 0) {
 #pragma unroll
     for (int u = 0; u < UP; ++u) {
-      const int e = tid + 256 * u, f = e / (mp / 4), j = (e % (mp / 4)) * 4;
+      const int e = tid + NTH * u, f = e / (mp / 4), j = (e % (mp / 4)) * 4;
       if (e < D * mp / 4) {
         f32x4 acc{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -346,7 +351,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
       }
     }
   } else {
-    for (int e = tid; e < D * mp / 4; e += 256) {
+    for (int e = tid; e < D * mp / 4; e += NTH) {
       const int f = e / (mp / 4), j = (e % (mp / 4)) * 4;
       put_w(f, j, merge_rest(f, j, f32x4{0.f, 0.f, 0.f, 0.f}, 0));
     }
@@ -370,7 +375,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   if constexpr (NT > 0) {
 #pragma unroll
     for (int u = 0; u < TPY; ++u) {
-      const int t = wave + 4 * u;
+      const int t = wave + NW * u;
       if (t < ntiles) {
         const int row0 = 32 * (t / ntj), col0 = 32 * (t % ntj);
         const size_t ob = (size_t)(col0 + r32) * YS + 8 * h;
@@ -384,7 +389,7 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
       }
     }
   } else {
-    for (int t = wave; t < ntiles; t += 4) {
+    for (int t = wave; t < ntiles; t += NW) {
       const int row0 = 32 * (t / ntj), col0 = 32 * (t % ntj);
       put_y(row0, col0, gemm_tile(zr, zr + P, mp, wtl, wtl + (size_t)D * YS, YS, row0, col0, mp, lane));
     }
@@ -393,12 +398,12 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
   store_v(vc);
   __syncthreads();
 
-  for (int T0 = t_begin; T0 < t_end; T0 += 128) {
-    const bool more = T0 + 128 < t_end;
+  for (int T0 = t_begin; T0 < t_end; T0 += STEP) {
+    const bool more = T0 + STEP < t_end;
     Pair8 qn[KD];
     if (more) {  // next step's V rows and Q, in flight during this step's products
-      load_v(T0 + 128, vc);
-      load_q(T0 + 128, qn);
+      load_v(T0 + STEP, vc);
+      load_q(T0 + STEP, qn);
     }
     const int tq = T0 + 32 * wave + r32;
     const bool qok = tq < t_end;
@@ -565,8 +570,8 @@ __global__ __launch_bounds__(256) void output_kernel(OutArgs a) {
 // LDS budget of one block; Kt goes to LDS only when everything fits in 160 KiB.
 constexpr size_t kLdsLimit = 160 * 1024;
 
-static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, bool kt_lds) {
-  const size_t ext = 96 + 16 * (size_t)conv_ksteps;
+static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, bool kt_lds, int nw) {
+  const size_t ext = 32 * (size_t)nw - 32 + 16 * (size_t)conv_ksteps;
   const size_t yl = (size_t)2 * d * (mp + 8) * 2;
   const size_t wl = (size_t)conv_ksteps * 2 * 64 * 8 * 2;
   const size_t kl = kt_lds ? (size_t)2 * mp * (d + 8) * 2 : 0;
@@ -576,29 +581,50 @@ static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, bool k
 }
 
 static bool kt_in_lds(bool bf16, int d, int mp, int conv_ksteps, int C) {
-  return lds_bytes(bf16, d, mp, conv_ksteps, C, true) <= kLdsLimit;
+  return lds_bytes(bf16, d, mp, conv_ksteps, C, true, 4) <= kLdsLimit;
+}
+
+// Waves per block. The online-softmax shapes (m > 64) usually fill a CU's LDS with one
+// 4-wave block, leaving one wave per SIMD to hide every load and product latency; where
+// the larger V tile of an 8-wave block still fits (and its registers allow two waves per
+// SIMD: bf16, d <= 64) the block takes 8 waves and 256-token steps.
+static int waves_per_block(bool bf16, int d, int mp, int conv_ksteps, int C) {
+  if (!bf16 || d > 64 || mp <= 64) return 4;
+  const bool kt = kt_in_lds(bf16, d, mp, conv_ksteps, C);
+  if (2 * lds_bytes(bf16, d, mp, conv_ksteps, C, kt, 4) <= kLdsLimit) return 4;
+  return lds_bytes(bf16, d, mp, conv_ksteps, C, kt, 8) <= kLdsLimit ? 8 : 4;
 }
 
 size_t output_lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C) {
-  return lds_bytes(bf16, d, mp, conv_ksteps, C, kt_in_lds(bf16, d, mp, conv_ksteps, C));
+  return lds_bytes(bf16, d, mp, conv_ksteps, C, kt_in_lds(bf16, d, mp, conv_ksteps, C),
+                   waves_per_block(bf16, d, mp, conv_ksteps, C));
+}
+
+int output_step_tokens(bool bf16, int d, int mp, int conv_ksteps, int C) {
+  return 32 * waves_per_block(bf16, d, mp, conv_ksteps, C);
 }
 
 // Kernel variant for a shape: register-resident softmax for m <= 64 with the usual
 // conv width (k-steps 4), online softmax otherwise.
 template <typename Tin, int D, int KS>
-static const void* pick_kernel(const OutArgs& a, bool kt_lds) {
+static const void* pick_kernel(const OutArgs& a, bool kt_lds, int nw) {
   if constexpr (KS == 4) {
     if (a.mp <= 64 && kt_lds) {
       const bool full = a.m == a.mp;
       if (a.mp == 32)
-        return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true>)
-                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false>);
-      return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true>)
-                  : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false>);
+        return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true, 4>)
+                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false, 4>);
+      return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true, 4>)
+                  : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4>);
     }
   }
-  return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false>)
-                : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false>);
+  if constexpr (!Input<Tin>::kSplit && D <= 64) {
+    if (nw == 8)
+      return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8>)
+                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8>);
+  }
+  return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 4>)
+                : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4>);
 }
 
 template <typename Tin, int D, int KS>
@@ -608,9 +634,10 @@ static int blocks_per_cu_t(int mp, int m, int C, size_t lds) {
   a.mp = mp;
   a.m = m;
   a.C = C;
-  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, mp, KS, C));
+  const int nw = waves_per_block(kBf16, D, mp, KS, C);
+  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, mp, KS, C), nw);
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 256, lds) != hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * nw, lds) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -639,9 +666,10 @@ template <typename Tin, int D, int KS>
 static hipError_t launch_t(const OutArgs& a, hipStream_t s) {
   constexpr bool kBf16 = !Input<Tin>::kSplit;
   const size_t lds = output_lds_bytes(kBf16, D, a.mp, KS, a.C);
-  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, a.mp, KS, a.C));
+  const int nw = waves_per_block(kBf16, D, a.mp, KS, a.C);
+  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, a.mp, KS, a.C), nw);
   void* args[] = {const_cast<OutArgs*>(&a)};
-  return hipLaunchKernel(fn, dim3(a.BH * a.G), dim3(256), args, lds, s);
+  return hipLaunchKernel(fn, dim3(a.BH * a.G), dim3(64 * nw), args, lds, s);
 }
 
 template <typename Tin, int D>
@@ -664,15 +692,19 @@ hipError_t launch_output(bool bf16, int d, int ks, const OutArgs& a, hipStream_t
 
 template <typename Tin, int D, int KS>
 static hipError_t attr_t(size_t bytes) {
-  const void* fns[6] = {
-      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false>),
-      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false>)};
+  const void* fns[8] = {
+      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 4>),
+      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4>)};
   int nf = 2;
   if constexpr (KS == 4) {
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true>);
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false>);
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true>);
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true, 4>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false, 4>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true, 4>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4>);
+  }
+  if constexpr (!Input<Tin>::kSplit && D <= 64) {
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8>);
   }
   for (int i = 0; i < nf; ++i) {
     const hipError_t e =

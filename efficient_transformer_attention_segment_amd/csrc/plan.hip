@@ -201,8 +201,9 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
     const int per_cu = nys::output_blocks_per_cu(bf16, d, p->ks, p->mp, m, p->C, out_lds);
     const long long slots =
         per_cu > 0 ? (long long)per_cu * std::max(1, prop.multiProcessorCount) : 512;
-    p->tok_per_block = (int)round_up(std::max<long long>(128, (work + slots - 1) / slots), 128);
-    p->tok_per_block = (int)std::min<long long>(p->tok_per_block, round_up(n, 128));
+    const int stp = nys::output_step_tokens(bf16, d, p->mp, p->ks, p->C);
+    p->tok_per_block = (int)round_up(std::max<long long>(stp, (work + slots - 1) / slots), stp);
+    p->tok_per_block = (int)std::min<long long>(p->tok_per_block, round_up(n, stp));
     p->G = ceil_div(n, p->tok_per_block);
   }
 
