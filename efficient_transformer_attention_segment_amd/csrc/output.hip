@@ -147,12 +147,19 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
         S = mfma_pair<true, kS>(ka, qb[s], S);
       }
     } else {
+      // Kt from L2, loaded in groups of KG k-steps (all at once unless registers are
+      // short: two waves per SIMD at d = 128)
+      constexpr int KG = (NW == 8 && D > 64) ? KD / 2 : KD;
       const uint16_t* kp = khl + (size_t)(32 * lt + r32) * D + 8 * h;
-      Pair8 ka[KD];
 #pragma unroll
-      for (int s = 0; s < KD; ++s) ka[s] = Pair8{ld8(kp + 16 * s), ld8(kp + (size_t)mp * D + 16 * s)};
+      for (int g = 0; g < KD; g += KG) {
+        Pair8 ka[KG];
 #pragma unroll
-      for (int s = 0; s < KD; ++s) S = mfma_pair<true, kS>(ka[s], qb[s], S);
+        for (int s = 0; s < KG; ++s)
+          ka[s] = Pair8{ld8(kp + 16 * (g + s)), ld8(kp + (size_t)mp * D + 16 * (g + s))};
+#pragma unroll
+        for (int s = 0; s < KG; ++s) S = mfma_pair<true, kS>(ka[s], qb[g + s], S);
+      }
     }
     return S;
   };
@@ -400,10 +407,13 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
 
   for (int T0 = t_begin; T0 < t_end; T0 += STEP) {
     const bool more = T0 + STEP < t_end;
-    Pair8 qn[KD];
-    if (more) {  // next step's V rows and Q, in flight during this step's products
+    // next step's V rows and Q, in flight during this step's products (Q only where the
+    // registers allow: not with two waves per SIMD at d = 128)
+    constexpr bool kQPre = !(NW == 8 && D > 64);
+    Pair8 qn[kQPre ? KD : 1];
+    if (more) {
       load_v(T0 + STEP, vc);
-      load_q(T0 + STEP, qn);
+      if constexpr (kQPre) load_q(T0 + STEP, qn);
     }
     const int tq = T0 + 32 * wave + r32;
     const bool qok = tq < t_end;
@@ -560,7 +570,10 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
       __syncthreads();  // every wave is done with this step's V tile
       store_v(vc);
 #pragma unroll
-      for (int s = 0; s < KD; ++s) qb[s] = qn[s];
+      for (int s = 0; s < KD; ++s) {
+        if constexpr (kQPre) qb[s] = qn[s];
+      }
+      if constexpr (!kQPre) load_q(T0 + STEP, qb);
       __syncthreads();
     }
   }
@@ -589,7 +602,7 @@ static bool kt_in_lds(bool bf16, int d, int mp, int conv_ksteps, int C) {
 // the larger V tile of an 8-wave block still fits (and its registers allow two waves per
 // SIMD: bf16, d <= 64) the block takes 8 waves and 256-token steps.
 static int waves_per_block(bool bf16, int d, int mp, int conv_ksteps, int C) {
-  if (!bf16 || d > 64 || mp <= 64) return 4;
+  if (!bf16 || mp <= 64) return 4;
   const bool kt = kt_in_lds(bf16, d, mp, conv_ksteps, C);
   if (2 * lds_bytes(bf16, d, mp, conv_ksteps, C, kt, 4) <= kLdsLimit) return 4;
   return lds_bytes(bf16, d, mp, conv_ksteps, C, kt, 8) <= kLdsLimit ? 8 : 4;
@@ -618,7 +631,7 @@ static const void* pick_kernel(const OutArgs& a, bool kt_lds, int nw) {
                   : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4>);
     }
   }
-  if constexpr (!Input<Tin>::kSplit && D <= 64) {
+  if constexpr (!Input<Tin>::kSplit) {
     if (nw == 8)
       return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8>)
                     : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8>);
@@ -702,7 +715,7 @@ static hipError_t attr_t(size_t bytes) {
     fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true, 4>);
     fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4>);
   }
-  if constexpr (!Input<Tin>::kSplit && D <= 64) {
+  if constexpr (!Input<Tin>::kSplit) {
     fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8>);
     fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8>);
   }
