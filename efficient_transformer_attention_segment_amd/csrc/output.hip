@@ -458,6 +458,10 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
       float M = kNegBig, L = 0.f;
       for (int lt = 0; lt < mp / 32; ++lt) {
         const f32x16 S = scores(lt, qb);
+        // without a register prefetch, the next step's Q goes into qb as soon as the
+        // last scores are formed, in flight during the products below
+        if constexpr (!kQPre)
+          if (more && lt == mp / 32 - 1) load_q(T0 + STEP, qb);
         float x[16];
         float mx = kNegBig;
 #pragma unroll
@@ -573,7 +577,6 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
       for (int s = 0; s < KD; ++s) {
         if constexpr (kQPre) qb[s] = qn[s];
       }
-      if constexpr (!kQPre) load_q(T0 + STEP, qb);
       __syncthreads();
     }
   }
