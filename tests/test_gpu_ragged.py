@@ -36,6 +36,10 @@ CASES = {
     "ragged_m1": (gen.Config("r5", 4, 1, 100, 64, 1, seed=65), [1, 2, 50, 100]),
     "ragged_len_m_and_m_plus_1": (gen.Config("r6", 2, 2, 200, 64, 8, seed=66), [8, 9]),
     "ragged_m32_step128": (gen.Config("r7", 2, 2, 1000, 64, 32, seed=67), [999, 129]),
+    # 8-wave output blocks (256-token steps): Kt read from L2 at d = 64, m = 256; and at
+    # d = 128 with lengths that cut a step and a block
+    "ragged_m256_8waves": (gen.Config("r8", 2, 1, 2048, 64, 256, seed=69), [2048, 700]),
+    "ragged_d128_8waves": (gen.Config("r9", 2, 1, 2304, 128, 128, seed=70), [1500, 2303]),
 }
 
 
