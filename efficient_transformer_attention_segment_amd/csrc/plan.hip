@@ -393,8 +393,11 @@ extern "C" nys_status nys_attn_profile_enable(nys_attn_plan* p, int max_calls) {
   for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
   p->prof_ev.clear();
   p->prof_ev.resize((kStages + 1) * (size_t)max_calls);
+  // Device-scope release: the markers sit between kernels of one stream, so no
+  // system-scope fence is needed; with one, every marker costs microseconds of GPU time
+  // that would be counted in the neighbouring stages.
   for (auto& e : p->prof_ev)
-    if (hipEventCreate(&e) != hipSuccess) {
+    if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) {
       p->prof_max = 0;
       return fail(NYS_E_LAUNCH, "event creation failed");
     }
