@@ -274,11 +274,11 @@ __global__ __launch_bounds__(512) void pinv_strip_kernel(CtxArgs a) {
     rmax = wave_max(rmax);
     if (lane == 0) part[mp] = rmax;
   }
-  // A_S (fp32 copy for inspection, hi/lo rows) and the unscaled Z_0 planes
+  // A_S (fp32 copy for inspection, hi/lo rows) and the unscaled Z_0 planes, fragment-major
   store_rows_f32(a.a_s + (size_t)bh * P, mp, row0, col0, at, lane);
-  store_rows_hl(plane(kPA), plane(kPA + 1), mp, row0, col0, at, lane);
-  store_rows_hl(plane(kPZc), plane(kPZc + 1), mp, row0, col0, at, lane);
-  store_cols_hl(plane(kPZr), plane(kPZr + 1), mp, row0, col0, at, lane);
+  store_rows_hl_frag(plane(kPA), plane(kPA + 1), mp, row0, col0, at, lane);
+  store_rows_hl_frag(plane(kPZc), plane(kPZc + 1), mp, row0, col0, at, lane);
+  store_cols_hl_frag(plane(kPZr), plane(kPZr + 1), mp, row0, col0, at, lane);
 }
 
 // alpha = 1 / (max column abs-sum * max row abs-sum) of head bh's A_S, from the partial
@@ -298,7 +298,9 @@ __device__ __forceinline__ float pinv_alpha(const CtxArgs& a, int bh, int lane) 
 
 // One product of an iteration for every head at once (mp > 64): one wave per 32 x 32
 // output tile, operands read from the head's planes in global memory (they stay in the
-// XCD's L2: a head's tiles run on one XCD). Successive phases are ordered by the launch
+// XCD's L2: a head's tiles run on one XCD). The planes written by the strip kernel and
+// by these phases are fragment-major (frag_off), so every operand load reads whole cache
+// lines; only the final Z leaves row-major. Successive phases are ordered by the launch
 // boundaries, so the m x m products of a head spread over many CUs instead of one.
 //   PH 0: X = A Z        -> X rows and columns (hi/lo), fp32 X
 //   PH 1: X^2 = X X      -> X^2 columns (hi/lo), fp32 X^2
@@ -318,21 +320,21 @@ __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
   float* own = a.own + (size_t)bh * 2 * P;
   if constexpr (PH == 0) {
     const int zc = (it & 1) ? kGZc1 : kPZc;
-    f32x16 x = gemm_tile(plane(kPA), plane(kPA + 1), mp, plane(zc), plane(zc + 1), mp, row0,
-                         col0, mp, lane);
+    f32x16 x = gemm_tile_frag(plane(kPA), plane(kPA + 1), plane(zc), plane(zc + 1), row0, col0,
+                              mp, lane);
     if (it == 0) x *= pinv_alpha(a, bh, lane);  // the Z_0 planes are unscaled
-    store_rows_hl(plane(kPXr), plane(kPXr + 1), mp, row0, col0, x, lane);
-    store_cols_hl(plane(kPXc), plane(kPXc + 1), mp, row0, col0, x, lane);
+    store_rows_hl_frag(plane(kPXr), plane(kPXr + 1), mp, row0, col0, x, lane);
+    store_cols_hl_frag(plane(kPXc), plane(kPXc + 1), mp, row0, col0, x, lane);
     store_rows_f32(own, mp, row0, col0, x, lane);
   } else if constexpr (PH == 1) {
-    const f32x16 x2 = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPXc), plane(kPXc + 1),
-                                mp, row0, col0, mp, lane);
-    store_cols_hl(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, x2, lane);
+    const f32x16 x2 = gemm_tile_frag(plane(kPXr), plane(kPXr + 1), plane(kPXc), plane(kPXc + 1),
+                                     row0, col0, mp, lane);
+    store_cols_hl_frag(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, x2, lane);
     store_rows_f32(own + P, mp, row0, col0, x2, lane);
   } else if constexpr (PH == 2) {
     const int j = col0 + (lane & 31);
-    const f32x16 x3 = gemm_tile(plane(kPXr), plane(kPXr + 1), mp, plane(kPX2T),
-                                plane(kPX2T + 1), mp, row0, col0, mp, lane);
+    const f32x16 x3 = gemm_tile_frag(plane(kPXr), plane(kPXr + 1), plane(kPX2T),
+                                     plane(kPX2T + 1), row0, col0, mp, lane);
     f32x16 tv;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -340,20 +342,20 @@ __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
       const float diag = (acc_row(row0, rr, lane) == j) ? 13.f : 0.f;
       tv[rr] = diag - 15.f * own[o] + 7.f * own[P + o] - x3[rr];
     }
-    store_cols_hl(plane(kGT), plane(kGT + 1), mp, row0, col0, tv, lane);
+    store_cols_hl_frag(plane(kGT), plane(kGT + 1), mp, row0, col0, tv, lane);
   } else {
     const int zr = (it & 1) ? kGZr1 : kPZr;
     const int zr_n = (it & 1) ? kPZr : kGZr1, zc_n = (it & 1) ? kPZc : kGZc1;
-    const f32x16 zv = gemm_tile(plane(zr), plane(zr + 1), mp, plane(kGT), plane(kGT + 1), mp,
-                                row0, col0, mp, lane) *
+    const f32x16 zv = gemm_tile_frag(plane(zr), plane(zr + 1), plane(kGT), plane(kGT + 1), row0,
+                                     col0, mp, lane) *
                       (it == 0 ? 0.25f * pinv_alpha(a, bh, lane) : 0.25f);
     if (it == a.iters - 1) {
       uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
       store_rows_hl(dst, dst + P, mp, row0, col0, zv, lane);
       store_rows_f32(a.z + (size_t)bh * P, mp, row0, col0, zv, lane);
     } else {
-      store_rows_hl(plane(zr_n), plane(zr_n + 1), mp, row0, col0, zv, lane);
-      store_cols_hl(plane(zc_n), plane(zc_n + 1), mp, row0, col0, zv, lane);
+      store_rows_hl_frag(plane(zr_n), plane(zr_n + 1), mp, row0, col0, zv, lane);
+      store_cols_hl_frag(plane(zc_n), plane(zc_n + 1), mp, row0, col0, zv, lane);
     }
   }
 }

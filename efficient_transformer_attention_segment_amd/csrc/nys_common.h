@@ -396,6 +396,63 @@ __device__ __forceinline__ void store_cols_hl(uint16_t* hi, uint16_t* lo, int ld
   }
 }
 
+// Fragment-major operand planes (ld x ld, ld a multiple of 32). Element (r, c) sits in
+// the 1 KiB block of row block r / 32 and k-step c / 16, at the slot of the lane that
+// takes it as an MFMA operand (lane r % 32 + 32 ((c % 16) / 8), element c % 8). One
+// operand load of a k-step then reads a whole contiguous block: eight full 128-byte
+// lines instead of 32-byte pieces of 32 lines.
+__device__ __forceinline__ size_t frag_off(int r, int c, int ld) {
+  return ((size_t)(r >> 5) * (ld >> 4) + (c >> 4)) * 512 + ((r & 31) + 32 * ((c >> 3) & 1)) * 8 +
+         (c & 7);
+}
+
+// C = A B^T tile at (row0, col0) with A and B^T both in fragment-major planes of width K.
+__device__ __forceinline__ f32x16 gemm_tile_frag(const uint16_t* ahi, const uint16_t* alo,
+                                                 const uint16_t* bhi, const uint16_t* blo,
+                                                 int row0, int col0, int K, int lane) {
+  const size_t oa = (size_t)(row0 >> 5) * (K >> 4) * 512 + 8 * lane;
+  const size_t ob = (size_t)(col0 >> 5) * (K >> 4) * 512 + 8 * lane;
+  f32x16 acc = zero16();
+#pragma unroll 8
+  for (int s = 0; s < (K >> 4); ++s) {
+    Pair8 a{ld8(ahi + oa + 512 * s), ld8(alo + oa + 512 * s)};
+    Pair8 b{ld8(bhi + ob + 512 * s), ld8(blo + ob + 512 * s)};
+    acc = mfma_pair<true, true>(a, b, acc);
+  }
+  return acc;
+}
+
+// store_rows_hl / store_cols_hl into fragment-major planes of width ld.
+__device__ __forceinline__ void store_rows_hl_frag(uint16_t* hi, uint16_t* lo, int ld, int row0,
+                                                   int col0, const f32x16& v, int lane) {
+  const int j = col0 + (lane & 31);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    uint16_t a, b;
+    split1(v[rr], a, b);
+    const size_t o = frag_off(acc_row(row0, rr, lane), j, ld);
+    hi[o] = a;
+    lo[o] = b;
+  }
+}
+
+__device__ __forceinline__ void store_cols_hl_frag(uint16_t* hi, uint16_t* lo, int ld, int row0,
+                                                   int col0, const f32x16& v, int lane) {
+  const int j = col0 + (lane & 31);
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    uint16_t a[4], b[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split1(v[4 * g + e], a[e], b[e]);
+    // columns row0 + 8g + 4h .. +3 of row j: four consecutive slots of one lane's chunk
+    const size_t o = frag_off(j, row0 + 8 * g + 4 * (lane >> 5), ld);
+    *reinterpret_cast<u32x2*>(hi + o) =
+        u32x2{(uint32_t)a[0] | ((uint32_t)a[1] << 16), (uint32_t)a[2] | ((uint32_t)a[3] << 16)};
+    *reinterpret_cast<u32x2*>(lo + o) =
+        u32x2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+  }
+}
+
 __device__ __forceinline__ void store_rows_f32(float* p, int ld, int row0, int col0,
                                                const f32x16& v, int lane) {
   const int j = col0 + (lane & 31);
