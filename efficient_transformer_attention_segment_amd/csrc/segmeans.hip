@@ -87,6 +87,76 @@ __global__ __launch_bounds__(256) void segmeans_kernel(const Tin* __restrict__ q
   }
 }
 
+// Short segments (at most one load instruction's RPW rows each): one wave takes SPW
+// consecutive segments of one (matrix, head), so SPW loads are in flight per wave instead
+// of one. Requires m % SPW == 0.
+template <typename Tin, int D, int SPW>
+__global__ __launch_bounds__(256) void segmeans_short_kernel(const Tin* __restrict__ q,
+                                                             const Tin* __restrict__ k,
+                                                             SegArgs a) {
+  constexpr int EPC = 16 / sizeof(Tin);
+  constexpr int CPR = D / EPC;
+  static_assert(CPR >= 1 && CPR <= 64 && (64 % CPR) == 0, "row must tile a wave");
+  const int lane = threadIdx.x & 63;
+  const int groups = a.m / SPW;
+  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= 2LL * a.BH * groups) return;  // whole waves only; the kernel has no barrier
+  const int j0 = (int)(task % groups) * SPW;
+  const int bh = (int)((task / groups) % a.BH);
+  const int which = (int)(task / ((long long)groups * a.BH));
+  const int c = lane % CPR, r = lane / CPR;
+  const int L = valid_length(a.lengths, bh, a.H, a.n, a.m);
+  const Tin* base = (which ? k : q) + (size_t)bh * a.n * D + c * EPC;
+  float x[SPW][8];
+  int rows[SPW];
+#pragma unroll
+  for (int g = 0; g < SPW; ++g) {
+    const int j = j0 + g;
+    const int start = (int)(((long long)j * L + a.m - 1) / a.m);
+    rows[g] = (int)(((long long)(j + 1) * L + a.m - 1) / a.m) - start;
+    const Tin* src = base + (size_t)(start + r) * D;
+    if constexpr (EPC == 8) {
+      Input<Tin>::load_raw(src, r < rows[g], x[g]);
+    } else {
+      const f32x4 v = r < rows[g] ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[g][e] = v[e];
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < SPW; ++g) {
+#pragma unroll
+    for (int o = CPR; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) x[g][e] += __shfl_xor(x[g][e], o);
+    if (lane < CPR) {
+      const int j = j0 + g;
+      const float inv_l = 1.0f / (float)rows[g];
+      float mean[8];
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) mean[e] = x[g][e] * inv_l;
+      float* dst = (which ? a.kt : a.qt) + ((size_t)bh * a.mp + j) * D + c * EPC;
+      uint16_t* hl =
+          (which ? a.kt_hl : a.qt_hl) + (size_t)bh * 2 * a.mp * D + (size_t)j * D + c * EPC;
+      *reinterpret_cast<f32x4*>(dst) = f32x4{mean[0], mean[1], mean[2], mean[3]};
+      if constexpr (EPC == 8) {
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{mean[4], mean[5], mean[6], mean[7]};
+        const Pair8 p = split8(mean);
+        st8(hl, p.hi);
+        st8(hl + (size_t)a.mp * D, p.lo);
+      } else {
+        uint16_t hb[4], lb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) split1(mean[e], hb[e], lb[e]);
+        *reinterpret_cast<u32x2*>(hl) = u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16),
+                                              (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+        *reinterpret_cast<u32x2*>(hl + (size_t)a.mp * D) =
+            u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+      }
+    }
+  }
+}
+
 // Long segments (more than 64 rows): one block of WPS (2, 4 or 8) waves per (matrix, head,
 // segment).
 // Wave w streams rows w, w + WPS, ... in whole-row loads as above (so every wave moves about
@@ -179,6 +249,13 @@ static hipError_t launch_segmeans_t(const void* q, const void* k, const SegArgs&
   if (lmax > 64) {
     hipLaunchKernelGGL((segmeans_split_kernel<Tin, D, 2>), dim3((unsigned)(2LL * a.BH * a.m)),
                        dim3(128), 0, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), a);
+    return hipGetLastError();
+  }
+  constexpr int RPW = 64 / (D / (16 / (int)sizeof(Tin)));  // rows per load instruction
+  if (lmax <= RPW && a.m % 4 == 0) {
+    const long long waves = 2LL * a.BH * (a.m / 4);  // one per 4 segments
+    hipLaunchKernelGGL((segmeans_short_kernel<Tin, D, 4>), dim3((unsigned)((waves + 3) / 4)),
+                       dim3(256), 0, s, static_cast<const Tin*>(q), static_cast<const Tin*>(k), a);
     return hipGetLastError();
   }
   const long long waves = 2LL * a.BH * a.m;  // one per (matrix, head, segment)
