@@ -205,6 +205,10 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
     p->tok_per_block = (int)round_up(std::max<long long>(stp, (work + slots - 1) / slots), stp);
     p->tok_per_block = (int)std::min<long long>(p->tok_per_block, round_up(n, stp));
     p->G = ceil_div(n, p->tok_per_block);
+    // the same number of blocks per head with their tokens balanced (512 tokens in blocks of
+    // 384 would leave one block a third of the other's work)
+    p->tok_per_block = (int)round_up(ceil_div(n, p->G), stp);
+    p->G = ceil_div(n, p->tok_per_block);
   }
 
   // workspace carve
