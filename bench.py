@@ -1,6 +1,7 @@
 """Benchmark of the Nystrom self-attention forward on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--config NAME|all]
+                    [--no-cpu-baseline] [--cpu-1thread]
 
 Workload: B=16, H=8, n=4096, d=64, m=64 landmarks (segments of 64 tokens), depthwise
 conv width 33, 6 pseudo-inverse iterations, bf16 I/O; seeded synthetic Q, K, V ~ N(0,1)
@@ -10,9 +11,12 @@ pseudo-inverse, landmark context, output softmax times Y, conv skip) with inputs
 resident in HBM; consecutive steps alternate between two independently seeded input
 sets so no step starts with its inputs cache-resident.
 
-Prints one JSON line: tokens/s (tokens = B*n per forward), the per-stage kernel times
-from HIP events recorded by the library on the forward's stream, the HBM roofline of the
-dominant kernel, and the fp64 CPU oracle timed on the host on a bounded sample.
+Untimed forwards for a fixed second come first (the GPU's clock ramp), then W warm-up
+steps, then exactly K timed steps. Prints one JSON line per workload: tokens/s (tokens =
+B*n per forward), the whole forward against its binding roofline term (HBM, MFMA or VALU,
+from algorithmic counts), per-kernel times from HIP events recorded by the library on the
+forward's stream (and from the committed rocprofv3 summary when it matches the sources),
+and the fp64 CPU oracle timed on the host on a bounded sample.
 """
 from __future__ import annotations
 
@@ -53,10 +57,71 @@ def stage_bytes(cfg, lengths=None) -> dict:
             "output": 2 * tok + full}      # read Q, V; write out
 
 
+# MI355X peaks (AMD's published figures): HBM3E, dense MFMA, vector fp32, and the
+# transcendental rate assumed for v_exp_f32 (a quarter of the fp32 lane rate: 16 lanes
+# per clock per CU at 2.4 GHz on 256 CUs).
+PEAK_HBM = 8.0e12          # B/s
+PEAK_MFMA_BF16 = 2.5e15    # flop/s
+PEAK_MFMA_F32 = 157.3e12   # flop/s
+PEAK_VALU_F32 = 157.3e12   # flop/s
+PEAK_EXP = 256 * 16 * 2.4e9
+
+
+def path_roofline(cfg, lengths=None) -> dict:
+    """The forward's roofline from algorithmic counts: t_roof = max(T_HBM, T_MFMA,
+    T_VALU) with
+      T_HBM  = (Q, K, V read once + out written once) / 8 TB/s;
+      T_MFMA = 8 n m d per head (the two scores and the two probability products) at the
+               dense bf16 rate (fp32 rate for fp32 I/O), plus the landmark work per head,
+               8 T m^3 (T iterations of four m x m products) + 4 m^2 d (A_S logits,
+               Y = Z W), counted as three bf16 products per product since the
+               pseudo-inverse runs on hi/lo bf16 pairs;
+      T_VALU = 2 W n d per head (the conv skip) at the fp32 vector rate + the (2 n m + m^2)
+               exponentials per head at the v_exp rate.
+    Only valid tokens count for a padded batch. Dense O(n^2) work is never counted."""
+    e = 2 if cfg.dtype == "bf16" else 4
+    tokens = cfg.n * cfg.B if lengths is None else sum(lengths)
+    th = cfg.H * tokens                      # token-heads processed
+    n_m_d = th * cfg.m * cfg.d
+    hbm = 3 * th * cfg.d * e + cfg.bh * cfg.n * cfg.d * e
+    land = cfg.bh * (8 * cfg.pinv_iters * cfg.m ** 3 + 4 * cfg.m ** 2 * cfg.d)
+    if cfg.dtype == "bf16":
+        t_mfma = 8 * n_m_d / PEAK_MFMA_BF16 + 3 * land / PEAK_MFMA_BF16
+    else:
+        t_mfma = 8 * n_m_d / PEAK_MFMA_F32 + land / PEAK_MFMA_F32
+    flops_mfma = 8 * n_m_d + land
+    t_valu = 2 * cfg.conv_width * th * cfg.d / PEAK_VALU_F32 + \
+        (2 * th * cfg.m + cfg.bh * cfg.m ** 2) / PEAK_EXP
+    terms = {"hbm": hbm / PEAK_HBM, "mfma": t_mfma, "valu": t_valu}
+    bound = max(terms, key=terms.get)
+    return {"bound": bound, "t_roof_s": terms[bound], "terms_s": terms,
+            "algorithmic_bytes": hbm, "mfma_flops": flops_mfma}
+
+
+def roofline_record(cfg, ms: float, lengths=None) -> dict:
+    """The forward as one unit against its binding roofline term: achieved = that term's
+    algorithmic work / measured time, frac = t_roof / t."""
+    pr = path_roofline(cfg, lengths)
+    t = ms * 1e-3
+    if pr["bound"] == "hbm":
+        achieved, peak, unit = pr["algorithmic_bytes"] / t / 1e9, PEAK_HBM / 1e9, "GB/s"
+    elif pr["bound"] == "mfma":
+        peak = (PEAK_MFMA_BF16 if cfg.dtype == "bf16" else PEAK_MFMA_F32) / 1e12
+        achieved, unit = pr["t_roof_s"] * peak / t, "TFLOP/s (bf16-equivalent)"
+    else:
+        achieved, peak, unit = pr["t_roof_s"] * PEAK_VALU_F32 / 1e12 / t, PEAK_VALU_F32 / 1e12, \
+            "TFLOP/s (fp32-equivalent)"
+    return {"kernel": "whole forward (all stages)", "bound": pr["bound"],
+            "achieved": achieved, "peak": peak, "unit": unit, "frac": pr["t_roof_s"] / t,
+            "t_roof_ms": pr["t_roof_s"] * 1e3,
+            "terms_ms": {k: v * 1e3 for k, v in pr["terms_s"].items()},
+            "algorithmic_bytes": pr["algorithmic_bytes"], "mfma_flops": pr["mfma_flops"]}
+
+
 def source_hash(stage: str) -> str:
     files = {"segment_means": ["segmeans.hip"], "pinv": ["context.hip"],
              "context": ["context.hip"], "output": ["output.hip"]}[stage]
-    files += ["nys_common.h", "nys_kernels.h"]
+    files += ["nys_common.h", "nys_kernels.h", "plan.hip"]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -77,31 +142,64 @@ def measured_traffic(stage: str, cfg_name: str):
     return rec.get("traffic_bytes_per_launch")
 
 
-def cpu_baseline(cfg, x, budget_s: float = 12.0, lengths=None) -> dict:
-    """Time the fp64 oracle (untuned) on the host: whole forwards of the workload,
-    repeated until about budget_s seconds have passed."""
-    import oracle
+def traced_kernel_us(cfg_name: str) -> dict:
+    """Kernel time of each stage per forward (us) from the committed rocprofv3
+    kernel-trace summary of this workload, when it was taken on the current sources."""
+    path = os.path.join(PROFILES, f"nystrom_forward_{cfg_name}_kernel_trace.txt")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as fh:
+        text = fh.read()
+    if "sources " + "/".join(source_hash(s) for s in STAGES) not in text:
+        return {}
+    out = {}
+    for line in text.splitlines():
+        parts = line.split()
+        if len(parts) == 3 and parts[0] == "stage_us":
+            out[parts[1]] = float(parts[2])
+    return out
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        cores = max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
+        return max([t.get("num_threads", 1) for t in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
-        cores = os.cpu_count() or 1
-    # one sampled block of heads per pass: every (b, h) of the workload
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(cfg, x, budget_s: float = 12.0, lengths=None, threads=None) -> dict:
+    """Time the fp64 oracle (untuned) on the host on a bounded sample of the workload:
+    its heads in order, one at a time, until about budget_s seconds have passed (whole
+    passes over all heads while the budget allows). tokens/s counts the tokens of the
+    sampled heads divided by H, i.e. B n tokens per full pass. threads: BLAS threads
+    (default: as configured)."""
+    import contextlib
+    import oracle
+    ctx = contextlib.nullcontext()
+    if threads is not None:
+        from threadpoolctl import threadpool_limits
+        ctx = threadpool_limits(limits=threads)
+    lens = [cfg.n] * cfg.B if lengths is None else list(lengths)
     heads = [(b, h) for b in range(cfg.B) for h in range(cfg.H)]
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        oracle.nystrom_forward(x.q, x.k, x.v, x.w, cfg.m, cfg.pinv_iters, heads=heads,
-                               lengths=lengths)
-        passes += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    tokens = cfg.tokens if lengths is None else sum(lengths)
-    return {"value": passes * tokens / dt, "unit": "tokens/s", "cores": int(cores),
+    with ctx:
+        cores = _blas_threads()
+        done, tok = 0, 0
+        t0 = time.perf_counter()
+        while True:
+            b, h = heads[done % len(heads)]
+            oracle.nystrom_forward(x.q, x.k, x.v, x.w, cfg.m, cfg.pinv_iters, heads=[(b, h)],
+                                   lengths=lengths)
+            done += 1
+            tok += lens[b]
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return {"value": tok / cfg.H / dt, "unit": "tokens/s", "cores": int(cores),
             "kind": "oracle",
-            "sample": f"{passes} full forward(s) of the workload ({cfg.bh} heads) in "
-                      f"{dt:.1f} s, numpy fp64, BLAS threads={cores}"}
+            "sample": f"{done} head forward(s) of the workload's {cfg.bh} heads "
+                      f"({done / cfg.bh:.2f} full passes) in {dt:.1f} s, numpy fp64, "
+                      f"BLAS threads={cores}"}
 
 
 # ------------------------------------------------------------------ profile summaries
@@ -112,21 +210,28 @@ def _short(name: str) -> str:
     return name.split("(")[0].replace("nys::", "")
 
 
+KERNEL_STAGE = (("segmeans", "segment_means"), ("pinv", "pinv"), ("context", "context"),
+                ("output", "output"))
+
+
 def summarize_trace(trace_dir: str, cfg_name: str, command: str,
                     title: str = "the Nystrom attention forward") -> str:
     """Per-kernel dispatch count and mean duration from a rocprofv3 --kernel-trace
     --stats database: over all dispatches (what --stats reports) and over the last 200
-    (the event-profiled forwards that bench.py's stage times come from)."""
+    (the event-profiled forwards that bench.py's stage times come from); then the kernel
+    time of each forward stage per forward over the last 200 forwards (one forward = one
+    output-kernel dispatch), tagged with the hash of the sources it was taken on."""
     import glob
     import sqlite3
     db = sorted(glob.glob(os.path.join(trace_dir, "**", "*.db"), recursive=True))[0]
     con = sqlite3.connect(db)
     rows = con.execute("select name, total_calls, average from top_kernels").fetchall()
+    seq = con.execute("select name, duration from kernels order by start").fetchall()
     per = {}
-    for name, dur in con.execute("select name, duration from kernels order by start"):
+    for name, dur in seq:
         per.setdefault(name, []).append(dur)
     lines = [f"Kernel trace of {title}, workload {cfg_name} "
-             f"({CONFIG_TEXT[cfg_name]}), one MI355X.", "",
+             f"({CONFIG_TEXT.get(cfg_name, cfg_name)}), one MI355X.", "",
              "Command (repository root; rocprofv3 wants the program right after --):",
              f"  {command}", "",
              f"{'kernel':64s} {'calls':>6s} {'avg_us':>9s} {'last200_us':>11s}"]
@@ -134,6 +239,17 @@ def summarize_trace(trace_dir: str, cfg_name: str, command: str,
         d = per.get(name, [])
         tail = sum(d[-200:]) / max(1, len(d[-200:])) / 1e3
         lines.append(f"{_short(name)[:64]:64s} {calls:6d} {avg:9.3f} {tail:11.3f}")
+    outs = [i for i, (name, _) in enumerate(seq) if _short(name).startswith("output_kernel")]
+    if len(outs) > 200 and title == "the Nystrom attention forward":
+        first = outs[-201] + 1
+        stage_us = {st: 0.0 for _, st in KERNEL_STAGE}
+        for name, dur in seq[first:outs[-1] + 1]:
+            for prefix, st in KERNEL_STAGE:
+                if _short(name).startswith(prefix):
+                    stage_us[st] += dur / 1e3 / 200
+        lines += ["", "Kernel time per forward over the last 200 forwards (us), sources "
+                  + "/".join(source_hash(s) for s in STAGES) + ":"]
+        lines += [f"stage_us {st} {stage_us[st]:.3f}" for _, st in KERNEL_STAGE]
     return "\n".join(lines) + "\n"
 
 
@@ -194,12 +310,18 @@ CONFIG_TEXT = {"long": "B=16 H=8 n=4096 d=64 m=64, conv width 33, 6 pseudo-inver
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    # a forward is ~0.13 ms: defaults give the GPU ~60 ms to reach steady clocks before
-    # ~0.25 s of timed work (short runs measure the clock ramp, not the kernels)
-    ap.add_argument("--steps", type=int, default=2000)
-    ap.add_argument("--warmup", type=int, default=500)
-    ap.add_argument("--config", default="long")
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--ramp-s", type=float, default=1.0,
+                    help="untimed forwards for this many seconds before the warm-up "
+                         "(reported as clock_ramp)")
+    ap.add_argument("--config", default="long",
+                    help="workload name, or 'all' for one JSON line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of oracle time for cpu_baseline")
+    ap.add_argument("--cpu-1thread", action="store_true",
+                    help="also time the oracle with one BLAS thread (cpu_baseline_1thread)")
     ap.add_argument("--ragged", action="store_true",
                     help="padded batch: seeded valid lengths in [n/2, n] per batch element "
                          "(tokens/s then counts valid tokens)")
@@ -251,17 +373,43 @@ def main():
         sys.exit(2)
 
     import torch
-    from efficient_transformer_attention_segment_amd import NystromAttention
     from efficient_transformer_attention_segment_amd import inputs as gen
 
-    cfg = gen.CONFIGS[args.config]
     torch.cuda.set_device(0)
-    if args.layer:
-        return layer_bench(args, cfg)
-    if args.backward:
-        return backward_bench(args, cfg)
-    if args.flash:
-        return flash_bench(args, cfg)
+    names = gen.CONFIG_ORDER if args.config == "all" else [args.config]
+    for name in names:
+        cfg = gen.CONFIGS[name]
+        if args.layer:
+            layer_bench(args, cfg)
+        elif args.backward:
+            backward_bench(args, cfg)
+        elif args.flash:
+            flash_bench(args, cfg)
+        else:
+            forward_bench(args, name)
+        torch.cuda.empty_cache()
+
+
+def clock_ramp(step, seconds: float) -> dict:
+    """Untimed forwards for a fixed wall time before the warm-up: the GPU leaves its idle
+    clocks only after some milliseconds of work, so a short timed run would otherwise
+    measure the ramp rather than the kernels."""
+    import torch
+    t0, done = time.perf_counter(), 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            step(done)
+            done += 1
+        torch.cuda.synchronize()
+    return {"seconds": round(time.perf_counter() - t0, 3), "forwards": done}
+
+
+def forward_bench(args, name: str):
+    """Steps of the Nystrom forward on one workload; one JSON line."""
+    import torch
+    from efficient_transformer_attention_segment_amd import NystromAttention
+    from efficient_transformer_attention_segment_amd import inputs as gen
+    cfg = gen.CONFIGS[name]
     sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
 
     def dev(a):
@@ -283,6 +431,7 @@ def main():
         q, k, v, w = dev_sets[i % 2]
         att.forward(q, k, v, w, out=outs[i % 2], lengths=lens_dev)
 
+    ramp = clock_ramp(step, args.ramp_s)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -295,7 +444,8 @@ def main():
     ms = start.elapsed_time(end) / args.steps
 
     # per-stage kernel times: HIP events the library records on the forward's stream
-    nprof = min(args.steps, 200)
+    # (each interval also holds the gap before its launch)
+    nprof = min(max(args.steps, 20), 200)
     att.profile_enable(nprof)
     for i in range(nprof):
         step(i)
@@ -313,11 +463,25 @@ def main():
     tokens = cfg.tokens if lengths is None else sum(lengths)
     value = tokens / (ms * 1e-3)
     sbytes = stage_bytes(cfg, lengths)
-    dom = max((s for s in STAGES if sbytes[s] > 0), key=lambda s: stage_ms[s])
-    achieved = sbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
-    path_bytes = (sbytes["context"] * 3 // 2 + cfg.bh * cfg.n * cfg.d
-                  * (2 if cfg.dtype == "bf16" else 4))  # Q, K, V valid rows once + out
-    path_roof_ms = path_bytes / (HBM_PEAK_GBS * 1e9) * 1e3
+    roof = roofline_record(cfg, ms, lengths)
+    traffic = None
+    if lengths is None:
+        parts = [measured_traffic(st, name) for st in ("segment_means", "context", "output")]
+        traffic = sum(parts) if all(p is not None for p in parts) else None
+    roof["traffic"] = traffic
+    traced = {} if lengths else traced_kernel_us(name)
+    kernels = {}
+    for st in STAGES:
+        rec_k = {"event_ms": stage_ms[st], "algorithmic_bytes": sbytes[st]}
+        if sbytes[st] > 0:
+            rec_k["event_hbm_frac"] = sbytes[st] / (stage_ms[st] * 1e-3) / PEAK_HBM
+        if st in traced:
+            rec_k["rocprof_us"] = traced[st]
+            if sbytes[st] > 0 and traced[st] > 0:
+                rec_k["rocprof_hbm_frac"] = sbytes[st] / (traced[st] * 1e-6) / PEAK_HBM
+        kernels[STAGE_KERNEL[st]] = rec_k
+    dom = max((st for st in STAGES if sbytes[st] > 0), key=lambda st: stage_ms[st])
+    dom_achieved = sbytes[dom] / (stage_ms[dom] * 1e-3) / 1e9
     rec = {
         "metric": METRIC,
         "value": value,
@@ -334,20 +498,26 @@ def main():
         "config": {"workload": f"nystrom_attention_forward_B{cfg.B}_H{cfg.H}_n{cfg.n}_"
                                f"d{cfg.d}_m{cfg.m}_conv{cfg.conv_width}_iters{cfg.pinv_iters}"
                                + ("_ragged" if lengths else ""),
+                   "name": name,
                    "B": cfg.B, "H": cfg.H, "n": cfg.n, "d": cfg.d, "m": cfg.m,
                    "conv_width": cfg.conv_width, "pinv_iters": cfg.pinv_iters,
                    "inputs": "two alternating seeded N(0,1) sets",
                    **({"lengths": lengths} if lengths else {})},
-        "roofline": {"kernel": STAGE_KERNEL[dom], "bound": "hbm", "achieved": achieved,
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": None if lengths else measured_traffic(dom, args.config)},
-        "stages_ms": stage_ms,
-        "stage_algorithmic_bytes": sbytes,
-        "path_roofline": {"bound": "hbm", "compulsory_bytes": path_bytes,
-                          "roofline_ms": path_roof_ms, "frac": path_roof_ms / ms},
+        "roofline": roof,
+        "dominant_kernel": {"kernel": STAGE_KERNEL[dom], "bound": "hbm",
+                            "achieved": dom_achieved, "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                            "frac": dom_achieved * 1e9 / PEAK_HBM,
+                            "timing": "HIP event interval on the forward's stream",
+                            "traffic": None if lengths else measured_traffic(dom, name)},
+        "kernels": kernels,
+        "clock_ramp": ramp,
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(cfg, sets[0], lengths=lengths)
+        rec["cpu_baseline"] = cpu_baseline(cfg, sets[0], budget_s=args.cpu_budget,
+                                           lengths=lengths)
+        if args.cpu_1thread:
+            rec["cpu_baseline_1thread"] = cpu_baseline(cfg, sets[0], budget_s=5.0,
+                                                       lengths=lengths, threads=1)
     att.close()
     print(json.dumps(rec), flush=True)
 

@@ -259,18 +259,7 @@ class NystromAttention:
         else:
             self._check("out", out, self.shape, dt)
         stream = torch.cuda.current_stream(q.device).cuda_stream
-        lens = None
-        if lengths is not None:
-            if isinstance(lengths, torch.Tensor) and lengths.device.type == "cuda":
-                self._check("lengths", lengths, (self.shape[0],), torch.int32)
-                lens = lengths
-            else:
-                vals = [int(x) for x in lengths]
-                if len(vals) != self.shape[0] or any(not (self.m <= x <= self.shape[2])
-                                                    for x in vals):
-                    raise ValueError(f"lengths must hold {self.shape[0]} values in "
-                                     f"[{self.m}, {self.shape[2]}]")
-                lens = torch.tensor(vals, dtype=torch.int32).to(q.device)
+        lens = self._lengths(lengths, q.device)
         t = None
         if taps is not None:
             t = Taps()
@@ -291,6 +280,9 @@ class NystromAttention:
     __call__ = forward
 
     def _lengths(self, lengths, device):
+        """``lengths`` as an int32 device tensor [B]: a device tensor is passed through
+        (its values are the caller's responsibility), a host sequence or CPU tensor is
+        checked to lie in [m, n] and copied; None stays None (all n)."""
         import torch
         if lengths is None:
             return None

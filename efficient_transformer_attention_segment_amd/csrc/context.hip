@@ -627,6 +627,47 @@ __global__ __launch_bounds__(1024) void pinv_global_kernel(CtxArgs a) {
   pinv_body<4>(a, bh, a.planes + (size_t)bh * kPlanes * a.mp * a.mp, red, red_part, red_col);
 }
 
+// Head, chunk and token range [c0, c1) of context block blk (without the pseudo-inverse
+// blocks), the range cut at the head's valid length (an empty chunk leaves M = -inf,
+// L = 0). Even split: blocks are mapped to (head, chunk) by xcd_map and chunk c is
+// [c chunk, (c + 1) chunk). Uneven split (uneven_ncu > 0, chosen on the host when the
+// fused pseudo-inverse blocks share CUs with context blocks): blocks are chunk-major
+// (block c BH + bh of the context range) and land round-robin on uneven_ncu CUs after the
+// npinv pseudo-inverse blocks; a context block on a CU that also holds a pseudo-inverse
+// block runs at about 0.7 of the speed of the others, so each head's tokens are split in
+// proportion to those weights over its chunks, in whole steps of 32 TG tokens.
+__device__ __forceinline__ void context_block(const CtxArgs& a, int blk, int& bh, int& c,
+                                              int& c0, int& c1) {
+  if (a.uneven_ncu == 0) {
+    xcd_map(blk, a.BH, a.C, bh, c);
+    c0 = c * a.chunk;
+    c1 = c0 + a.chunk;
+  } else {
+    bh = blk % a.BH;
+    c = blk / a.BH;
+    const int ncu = a.uneven_ncu, step = 32 * a.TG, nsteps = (a.n + step - 1) / step;
+    auto weight = [&](int cc) {
+      const long long b = (long long)a.npinv + (long long)cc * a.BH + bh;
+      return (b >= ncu && (int)(b % ncu) < a.npinv) ? 0.7 : 1.0;
+    };
+    double total = 0.0;
+    for (int cc = 0; cc < a.C; ++cc) total += weight(cc);
+    double cum = 0.0;
+    int start = 0;
+    c0 = c1 = 0;
+    for (int cc = 0; cc <= c; ++cc) {
+      cum += weight(cc);
+      const int end = cc == a.C - 1
+                          ? a.n
+                          : min(a.n, step * (int)llround((double)nsteps * cum / total));
+      c0 = min(start, end);
+      c1 = end;
+      start = max(start, end);
+    }
+  }
+  c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), c1);
+}
+
 // Merge the TG token groups of each landmark group (fixed order) and write the block's
 // partial state: W^T [feature][landmark] unnormalised, running max (log2 units) and sum.
 // mb: LDS scratch of LG * (TG - 1) slots; the caller synchronises before reusing LDS.
@@ -690,17 +731,8 @@ __device__ __forceinline__ void flash_reg_body(const CtxArgs& a, int blk, char* 
   const int r32 = lane & 31, h = lane >> 5;
   const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
   const int mp = a.mp;
-  int bh, c;
-  if (a.chunk_tab != nullptr) {  // chunk-major blocks (the chunk table's order)
-    bh = blk % a.BH;
-    c = blk / a.BH;
-  } else {
-    xcd_map(blk, a.BH, a.C, bh, c);
-  }
-  // the chunk, cut at the head's valid length (an empty chunk leaves M = -inf, L = 0)
-  const int* ct = a.chunk_tab != nullptr ? a.chunk_tab + 2 * ((size_t)bh * a.C + c) : nullptr;
-  const int c0 = ct != nullptr ? ct[0] : c * a.chunk;
-  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), ct != nullptr ? ct[1] : c0 + a.chunk);
+  int bh, c, c0, c1;
+  context_block(a, blk, bh, c, c0, c1);
   const Tin* K = static_cast<const Tin*>(a.k) + (size_t)bh * a.n * D;
   const Tin* V = static_cast<const Tin*>(a.v) + (size_t)bh * a.n * D;
 
@@ -862,17 +894,8 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
   const int r32 = lane & 31, h = lane >> 5;
   const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
   const int mp = a.mp;
-  int bh, c;
-  if (a.chunk_tab != nullptr) {  // chunk-major blocks (the chunk table's order)
-    bh = blk % a.BH;
-    c = blk / a.BH;
-  } else {
-    xcd_map(blk, a.BH, a.C, bh, c);
-  }
-  // the chunk, cut at the head's valid length (an empty chunk leaves M = -inf, L = 0)
-  const int* ct = a.chunk_tab != nullptr ? a.chunk_tab + 2 * ((size_t)bh * a.C + c) : nullptr;
-  const int c0 = ct != nullptr ? ct[0] : c * a.chunk;
-  const int c1 = min(valid_length(a.lengths, bh, a.H, a.n, a.m), ct != nullptr ? ct[1] : c0 + a.chunk);
+  int bh, c, c0, c1;
+  context_block(a, blk, bh, c, c0, c1);
   const uint16_t* K = static_cast<const uint16_t*>(a.k) + (size_t)bh * a.n * D;
   const uint16_t* V = static_cast<const uint16_t*>(a.v) + (size_t)bh * a.n * D;
 

@@ -34,8 +34,8 @@ struct CtxArgs {
   uint16_t* z_hl;         // [BH][2][mp][mp]  final Z, row-major hi/lo
   float* part_w;          // [BH][C][d][mp]   per-chunk unnormalised (Bbar V)^T
   float* part_ml;         // [BH][C][2][mp]   per-chunk running max (log2 units), sum
-  const int* chunk_tab;   // [BH][C][2] token range [c0, c1) of each context chunk, or
-                          // nullptr: chunk c is [c * chunk, (c + 1) * chunk)
+  int uneven_ncu;         // 0: chunk c is [c * chunk, (c + 1) * chunk); else the CU count
+                          // of the uneven split (see chunk_range in context.hip)
   int BH, H, n, d, m, mp, iters, chunk, C, LG, TG;
   int npinv;              // pseudo-inverse blocks at the front of the context grid (0 or BH)
   int ring_ni;            // bf16 context: 1 KiB LDS-DMA loads per wave per K or V tile

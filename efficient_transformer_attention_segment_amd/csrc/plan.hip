@@ -5,8 +5,9 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
-#include <mutex>
 #include <cmath>
+#include <cstdio>
+#include <mutex>
 #include <cstdint>
 #include <cstdlib>
 #include <new>
@@ -27,59 +28,56 @@ nys_status fail(nys_status st, const std::string& msg) {
 }
 
 constexpr int kStages = 4;  // segment means, pseudo-inverse, landmark context, output
+const char* const kStageName[kStages] = {"segment means", "pseudo-inverse", "landmark context",
+                                         "output"};
+
+// Debug switches, read from the environment at each call (debugging only; none of them
+// changes a result):
+//   NYS_FAULT=alloc   nys_attn_create fails as if the workspace allocation had failed
+//   NYS_FAULT=launch  forward and backward fail as if a kernel launch had failed, before
+//                     anything is enqueued
+//   NYS_DEBUG_SYNC=1  forward and backward wait for the stream after every launch and
+//                     name the stage whose kernel failed (slow; localises device faults)
+//   NYS_LOG=1         nys_attn_create prints the plan (tiles, grids, workspace) to stderr
+bool env_is(const char* name, const char* value) {
+  const char* e = std::getenv(name);
+  return e != nullptr && std::strcmp(e, value) == 0;
+}
+bool env_on(const char* name) {
+  const char* e = std::getenv(name);
+  return e != nullptr && e[0] != '\0' && std::strcmp(e, "0") != 0;
+}
 
 size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 long long round_up(long long a, long long b) { return ((a + b - 1) / b) * b; }
 
-// Token ranges of the context chunks when the fused pseudo-inverse blocks share CUs with
-// context blocks. Workgroups of one launch are placed round-robin over the CUs (block b
-// on CU b mod ncu while they all fit at once: measured with per-block clocks), so a
-// context block b >= ncu with b mod ncu < npinv runs next to a pseudo-inverse block and
-// progresses at about 0.7 of the speed of the others. With the table the context blocks
-// are taken chunk-major (block npinv + c * BH + bh holds chunk c of head bh; with BH a
-// multiple of 8 a head's blocks still share one XCD), so every head has chunks on both
-// kinds of CU, and each head's tokens are split in proportion to those speeds, in whole
-// steps. Returns false (uniform chunks, head-major blocks) when the launch does not fit
-// in one round of resident blocks or no context block shares a CU.
-bool uneven_chunks(int BH, int C, int n, int step, int npinv, int ncu, int slots_per_cu,
-                   std::vector<int>& tab) {
+// Whether the context chunks are split unevenly (the split itself is computed per block
+// on the device, context_block in context.hip). Workgroups of one launch are placed
+// round-robin over the CUs (block b on CU b mod ncu while they all fit at once: measured
+// with per-block clocks), so a context block b >= ncu with b mod ncu < npinv runs next to
+// a pseudo-inverse block and progresses at about 0.7 of the speed of the others. With the
+// uneven split the context blocks are taken chunk-major (block npinv + c BH + bh holds
+// chunk c of head bh; with BH a multiple of 8 a head's blocks still share one XCD), so
+// every head has chunks on both kinds of CU, and each head's tokens are split in
+// proportion to those speeds. False (uniform chunks, head-major blocks) when the launch
+// does not fit in one round of resident blocks or no context block shares a CU.
+bool uneven_chunks(int BH, int C, int npinv, int ncu, int slots_per_cu) {
   const long long blocks = (long long)npinv + (long long)BH * C;
   if (npinv <= 0 || npinv >= ncu || C < 2 || (BH & 7) != 0 ||
       blocks > (long long)slots_per_cu * ncu || blocks <= ncu)
     return false;
-  constexpr double kShared = 0.7;
-  std::vector<double> w((size_t)BH * C, 1.0);
-  bool any = false;
-  for (int blk = 0; blk < BH * C; ++blk) {
-    const int bh = blk % BH, c = blk / BH;
-    const long long b = npinv + blk;
-    if (b >= ncu && (int)(b % ncu) < npinv) {
-      w[(size_t)bh * C + c] = kShared;
-      any = true;
-    }
-  }
-  if (!any) return false;
-  tab.assign((size_t)BH * C * 2, 0);
-  const int nsteps = ceil_div(n, step);
-  for (int bh = 0; bh < BH; ++bh) {
-    double total = 0.0;
-    for (int c = 0; c < C; ++c) total += w[(size_t)bh * C + c];
-    double cum = 0.0;
-    int start = 0;
-    for (int c = 0; c < C; ++c) {
-      cum += w[(size_t)bh * C + c];
-      const int end = c == C - 1 ? n
-                                 : std::min(n, step * (int)std::lround(nsteps * cum / total));
-      tab[2 * ((size_t)bh * C + c)] = std::min(start, end);
-      tab[2 * ((size_t)bh * C + c) + 1] = end;
-      start = std::max(start, end);
-    }
-  }
-  return true;
+  for (long long b = npinv; b < blocks; ++b)
+    if (b >= ncu && (int)(b % ncu) < npinv) return true;
+  return false;
 }
 
 }  // namespace
+
+// Byte offsets of the workspace's sub-buffers (256-byte aligned).
+struct WsLayout {
+  size_t qt, kt, qhl, khl, as, z, pl, own, apart, zhl, pw, pml, w, y;
+};
 
 struct nys_attn_plan {
   int B, H, n, d, m, mp, W, half, iters, ks;
@@ -89,6 +87,8 @@ struct nys_attn_plan {
   int device;
   char* ws;
   size_t ws_bytes;
+  WsLayout lay;
+  bool debug_taps;  // the workspace holds the fp32 W and Y tap buffers
   nys::SegArgs seg;
   nys::CtxArgs ctx;
   nys::OutArgs out;
@@ -116,28 +116,28 @@ static nys_status validate_shape(int B, int H, int n, int d, int m, int W, int i
   return NYS_OK;
 }
 
-extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n, int d, int m,
-                                      int conv_width, int pinv_iters, nys_dtype dtype) {
-  if (plan == nullptr) return fail(NYS_E_ARG, "plan out-pointer is NULL");
-  *plan = nullptr;
-  nys_status st = validate_shape(B, H, n, d, m, conv_width, pinv_iters, dtype);
-  if (st != NYS_OK) return st;
-
+// Current device, checked to be a gfx950 part; its properties in *prop.
+static nys_status current_device(int* dev, hipDeviceProp_t* prop) {
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
     (void)hipGetLastError();
     return fail(NYS_E_DEVICE, "no HIP device available");
   }
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return fail(NYS_E_DEVICE, "hipGetDevice failed");
-  hipDeviceProp_t prop;
-  if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+  if (hipGetDevice(dev) != hipSuccess) return fail(NYS_E_DEVICE, "hipGetDevice failed");
+  if (hipGetDeviceProperties(prop, *dev) != hipSuccess)
     return fail(NYS_E_DEVICE, "hipGetDeviceProperties failed");
-  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
-    return fail(NYS_E_DEVICE, std::string("device is ") + prop.gcnArchName + ", need gfx950");
+  if (std::strncmp(prop->gcnArchName, "gfx950", 6) != 0)
+    return fail(NYS_E_DEVICE, std::string("device is ") + prop->gcnArchName + ", need gfx950");
+  return NYS_OK;
+}
 
-  nys_attn_plan* p = new (std::nothrow) nys_attn_plan();
-  if (p == nullptr) return fail(NYS_E_NOMEM, "host allocation failed");
+// Everything of a plan but its workspace pointers: shapes, tiling, launch geometry (from
+// the device's CU count and the runtime's occupancy figures), kernel LDS limits and the
+// workspace layout (p->lay, p->ws_bytes). debug_taps: reserve the fp32 W and Y buffers
+// that nys_attn_forward_debug fills. Allocates nothing.
+static nys_status plan_init(nys_attn_plan* p, int B, int H, int n, int d, int m,
+                            int conv_width, int pinv_iters, nys_dtype dtype, int dev,
+                            const hipDeviceProp_t& prop, bool debug_taps) {
   p->B = B; p->H = H; p->n = n; p->d = d; p->m = m; p->W = conv_width;
   p->half = (conv_width - 1) / 2; p->iters = pinv_iters; p->dtype = dtype;
   p->device = dev;
@@ -159,13 +159,9 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   nys::context_ring_geometry(d, c);
   const size_t ctx_lds = nys::context_lds_bytes(bf16, d, c);
   const size_t max_lds = (size_t)prop.sharedMemPerBlock;
-  if (ctx_lds > max_lds) {
-    delete p;
-    return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
-  }
+  if (ctx_lds > max_lds) return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
   if (nys::configure_context(bf16, d, p->mp, ctx_lds) != hipSuccess) {
     (void)hipGetLastError();
-    delete p;
     return fail(NYS_E_LAUNCH, "could not set kernel LDS limits");
   }
   // Context blocks: about one resident round of them next to the fused pseudo-inverse
@@ -185,13 +181,9 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
   p->C = ceil_div(n, p->chunk);
   c.chunk = p->chunk; c.C = p->C;
   const size_t out_lds = nys::output_lds_bytes(bf16, d, p->mp, p->ks, p->C);
-  if (out_lds > max_lds) {
-    delete p;
-    return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
-  }
+  if (out_lds > max_lds) return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
   if (nys::configure_output(bf16, d, p->ks, out_lds) != hipSuccess) {
     (void)hipGetLastError();
-    delete p;
     return fail(NYS_E_LAUNCH, "could not set kernel LDS limits");
   }
   // Output blocks: one resident round of them (the prologue of every block merges the
@@ -210,8 +202,13 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
     p->tok_per_block = (int)round_up(ceil_div(n, p->G), stp);
     p->G = ceil_div(n, p->tok_per_block);
   }
+  const bool uneven = p->fused && uneven_chunks(p->BH, p->C, p->BH, prop.multiProcessorCount,
+                                                ctx_per_cu);
+  c.uneven_ncu = uneven ? prop.multiProcessorCount : 0;
+  c.scale = 1.0f / std::sqrt((float)d);
+  c.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)d));
 
-  // workspace carve
+  // workspace layout
   const size_t BHs = (size_t)p->BH, mp = (size_t)p->mp, dd = (size_t)d;
   const size_t P = mp * mp;
   size_t off = 0;
@@ -220,69 +217,100 @@ extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n,
     off = align256(off + bytes);
     return o;
   };
-  const size_t o_qt = take(BHs * mp * dd * 4), o_kt = take(BHs * mp * dd * 4);
-  const size_t o_qhl = take(BHs * 2 * mp * dd * 2), o_khl = take(BHs * 2 * mp * dd * 2);
-  const size_t o_as = take(BHs * P * 4), o_z = take(BHs * P * 4);
-  const size_t o_pl = take(p->mp > 64 ? BHs * nys::kPlanes * P * 2 : 0);
-  const size_t o_own = take(p->mp > 64 ? BHs * 2 * P * 4 : 0);
-  const size_t o_apart = take(p->mp > 64 ? BHs * (mp / 32) * (mp + 1) * 4 : 0);
-  const size_t o_zhl = take(BHs * 2 * P * 2);
-  const size_t o_pw = take(BHs * p->C * mp * dd * 4), o_pml = take(BHs * p->C * 2 * mp * 4);
-  const size_t o_w = take(BHs * mp * dd * 4), o_y = take(BHs * mp * dd * 4);
-  std::vector<int> chunk_tab;
-  const bool uneven = p->fused &&
-                      uneven_chunks(p->BH, p->C, n, step, p->BH, prop.multiProcessorCount,
-                                    ctx_per_cu,
-                                    chunk_tab);
-  const size_t o_ct = take(uneven ? chunk_tab.size() * sizeof(int) : 0);
+  WsLayout& L = p->lay;
+  L.qt = take(BHs * mp * dd * 4); L.kt = take(BHs * mp * dd * 4);
+  L.qhl = take(BHs * 2 * mp * dd * 2); L.khl = take(BHs * 2 * mp * dd * 2);
+  L.as = take(BHs * P * 4); L.z = take(BHs * P * 4);
+  L.pl = take(p->mp > 64 ? BHs * nys::kPlanes * P * 2 : 0);
+  L.own = take(p->mp > 64 ? BHs * 2 * P * 4 : 0);
+  L.apart = take(p->mp > 64 ? BHs * (mp / 32) * (mp + 1) * 4 : 0);
+  L.zhl = take(BHs * 2 * P * 2);
+  L.pw = take(BHs * p->C * mp * dd * 4); L.pml = take(BHs * p->C * 2 * mp * 4);
+  L.w = take(debug_taps ? BHs * mp * dd * 4 : 0);
+  L.y = take(debug_taps ? BHs * mp * dd * 4 : 0);
   p->ws_bytes = off;
   p->ws = nullptr;
-
-  const char* fault = std::getenv("NYS_FAULT");
-  if (fault != nullptr && std::strcmp(fault, "alloc") == 0) {
-    delete p;
-    return fail(NYS_E_NOMEM, "workspace allocation failed (NYS_FAULT=alloc)");
-  }
-  if (p->ws_bytes > 0) {
-    if (hipMalloc(reinterpret_cast<void**>(&p->ws), p->ws_bytes) != hipSuccess) {
-      (void)hipGetLastError();
-      delete p;
-      return fail(NYS_E_NOMEM, "workspace allocation failed");
-    }
-    if (hipMemset(p->ws, 0, p->ws_bytes) != hipSuccess ||
-        (uneven && hipMemcpy(p->ws + o_ct, chunk_tab.data(), chunk_tab.size() * sizeof(int),
-                             hipMemcpyHostToDevice) != hipSuccess)) {
-      (void)hipFree(p->ws);
-      delete p;
-      return fail(NYS_E_LAUNCH, "workspace set-up failed");
-    }
-  }
-  char* ws = p->ws;
-  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
-  auto U = [&](size_t o) { return reinterpret_cast<uint16_t*>(ws + o); };
-
-  p->seg = nys::SegArgs{nullptr, p->BH, H, n, m, p->mp, F(o_qt), F(o_kt), U(o_qhl), U(o_khl)};
-
-  c.qt = F(o_qt); c.qt_hl = U(o_qhl); c.kt_hl = U(o_khl);
-  c.a_s = F(o_as); c.z = F(o_z); c.planes = U(o_pl); c.own = F(o_own); c.alpha_part = F(o_apart); c.z_hl = U(o_zhl);
-  c.part_w = F(o_pw); c.part_ml = F(o_pml);
-  c.chunk_tab = uneven ? reinterpret_cast<const int*>(ws + o_ct) : nullptr;
-  c.scale = 1.0f / std::sqrt((float)d);
-  c.scale_log2e = (float)(1.4426950408889634 / std::sqrt((double)d));
+  p->debug_taps = debug_taps;
 
   nys::OutArgs& o = p->out;
   std::memset(&o, 0, sizeof(o));
-  o.kt = F(o_kt); o.kt_hl = U(o_khl); o.z_hl = U(o_zhl); o.part_w = F(o_pw); o.part_ml = F(o_pml);
-  o.w_tap = F(o_w); o.y_tap = F(o_y);  // enabled per call (debug forwards only)
   o.BH = p->BH; o.H = H; o.n = n; o.m = m; o.mp = p->mp; o.W = conv_width; o.half = p->half;
   o.tok_per_block = p->tok_per_block; o.G = p->G; o.C = p->C;
   o.scale_log2e = c.scale_log2e;
 
+  if (env_on("NYS_LOG"))
+    std::fprintf(stderr,
+                 "[nys_attn] plan B=%d H=%d n=%d d=%d m=%d (mp %d) W=%d iters=%d %s: "
+                 "pseudo-inverse %s; context %d chunks of %d tokens (%s), %d blocks of %d "
+                 "threads, %zu B LDS; output %d blocks per head of %d tokens, %zu B LDS; "
+                 "workspace %zu B\n",
+                 B, H, n, d, m, p->mp, conv_width, pinv_iters, bf16 ? "bf16" : "fp32",
+                 p->fused ? "in the context launch" : "separate launches", p->C, p->chunk,
+                 uneven ? "uneven split" : "even split", c.npinv + p->BH * p->C,
+                 64 * p->LG * p->TG, ctx_lds, p->G, p->tok_per_block, out_lds, p->ws_bytes);
   p->prof_max = 0;
   p->prof_count = 0;
   p->bws = nullptr;
   p->bws_bytes = 0;
   std::memset(&p->bwd, 0, sizeof(p->bwd));
+  return NYS_OK;
+}
+
+// Point the plan's kernel arguments at a workspace laid out by plan_init.
+static void plan_bind(nys_attn_plan* p, char* ws) {
+  p->ws = ws;
+  const WsLayout& L = p->lay;
+  auto F = [&](size_t o) { return reinterpret_cast<float*>(ws + o); };
+  auto U = [&](size_t o) { return reinterpret_cast<uint16_t*>(ws + o); };
+  p->seg = nys::SegArgs{nullptr, p->BH, p->H, p->n, p->m, p->mp, F(L.qt), F(L.kt), U(L.qhl),
+                        U(L.khl)};
+  nys::CtxArgs& c = p->ctx;
+  c.qt = F(L.qt); c.qt_hl = U(L.qhl); c.kt_hl = U(L.khl);
+  c.a_s = F(L.as); c.z = F(L.z); c.planes = U(L.pl); c.own = F(L.own);
+  c.alpha_part = F(L.apart); c.z_hl = U(L.zhl);
+  c.part_w = F(L.pw); c.part_ml = F(L.pml);
+  nys::OutArgs& o = p->out;
+  o.kt = F(L.kt); o.kt_hl = U(L.khl); o.z_hl = U(L.zhl); o.part_w = F(L.pw); o.part_ml = F(L.pml);
+  o.w_tap = p->debug_taps ? F(L.w) : nullptr;  // enabled per call (debug forwards only)
+  o.y_tap = p->debug_taps ? F(L.y) : nullptr;
+}
+
+extern "C" nys_status nys_attn_create(nys_attn_plan** plan, int B, int H, int n, int d, int m,
+                                      int conv_width, int pinv_iters, nys_dtype dtype) {
+  if (plan == nullptr) return fail(NYS_E_ARG, "plan out-pointer is NULL");
+  *plan = nullptr;
+  nys_status st = validate_shape(B, H, n, d, m, conv_width, pinv_iters, dtype);
+  if (st != NYS_OK) return st;
+  int dev = 0;
+  hipDeviceProp_t prop;
+  if ((st = current_device(&dev, &prop)) != NYS_OK) return st;
+
+  nys_attn_plan* p = new (std::nothrow) nys_attn_plan();
+  if (p == nullptr) return fail(NYS_E_NOMEM, "host allocation failed");
+  if ((st = plan_init(p, B, H, n, d, m, conv_width, pinv_iters, dtype, dev, prop, true)) !=
+      NYS_OK) {
+    delete p;
+    return st;
+  }
+  if (env_is("NYS_FAULT", "alloc")) {
+    delete p;
+    return fail(NYS_E_NOMEM, "workspace allocation failed (NYS_FAULT=alloc)");
+  }
+  char* ws = nullptr;
+  if (p->ws_bytes > 0) {
+    if (hipMalloc(reinterpret_cast<void**>(&ws), p->ws_bytes) != hipSuccess) {
+      (void)hipGetLastError();
+      delete p;
+      return fail(NYS_E_NOMEM, "workspace allocation failed");
+    }
+    // zero once: landmark rows m..mp-1 stay zero for the plan's lifetime
+    if (hipMemset(ws, 0, p->ws_bytes) != hipSuccess) {
+      (void)hipFree(ws);
+      delete p;
+      return fail(NYS_E_LAUNCH, "workspace set-up failed");
+    }
+  }
+  plan_bind(p, ws);
   *plan = p;
   g_err.clear();
   return NYS_OK;
@@ -309,8 +337,11 @@ static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, c
   if (taps && taps->attn && misaligned(taps->attn))
     return fail(NYS_E_ARG, "taps->attn must be 16-byte aligned");
 
+  if (env_is("NYS_FAULT", "launch"))
+    return fail(NYS_E_LAUNCH, "kernel launch failed (NYS_FAULT=launch)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   const bool bf16 = p->dtype == NYS_BF16;
+  const bool dsync = env_on("NYS_DEBUG_SYNC");
   const bool prof = p->prof_count < p->prof_max;
   hipEvent_t* ev = prof ? &p->prof_ev[(kStages + 1) * p->prof_count] : nullptr;
   auto chk = [&](hipError_t e, const char* what) -> bool {
@@ -320,7 +351,18 @@ static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, c
     }
     return true;
   };
-  auto mark = [&](int i) { return !prof || chk(hipEventRecord(ev[i], s), "event record"); };
+  // stage i's launch(es) are enqueued: record its end marker, and with NYS_DEBUG_SYNC
+  // wait for them and name the stage if its kernel failed
+  auto mark = [&](int i) {
+    if (dsync && i > 0) {
+      const hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) {
+        g_err = std::string(kStageName[i - 1]) + " kernel failed: " + hipGetErrorString(e);
+        return false;
+      }
+    }
+    return !prof || chk(hipEventRecord(ev[i], s), "event record");
+  };
   nys::SegArgs sg = p->seg;
   sg.lengths = lengths;
   nys::CtxArgs c = p->ctx;
@@ -533,6 +575,8 @@ extern "C" nys_status nys_attn_backward(nys_attn_plan* p, const void* q, const v
   const size_t wbytes = (size_t)p->H * p->W * 4;
   if (ranges_overlap(dconv_w, wbytes, conv_w, wbytes))
     return fail(NYS_E_ARG, "dconv_w must not overlap conv_w");
+  if (env_is("NYS_FAULT", "launch"))
+    return fail(NYS_E_LAUNCH, "kernel launch failed (NYS_FAULT=launch)");
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (p->BH == 0) {
     if (hipMemsetAsync(dconv_w, 0, wbytes, s) != hipSuccess)
@@ -558,12 +602,22 @@ extern "C" nys_status nys_attn_backward(nys_attn_plan* p, const void* q, const v
   b.dk = static_cast<uint16_t*>(dk);
   b.dv = static_cast<uint16_t*>(dv);
   b.dconv_w = dconv_w;
-  hipError_t e = nys::launch_segmeans(true, p->d, q, k, sg, s);
-  if (e == hipSuccess && !p->fused) e = nys::launch_pinv(p->d, c, s);
-  if (e == hipSuccess) e = nys::launch_context(true, p->d, c, s);
-  if (e == hipSuccess) e = nys::launch_backward(b, s);
-  if (e != hipSuccess) return fail(NYS_E_LAUNCH, std::string("backward launch: ") + hipGetErrorString(e));
-  return NYS_OK;
+  const bool dsync = env_on("NYS_DEBUG_SYNC");
+  const char* what = "";
+  hipError_t e = hipSuccess;
+  // one stage's launch result (and, with NYS_DEBUG_SYNC, its completion)
+  auto stage = [&](const char* name, hipError_t le) {
+    what = name;
+    e = le;
+    if (e == hipSuccess && dsync) e = hipStreamSynchronize(s);
+    return e == hipSuccess;
+  };
+  if (stage("segment means", nys::launch_segmeans(true, p->d, q, k, sg, s)) &&
+      (p->fused || stage("pseudo-inverse", nys::launch_pinv(p->d, c, s))) &&
+      stage("landmark context", nys::launch_context(true, p->d, c, s)) &&
+      stage("gradient kernels", nys::launch_backward(b, s)))
+    return NYS_OK;
+  return fail(NYS_E_LAUNCH, std::string("backward: ") + what + ": " + hipGetErrorString(e));
 }
 
 // ------------------------------------------------------------------ projections

@@ -44,7 +44,7 @@ typedef enum { NYS_F32 = 0, NYS_BF16 = 1 } nys_dtype;
 typedef enum {
   NYS_OK = 0,
   NYS_E_ARG = 1,         /* invalid argument (null pointer, bad shape, misalignment) */
-  NYS_E_UNSUPPORTED = 2, /* valid but not built: n % m != 0, d not in {32,64,128}, ... */
+  NYS_E_UNSUPPORTED = 2, /* valid but not built: d not in {32,64,128}, m > 256, ...      */
   NYS_E_NOMEM = 3,       /* device workspace allocation failed                         */
   NYS_E_DEVICE = 4,      /* no HIP device, or the current device is not gfx950          */
   NYS_E_LAUNCH = 5       /* a kernel launch or a HIP runtime call failed                */
@@ -68,6 +68,8 @@ typedef struct {
  *   d in {32, 64, 128} (other positive d: NYS_E_UNSUPPORTED);
  *   conv_width odd, 1 <= conv_width <= 65;
  *   0 <= pinv_iters <= 100;  dtype NYS_F32 or NYS_BF16; n*d < 2^31.
+ * Shapes whose kernels need more LDS than the device offers (fp32 with d = 128 and
+ * m > 96) are NYS_E_UNSUPPORTED.
  * On success *plan is set; on failure *plan = NULL (when plan itself is non-NULL).
  * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED, NYS_E_DEVICE (no device / not gfx950, checked
  * after argument validation), NYS_E_NOMEM. */

@@ -174,8 +174,9 @@ def nystrom_forward(q, k, v, conv_w, m: int, iters: int = 6, heads=None,
 
 
 def exact_attention_head(q, k, v) -> np.ndarray:
-    """The quantity being approximated (M1): softmax(Q K^T / sqrt(d)) V, formed densely.
-    Used only by the oracle's own pins on small n."""
+    """The quantity being approximated (M1): softmax(Q K^T / sqrt(d)) V, formed densely
+    (small n only). It is the expected value of the m = n reduction checks; pinned against
+    torch's dense scaled-dot-product attention and pure-Python loops."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)

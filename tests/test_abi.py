@@ -147,3 +147,4 @@ def test_flash_validation_without_gpu():
     import torch
     if not torch.cuda.is_available():
         assert L.nys_flash_attention(*args) == _lib.NYS_E_DEVICE
+

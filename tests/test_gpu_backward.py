@@ -95,12 +95,13 @@ def test_backward_parity(name):
     _check(cfg, lengths)
 
 
-def test_backward_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_backward_full_size_every_head():
     """The long workload (B 16, H 8, n 4096, d 64, m 64) computed whole on the GPU; every
-    batch element of head 3 checked against the oracle (which also fixes dw[3])."""
+    element of dq, dk, dv of every head and all of dw checked against the oracle."""
     cfg = gen.CONFIGS["long"]
-    log(f"[gpu] backward at full size {cfg}, checking head 3 of every batch element")
-    _check(cfg, None, heads=[(b, 3) for b in range(cfg.B)])
+    log(f"[gpu] backward at full size {cfg}, every head")
+    _check(cfg, None)
 
 
 def test_backward_repeatable():

@@ -67,9 +67,10 @@ def test_flash_parity(case):
     _check(x, chunk, causal, [(b, h) for b in range(B) for h in range(H)])
 
 
+@pytest.mark.timeout(600)
 @pytest.mark.parametrize("causal", [False, True])
-def test_flash_full_size_sampled(causal):
-    """B 16, H 8, n 4096, d 64, chunk 256 computed whole; three heads checked."""
+def test_flash_full_size_every_head(causal):
+    """B 16, H 8, n 4096, d 64, chunk 256 computed whole; every element of every head."""
     log(f"[gpu] mixed-chunk at full size, causal={causal}")
     x = _inputs(16, 8, 4096, 64, seed=1003)
-    _check(x, 256, causal, [(0, 0), (7, 3), (15, 7)])
+    _check(x, 256, causal, [(b, h) for b in range(16) for h in range(8)])

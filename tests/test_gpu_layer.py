@@ -4,21 +4,30 @@ oracle/projections.py, through the C ABI.
 
 Criteria. A projection output is a bf16 rounding of an fp32-accumulated dot product of
 exact bf16 inputs, so it must lie within half a bf16 ulp of the exact fp64 value plus
-the fp32 accumulation error (bounded here by 1e-5 of the output RMS). The layer is held
-to the bf16 I/O parity bound, max|GPU - oracle| <= 2e-2 RMS, with the oracle's Q, K, V
-rounded to bf16 as the device stores them.
+the fp32 accumulation error (bounded here by 1e-5 of the output RMS). The layer stores
+Q, K, V and the attention output O in bf16 on the device, so its reference applies the
+same storage rounding to the oracle's Q, K, V and O; the layer output y is bf16 as well,
+and its own rounding alone (half an ulp of the largest |y|, about 2e-2 of the RMS on the
+full-size workload, whose largest outputs reach 10 times the RMS) is not arithmetic
+error. No page fixes a tolerance for the layer. The one used: the error beyond half a
+bf16 ulp of y must stay <= 5e-3 RMS (LAYER_EXCESS; the full max-abs error and the
+rounding floor are printed next to it). It is looser than the core's 2e-3 because the
+core's own error in O (up to ~1e-3 of its RMS), and the bf16 rounding steps of O that this
+error flips, pass through the output projection: measured 2.3e-3 at B=2, H=4, D=256.
 """
 import numpy as np
 import pytest
 
 import oracle
 from efficient_transformer_attention_segment_amd import inputs as gen
-from hip_path import bf16_ulp, dev_tensor, log, rel_max_err
+from hip_path import bf16_ulp, dev_tensor, excess_over_rounding, log, rel_max_err
 
 pytestmark = pytest.mark.gpu
 
 # (B, H, n, d, D): ragged token tiles (B n not a multiple of 128), feature tiles that
 # end mid-tile (3 H d or D not multiples of 128), one k-slab (64) and many.
+LAYER_EXCESS = 5e-3
+
 PROJ_SHAPES = [
     (1, 1, 64, 64, 64),
     (2, 2, 100, 64, 128),
@@ -92,6 +101,17 @@ def test_out_projection(shape):
     _within_rounding(got, oracle.out_project(o, li.w_o), "y")
 
 
+def _layer_ref(li, lengths=None, b=None):
+    """Oracle layer output with the device's storage formats: Q, K, V and the attention
+    output O rounded to bf16 before they are used again (batch element b, or all)."""
+    cfg = li.cfg
+    sl = slice(None) if b is None else slice(b, b + 1)
+    q, k, v = (_bf16_round(t) for t in oracle.qkv_project(li.x[sl], li.w_qkv, cfg.H, cfg.d))
+    lens = None if lengths is None else (lengths if b is None else [lengths[b]])
+    o, _ = oracle.nystrom_forward(q, k, v, li.w, cfg.m, cfg.pinv_iters, lengths=lens)
+    return oracle.out_project(_bf16_round(o), li.w_o)
+
+
 def _layer_gpu(li, lengths=None, keep=None):
     import torch
     from efficient_transformer_attention_segment_amd import NystromLayer
@@ -124,28 +144,33 @@ def test_layer_parity(name):
     log(f"[gpu] layer case {name}: {cfg} D={D} lengths={lengths}")
     li = gen.make_layer_inputs(cfg, D)
     got = _layer_gpu(li, lengths)
-    ref = oracle.nystrom_layer(li.x, li.w_qkv, li.w_o, li.w, cfg.H, cfg.d, cfg.m,
-                               cfg.pinv_iters, lengths=lengths, qkv_round=_bf16_round)
+    ref = _layer_ref(li, lengths)
     lens = lengths or [cfg.n] * cfg.B
-    # error relative to the RMS over valid rows (padding rows are exact zeros, checked below)
-    err = rel_max_err(np.concatenate([got[b, :L] for b, L in enumerate(lens)]),
-                      np.concatenate([ref[b, :L] for b, L in enumerate(lens)]))
+    # errors relative to the RMS over valid rows (padding rows are exact zeros, checked below)
+    gv = np.concatenate([got[b, :L] for b, L in enumerate(lens)])
+    rv = np.concatenate([ref[b, :L] for b, L in enumerate(lens)])
+    err, ex = rel_max_err(gv, rv), excess_over_rounding(gv, rv, "bf16")
     pad = max(float(np.abs(got[b, L:]).max()) if L < cfg.n else 0.0 for b, L in enumerate(lens))
-    log(f"[gpu]   rel max err {err:.3e}, padding |y| {pad}")
-    assert err <= 2e-2
+    log(f"[gpu]   rel max err {err:.3e}, beyond bf16 rounding {ex:.3e}, padding |y| {pad}")
+    assert ex <= LAYER_EXCESS
     assert pad == 0.0
 
 
-def test_layer_full_size_sampled():
+@pytest.mark.timeout(600)
+def test_layer_full_size_every_element():
     """The long workload (B 16, H 8, n 4096, d 64, m 64) with model width 512 computed
-    whole on the GPU; batch element 5 checked against the oracle in full."""
+    whole on the GPU; every batch element checked against the oracle in full, one at a
+    time (errors relative to the RMS over the whole output)."""
+    from hip_path import HeadStats
     cfg = gen.CONFIGS["long"]
-    b = 5
-    log(f"[gpu] layer at full size {cfg}, D=512, checking batch element {b}")
+    log(f"[gpu] layer at full size {cfg}, D=512, every batch element")
     li = gen.make_layer_inputs(cfg, 512)
-    got = _layer_gpu(li, keep=b)
-    ref = oracle.nystrom_layer(li.x[b:b + 1], li.w_qkv, li.w_o, li.w, cfg.H, cfg.d, cfg.m,
-                               cfg.pinv_iters, qkv_round=_bf16_round)[0]
-    err = rel_max_err(got, ref)
-    log(f"[gpu]   rel max err {err:.3e}")
-    assert err <= 2e-2
+    got = _layer_gpu(li)
+    st, floor = HeadStats("bf16"), HeadStats("f32")
+    for b in range(cfg.B):
+        ref = _layer_ref(li, b=b)[0]
+        st.add(got[b], ref)
+        floor.add(_bf16_round(ref), ref)
+    log(f"[gpu]   rel max err {st.rel:.3e} (bf16 rounding floor {floor.rel:.3e}), "
+        f"beyond bf16 rounding {st.excess:.3e}")
+    assert st.excess <= LAYER_EXCESS

@@ -7,15 +7,17 @@ the full output's RMS on iid inputs. A third check bounds the error beyond the b
 storage rounding of the exact result (half an ulp per element) by 2e-3 * rms: it
 separates arithmetic error from the output format, which alone can exceed tau once
 |out| reaches 4 (structured inputs). Stage taps are checked against the oracle's
-intermediates. Full-size workloads compare every element of a sample of (batch, head)
-pairs; heads are independent, so each sampled head is checked exactly.
+intermediates. Full-size workloads compare every element of every (batch, head), one
+head at a time (the oracle runs per head; errors are relative to the RMS over the whole
+tensor, as if it had been compared at once).
 """
 import numpy as np
 import pytest
 
 import oracle
 from efficient_transformer_attention_segment_amd import inputs as gen
-from hip_path import excess_over_rounding, log, rel_max_err, run_hip, tau_for
+from hip_path import (HeadStats, excess_over_rounding, host, log, rel_max_err, run_hip,
+                      run_hip_dev, stage_tol, tau_for)
 
 pytestmark = pytest.mark.gpu
 
@@ -33,12 +35,12 @@ def _stage_errors(x, taps, heads):
     return errs
 
 
-# Stage tolerances (max error relative to the stage's RMS). Landmarks are fp32 sums;
-# A_S, Z, W, Y come from hi/lo bf16 products (about 17-bit operands, fp32 accumulate)
-# and the six-step iteration amplifies the relative error of its small-singular-value
-# directions by up to 3.25 per step.
-STAGE_TOL = {"q_land": 1e-5, "k_land": 1e-5, "a_s": 1e-4, "z": 1e-2, "w": 1e-3,
-             "y": 1e-2}
+STAGES = ("q_land", "k_land", "a_s", "z", "w", "y")
+# GPU Z against the SVD closed form of its own A_S, and the Moore-Penrose symmetry of
+# A Z and Z A (relative to their largest entries): about ten times the worst measured
+# (3.0e-4 and 6.3e-5, m = 32 .. 256, iid and clustered inputs)
+PINV_CF_TOL = 3e-3
+PINV_SYM_TOL = 6e-4
 
 SMALL = {
     "tiny_f32": gen.CONFIGS["tiny"],
@@ -66,6 +68,14 @@ SMALL = {
     "m128_iters0": gen.Config("m128i0", 1, 2, 1024, 64, 128, pinv_iters=0, seed=39),
     "m128_iters1": gen.Config("m128i1", 1, 2, 1024, 64, 128, pinv_iters=1, seed=40),
     "m160_iters3": gen.Config("m160i3", 1, 3, 960, 32, 160, pinv_iters=3, seed=41),
+    # fp32 I/O with m > 64: online softmax over landmark tiles in the output kernel, fp32
+    # register staging in the context kernel, the multi-launch pseudo-inverse
+    "f32_m96_d64": gen.Config("f32m96", 1, 2, 960, 64, 96, dtype=gen.F32, seed=42),
+    "f32_m128_d64": gen.Config("f32m128", 2, 2, 1024, 64, 128, dtype=gen.F32, seed=43),
+    "f32_m256_d32": gen.Config("f32m256", 1, 1, 2048, 32, 256, dtype=gen.F32, seed=44),
+    "f32_m128_d64_iters0": gen.Config("f32m128i0", 1, 2, 512, 64, 128, dtype=gen.F32,
+                                      pinv_iters=0, seed=45),
+    "f32_m96_d128": gen.Config("f32m96d128", 1, 2, 384, 128, 96, dtype=gen.F32, seed=46),
 }
 
 
@@ -87,7 +97,7 @@ def test_small_case_parity_and_stages(name):
     assert e_full <= tau
     assert e_attn <= tau
     assert e_ex <= 2e-3
-    for key, tol in STAGE_TOL.items():
+    for key, tol in stage_tol(cfg).items():
         assert errs[key] <= tol, (key, errs[key])
 
 
@@ -135,36 +145,79 @@ def test_m_equals_n_converged_is_exact_attention(n):
 FULL = ["tiny", "bert", "long", "large_m", "very_long"]
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name", FULL)
-def test_full_workloads_sampled_heads(name):
+def test_full_workloads_every_head(name):
+    """Each workload computed whole on the GPU in the benchmark's launch configuration;
+    every element of every head compared with the oracle, head by head: the full output,
+    the attention part (fp32 tap), the error beyond bf16 storage rounding, and every stage
+    tap."""
     cfg = gen.CONFIGS[name]
     log(f"[gpu] full workload {name}: {cfg}")
     x = gen.make_inputs(cfg)
-    out, taps = run_hip(x, taps=True)
-    rng = np.random.default_rng(7)
-    heads = {(0, 0), (cfg.B - 1, cfg.H - 1)}
-    while len(heads) < min(4, cfg.bh):
-        heads.add((int(rng.integers(cfg.B)), int(rng.integers(cfg.H))))
-    heads = sorted(heads)
-    ref, ref_attn = oracle.nystrom_forward(x.q, x.k, x.v, x.w, cfg.m, cfg.pinv_iters,
-                                           heads=heads)
-    got = np.stack([out[b, h] for b, h in heads])
-    got_attn = np.stack([taps["attn"][b * cfg.H + h] for b, h in heads])
+    out, taps = run_hip_dev(x, taps=True)
+    full, attn, floor = HeadStats(cfg.dtype), HeadStats("f32"), HeadStats("f32")
+    stages = {key: 0.0 for key in STAGES}
+    for b in range(cfg.B):
+        for h in range(cfg.H):
+            i = b * cfg.H + h
+            ref, ref_attn, (st,) = oracle.nystrom_forward(
+                x.q, x.k, x.v, x.w, cfg.m, cfg.pinv_iters, heads=[(b, h)], return_stages=True)
+            full.add(host(out[b, h]), ref[0])
+            attn.add(host(taps["attn"][i]), ref_attn[0])
+            if cfg.dtype == gen.BF16:  # bf16 storage rounding of the exact result alone
+                rb = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(ref[0].astype(np.float32)))
+                floor.add(rb.astype(np.float64), ref[0])
+            for key in stages:
+                stages[key] = max(stages[key], rel_max_err(host(taps[key][i]), st[key]))
+        if cfg.B > 1 and (b + 1) % max(1, cfg.B // 4) == 0:
+            log(f"[gpu]   {name}: {(b + 1) * cfg.H} of {cfg.bh} heads compared")
     tau = tau_for(cfg.dtype)
-    e_full, e_attn = rel_max_err(got, ref), rel_max_err(got_attn, ref_attn)
-    floor = 0.0
-    if cfg.dtype == gen.BF16:  # bf16 storage rounding of the exact result alone
-        r32 = ref.astype(np.float32)
-        rb = gen.bf16_bits_to_f32(gen.f32_to_bf16_bits(r32)).astype(np.float64)
-        floor = rel_max_err(rb, ref)
-    e_ex = excess_over_rounding(got, ref, cfg.dtype)
-    log(f"[gpu] {name}: heads {heads} full {e_full:.3e} (bf16 floor {floor:.3e}) "
-        f"beyond-rounding {e_ex:.3e} attn {e_attn:.3e}")
-    assert e_full <= tau
-    assert e_attn <= tau
-    assert e_ex <= 2e-3
-    # every head: finite, and the conv-free part is a convex-ish mix (|attn| <= max|Y|)
-    assert np.isfinite(out).all()
+    log(f"[gpu] {name}: all {cfg.bh} heads: full {full.rel:.3e} (bf16 floor {floor.rel:.3e}) "
+        f"beyond-rounding {full.excess:.3e} attn {attn.rel:.3e}  stages "
+        + " ".join(f"{k}={v:.2e}" for k, v in stages.items()))
+    assert full.rel <= tau
+    assert attn.rel <= tau
+    assert full.excess <= 2e-3
+    for key, tol in stage_tol(cfg, full_size=True).items():
+        assert stages[key] <= tol, (key, stages[key])
+
+
+def _svd_closed_form(a: np.ndarray, iters: int) -> np.ndarray:
+    """Z_T of the iteration from the SVD of A = U S V^T: every iterate is
+    V diag(x_i / s_i) U^T, where x_i = s_i z_i follows the scalar map
+    x -> x (13 - 15 x + 7 x^2 - x^3) / 4 from x_i(0) = alpha s_i^2."""
+    u, s, vt = np.linalg.svd(a)
+    alpha = 1.0 / (np.abs(a).sum(axis=0).max() * np.abs(a).sum(axis=1).max())
+    keep = s > 0
+    x = alpha * s[keep] ** 2
+    for _ in range(iters):
+        x = x * (13.0 - 15.0 * x + 7.0 * x * x - x ** 3) / 4.0
+    return (vt[keep].T * (x / s[keep])) @ u[:, keep].T
+
+
+@pytest.mark.parametrize("m,iters,family", [(32, 6, "iid"), (64, 1, "clustered"),
+                                            (64, 6, "clustered"), (64, 6, "iid"),
+                                            (128, 6, "clustered"), (256, 3, "iid")])
+def test_pinv_moore_penrose_properties(m, iters, family):
+    """The GPU's Z against properties the page's iterative Moore-Penrose inverse has at
+    every step, computed from the GPU's own A_S tap (so landmark rounding is not part of
+    the comparison): the SVD closed form of Z_T, and Moore-Penrose conditions 3 and 4
+    (A Z and Z A symmetric), in fp64 from the fp32 taps."""
+    cfg = gen.Config(f"mp{m}", 1, 2, 16 * m, 64, m, pinv_iters=iters, seed=90 + m + iters)
+    log(f"[gpu] pseudo-inverse properties m={m} iters={iters} {family}")
+    x = gen.make_inputs(cfg, family=family)
+    _, taps = run_hip(x, taps=True)
+    worst_cf = worst_sym = 0.0
+    for i in range(cfg.bh):
+        a, z = taps["a_s"][i], taps["z"][i]
+        worst_cf = max(worst_cf, rel_max_err(z, _svd_closed_form(a, iters)))
+        az, za = a @ z, z @ a
+        worst_sym = max(worst_sym, np.abs(az - az.T).max() / np.abs(az).max(),
+                        np.abs(za - za.T).max() / np.abs(za).max())
+    log(f"[gpu]   Z vs closed form {worst_cf:.3e}  symmetry of AZ, ZA {worst_sym:.3e}")
+    assert worst_cf <= PINV_CF_TOL
+    assert worst_sym <= PINV_SYM_TOL
 
 
 def test_deterministic_and_plan_reuse():
@@ -185,6 +238,15 @@ def test_deterministic_and_plan_reuse():
     oa3, _ = run_hip(xa)
     assert np.array_equal(oa1, oa2) and np.array_equal(oa1, oa3)
     assert not np.array_equal(oa1, ob1)
+
+
+def test_fp32_d128_large_m_is_unsupported():
+    """fp32 I/O stages V as hi/lo bf16 tiles, so at d = 128 an output block with more than
+    96 landmarks needs more than the 160 KiB of LDS: create refuses it cleanly."""
+    from efficient_transformer_attention_segment_amd import _lib
+    with pytest.raises(_lib.NysError) as ei:
+        _lib.nys_attn_create(1, 2, 512, 128, 128, 33, 6, _lib.NYS_F32)
+    assert ei.value.status == _lib.NYS_E_UNSUPPORTED and "LDS" in str(ei.value)
 
 
 def test_empty_problem_is_a_no_op():
@@ -242,3 +304,43 @@ def test_stage_profile_events():
     t = att.profile_read(3)
     att.close()
     assert len(t) == 3 and all(v > 0 for row in t for v in row)
+
+
+def test_launch_fault_injection(monkeypatch):
+    """NYS_FAULT=launch: forward and backward report NYS_E_LAUNCH before enqueueing
+    anything; without it the same plan runs normally."""
+    import torch
+    from efficient_transformer_attention_segment_amd import NystromAttention, _lib
+    cfg = gen.Config("fault", 1, 2, 256, 64, 32, seed=81)
+    x = gen.make_inputs(cfg)
+    att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m)
+    try:
+        from hip_path import upload
+        q, k, v, w = upload(x)
+        monkeypatch.setenv("NYS_FAULT", "launch")
+        with pytest.raises(_lib.NysError) as ei:
+            att.forward(q, k, v, w)
+        assert ei.value.status == _lib.NYS_E_LAUNCH and "NYS_FAULT" in str(ei.value)
+        with pytest.raises(_lib.NysError) as ei:
+            att.backward(q, k, v, w, q)
+        assert ei.value.status == _lib.NYS_E_LAUNCH
+        monkeypatch.delenv("NYS_FAULT")
+        out = att.forward(q, k, v, w)
+        torch.cuda.synchronize()
+        assert torch.isfinite(out.float()).all()
+    finally:
+        att.close()
+
+
+def test_debug_sync_and_plan_log(monkeypatch, capfd):
+    """NYS_LOG=1 prints the plan at create time; NYS_DEBUG_SYNC=1 (a wait after every
+    launch) leaves the result bit-identical."""
+    cfg = gen.Config("dbg", 2, 2, 512, 64, 64, seed=82)
+    x = gen.make_inputs(cfg)
+    ref, _ = run_hip(x)
+    monkeypatch.setenv("NYS_LOG", "1")
+    monkeypatch.setenv("NYS_DEBUG_SYNC", "1")
+    got, _ = run_hip(x)
+    err = capfd.readouterr().err
+    assert "[nys_attn] plan B=2 H=2 n=512 d=64 m=64" in err and "workspace" in err
+    assert np.array_equal(got, ref)

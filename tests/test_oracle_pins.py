@@ -28,6 +28,7 @@ def _ns(**over):
         depthwise_conv_seq=orc.depthwise_conv_seq,
         nystrom_head=orc.nystrom_head,
         nystrom_forward=orc.nystrom_forward,
+        exact_attention_head=orc.exact_attention_head,
     )
     for k, v in over.items():
         setattr(ns, k, v)
@@ -166,6 +167,38 @@ def _sdpa(q, k, v):
     return torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v))[0, 0].numpy()
 
 
+def pin_exact_attention(ns) -> float:
+    """The dense quantity being approximated (page, "Proposed method": softmax of the
+    scaled scores Q K^T / sqrt(d), applied to V) against torch's fp64 dense
+    scaled-dot-product attention on square and non-square shapes, and against pure-Python
+    loops (max-shifted exponentials, one sum per row) on a tiny input."""
+    import math
+    rng = np.random.default_rng(43)
+    worst = 0.0
+    for n, nk, d, dv in ((5, 5, 3, 3), (17, 9, 8, 5), (64, 64, 32, 32)):
+        q = rng.standard_normal((n, d)) * 1.5
+        k = rng.standard_normal((nk, d))
+        v = rng.standard_normal((nk, dv))
+        got = ns.exact_attention_head(q, k, v)
+        ref = _sdpa(q, k, v)
+        worst = max(worst, np.abs(got - ref).max() / np.abs(ref).max())
+    n, nk, d, dv = 4, 6, 3, 2
+    q = rng.standard_normal((n, d)) * 2.0
+    k = rng.standard_normal((nk, d))
+    v = rng.standard_normal((nk, dv))
+    got = ns.exact_attention_head(q, k, v)
+    for i in range(n):
+        logits = [sum(float(q[i, c]) * float(k[j, c]) for c in range(d)) / math.sqrt(d)
+                  for j in range(nk)]
+        top = max(logits)
+        e = [math.exp(x - top) for x in logits]
+        tot = sum(e)
+        for c in range(dv):
+            ref = sum(e[j] * float(v[j, c]) for j in range(nk)) / tot
+            worst = max(worst, abs(ref - float(got[i, c])))
+    return worst
+
+
 def pin_m_equals_n(ns) -> float:
     """One token per segment and a converged pseudo-inverse: S_hat = S S^+ S = S, so
     the Nystrom output is exact softmax attention (torch's dense SDPA, fp64 CPU)."""
@@ -296,6 +329,7 @@ PINS = {
     "pinv_limit": (pin_pinv_limit, 1e-8),
     "residual_cubing": (pin_residual_cubing, 1e-12),
     "m_equals_n": (pin_m_equals_n, 1e-9),
+    "exact_attention": (pin_exact_attention, 1e-13),
     "block_separated": (pin_block_separated, 1e-8),
     "single_landmark": (pin_single_landmark, 1e-13),
     "conv_library": (pin_conv_library, 1e-13),
@@ -402,6 +436,18 @@ def _head_swapped_factors(q, k, v, m, iters):
     return st
 
 
+def _exact_no_scale(q, k, v):
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    return orc.softmax_rows(q @ k.T) @ v
+
+
+def _exact_column_softmax(q, k, v):
+    q, k, v = (np.asarray(a, dtype=np.float64) for a in (q, k, v))
+    s = (q @ k.T) / np.sqrt(q.shape[1])
+    e = np.exp(s - s.max(axis=0, keepdims=True))
+    return (e / e.sum(axis=0, keepdims=True)) @ v
+
+
 MUTANTS = {
     "pinv_no_transpose": dict(iterative_pinv=_pinv_no_transpose),
     "pinv_dropped_term": dict(iterative_pinv=_pinv_dropped_term),
@@ -415,6 +461,8 @@ MUTANTS = {
     "softmax_cols": dict(softmax_rows=_softmax_cols),
     "head_wrong_scale": dict(nystrom_head=_head_wrong_scale),
     "head_swapped_factors": dict(nystrom_head=_head_swapped_factors),
+    "exact_no_scale": dict(exact_attention_head=_exact_no_scale),
+    "exact_column_softmax": dict(exact_attention_head=_exact_column_softmax),
 }
 
 
