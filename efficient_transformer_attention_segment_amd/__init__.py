@@ -10,7 +10,7 @@ _EXPORTS = {
     "nys_attn_profile_read", "nys_attn_destroy", "nys_attn_last_error", "Taps",
     "NYS_F32", "NYS_BF16", "nys_attn_forward_varlen", "nys_proj_qkv", "nys_proj_out",
     "NystromLayer", "nys_attn_backward", "flash_mixed_chunk", "nys_flash_workspace_bytes",
-    "nys_flash_states", "nys_flash_attend", "nys_flash_attention",
+    "nys_flash_states", "nys_flash_attend", "nys_flash_attention", "nys_attn_forward_noalloc",
 }
 
 

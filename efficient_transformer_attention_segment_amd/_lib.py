@@ -53,6 +53,7 @@ SIGNATURES = {
                                                                       _c_void_p]),
     "nys_proj_qkv": (_c_int, [_c_void_p] * 5 + [_c_int] * 5 + [_c_void_p]),
     "nys_proj_out": (_c_int, [_c_void_p] * 3 + [_c_int] * 5 + [_c_void_p]),
+    "nys_attn_forward_noalloc": (_c_int, [_c_int] * 8 + [_c_void_p] * 6),
     "nys_attn_destroy": (None, [_c_void_p]),
     "nys_attn_last_error": (ctypes.c_char_p, []),
 }
@@ -116,6 +117,12 @@ def nys_attn_forward_varlen(plan, q, k, v, conv_w, lengths, out, stream,
     _check(_LIB.nys_attn_forward_varlen(plan, q, k, v, conv_w, lengths, out, stream,
                                         ctypes.byref(taps) if taps is not None else None),
            "nys_attn_forward_varlen")
+
+
+def nys_attn_forward_noalloc(B, H, n, d, m, conv_width, pinv_iters, dtype, q, k, v, conv_w, out,
+                             stream) -> None:
+    _check(_LIB.nys_attn_forward_noalloc(B, H, n, d, m, conv_width, pinv_iters, dtype, q, k, v,
+                                         conv_w, out, stream), "nys_attn_forward_noalloc")
 
 
 def nys_attn_workspace_bytes(plan) -> int:

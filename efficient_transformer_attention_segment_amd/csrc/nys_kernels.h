@@ -156,6 +156,8 @@ hipError_t configure_proj();
 
 hipError_t launch_segmeans(bool bf16, int d, const void* q, const void* k, const SegArgs& a,
                            hipStream_t s);
+// Zero the landmark rows m..mp-1 of every head (fp32 means and hi/lo planes of Q and K).
+hipError_t launch_clear_landmark_padding(int d, const SegArgs& a, hipStream_t s);
 // Separate pseudo-inverse launch, used only when it is not fused (mp > 64).
 hipError_t launch_pinv(int d, const CtxArgs& a, hipStream_t s);
 hipError_t launch_context(bool bf16, int d, const CtxArgs& a, hipStream_t s);

@@ -429,6 +429,84 @@ extern "C" nys_status nys_attn_forward_varlen(nys_attn_plan* plan, const void* q
   return forward_impl(plan, q, k, v, conv_w, lengths, out, stream, taps);
 }
 
+// ------------------------------------------------------------------ allocation-free forward
+// The workspace of nys_attn_forward_noalloc: one static device array per GPU, held for
+// the life of the process. In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address comes from hipGetSymbolAddress, once per device.
+static constexpr size_t kScratchBytes = (size_t)NYS_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+namespace {
+struct NoallocDevice {
+  bool ready;
+  hipDeviceProp_t prop;
+  char* scratch;  // device address of this device's copy of `scratch`
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_noalloc_mu;
+NoallocDevice g_noalloc[kMaxDevices];
+}  // namespace
+
+// Properties and scratch address of the current device, looked up on its first call.
+static nys_status noalloc_device(int* dev, const NoallocDevice** out) {
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) {
+    (void)hipGetLastError();
+    return fail(NYS_E_DEVICE, "no HIP device available");
+  }
+  if (hipGetDevice(dev) != hipSuccess) return fail(NYS_E_DEVICE, "hipGetDevice failed");
+  if (*dev < 0 || *dev >= kMaxDevices) return fail(NYS_E_DEVICE, "device index out of range");
+  std::lock_guard<std::mutex> lock(g_noalloc_mu);
+  NoallocDevice& nd = g_noalloc[*dev];
+  if (!nd.ready) {
+    int d2 = 0;
+    nys_status st = current_device(&d2, &nd.prop);
+    if (st != NYS_OK) return st;
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      (void)hipGetLastError();
+      return fail(NYS_E_DEVICE, std::string("scratch symbol lookup failed: ") +
+                                    hipGetErrorString(e));
+    }
+    nd.scratch = static_cast<char*>(ptr);
+    nd.ready = true;
+  }
+  *out = &nd;
+  return NYS_OK;
+}
+
+extern "C" nys_status nys_attn_forward_noalloc(int B, int H, int n, int d, int m, int conv_width,
+                                               int pinv_iters, nys_dtype dtype, const void* q,
+                                               const void* k, const void* v,
+                                               const float* conv_w, void* out, void* stream) {
+  nys_status st = validate_shape(B, H, n, d, m, conv_width, pinv_iters, dtype);
+  if (st != NYS_OK) return st;
+  if (B * H == 0) return NYS_OK;
+  int dev = 0;
+  const NoallocDevice* nd = nullptr;
+  if ((st = noalloc_device(&dev, &nd)) != NYS_OK) return st;
+  nys_attn_plan p{};
+  if ((st = plan_init(&p, B, H, n, d, m, conv_width, pinv_iters, dtype, dev, nd->prop, false)) !=
+      NYS_OK)
+    return st;
+  if (p.ws_bytes > kScratchBytes)
+    return fail(NYS_E_UNSUPPORTED, "shape needs " + std::to_string(p.ws_bytes) +
+                                       " bytes of workspace; the static scratch of the "
+                                       "allocation-free forward holds " +
+                                       std::to_string(kScratchBytes));
+  plan_bind(&p, nd->scratch);
+  // Landmark rows m..mp-1 must read as zero; the scratch keeps whatever an earlier call
+  // left there, so they are cleared before the forward (a kernel, not a memset).
+  if (p.mp > p.m) {
+    const hipError_t e = nys::launch_clear_landmark_padding(p.d, p.seg,
+                                                            static_cast<hipStream_t>(stream));
+    if (e != hipSuccess)
+      return fail(NYS_E_LAUNCH, std::string("landmark padding clear: ") + hipGetErrorString(e));
+  }
+  return forward_impl(&p, q, k, v, conv_w, nullptr, out, stream, nullptr);
+}
+
 extern "C" size_t nys_attn_workspace_bytes(const nys_attn_plan* plan) {
   return plan ? plan->ws_bytes : 0;
 }

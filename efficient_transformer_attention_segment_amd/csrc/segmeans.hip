@@ -266,6 +266,29 @@ static hipError_t launch_segmeans_t(const void* q, const void* k, const SegArgs&
   return hipGetLastError();
 }
 
+// Landmark rows m..mp-1 of head blockIdx.x set to zero: fp32 means of Q and K and both
+// hi/lo planes of each (a plan's workspace keeps them zero from its creation; a reused
+// scratch buffer does not).
+__global__ __launch_bounds__(256) void clear_landmark_padding_kernel(SegArgs a, int d) {
+  const size_t bh = blockIdx.x;
+  const int per = (a.mp - a.m) * d;
+  for (int e = threadIdx.x; e < per; e += blockDim.x) {
+    const size_t off = (size_t)a.m * d + e;  // row m + e / d, column e % d
+    a.qt[bh * a.mp * d + off] = 0.f;
+    a.kt[bh * a.mp * d + off] = 0.f;
+    for (int plane = 0; plane < 2; ++plane) {
+      const size_t o = (bh * 2 + plane) * a.mp * d + off;
+      a.qt_hl[o] = 0;
+      a.kt_hl[o] = 0;
+    }
+  }
+}
+
+hipError_t launch_clear_landmark_padding(int d, const SegArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(clear_landmark_padding_kernel, dim3((unsigned)a.BH), dim3(256), 0, s, a, d);
+  return hipGetLastError();
+}
+
 hipError_t launch_segmeans(bool bf16, int d, const void* q, const void* k, const SegArgs& a,
                            hipStream_t s) {
   if (bf16) {

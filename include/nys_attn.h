@@ -110,6 +110,28 @@ nys_status nys_attn_forward_varlen(nys_attn_plan *plan, const void *q, const voi
                                    const void *v, const float *conv_w, const int *lengths,
                                    void *out, void *stream, const nys_attn_taps *taps);
 
+/* Allocation-free forward, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It computes
+ * exactly what nys_attn_forward computes for a plan of the same shape (same kernels, same
+ * launch geometry), without a plan: the workspace is one static device array of
+ * NYS_NOALLOC_SCRATCH_BYTES bytes per GPU, held by each GPU the library runs on until the
+ * process ends. The call allocates nothing (no hipMalloc, hipFree or allocating library
+ * routine); it launches a small clearing kernel before the forward when m is not a
+ * multiple of 32.
+ *   B, H, n, d, m, conv_width, pinv_iters, dtype : as for nys_attn_create
+ *   q, k, v, conv_w, out, stream                 : as for nys_attn_forward
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU (on
+ * different streams, or from different threads without ordering) race and give undefined
+ * results; calls ordered on one stream are safe. B*H == 0 does nothing.
+ * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED (as for nys_attn_create, and shapes whose workspace
+ * exceeds NYS_NOALLOC_SCRATCH_BYTES: the five workloads of the benchmark fit), NYS_E_DEVICE
+ * (no device / not gfx950 / the scratch symbol cannot be looked up), NYS_E_LAUNCH. */
+#define NYS_NOALLOC_SCRATCH_BYTES (160u * 1024u * 1024u)
+nys_status nys_attn_forward_noalloc(int B, int H, int n, int d, int m, int conv_width,
+                                    int pinv_iters, nys_dtype dtype, const void *q,
+                                    const void *k, const void *v, const float *conv_w,
+                                    void *out, void *stream);
+
 /* Backward pass: gradients of L = sum(out * dout) for the forward of this plan, i.e. the
  * derivative of the method of the Nystromformer review page ("Proposed method", bullets
  * M1..M6), including the alpha scaling of the pseudo-inverse start and the conv skip.

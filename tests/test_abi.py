@@ -148,3 +148,16 @@ def test_flash_validation_without_gpu():
     if not torch.cuda.is_available():
         assert L.nys_flash_attention(*args) == _lib.NYS_E_DEVICE
 
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 1, 64, 32, 8, 33, 6, -1), _lib.NYS_E_ARG),          # bad dtype
+    ((1, 1, 64, 32, 128, 33, 6, 1), _lib.NYS_E_ARG),         # m > n
+    ((1, 1, 64, 32, 8, 32, 6, 1), _lib.NYS_E_ARG),           # even conv width
+    ((1, 1, 64, 48, 8, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),   # d not built
+    ((1, 1, 1024, 32, 512, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),  # m > 256
+])
+def test_noalloc_forward_validates_before_any_device_call(args, status):
+    null = ctypes.c_void_p(0)
+    st = _lib.lib().nys_attn_forward_noalloc(*args, null, null, null, null, null, None)
+    assert st == status
+    assert _lib.nys_attn_last_error()
