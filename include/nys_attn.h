@@ -38,8 +38,14 @@ extern "C" {
 /* Opaque plan: holds the shapes and the device workspace of one problem size. */
 typedef struct nys_attn_plan nys_attn_plan;
 
-/* Element type of q, k, v and out. */
+/* Element type of q, k, v and out. A C caller may pass any int; the library validates
+ * it. Compiled as C++ the enum gets a fixed int underlying type (the same size and ABI
+ * as the C enum), so every int value is a valid nys_dtype there as well. */
+#ifdef __cplusplus
+typedef enum nys_dtype_e : int { NYS_F32 = 0, NYS_BF16 = 1 } nys_dtype;
+#else
 typedef enum { NYS_F32 = 0, NYS_BF16 = 1 } nys_dtype;
+#endif
 
 typedef enum {
   NYS_OK = 0,
