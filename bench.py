@@ -532,11 +532,17 @@ def backward_bench(args, cfg):
     sets = [gen.make_inputs(cfg), gen.make_inputs(cfg, seed=cfg.seed + 1000)]
 
     def dev(a):
-        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        if cfg.dtype == gen.BF16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
 
     rng = np.random.default_rng(cfg.seed + 555)
-    gs = [dev(gen.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.H, cfg.n, cfg.d),
-                                                       dtype=np.float32))) for _ in sets]
+
+    def draw():
+        g = rng.standard_normal((cfg.B, cfg.H, cfg.n, cfg.d), dtype=np.float32)
+        return gen.f32_to_bf16_bits(g) if cfg.dtype == gen.BF16 else g
+
+    gs = [dev(draw()) for _ in sets]
     dev_sets = [(dev(s.q_dev), dev(s.k_dev), dev(s.v_dev), torch.from_numpy(s.w).cuda())
                 for s in sets]
     att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, cfg.conv_width,
@@ -556,8 +562,9 @@ def backward_bench(args, cfg):
     ev[1].record()
     torch.cuda.synchronize()
     ms = ev[0].elapsed_time(ev[1]) / args.steps
-    e = 2
+    e = 2 if cfg.dtype == gen.BF16 else 4
     compulsory = 7 * cfg.bh * cfg.n * cfg.d * e   # read Q, K, V, dO; write dQ, dK, dV
+    general = cfg.dtype != gen.BF16 or cfg.m > 64
     roof_ms = compulsory / (HBM_PEAK_GBS * 1e9) * 1e3
     rec = {
         "metric": "Nystrom attn backward tokens/s",
@@ -568,6 +575,7 @@ def backward_bench(args, cfg):
         "config": {"workload": f"nystrom_attention_backward_B{cfg.B}_H{cfg.H}_n{cfg.n}_"
                                f"d{cfg.d}_m{cfg.m}_conv{cfg.conv_width}_iters{cfg.pinv_iters}",
                    "B": cfg.B, "H": cfg.H, "n": cfg.n, "d": cfg.d, "m": cfg.m,
+                   "path": "general (batched fp32 products)" if general else "fused kernels",
                    "inputs": "two alternating seeded N(0,1) sets, dout N(0,1)"},
         "path_roofline": {"bound": "hbm", "compulsory_bytes": compulsory,
                           "roofline_ms": roof_ms, "frac": roof_ms / ms},

@@ -17,8 +17,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnysattn.so")
-SOURCES = ["segmeans.hip", "context.hip", "output.hip", "proj.hip", "backward.hip", "flash.hip",
-           "plan.hip"]
+SOURCES = ["segmeans.hip", "context.hip", "output.hip", "proj.hip", "backward.hip",
+           "backward_general.hip", "flash.hip", "plan.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -1,0 +1,575 @@
+// General backward pass of the Nystrom self-attention (Nystromformer review page,
+// "Proposed method", bullets M1..M6): the gradients of L = sum(out * dout) for any shape
+// the forward supports (m up to 256, fp32 or bf16 I/O, padded batches), as a sequence of
+// batched fp32 products and small row and element kernels. The fused kernels of
+// backward.hip cover bf16 with m <= 64; this path covers the rest.
+//
+// Per (batch, head) with valid length L, s = 1/sqrt(d), landmarks Qt, Kt from the
+// forward's segment-means kernel:
+//   F = softmax_row(s Q Kt^T) [n][mp]     A = softmax_row(s Qt Kt^T) [mp][mp]
+//   B = softmax_row(s Qt K^T) [mp][n]     W = B V, Z_0 = alpha A^T, T steps of
+//   X = A Z, P = 7I - X, Q1 = 15I - X P, R = 13I - X Q1, Z' = Z R / 4 (Z_k, X_k kept),
+//   Y = Z_T W, then
+//   dF = dO Y^T, dSF = F o (dF - rowsum(F o dF)), dQ = s dSF Kt, dKt = s dSF^T Q,
+//   dY = F^T dO, dZ = dY W^T, dW = Z_T^T dY, the reverse sweep through the steps to dA,
+//   the alpha term, dSA = A o (dA - rowsum(A o dA)), dQt = s dSA Kt, dKt += s dSA^T Qt,
+//   dB = dW V^T, dSB = B o (dB - rowsum(B o dB)), dK = s dSB^T Qt, dQt += s dSB K,
+//   dV = B^T dW + conv^T(dO), dQ += dQt[seg(t)] / |seg|, dK += dKt[seg(t)] / |seg|,
+//   dw[k] = sum_t dO[t] . V[t + k - (W-1)/2].
+// F and B are held whole (n x mp per head: memory linear in n). Rows and columns of
+// token index t >= L are zero everywhere; padding rows of q, k, v and dout are not read.
+#include "nys_common.h"
+#include "nys_kernels.h"
+
+namespace nys {
+
+// ------------------------------------------------------------------ batched product
+// C[b] = alpha op(A[b]) op(B[b]) + beta C[b] + diag I (diagonal entries i = j < diag_n),
+// C fp32 M x N (ldc), op(A) M x K: A stored [M][K] (lda) or, with TA, [K][M]; op(B)
+// K x N: B stored [K][N] (ldb) or, with TB, [N][K]. Element types float or bf16 bits.
+// Token masking (mask bits: 1 = M, 2 = N, 4 = K is a token dimension): indices at or
+// past the batch entry's valid length read as zero (those memory rows are never read)
+// and C entries in masked rows / columns are written as zero.
+struct GemmArgs {
+  const void* A;
+  const void* B;
+  float* C;
+  long long sA, sB, sC;  // batch strides in elements
+  int lda, ldb, ldc;
+  int M, N, K;
+  float alpha, beta, diag;
+  int diag_n;
+  int mask;
+  const int* lengths;
+  int H, n, m;
+};
+
+template <typename T>
+__device__ __forceinline__ float ld_elem(const T* p);
+template <>
+__device__ __forceinline__ float ld_elem<float>(const float* p) { return *p; }
+template <>
+__device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p) {
+  return __uint_as_float((uint32_t)*p << 16);
+}
+
+constexpr int kGT = 64, kGK = 16, kGS = kGT + 4;
+
+template <typename TAe, typename TBe, bool TA, bool TB>
+__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
+  __shared__ __align__(16) float As[kGK][kGS];
+  __shared__ __align__(16) float Bs[kGK][kGS];
+  const int b = blockIdx.z, tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int row0 = blockIdx.y * kGT, col0 = blockIdx.x * kGT;
+  const int L = valid_length(g.lengths, b, g.H, g.n, g.m);
+  const int lm = (g.mask & 1) ? min(g.M, L) : g.M;
+  const int ln = (g.mask & 2) ? min(g.N, L) : g.N;
+  const int lk = (g.mask & 4) ? min(g.K, L) : g.K;
+  const TAe* A = static_cast<const TAe*>(g.A) + (size_t)b * g.sA;
+  const TBe* B = static_cast<const TBe*>(g.B) + (size_t)b * g.sB;
+  float acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
+  for (int k0 = 0; k0 < lk; k0 += kGK) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      // A tile: 64 rows x 16 k, threads along the stored contiguous index
+      const int ai = TA ? e % kGT : e / kGK, ak = TA ? e / kGT : e % kGK;
+      const int i = row0 + ai, k = k0 + ak;
+      As[ak][ai] = (i < lm && k < lk)
+                       ? ld_elem(A + (TA ? (size_t)k * g.lda + i : (size_t)i * g.lda + k))
+                       : 0.f;
+      // B tile: 16 k x 64 columns
+      const int bk = TB ? e % kGK : e / kGT, bj = TB ? e / kGK : e % kGT;
+      const int j = col0 + bj, kb = k0 + bk;
+      Bs[bk][bj] = (j < ln && kb < lk)
+                       ? ld_elem(B + (TB ? (size_t)j * g.ldb + kb : (size_t)kb * g.ldb + j))
+                       : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < kGK; ++kk) {
+      const f32x4 av = *reinterpret_cast<const f32x4*>(&As[kk][4 * ty]);
+      const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk][4 * tx]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+    }
+    __syncthreads();
+  }
+  float* C = g.C + (size_t)b * g.sC;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int i = row0 + 4 * ty + r;
+    if (i >= g.M) continue;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int j = col0 + 4 * tx + c;
+      if (j >= g.N) continue;
+      float* p = C + (size_t)i * g.ldc + j;
+      float v = g.alpha * acc[r][c];
+      if (g.beta != 0.f) v += g.beta * *p;
+      if (i == j && i < g.diag_n) v += g.diag;
+      if (i >= lm || j >= ln) v = 0.f;
+      *p = v;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ row kernels
+// Valid extent of a row/column dimension: 0 = all, 1 = the m landmarks, 2 = the batch
+// entry's valid length.
+__device__ __forceinline__ int extent(int mode, int full, int m, int L) {
+  return mode == 0 ? full : (mode == 1 ? min(full, m) : min(full, L));
+}
+
+struct RowArgs {
+  float* X;        // [batch][rows][cols] (ld = cols)
+  const float* P;  // softmax probabilities (dsoftmax only)
+  int rows, cols, rmode, cmode;
+  float scale;
+  const int* lengths;
+  int H, n, m;
+};
+
+// In place: X <- softmax over the valid columns of scale * X, per valid row; everything
+// else zero. One wave per row.
+__global__ __launch_bounds__(256) void row_softmax_kernel(RowArgs a, int nrows_total) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows_total) return;
+  const int b = (int)(row / a.rows), r = (int)(row % a.rows);
+  const int L = valid_length(a.lengths, b, a.H, a.n, a.m);
+  const int vr = extent(a.rmode, a.rows, a.m, L), vc = extent(a.cmode, a.cols, a.m, L);
+  float* x = a.X + (size_t)row * a.cols;
+  if (r >= vr) {
+    for (int j = lane; j < a.cols; j += 64) x[j] = 0.f;
+    return;
+  }
+  float mx = kNegBig;
+  for (int j = lane; j < vc; j += 64) mx = fmaxf(mx, a.scale * x[j]);
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int j = lane; j < vc; j += 64) sum += expf(a.scale * x[j] - mx);
+  const float inv = 1.f / wave_sum(sum);
+  for (int j = lane; j < a.cols; j += 64) x[j] = j < vc ? expf(a.scale * x[j] - mx) * inv : 0.f;
+}
+
+// In place on the upstream gradient dP of a row softmax P: X <- P o (X - rowsum(P o X)),
+// zero outside the valid rows and columns. One wave per row.
+__global__ __launch_bounds__(256) void row_dsoftmax_kernel(RowArgs a, int nrows_total) {
+  const int lane = threadIdx.x & 63;
+  const long long row = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (row >= nrows_total) return;
+  const int b = (int)(row / a.rows), r = (int)(row % a.rows);
+  const int L = valid_length(a.lengths, b, a.H, a.n, a.m);
+  const int vr = extent(a.rmode, a.rows, a.m, L), vc = extent(a.cmode, a.cols, a.m, L);
+  float* x = a.X + (size_t)row * a.cols;
+  const float* p = a.P + (size_t)row * a.cols;
+  if (r >= vr) {
+    for (int j = lane; j < a.cols; j += 64) x[j] = 0.f;
+    return;
+  }
+  float dot = 0.f;
+  for (int j = lane; j < vc; j += 64) dot += p[j] * x[j];
+  dot = wave_sum(dot);
+  for (int j = lane; j < a.cols; j += 64) x[j] = j < vc ? p[j] * (x[j] - dot) : 0.f;
+}
+
+// ------------------------------------------------------------------ landmark kernels
+// alpha = 1 / (max column abs-sum * max row abs-sum) of A (m x m valid part of mp x mp),
+// the maximising column jc and row ir (first index on ties), and Z_0 = alpha A^T.
+// One block per head.
+__global__ __launch_bounds__(256) void alpha_z0_kernel(const float* A, float* Z0, float* alpha,
+                                                       int* amax, int mp, int m,
+                                                       long long sZ0) {
+  __shared__ float colsum[256], rowsum[256];
+  __shared__ float sal;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* a = A + (size_t)b * mp * mp;
+  if (tid < m) {
+    float cs = 0.f, rs = 0.f;
+    for (int i = 0; i < m; ++i) cs += fabsf(a[(size_t)i * mp + tid]);
+    for (int j = 0; j < m; ++j) rs += fabsf(a[(size_t)tid * mp + j]);
+    colsum[tid] = cs;
+    rowsum[tid] = rs;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int jc = 0, ir = 0;
+    for (int j = 1; j < m; ++j)
+      if (colsum[j] > colsum[jc]) jc = j;
+    for (int i = 1; i < m; ++i)
+      if (rowsum[i] > rowsum[ir]) ir = i;
+    const float c = colsum[jc], r = rowsum[ir];
+    sal = 1.f / (c * r);
+    alpha[4 * b + 0] = sal;
+    alpha[4 * b + 1] = c;
+    alpha[4 * b + 2] = r;
+    alpha[4 * b + 3] = 0.f;
+    amax[2 * b + 0] = jc;
+    amax[2 * b + 1] = ir;
+  }
+  __syncthreads();
+  float* z = Z0 + (size_t)b * sZ0;
+  for (int e = tid; e < mp * mp; e += blockDim.x) {
+    const int i = e / mp, j = e % mp;
+    z[e] = sal * a[(size_t)j * mp + i];
+  }
+}
+
+// Gradient through Z_0 = alpha A^T and alpha = 1 / (c r), c = colsum_jc(|A|),
+// r = rowsum_ir(|A|): dA += alpha G0^T, d(alpha) = sum G0 o A^T,
+// dA[:, jc] -= d(alpha) alpha / c * sign(A[:, jc]), dA[ir, :] -= d(alpha) alpha / r * sign.
+// One block per head; dA [mp][mp] updated in place.
+__global__ __launch_bounds__(256) void alpha_backward_kernel(const float* A, const float* G0,
+                                                             long long sG0, float* dA,
+                                                             const float* alpha, const int* amax,
+                                                             int mp, int m) {
+  __shared__ float red[4];
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* a = A + (size_t)b * mp * mp;
+  const float* g = G0 + (size_t)b * sG0;
+  float* da = dA + (size_t)b * mp * mp;
+  const float al = alpha[4 * b], c = alpha[4 * b + 1], r = alpha[4 * b + 2];
+  const int jc = amax[2 * b], ir = amax[2 * b + 1];
+  float part = 0.f;
+  for (int e = tid; e < mp * mp; e += blockDim.x) {
+    const int i = e / mp, j = e % mp;
+    part += g[e] * a[(size_t)j * mp + i];
+  }
+  part = wave_sum(part);
+  if ((tid & 63) == 0) red[tid >> 6] = part;
+  __syncthreads();
+  const float dal = red[0] + red[1] + red[2] + red[3];
+  for (int e = tid; e < mp * mp; e += blockDim.x) {
+    const int i = e / mp, j = e % mp;
+    float v = da[e] + al * g[(size_t)j * mp + i];
+    const float aij = a[e];
+    const float sg = aij > 0.f ? 1.f : (aij < 0.f ? -1.f : 0.f);
+    if (j == jc && i < m) v -= dal * al / c * sg;
+    if (i == ir && j < m) v -= dal * al / r * sg;
+    da[e] = v;
+  }
+}
+
+// Y = -X (elementwise copy with negation) plus k I on the first m diagonal entries, on
+// mp x mp matrices of `batch` heads (for P = 7I - X).
+__global__ __launch_bounds__(256) void eye_minus_kernel(float* Y, const float* X, long long sY,
+                                                        long long sX, int mp, int m, float k,
+                                                        int batch) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)batch * mp * mp) return;
+  const int b = (int)(e / ((long long)mp * mp)), w = (int)(e % ((long long)mp * mp));
+  const int i = w / mp, j = w % mp;
+  Y[(size_t)b * sY + w] = ((i == j && i < m) ? k : 0.f) - X[(size_t)b * sX + w];
+}
+
+// Y += alpha X elementwise on `count` floats.
+__global__ __launch_bounds__(256) void axpy_kernel(float* Y, const float* X, float alpha,
+                                                   long long count) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e < count) Y[e] += alpha * X[e];
+}
+
+// ------------------------------------------------------------------ token kernels
+// dX[t] += dXt[seg(t)] / |seg(t)| for t < L (segment means backward), rows [BH][n][d].
+__global__ __launch_bounds__(256) void segment_scatter_kernel(float* dX, const float* dXt,
+                                                              int n, int d, int mp, int m,
+                                                              const int* lengths, int H) {
+  const int b = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int L = valid_length(lengths, b, H, n, m);
+  if (e >= (long long)L * d) return;
+  const int t = (int)(e / d), f = (int)(e % d);
+  const int j = (int)(((long long)t * m) / L);
+  const int start = (int)(((long long)j * L + m - 1) / m);
+  const int end = (int)(((long long)(j + 1) * L + m - 1) / m);
+  dX[((size_t)b * n + t) * d + f] += dXt[((size_t)b * mp + j) * d + f] / (float)(end - start);
+}
+
+// dV[t] += sum_k w[h][k] dO[t - k + half] over the valid tokens (the transposed conv).
+template <typename T>
+__global__ __launch_bounds__(256) void conv_transpose_kernel(float* dV, const T* dO,
+                                                             const float* w, int n, int d,
+                                                             int W, int H, int m,
+                                                             const int* lengths) {
+  const int b = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const int L = valid_length(lengths, b, H, n, m);
+  if (e >= (long long)L * d) return;
+  const int t = (int)(e / d), f = (int)(e % d), half = (W - 1) / 2;
+  const float* wh = w + (size_t)(b % H) * W;
+  const T* o = dO + (size_t)b * n * d;
+  float acc = 0.f;
+  for (int k = 0; k < W; ++k) {
+    const int src = t - k + half;
+    if (src >= 0 && src < L) acc += wh[k] * ld_elem(o + (size_t)src * d + f);
+  }
+  dV[((size_t)b * n + t) * d + f] += acc;
+}
+
+// Partial conv-weight gradient of one (head, token chunk): part[b][chunk][k] =
+// sum over the chunk's valid t of dO[t] . V[t + k - half] (V zero outside [0, L)).
+template <typename T>
+__global__ __launch_bounds__(256) void dw_partial_kernel(float* part, const T* dO, const T* V,
+                                                         int n, int d, int W, int H, int m,
+                                                         const int* lengths, int chunk,
+                                                         int nchunks) {
+  __shared__ float red[4][72];
+  const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  const int L = valid_length(lengths, b, H, n, m);
+  const int t0 = c * chunk, t1 = min(t0 + chunk, L), half = (W - 1) / 2;
+  const T* o = dO + (size_t)b * n * d;
+  const T* v = V + (size_t)b * n * d;
+  float acc[72];
+  for (int k = 0; k < W; ++k) acc[k] = 0.f;
+  for (long long e = tid; e < (long long)max(0, t1 - t0) * d; e += 256) {
+    const int t = t0 + (int)(e / d), f = (int)(e % d);
+    const float go = ld_elem(o + (size_t)t * d + f);
+    for (int k = 0; k < W; ++k) {
+      const int src = t + k - half;
+      if (src >= 0 && src < L) acc[k] += go * ld_elem(v + (size_t)src * d + f);
+    }
+  }
+  for (int k = 0; k < W; ++k) {
+    const float s = wave_sum(acc[k]);
+    if ((tid & 63) == 0) red[tid >> 6][k] = s;
+  }
+  __syncthreads();
+  if (tid < W)
+    part[((size_t)b * nchunks + c) * W + tid] = red[0][tid] + red[1][tid] + red[2][tid] + red[3][tid];
+}
+
+// dw[h][k] = sum over batch entries of head h and chunks of the partials (fixed order).
+__global__ __launch_bounds__(128) void dw_reduce_kernel(float* dw, const float* part, int B, int H,
+                                                        int W, int nchunks) {
+  const int h = blockIdx.x, k = threadIdx.x;
+  if (k >= W) return;
+  float s = 0.f;
+  for (int bb = 0; bb < B; ++bb)
+    for (int c = 0; c < nchunks; ++c) s += part[(((size_t)bb * H + h) * nchunks + c) * W + k];
+  dw[(size_t)h * W + k] = s;
+}
+
+// out[b][t][:] = src (fp32) in the I/O type for t < L, zero on padding rows.
+template <typename T>
+__global__ __launch_bounds__(256) void store_grad_kernel(T* out, const float* src, int n, int d,
+                                                         int H, int m, const int* lengths) {
+  const int b = blockIdx.y;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (long long)n * d) return;
+  const int L = valid_length(lengths, b, H, n, m);
+  const size_t o = (size_t)b * n * d + e;
+  const float v = e / d < L ? src[o] : 0.f;
+  if constexpr (sizeof(T) == 4) out[o] = v;
+  else out[o] = __builtin_bit_cast(uint16_t, bf16_rne(v));
+}
+
+// Zero `count` floats.
+__global__ __launch_bounds__(256) void zero_kernel(float* p, long long count) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (e < count) p[e] = 0.f;
+}
+
+// ------------------------------------------------------------------ host sequence
+namespace {
+
+struct Runner {
+  const GenBwdArgs& a;
+  hipStream_t s;
+  hipError_t err = hipSuccess;
+
+  // C = alpha op(A) op(B) + beta C + diag I, batched over the BH heads
+  template <typename TAe, typename TBe, bool TA, bool TB>
+  void gemm(const TAe* A, long long sA, int lda, const TBe* B, long long sB, int ldb, float* C,
+            long long sC, int ldc, int M, int N, int K, float alpha, float beta, int mask,
+            float diag = 0.f, int diag_n = 0) {
+    if (err != hipSuccess) return;
+    GemmArgs g{A, B, C, sA, sB, sC, lda, ldb, ldc, M, N, K, alpha, beta, diag, diag_n, mask,
+               a.lengths, a.H, a.n, a.m};
+    const dim3 grid((N + kGT - 1) / kGT, (M + kGT - 1) / kGT, a.BH);
+    hipLaunchKernelGGL((gemm_kernel<TAe, TBe, TA, TB>), grid, dim3(256), 0, s, g);
+    err = hipGetLastError();
+  }
+  void softmax(float* X, int rows, int cols, int rmode, int cmode, float scale) {
+    if (err != hipSuccess) return;
+    RowArgs r{X, nullptr, rows, cols, rmode, cmode, scale, a.lengths, a.H, a.n, a.m};
+    const long long total = (long long)a.BH * rows;
+    hipLaunchKernelGGL(row_softmax_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, r,
+                       (int)total);
+    err = hipGetLastError();
+  }
+  void dsoftmax(float* X, const float* P, int rows, int cols, int rmode, int cmode) {
+    if (err != hipSuccess) return;
+    RowArgs r{X, P, rows, cols, rmode, cmode, 1.f, a.lengths, a.H, a.n, a.m};
+    const long long total = (long long)a.BH * rows;
+    hipLaunchKernelGGL(row_dsoftmax_kernel, dim3((unsigned)((total + 3) / 4)), dim3(256), 0, s, r,
+                       (int)total);
+    err = hipGetLastError();
+  }
+  void axpy(float* Y, const float* X, float alpha, long long count) {
+    if (err != hipSuccess) return;
+    hipLaunchKernelGGL(axpy_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, s, Y, X,
+                       alpha, count);
+    err = hipGetLastError();
+  }
+};
+
+template <typename T>
+hipError_t run(const GenBwdArgs& a, hipStream_t s) {
+  Runner r{a, s};
+  const int BH = a.BH, n = a.n, d = a.d, mp = a.mp, m = a.m, T_ = a.iters;
+  const long long nd = (long long)n * d, nm = (long long)n * mp, md = (long long)mp * d,
+                  mm = (long long)mp * mp;
+  const float sc = a.scale;
+  const T* q = static_cast<const T*>(a.q);
+  const T* k = static_cast<const T*>(a.k);
+  const T* v = static_cast<const T*>(a.v);
+  const T* dO = static_cast<const T*>(a.dout);
+  constexpr int kM = 1, kN = 2, kK = 4;  // token-dimension masks
+  // ---- forward recomputation (landmarks qt, kt come from the segment-means kernel)
+  // F = softmax_row(s Q Kt^T): rows = tokens, columns = landmarks
+  r.gemm<T, float, false, true>(q, nd, d, a.kt, md, d, a.F, nm, mp, n, mp, d, 1.f, 0.f, kM);
+  r.softmax(a.F, n, mp, 2, 1, sc);
+  // A = softmax_row(s Qt Kt^T)
+  r.gemm<float, float, false, true>(a.qt, md, d, a.kt, md, d, a.A, mm, mp, mp, mp, d, 1.f, 0.f, 0);
+  r.softmax(a.A, mp, mp, 1, 1, sc);
+  // B = softmax_row(s Qt K^T): rows = landmarks, columns = tokens
+  r.gemm<float, T, false, true>(a.qt, md, d, k, nd, d, a.Bm, nm, n, mp, n, d, 1.f, 0.f, kN);
+  r.softmax(a.Bm, mp, n, 1, 2, sc);
+  // W = B V
+  r.gemm<float, T, false, false>(a.Bm, nm, n, v, nd, d, a.Wc, md, d, mp, d, n, 1.f, 0.f, kK);
+  // alpha, Z_0 = alpha A^T, then the iteration with every Z_k and X_k kept
+  const long long zst = (long long)(T_ + 1) * mm, xst = (long long)std::max(T_, 1) * mm;
+  if (r.err == hipSuccess) {
+    hipLaunchKernelGGL(alpha_z0_kernel, dim3(BH), dim3(256), 0, s, a.A, a.Zs, a.alpha, a.amax, mp,
+                       m, zst);
+    r.err = hipGetLastError();
+  }
+  for (int it = 0; it < T_; ++it) {
+    float* Z = a.Zs + it * mm;
+    float* X = a.Xs + it * mm;
+    r.gemm<float, float, false, false>(a.A, mm, mp, Z, zst, mp, X, xst, mp, mp, mp, mp, 1.f, 0.f, 0);
+    if (r.err == hipSuccess) {  // P = 7I - X
+      hipLaunchKernelGGL(eye_minus_kernel, dim3((unsigned)((BH * mm + 255) / 256)), dim3(256), 0, s,
+                         a.P, X, mm, xst, mp, m, 7.f, BH);
+      r.err = hipGetLastError();
+    }
+    // Q1 = 15I - X P, R = 13I - X Q1, Z' = Z R / 4
+    r.gemm<float, float, false, false>(X, xst, mp, a.P, mm, mp, a.Q1, mm, mp, mp, mp, mp, -1.f, 0.f,
+                                       0, 15.f, m);
+    r.gemm<float, float, false, false>(X, xst, mp, a.Q1, mm, mp, a.R, mm, mp, mp, mp, mp, -1.f, 0.f,
+                                       0, 13.f, m);
+    r.gemm<float, float, false, false>(Z, zst, mp, a.R, mm, mp, Z + mm, zst, mp, mp, mp, mp, 0.25f,
+                                       0.f, 0);
+  }
+  const float* ZT = a.Zs + (long long)T_ * mm;
+  // Y = Z_T W
+  r.gemm<float, float, false, false>(ZT, zst, mp, a.Wc, md, d, a.Y, md, d, mp, d, mp, 1.f, 0.f, 0);
+
+  // ---- backward
+  // dF = dO Y^T (into G1), dSF = F o (dF - rowsum(F o dF))
+  r.gemm<T, float, false, true>(dO, nd, d, a.Y, md, d, a.G1, nm, mp, n, mp, d, 1.f, 0.f, kM);
+  r.dsoftmax(a.G1, a.F, n, mp, 2, 1);
+  // dQ = s dSF Kt; dKt = s dSF^T Q; dY = F^T dO
+  r.gemm<float, float, false, false>(a.G1, nm, mp, a.kt, md, d, a.dQ, nd, d, n, d, mp, sc, 0.f, kM);
+  r.gemm<float, T, true, false>(a.G1, nm, mp, q, nd, d, a.dKt, md, d, mp, d, n, sc, 0.f, kK);
+  r.gemm<float, T, true, false>(a.F, nm, mp, dO, nd, d, a.dY, md, d, mp, d, n, 1.f, 0.f, kK);
+  // dZ_T = dY W^T, dW = Z_T^T dY
+  float* G = a.Gz;  // running dZ_{k+1}
+  r.gemm<float, float, false, true>(a.dY, md, d, a.Wc, md, d, G, mm, mp, mp, mp, d, 1.f, 0.f, 0);
+  r.gemm<float, float, true, false>(ZT, zst, mp, a.dY, md, d, a.dW, md, d, mp, d, mp, 1.f, 0.f, 0);
+  // reverse sweep: dA accumulates dX Z_k^T over the steps (the first step overwrites it);
+  // G becomes dZ_k
+  if (T_ == 0 && r.err == hipSuccess) {
+    hipLaunchKernelGGL(zero_kernel, dim3((unsigned)((BH * mm + 255) / 256)), dim3(256), 0, s, a.dA,
+                       (long long)BH * mm);
+    r.err = hipGetLastError();
+  }
+  float* Gn = a.Gn;
+  for (int it = T_ - 1; it >= 0; --it) {
+    const float* Z = a.Zs + it * mm;
+    const float* X = a.Xs + it * mm;
+    // recompute P, Q1, R of this step
+    if (r.err == hipSuccess) {
+      hipLaunchKernelGGL(eye_minus_kernel, dim3((unsigned)((BH * mm + 255) / 256)), dim3(256), 0, s,
+                         a.P, X, mm, xst, mp, m, 7.f, BH);
+      r.err = hipGetLastError();
+    }
+    r.gemm<float, float, false, false>(X, xst, mp, a.P, mm, mp, a.Q1, mm, mp, mp, mp, mp, -1.f, 0.f,
+                                       0, 15.f, m);
+    r.gemm<float, float, false, false>(X, xst, mp, a.Q1, mm, mp, a.R, mm, mp, mp, mp, mp, -1.f, 0.f,
+                                       0, 13.f, m);
+    // Z' = Z R / 4: dZk = G R^T / 4, dR = Z^T G / 4
+    r.gemm<float, float, false, true>(G, mm, mp, a.R, mm, mp, Gn, mm, mp, mp, mp, mp, 0.25f, 0.f, 0);
+    r.gemm<float, float, true, false>(Z, zst, mp, G, mm, mp, a.dR, mm, mp, mp, mp, mp, 0.25f, 0.f, 0);
+    // R = 13I - X Q1: dX = -dR Q1^T, dQ1 = -X^T dR
+    r.gemm<float, float, false, true>(a.dR, mm, mp, a.Q1, mm, mp, a.dX, mm, mp, mp, mp, mp, -1.f, 0.f, 0);
+    r.gemm<float, float, true, false>(X, xst, mp, a.dR, mm, mp, a.dQ1, mm, mp, mp, mp, mp, -1.f, 0.f, 0);
+    // Q1 = 15I - X P: dX -= dQ1 P^T, dP = -X^T dQ1
+    r.gemm<float, float, false, true>(a.dQ1, mm, mp, a.P, mm, mp, a.dX, mm, mp, mp, mp, mp, -1.f, 1.f, 0);
+    r.gemm<float, float, true, false>(X, xst, mp, a.dQ1, mm, mp, a.dP, mm, mp, mp, mp, mp, -1.f, 0.f, 0);
+    // P = 7I - X: dX -= dP
+    r.axpy(a.dX, a.dP, -1.f, (long long)BH * mm);
+    // X = A Z: dA += dX Z^T, dZk += A^T dX
+    r.gemm<float, float, false, true>(a.dX, mm, mp, Z, zst, mp, a.dA, mm, mp, mp, mp, mp, 1.f,
+                                      it == T_ - 1 ? 0.f : 1.f, 0);
+    r.gemm<float, float, true, false>(a.A, mm, mp, a.dX, mm, mp, Gn, mm, mp, mp, mp, mp, 1.f, 1.f, 0);
+    float* t = G;
+    G = Gn;
+    Gn = t;
+  }
+  // Z_0 = alpha A^T and the alpha term
+  if (r.err == hipSuccess) {
+    hipLaunchKernelGGL(alpha_backward_kernel, dim3(BH), dim3(256), 0, s, a.A, G, mm, a.dA, a.alpha,
+                       a.amax, mp, m);
+    r.err = hipGetLastError();
+  }
+  // dSA = A o (dA - rowsum(A o dA)); dQt = s dSA Kt; dKt += s dSA^T Qt
+  r.dsoftmax(a.dA, a.A, mp, mp, 1, 1);
+  r.gemm<float, float, false, false>(a.dA, mm, mp, a.kt, md, d, a.dQt, md, d, mp, d, mp, sc, 0.f, 0);
+  r.gemm<float, float, true, false>(a.dA, mm, mp, a.qt, md, d, a.dKt, md, d, mp, d, mp, sc, 1.f, 0);
+  // dB = dW V^T (into G2), dSB = B o (dB - rowsum(B o dB))
+  r.gemm<float, T, false, true>(a.dW, md, d, v, nd, d, a.G2, nm, n, mp, n, d, 1.f, 0.f, kN);
+  r.dsoftmax(a.G2, a.Bm, mp, n, 1, 2);
+  // dK = s dSB^T Qt; dQt += s dSB K; dV = B^T dW
+  r.gemm<float, float, true, false>(a.G2, nm, n, a.qt, md, d, a.dK, nd, d, n, d, mp, sc, 0.f, kM);
+  r.gemm<float, T, false, false>(a.G2, nm, n, k, nd, d, a.dQt, md, d, mp, d, n, sc, 1.f, kK);
+  r.gemm<float, float, true, false>(a.Bm, nm, n, a.dW, md, d, a.dV, nd, d, n, d, mp, 1.f, 0.f, kM);
+  if (r.err != hipSuccess) return r.err;
+  // segment means: dQ += dQt[seg] / |seg|, dK += dKt[seg] / |seg|
+  const dim3 tok((unsigned)((nd + 255) / 256), BH);
+  hipLaunchKernelGGL(segment_scatter_kernel, tok, dim3(256), 0, s, a.dQ, a.dQt, n, d, mp, m,
+                     a.lengths, a.H);
+  hipLaunchKernelGGL(segment_scatter_kernel, tok, dim3(256), 0, s, a.dK, a.dKt, n, d, mp, m,
+                     a.lengths, a.H);
+  // conv skip: dV += conv^T(dO); dw
+  hipLaunchKernelGGL((conv_transpose_kernel<T>), tok, dim3(256), 0, s, a.dV, dO, a.conv_w, n, d,
+                     a.W, a.H, m, a.lengths);
+  const int nch = (n + a.dw_chunk - 1) / a.dw_chunk;
+  hipLaunchKernelGGL((dw_partial_kernel<T>), dim3(nch, BH), dim3(256), 0, s, a.dw_part, dO, v, n,
+                     d, a.W, a.H, m, a.lengths, a.dw_chunk, nch);
+  hipLaunchKernelGGL(dw_reduce_kernel, dim3(a.H), dim3(128), 0, s, a.dconv_w, a.dw_part, a.B, a.H,
+                     a.W, nch);
+  // outputs in the I/O type, padding rows zero
+  hipLaunchKernelGGL((store_grad_kernel<T>), tok, dim3(256), 0, s, static_cast<T*>(a.dq), a.dQ,
+                     n, d, a.H, m, a.lengths);
+  hipLaunchKernelGGL((store_grad_kernel<T>), tok, dim3(256), 0, s, static_cast<T*>(a.dk), a.dK,
+                     n, d, a.H, m, a.lengths);
+  hipLaunchKernelGGL((store_grad_kernel<T>), tok, dim3(256), 0, s, static_cast<T*>(a.dv), a.dV,
+                     n, d, a.H, m, a.lengths);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_backward_general(const GenBwdArgs& a, hipStream_t s) {
+  return a.bf16 ? run<uint16_t>(a, s) : run<float>(a, s);
+}
+
+}  // namespace nys

@@ -123,6 +123,38 @@ struct BwdArgs {
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);
 hipError_t configure_backward();
 
+// General backward (any m <= 256, fp32 or bf16 I/O): batched fp32 products over the
+// heads with the factors F and B held whole (backward_general.hip). Workspace buffers are
+// fp32 and per head: [n][mp] F, G1; [mp][n] Bm, G2; [mp][mp] A, P, Q1, R, Gz, Gn, dR, dX,
+// dQ1, dP, dA; [T+1][mp][mp] Zs; [max(T,1)][mp][mp] Xs; [mp][d] Wc (= B V), Y, dY, dW, dQt, dKt;
+// [n][d] dQ, dK, dV; [4] alpha; [2] amax (int); [ceil(n / dw_chunk)][W] dw_part.
+struct GenBwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* conv_w;
+  const int* lengths;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dconv_w;
+  const float* qt;  // [BH][mp][d] landmarks (segment-means kernel), rows >= m zero
+  const float* kt;
+  float *F, *G1, *Bm, *G2;
+  float *A, *P, *Q1, *R, *Gz, *Gn, *dR, *dX, *dQ1, *dP, *dA;
+  float *Zs, *Xs;
+  float *Wc, *Y, *dY, *dW, *dQt, *dKt;
+  float *dQ, *dK, *dV;
+  float* alpha;
+  int* amax;
+  float* dw_part;
+  int B, H, BH, n, d, m, mp, W, iters, dw_chunk;
+  float scale;
+  bool bf16;
+};
+hipError_t launch_backward_general(const GenBwdArgs& a, hipStream_t s);
+
 // FLASH mixed-chunk attention (bf16 I/O): chunk states, global sums, local + global.
 struct FlashArgs {
   const uint16_t* q;        // [BH][n][d]

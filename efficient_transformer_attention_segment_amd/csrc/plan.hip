@@ -97,6 +97,9 @@ struct nys_attn_plan {
   char* bws;                        // backward workspace (first backward call), or null
   size_t bws_bytes;
   nys::BwdArgs bwd;
+  char* gws;                        // general-backward workspace (first such call), or null
+  size_t gws_bytes;
+  nys::GenBwdArgs gen;
 };
 
 static nys_status validate_shape(int B, int H, int n, int d, int m, int W, int iters,
@@ -253,6 +256,9 @@ static nys_status plan_init(nys_attn_plan* p, int B, int H, int n, int d, int m,
   p->bws = nullptr;
   p->bws_bytes = 0;
   std::memset(&p->bwd, 0, sizeof(p->bwd));
+  p->gws = nullptr;
+  p->gws_bytes = 0;
+  std::memset(&p->gen, 0, sizeof(p->gen));
   return NYS_OK;
 }
 
@@ -557,6 +563,7 @@ extern "C" void nys_attn_destroy(nys_attn_plan* p) {
   for (hipEvent_t e : p->prof_ev) (void)hipEventDestroy(e);
   if (p->ws) (void)hipFree(p->ws);
   if (p->bws) (void)hipFree(p->bws);
+  if (p->gws) (void)hipFree(p->gws);
   delete p;
 }
 
@@ -627,19 +634,66 @@ static nys_status backward_setup(nys_attn_plan* p) {
   return NYS_OK;
 }
 
+// Tokens per block of the general backward's conv-weight partial sums.
+static constexpr int kDwChunk = 256;
+
+// Carves (or, with base == nullptr, sizes) the general-backward workspace into p->gen.
+static size_t carve_general(nys_attn_plan* p, char* base) {
+  const size_t BHs = (size_t)p->BH, mp = (size_t)p->mp, dd = (size_t)p->d, n = (size_t)p->n;
+  const size_t mm = mp * mp, T = (size_t)p->iters;
+  const size_t nch = (n + kDwChunk - 1) / kDwChunk;
+  size_t off = 0;
+  auto take = [&](size_t floats) {
+    size_t o = off;
+    off = align256(off + floats * 4);
+    return base ? reinterpret_cast<float*>(base + o) : nullptr;
+  };
+  nys::GenBwdArgs& g = p->gen;
+  g.F = take(BHs * n * mp); g.G1 = take(BHs * n * mp);
+  g.Bm = take(BHs * mp * n); g.G2 = take(BHs * mp * n);
+  for (float** t : {&g.A, &g.P, &g.Q1, &g.R, &g.Gz, &g.Gn, &g.dR, &g.dX, &g.dQ1, &g.dP, &g.dA})
+    *t = take(BHs * mm);
+  g.Zs = take(BHs * (T + 1) * mm);
+  g.Xs = take(BHs * std::max<size_t>(T, 1) * mm);
+  for (float** t : {&g.Wc, &g.Y, &g.dY, &g.dW, &g.dQt, &g.dKt}) *t = take(BHs * mp * dd);
+  for (float** t : {&g.dQ, &g.dK, &g.dV}) *t = take(BHs * n * dd);
+  g.alpha = take(BHs * 4);
+  g.amax = reinterpret_cast<int*>(take(BHs * 2));
+  g.dw_part = take(BHs * nch * p->W);
+  g.B = p->B; g.H = p->H; g.BH = p->BH; g.n = p->n; g.d = p->d; g.m = p->m; g.mp = p->mp;
+  g.W = p->W; g.iters = p->iters; g.dw_chunk = kDwChunk;
+  g.scale = p->ctx.scale;
+  g.bf16 = p->dtype == NYS_BF16;
+  g.qt = p->seg.qt;
+  g.kt = p->seg.kt;
+  return off;
+}
+
+static nys_status general_setup(nys_attn_plan* p) {
+  if (p->gws) return NYS_OK;
+  if (p->BH > 65535) return fail(NYS_E_UNSUPPORTED, "backward: B*H > 65535");
+  const size_t bytes = carve_general(p, nullptr);
+  if (hipMalloc(reinterpret_cast<void**>(&p->gws), bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    p->gws = nullptr;
+    return fail(NYS_E_NOMEM, "backward workspace allocation failed");
+  }
+  p->gws_bytes = bytes;
+  carve_general(p, p->gws);
+  return NYS_OK;
+}
+
 extern "C" nys_status nys_attn_backward(nys_attn_plan* p, const void* q, const void* k,
                                         const void* v, const float* conv_w, const int* lengths,
                                         const void* dout, void* dq, void* dk, void* dv,
                                         float* dconv_w, void* stream) {
   if (p == nullptr) return fail(NYS_E_ARG, "plan is NULL");
-  if (p->dtype != NYS_BF16) return fail(NYS_E_UNSUPPORTED, "backward: bf16 plans only");
-  if (p->mp > 64) return fail(NYS_E_UNSUPPORTED, "backward: m <= 64 only");
   if (!q || !k || !v || !conv_w || !dout || !dq || !dk || !dv || !dconv_w)
     return fail(NYS_E_ARG, "NULL tensor pointer");
   for (const void* t : {q, k, v, dout, (const void*)dq, (const void*)dk, (const void*)dv})
     if ((reinterpret_cast<uintptr_t>(t) & 15u) != 0)
       return fail(NYS_E_ARG, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
-  const size_t bytes = (size_t)p->BH * p->n * p->d * 2;
+  const size_t bytes = (size_t)p->BH * p->n * p->d * (p->dtype == NYS_BF16 ? 2 : 4);
   const void* outs[] = {dq, dk, dv};
   const void* ins[] = {q, k, v, dout};
   for (int i = 0; i < 3; ++i) {
@@ -661,6 +715,28 @@ extern "C" nys_status nys_attn_backward(nys_attn_plan* p, const void* q, const v
       return fail(NYS_E_LAUNCH, "dconv_w clear failed");
     return NYS_OK;
   }
+  // the fused kernels cover bf16 with m <= 64; everything else (and NYS_BACKWARD=general)
+  // takes the general path
+  const bool general = p->dtype != NYS_BF16 || p->mp > 64 || env_is("NYS_BACKWARD", "general");
+  const bool dsync = env_on("NYS_DEBUG_SYNC");
+  if (general) {
+    nys_status st = general_setup(p);
+    if (st != NYS_OK) return st;
+    nys::SegArgs sg = p->seg;
+    sg.lengths = lengths;
+    nys::GenBwdArgs g = p->gen;
+    g.q = q; g.k = k; g.v = v; g.dout = dout; g.conv_w = conv_w; g.lengths = lengths;
+    g.dq = dq; g.dk = dk; g.dv = dv; g.dconv_w = dconv_w;
+    hipError_t e = nys::launch_segmeans(p->dtype == NYS_BF16, p->d, q, k, sg, s);
+    if (e == hipSuccess && dsync) e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+      return fail(NYS_E_LAUNCH, std::string("backward: segment means: ") + hipGetErrorString(e));
+    e = nys::launch_backward_general(g, s);
+    if (e == hipSuccess && dsync) e = hipStreamSynchronize(s);
+    if (e != hipSuccess)
+      return fail(NYS_E_LAUNCH, std::string("backward: general kernels: ") + hipGetErrorString(e));
+    return NYS_OK;
+  }
   nys_status st = backward_setup(p);
   if (st != NYS_OK) return st;
   nys::SegArgs sg = p->seg;
@@ -680,7 +756,6 @@ extern "C" nys_status nys_attn_backward(nys_attn_plan* p, const void* q, const v
   b.dk = static_cast<uint16_t*>(dk);
   b.dv = static_cast<uint16_t*>(dv);
   b.dconv_w = dconv_w;
-  const bool dsync = env_on("NYS_DEBUG_SYNC");
   const char* what = "";
   hipError_t e = hipSuccess;
   // one stage's launch result (and, with NYS_DEBUG_SYNC, its completion)

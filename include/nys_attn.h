@@ -142,16 +142,21 @@ nys_status nys_attn_forward_noalloc(int B, int H, int n, int d, int m, int conv_
  * derivative of the method of the Nystromformer review page ("Proposed method", bullets
  * M1..M6), including the alpha scaling of the pseudo-inverse start and the conv skip.
  *   q, k, v, conv_w, lengths : as for nys_attn_forward_varlen (lengths may be NULL)
- *   dout   : device bf16 [B][H][n][d], the upstream gradient of out
- *   dq, dk, dv : device bf16 [B][H][n][d], written (rows >= lengths[b] are zero)
+ *   dout   : device [B][H][n][d] in the plan's dtype, the upstream gradient of out
+ *   dq, dk, dv : device [B][H][n][d] in the plan's dtype, written (rows >= lengths[b] zero)
  *   dconv_w: device fp32 [H][conv_width], written (summed over the batch)
- * The forward's segment means and landmark context are recomputed on the stream first;
- * the call does not need a preceding forward. Preconditions: a bf16 plan with m <= 64;
- * 16-byte aligned tensors; dq, dk, dv distinct from each other and from q, k, v, dout;
- * dconv_w distinct from conv_w. The first call on a plan allocates its backward workspace
- * (about BH (2 n d + (2 iters + 1) mp^2 + 3 C mp d) * 4 bytes; freed by nys_attn_destroy).
- * Shares the plan workspace with nys_attn_forward: one call at a time per plan.
- * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED (fp32 plan, m > 64), NYS_E_NOMEM, NYS_E_LAUNCH. */
+ * Every plan is supported. bf16 plans with m <= 64 run fused kernels that recompute the
+ * forward's segment means and landmark context; the first call allocates their workspace
+ * (about BH (2 n d + (2 iters + 1) mp^2 + 3 C mp d) * 4 bytes). fp32 plans and m > 64 run
+ * the general path: batched fp32 products with the factors softmax(s Q Kt^T) and
+ * softmax(s Qt K^T) held whole; its first call allocates about
+ * BH (4 n mp + (iters + 13) mp^2 + 3 n d + 6 mp d) * 4 bytes (mp = m rounded up to 32;
+ * linear in n). Setting NYS_BACKWARD=general selects the general path for any plan.
+ * Neither needs a preceding forward. Preconditions: 16-byte aligned tensors; dq, dk, dv
+ * distinct from each other and from q, k, v, dout; dconv_w distinct from conv_w;
+ * B*H <= 65535 on the general path. Shares the plan workspace with nys_attn_forward:
+ * one call at a time per plan.
+ * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED, NYS_E_NOMEM, NYS_E_LAUNCH. */
 nys_status nys_attn_backward(nys_attn_plan *plan, const void *q, const void *k, const void *v,
                              const float *conv_w, const int *lengths, const void *dout,
                              void *dq, void *dk, void *dv, float *dconv_w, void *stream);

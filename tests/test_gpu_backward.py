@@ -1,22 +1,24 @@
 """GPU parity of the backward pass (nys_attn_backward) against the fp64 gradient oracle
-(oracle/backward.py), through the C ABI.
+(oracle/backward.py), through the C ABI: the fused kernels (bf16, m <= 64) and the general
+path (fp32 plans, m > 64, or NYS_BACKWARD=general).
 
 Criterion (no tolerance is stated for gradients; this one follows from the arithmetic):
-the gradients are stored in bf16, so the best possible result is the exact gradient
+bf16 gradients are stored in bf16, so the best possible result is the exact gradient
 rounded to bf16, up to half a bf16 ulp per element, which relative to the RMS reaches
 ~2.3e-2 on these heavy-tailed tensors. The computation itself (fp32 accumulation, bf16
-token operands, landmark operands as hi/lo bf16 pairs) must add at most 2e-3 * RMS on
-top, per (batch, head): |GPU - oracle| <= ulp/2 + 2e-3 * rms(oracle head) elementwise
-over the valid rows, with exact zeros on padding rows. dconv_w (fp32 output) must agree
-to 2e-3 * rms. Inputs are the exact bf16 values the device sees; dout is a seeded N(0, 1)
-draw rounded to bf16.
+token operands, landmark operands as hi/lo bf16 pairs on the fused path, fp32 products
+on the general path) must add at most 2e-3 * RMS on top, per (batch, head):
+|GPU - oracle| <= ulp/2 + 2e-3 * rms(oracle head) elementwise over the valid rows, with
+exact zeros on padding rows. fp32 gradients (no storage rounding) must agree to
+2e-3 * rms, and so must dconv_w. Inputs are the exact values the device sees; dout is a
+seeded N(0, 1) draw in the plan's dtype.
 """
 import numpy as np
 import pytest
 
 import oracle
 from efficient_transformer_attention_segment_amd import inputs as gen
-from hip_path import dev_tensor, excess_over_rounding, log, rel_max_err
+from hip_path import bf16_ulp, dev_tensor, excess_over_rounding, log, rel_max_err
 
 pytestmark = pytest.mark.gpu
 
@@ -34,13 +36,26 @@ CASES = {
     "conv_w65": (gen.Config("b8", 1, 1, 300, 64, 32, conv_width=65, seed=308), None),
     "iters0": (gen.Config("b9", 1, 2, 128, 32, 16, pinv_iters=0, seed=309), None),
     "m1": (gen.Config("b10", 2, 1, 100, 64, 1, seed=310), [100, 37]),
+    # general path: m > 64, fp32 plans
+    "general_m96_d32_uneven": (gen.Config("g1", 1, 2, 1000, 32, 96, seed=311), None),
+    "general_m128_d64": (gen.Config("g2", 1, 2, 1024, 64, 128, seed=312), None),
+    "general_m256_d64_ragged": (gen.Config("g3", 2, 1, 2048, 64, 256, seed=313), [2048, 700]),
+    "general_m128_d128_iters1": (gen.Config("g4", 1, 2, 512, 128, 128, pinv_iters=1, seed=314),
+                                 None),
+    "general_f32_m64": (gen.Config("g5", 1, 2, 512, 64, 64, dtype=gen.F32, seed=315), None),
+    "general_f32_m40_d128_ragged": (gen.Config("g6", 2, 2, 300, 128, 40, dtype=gen.F32,
+                                               seed=316), [300, 123]),
+    "general_f32_m160_iters0_w65": (gen.Config("g7", 1, 1, 640, 32, 160, conv_width=65,
+                                               pinv_iters=0, dtype=gen.F32, seed=317), None),
 }
 
 
 def _dout(cfg, seed):
     rng = np.random.default_rng(seed + 555)
-    bits = gen.f32_to_bf16_bits(rng.standard_normal((cfg.B, cfg.H, cfg.n, cfg.d),
-                                                    dtype=np.float32))
+    g = rng.standard_normal((cfg.B, cfg.H, cfg.n, cfg.d), dtype=np.float32)
+    if cfg.dtype == gen.F32:
+        return g, g.astype(np.float64)
+    bits = gen.f32_to_bf16_bits(g)
     return bits, gen.bf16_bits_to_f32(bits).astype(np.float64)
 
 
@@ -49,10 +64,10 @@ def run_backward(x, g_bits, lengths=None):
     from efficient_transformer_attention_segment_amd import NystromAttention
     cfg = x.cfg
     att = NystromAttention(cfg.B, cfg.H, cfg.n, cfg.d, cfg.m, cfg.conv_width, cfg.pinv_iters,
-                           "bf16")
-    q, k, v = (dev_tensor(a, "bf16") for a in (x.q_dev, x.k_dev, x.v_dev))
+                           cfg.dtype)
+    q, k, v = (dev_tensor(a, cfg.dtype) for a in (x.q_dev, x.k_dev, x.v_dev))
     w = torch.from_numpy(np.ascontiguousarray(x.w)).to("cuda")
-    g = dev_tensor(g_bits, "bf16")
+    g = dev_tensor(g_bits, cfg.dtype)
     dq, dk, dv, dw = att.backward(q, k, v, w, g, lengths=lengths)
     torch.cuda.synchronize()
     out = [t.float().cpu().numpy().astype(np.float64) for t in (dq, dk, dv, dw)]
@@ -75,7 +90,7 @@ def _check(cfg, lengths, heads=None):
         for name, gt, rf in (("dq", got[0], rq), ("dk", got[1], rk), ("dv", got[2], rv)):
             gg, rr = gt[b, h, :L], rf[i, :L]
             worst[name][0] = max(worst[name][0], rel_max_err(gg, rr))
-            worst[name][1] = max(worst[name][1], excess_over_rounding(gg, rr, "bf16"))
+            worst[name][1] = max(worst[name][1], excess_over_rounding(gg, rr, cfg.dtype))
             if L < cfg.n:
                 pad = max(pad, float(np.abs(gt[b, h, L:]).max()))
     hs = sorted({h for _, h in pairs})
@@ -95,11 +110,35 @@ def test_backward_parity(name):
     _check(cfg, lengths)
 
 
-@pytest.mark.timeout(600)
-def test_backward_full_size_every_head():
-    """The long workload (B 16, H 8, n 4096, d 64, m 64) computed whole on the GPU; every
-    element of dq, dk, dv of every head and all of dw checked against the oracle."""
-    cfg = gen.CONFIGS["long"]
+@pytest.mark.parametrize("name", ["d64_m64_bert_like", "ragged_m16", "m1"])
+def test_general_path_on_fused_shapes(name, monkeypatch):
+    """NYS_BACKWARD=general runs the general path on shapes the fused kernels cover: it
+    meets the same bound against the oracle, and agrees with the fused kernels."""
+    cfg, lengths = CASES[name]
+    log(f"[gpu] backward (general path forced) {name}: {cfg} lengths={lengths}")
+    x = gen.make_inputs(cfg)
+    g_bits, _ = _dout(cfg, cfg.seed)
+    fused = run_backward(x, g_bits, lengths)
+    monkeypatch.setenv("NYS_BACKWARD", "general")
+    _check(cfg, lengths)
+    general = run_backward(x, g_bits, lengths)
+    # two bf16 roundings of nearly equal values may sit one ulp apart
+    for nm, a_, b_ in zip(("dq", "dk", "dv", "dw"), fused, general):
+        diff = np.abs(b_ - a_)
+        if nm != "dw":
+            diff = np.maximum(diff - bf16_ulp(np.maximum(np.abs(a_), np.abs(b_))), 0.0)
+        e = float(diff.max()) / float(np.sqrt(np.mean(np.square(a_))))
+        log(f"[gpu]   general vs fused {nm}: beyond one ulp {e:.3e}")
+        assert e <= 4e-3
+
+
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name", ["long", "large_m", "very_long"])
+def test_backward_full_size_every_head(name):
+    """A full workload computed whole on the GPU (long: fused kernels; large_m, m = 256,
+    and very_long, n = 65536: the general path); every element of dq, dk, dv of every head
+    and all of dw checked against the oracle."""
+    cfg = gen.CONFIGS[name]
     log(f"[gpu] backward at full size {cfg}, every head")
     _check(cfg, None)
 

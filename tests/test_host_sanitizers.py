@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "efficient_transformer_attention_segment_amd", "csrc")
 BUILD = os.path.join(ROOT, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
-OTHER = ["segmeans", "context", "output", "proj", "backward", "flash"]
+OTHER = ["segmeans", "context", "output", "proj", "backward", "backward_general", "flash"]
 # host-only instrumentation: each sanitizer flag follows -Xarch_host
 SAN = "-Xarch_host -fsanitize=address -Xarch_host -fsanitize=undefined " \
       "-Xarch_host -fno-sanitize-recover=all -Xarch_host -fno-omit-frame-pointer"
