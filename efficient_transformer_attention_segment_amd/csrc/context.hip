@@ -77,7 +77,7 @@ __device__ __forceinline__ void pinv_body(const CtxArgs& a, int bh, uint16_t* pl
     for (int u = 0; u < TPW0; ++u) {
       const int t = wave + nw * u;
       if (t < ntiles)
-        at[u] = gemm_tile(qh, qh + (size_t)mp * dd, dd, kh, kh + (size_t)mp * dd, dd,
+        at[u] = gemm_tile_rt(qh, qh + (size_t)mp * dd, dd, kh, kh + (size_t)mp * dd, dd,
                           32 * (t / nt), 32 * (t % nt), dd, lane) * a.scale_log2e;
     }
   }
@@ -221,8 +221,8 @@ __global__ __launch_bounds__(512) void pinv_strip_kernel(CtxArgs a) {
   auto plane = [&](int idx) { return pl + (size_t)idx * P; };
   const uint16_t* qh = a.qt_hl + (size_t)bh * 2 * mp * dd;
   const uint16_t* kh = a.kt_hl + (size_t)bh * 2 * mp * dd;
-  f32x16 at = gemm_tile(qh, qh + (size_t)mp * dd, dd, kh, kh + (size_t)mp * dd, dd, row0, col0,
-                        dd, lane) * a.scale_log2e;
+  f32x16 at = gemm_tile_rt(qh, qh + (size_t)mp * dd, dd, kh, kh + (size_t)mp * dd, dd, row0,
+                           col0, dd, lane) * a.scale_log2e;
   auto lrow = [&](int rr) { return acc_row(0, rr, lane); };  // row within the strip
   // row maxima over the m real columns: half-wave, then across the column tiles
 #pragma unroll
@@ -307,10 +307,11 @@ __device__ __forceinline__ float pinv_alpha(const CtxArgs& a, int bh, int lane) 
 //   PH 2: T = 13I - 15X + 7X^2 - X X^2 -> T columns (hi/lo)
 //   PH 3: Z <- Z T / 4   -> Z rows and columns of the other Z pair; after the last
 //                           iteration fp32 Z and the row-major hi/lo copy for the output
-template <int PH>
+template <int PH, int KS>
 __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
+  __shared__ float st[32 * kStageLd];
   const int lane = threadIdx.x;
-  const int mp = a.mp, nt = mp / 32;
+  constexpr int mp = 16 * KS, nt = mp / 32;
   int bh, t;
   xcd_map(blockIdx.x, a.BH, nt * nt, bh, t);
   const size_t P = (size_t)mp * mp;
@@ -320,21 +321,23 @@ __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
   float* own = a.own + (size_t)bh * 2 * P;
   if constexpr (PH == 0) {
     const int zc = (it & 1) ? kGZc1 : kPZc;
-    f32x16 x = gemm_tile_frag(plane(kPA), plane(kPA + 1), plane(zc), plane(zc + 1), row0, col0,
-                              mp, lane);
+    f32x16 x = gemm_tile_frag<KS>(plane(kPA), plane(kPA + 1), plane(zc), plane(zc + 1), row0,
+                                  col0, lane);
     if (it == 0) x *= pinv_alpha(a, bh, lane);  // the Z_0 planes are unscaled
-    store_rows_hl_frag(plane(kPXr), plane(kPXr + 1), mp, row0, col0, x, lane);
-    store_cols_hl_frag(plane(kPXc), plane(kPXc + 1), mp, row0, col0, x, lane);
-    store_rows_f32(own, mp, row0, col0, x, lane);
+    stage_tile(st, x, lane);
+    stage_store_frag<false>(plane(kPXr), plane(kPXr + 1), mp, row0, col0, st, lane);
+    stage_store_frag<true>(plane(kPXc), plane(kPXc + 1), mp, row0, col0, st, lane);
+    stage_store_f32(own, mp, row0, col0, st, lane);
   } else if constexpr (PH == 1) {
-    const f32x16 x2 = gemm_tile_frag(plane(kPXr), plane(kPXr + 1), plane(kPXc), plane(kPXc + 1),
-                                     row0, col0, mp, lane);
-    store_cols_hl_frag(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, x2, lane);
-    store_rows_f32(own + P, mp, row0, col0, x2, lane);
+    const f32x16 x2 = gemm_tile_frag<KS>(plane(kPXr), plane(kPXr + 1), plane(kPXc),
+                                         plane(kPXc + 1), row0, col0, lane);
+    stage_tile(st, x2, lane);
+    stage_store_frag<true>(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, st, lane);
+    stage_store_f32(own + P, mp, row0, col0, st, lane);
   } else if constexpr (PH == 2) {
     const int j = col0 + (lane & 31);
-    const f32x16 x3 = gemm_tile_frag(plane(kPXr), plane(kPXr + 1), plane(kPX2T),
-                                     plane(kPX2T + 1), row0, col0, mp, lane);
+    const f32x16 x3 = gemm_tile_frag<KS>(plane(kPXr), plane(kPXr + 1), plane(kPX2T),
+                                         plane(kPX2T + 1), row0, col0, lane);
     f32x16 tv;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
@@ -342,20 +345,22 @@ __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
       const float diag = (acc_row(row0, rr, lane) == j) ? 13.f : 0.f;
       tv[rr] = diag - 15.f * own[o] + 7.f * own[P + o] - x3[rr];
     }
-    store_cols_hl_frag(plane(kGT), plane(kGT + 1), mp, row0, col0, tv, lane);
+    stage_tile(st, tv, lane);
+    stage_store_frag<true>(plane(kGT), plane(kGT + 1), mp, row0, col0, st, lane);
   } else {
     const int zr = (it & 1) ? kGZr1 : kPZr;
     const int zr_n = (it & 1) ? kPZr : kGZr1, zc_n = (it & 1) ? kPZc : kGZc1;
-    const f32x16 zv = gemm_tile_frag(plane(zr), plane(zr + 1), plane(kGT), plane(kGT + 1), row0,
-                                     col0, mp, lane) *
+    const f32x16 zv = gemm_tile_frag<KS>(plane(zr), plane(zr + 1), plane(kGT), plane(kGT + 1),
+                                         row0, col0, lane) *
                       (it == 0 ? 0.25f * pinv_alpha(a, bh, lane) : 0.25f);
+    stage_tile(st, zv, lane);
     if (it == a.iters - 1) {
       uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
-      store_rows_hl(dst, dst + P, mp, row0, col0, zv, lane);
-      store_rows_f32(a.z + (size_t)bh * P, mp, row0, col0, zv, lane);
+      stage_store_rows_hl(dst, dst + P, mp, row0, col0, st, lane);
+      stage_store_f32(a.z + (size_t)bh * P, mp, row0, col0, st, lane);
     } else {
-      store_rows_hl_frag(plane(zr_n), plane(zr_n + 1), mp, row0, col0, zv, lane);
-      store_cols_hl_frag(plane(zc_n), plane(zc_n + 1), mp, row0, col0, zv, lane);
+      stage_store_frag<false>(plane(zr_n), plane(zr_n + 1), mp, row0, col0, st, lane);
+      stage_store_frag<true>(plane(zc_n), plane(zc_n + 1), mp, row0, col0, st, lane);
     }
   }
 }
@@ -1094,10 +1099,19 @@ static hipError_t launch_pinv_t(const CtxArgs& a, hipStream_t s) {
   const int tiles = (a.mp / 32) * (a.mp / 32);
   const dim3 grid(a.BH * tiles), block(64);
   for (int it = 0; it < a.iters && e == hipSuccess; ++it) {
-    hipLaunchKernelGGL((pinv_phase_kernel<0>), grid, block, 0, s, a, it);
-    hipLaunchKernelGGL((pinv_phase_kernel<1>), grid, block, 0, s, a, it);
-    hipLaunchKernelGGL((pinv_phase_kernel<2>), grid, block, 0, s, a, it);
-    hipLaunchKernelGGL((pinv_phase_kernel<3>), grid, block, 0, s, a, it);
+    switch (a.mp) {
+#define NYS_PHASES(MP)                                                               \
+  case MP:                                                                           \
+    hipLaunchKernelGGL((pinv_phase_kernel<0, MP / 16>), grid, block, 0, s, a, it);   \
+    hipLaunchKernelGGL((pinv_phase_kernel<1, MP / 16>), grid, block, 0, s, a, it);   \
+    hipLaunchKernelGGL((pinv_phase_kernel<2, MP / 16>), grid, block, 0, s, a, it);   \
+    hipLaunchKernelGGL((pinv_phase_kernel<3, MP / 16>), grid, block, 0, s, a, it);   \
+    break;
+      NYS_PHASES(96) NYS_PHASES(128) NYS_PHASES(160) NYS_PHASES(192) NYS_PHASES(224)
+      NYS_PHASES(256)
+#undef NYS_PHASES
+      default: return hipErrorInvalidValue;
+    }
     e = hipGetLastError();
   }
   return e;

@@ -361,6 +361,54 @@ __device__ __forceinline__ f32x16 gemm_tile_k(const uint16_t* ahi, const uint16_
   return acc;
 }
 
+// Software-pipelined tile products with a compile-time depth of KS 16-wide k-steps: the
+// operands of the next PF k-steps are in flight while the current one is multiplied, so a
+// deep product costs about one memory latency instead of one per k-step (a loop over a
+// runtime depth waits for every k-step's loads before its MFMAs). A and B^T as row-major
+// hi/lo planes (lda, ldb), as in gemm_tile.
+template <int KS, int PF = 4>
+__device__ __forceinline__ f32x16 gemm_tile_p(const uint16_t* ahi, const uint16_t* alo, int lda,
+                                              const uint16_t* bhi, const uint16_t* blo, int ldb,
+                                              int row0, int col0, int lane) {
+  constexpr int R = PF < KS ? PF : KS;
+  const int r = lane & 31, h = lane >> 5;
+  const size_t oa = (size_t)(row0 + r) * lda + 8 * h;
+  const size_t ob = (size_t)(col0 + r) * ldb + 8 * h;
+  Pair8 a[R], b[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    a[s] = Pair8{ld8(ahi + oa + 16 * s), ld8(alo + oa + 16 * s)};
+    b[s] = Pair8{ld8(bhi + ob + 16 * s), ld8(blo + ob + 16 * s)};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  f32x16 acc = zero16();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    acc = mfma_pair<true, true>(a[s % R], b[s % R], acc);
+    if (s + R < KS) {
+      a[s % R] = Pair8{ld8(ahi + oa + 16 * (s + R)), ld8(alo + oa + 16 * (s + R))};
+      b[s % R] = Pair8{ld8(bhi + ob + 16 * (s + R)), ld8(blo + ob + 16 * (s + R))};
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of the next k-steps
+  }
+  return acc;
+}
+
+// gemm_tile with a runtime depth K (a multiple of 32, at most 256), dispatched to the
+// pipelined product of that depth.
+__device__ __forceinline__ f32x16 gemm_tile_rt(const uint16_t* ahi, const uint16_t* alo, int lda,
+                                               const uint16_t* bhi, const uint16_t* blo, int ldb,
+                                               int row0, int col0, int K, int lane) {
+  switch (K >> 4) {
+#define NYS_GT_CASE(N) \
+    case N: return gemm_tile_p<N>(ahi, alo, lda, bhi, blo, ldb, row0, col0, lane);
+    NYS_GT_CASE(2) NYS_GT_CASE(4) NYS_GT_CASE(6) NYS_GT_CASE(8) NYS_GT_CASE(10)
+    NYS_GT_CASE(12) NYS_GT_CASE(14)
+#undef NYS_GT_CASE
+    default: return gemm_tile_p<16>(ahi, alo, lda, bhi, blo, ldb, row0, col0, lane);
+  }
+}
+
 // Element (i, j) held by register rr of an accumulator tile at (row0, col0).
 __device__ __forceinline__ int acc_row(int row0, int rr, int lane) {
   return row0 + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
@@ -406,18 +454,31 @@ __device__ __forceinline__ size_t frag_off(int r, int c, int ld) {
          (c & 7);
 }
 
-// C = A B^T tile at (row0, col0) with A and B^T both in fragment-major planes of width K.
+// C = A B^T tile at (row0, col0) with A and B^T both in fragment-major planes of depth
+// 16 KS, software-pipelined like gemm_tile_p (PF k-steps of operands in flight).
+template <int KS, int PF = 4>
 __device__ __forceinline__ f32x16 gemm_tile_frag(const uint16_t* ahi, const uint16_t* alo,
                                                  const uint16_t* bhi, const uint16_t* blo,
-                                                 int row0, int col0, int K, int lane) {
-  const size_t oa = (size_t)(row0 >> 5) * (K >> 4) * 512 + 8 * lane;
-  const size_t ob = (size_t)(col0 >> 5) * (K >> 4) * 512 + 8 * lane;
+                                                 int row0, int col0, int lane) {
+  constexpr int R = PF < KS ? PF : KS;
+  const size_t oa = (size_t)(row0 >> 5) * KS * 512 + 8 * lane;
+  const size_t ob = (size_t)(col0 >> 5) * KS * 512 + 8 * lane;
+  Pair8 a[R], b[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    a[s] = Pair8{ld8(ahi + oa + 512 * s), ld8(alo + oa + 512 * s)};
+    b[s] = Pair8{ld8(bhi + ob + 512 * s), ld8(blo + ob + 512 * s)};
+  }
+  __builtin_amdgcn_sched_barrier(0);
   f32x16 acc = zero16();
-#pragma unroll 8
-  for (int s = 0; s < (K >> 4); ++s) {
-    Pair8 a{ld8(ahi + oa + 512 * s), ld8(alo + oa + 512 * s)};
-    Pair8 b{ld8(bhi + ob + 512 * s), ld8(blo + ob + 512 * s)};
-    acc = mfma_pair<true, true>(a, b, acc);
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    acc = mfma_pair<true, true>(a[s % R], b[s % R], acc);
+    if (s + R < KS) {
+      a[s % R] = Pair8{ld8(ahi + oa + 512 * (s + R)), ld8(alo + oa + 512 * (s + R))};
+      b[s % R] = Pair8{ld8(bhi + ob + 512 * (s + R)), ld8(blo + ob + 512 * (s + R))};
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the refill ahead of the next k-steps
   }
   return acc;
 }
@@ -450,6 +511,74 @@ __device__ __forceinline__ void store_cols_hl_frag(uint16_t* hi, uint16_t* lo, i
         u32x2{(uint32_t)a[0] | ((uint32_t)a[1] << 16), (uint32_t)a[2] | ((uint32_t)a[3] << 16)};
     *reinterpret_cast<u32x2*>(lo + o) =
         u32x2{(uint32_t)b[0] | ((uint32_t)b[1] << 16), (uint32_t)b[2] | ((uint32_t)b[3] << 16)};
+  }
+}
+
+// ---------------------------------------------------------------- staged tile stores
+// A wave's 32x32 accumulator tile parked in LDS (fp32, [32][33]: the pad keeps column reads
+// conflict-free), so that its stores leave as 16-byte runs: 8 consecutive k values of one
+// fragment-major row or column (two bf16 planes), or 4 consecutive columns of a row-major
+// fp32 matrix, instead of one 2- or 4-byte store per element. The caller's wave owns `st`
+// (32 * 33 floats) and separates successive uses of it with a wave barrier.
+constexpr int kStageLd = 33;
+
+__device__ __forceinline__ void stage_tile(float* st, const f32x16& v, int lane) {
+  const int c = lane & 31;
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) st[acc_row(0, rr, lane) * kStageLd + c] = v[rr];
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): the tile is in LDS for every lane
+}
+
+// Rows (transpose = false) or columns (true) of the staged tile at (row0, col0) into the
+// fragment-major hi/lo planes of width ld (frag_off): per 16-wide k-step one 16-byte run
+// per lane and plane.
+template <bool kCols>
+__device__ __forceinline__ void stage_store_frag(uint16_t* hi, uint16_t* lo, int ld, int row0,
+                                                 int col0, const float* st, int lane) {
+  const int r = lane & 31, half = lane >> 5;
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {  // the two k-steps the 32-wide tile spans
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int k = 16 * s + 8 * half + e;
+      x[e] = kCols ? st[k * kStageLd + r] : st[r * kStageLd + k];
+    }
+    const Pair8 p = split8(x);
+    // row (col0 + r, k from row0) for columns, (row0 + r, k from col0) for rows
+    const size_t o = kCols ? frag_off(col0 + r, row0 + 16 * s + 8 * half, ld)
+                           : frag_off(row0 + r, col0 + 16 * s + 8 * half, ld);
+    st8(hi + o, p.hi);
+    st8(lo + o, p.lo);
+  }
+}
+
+// The staged tile into a row-major fp32 matrix (ld) or row-major hi/lo bf16 planes:
+// 16-byte runs of 4 (fp32) or 8 (bf16) consecutive columns.
+__device__ __forceinline__ void stage_store_f32(float* p, int ld, int row0, int col0,
+                                                const float* st, int lane) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int row = 8 * it + (lane >> 3), c4 = 4 * (lane & 7);
+    const float* q = st + row * kStageLd + c4;
+    *reinterpret_cast<f32x4*>(p + (size_t)(row0 + row) * ld + col0 + c4) =
+        f32x4{q[0], q[1], q[2], q[3]};
+  }
+}
+
+__device__ __forceinline__ void stage_store_rows_hl(uint16_t* hi, uint16_t* lo, int ld, int row0,
+                                                    int col0, const float* st, int lane) {
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int row = 16 * it + (lane >> 2), c8 = 8 * (lane & 3);
+    float x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = st[row * kStageLd + c8 + e];
+    const Pair8 pr = split8(x);
+    const size_t o = (size_t)(row0 + row) * ld + col0 + c8;
+    st8(hi + o, pr.hi);
+    st8(lo + o, pr.lo);
   }
 }
 

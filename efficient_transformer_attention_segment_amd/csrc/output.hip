@@ -398,7 +398,8 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   } else {
     for (int t = wave; t < ntiles; t += NW) {
       const int row0 = 32 * (t / ntj), col0 = 32 * (t % ntj);
-      put_y(row0, col0, gemm_tile(zr, zr + P, mp, wtl, wtl + (size_t)D * YS, YS, row0, col0, mp, lane));
+      put_y(row0, col0,
+            gemm_tile_rt(zr, zr + P, mp, wtl, wtl + (size_t)D * YS, YS, row0, col0, mp, lane));
     }
   }
   __syncthreads();  // the V rows take over the W^T region
