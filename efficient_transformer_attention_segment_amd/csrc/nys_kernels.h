@@ -71,6 +71,8 @@ struct OutArgs {
   const uint16_t* z_hl;   // [BH][2][mp][mp]
   const float* part_w;    // [BH][C][d][mp]
   const float* part_ml;   // [BH][C][2][mp]
+  uint16_t* yt;           // [BH][2][d][mp + 8] Y^T planes staged per head (the
+                          // online-softmax variants; see output_stages_y)
   int BH, H, n, m, mp, W, half, tok_per_block, G, C;
   float scale_log2e;
 };
@@ -194,6 +196,10 @@ hipError_t launch_clear_landmark_padding(int d, const SegArgs& a, hipStream_t s)
 hipError_t launch_pinv(int d, const CtxArgs& a, hipStream_t s);
 hipError_t launch_context(bool bf16, int d, const CtxArgs& a, hipStream_t s);
 hipError_t launch_output(bool bf16, int d, int conv_ksteps, const OutArgs& a, hipStream_t s);
+// True when the output launch for this shape first merges the context states and forms
+// Y = Z W once per head (into OutArgs::yt) instead of in every block's prologue.
+bool output_stages_y(bool bf16, int d, int mp, int conv_ksteps, int C);
+constexpr int kMaxChunks = 16;  // context chunks per head the output merge supports
 
 // Dynamic LDS each launch needs (bytes), and one-time kernel attribute setup.
 // pinv fused into the context launch?

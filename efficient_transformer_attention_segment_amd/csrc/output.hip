@@ -47,11 +47,20 @@ __device__ __forceinline__ int score_landmark(int lt, int rr, int h) {
   return 32 * lt + 8 * (rr >> 2) + 4 * h + (rr & 3);
 }
 
+// Landmark tiles whose Kt lo plane a lane can hold in registers (128 VGPRs at most).
+template <int D>
+constexpr int split_tiles() {
+  return 16384 / (32 * D) < 8 ? 16384 / (32 * D) : 8;
+}
+
 // NT: landmark tiles handled with all scores in registers (1 or 2), or 0 for the
 // online softmax over a runtime number of tiles. kFull: m == 32 * NT (no masking).
 // NW: waves per block (4, or 8 where one block fills a CU's LDS); a step covers 32 NW
-// tokens.
-template <typename Tin, int D, int KS, bool kKtLds, int NT, bool kFull, int NW>
+// tokens. kKtSplit (bf16 online-softmax shapes whose Kt does not fit beside Y^T): Kt is
+// the same for every step, so its hi plane is kept in LDS (staged after Y is formed, in
+// the region the W^T merge used) and each lane keeps its fragments of the lo plane in
+// registers for the whole block, instead of reading Kt from L2 every step.
+template <typename Tin, int D, int KS, bool kKtLds, int NT, bool kFull, int NW, bool kKtSplit>
 __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   extern __shared__ __align__(16) char lds[];
   constexpr bool kS = Input<Tin>::kSplit;
@@ -63,6 +72,9 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   constexpr int NCH = (EXT * (D / 8) + NTH - 1) / NTH;  // 8-element V chunks per thread
   static_assert(32 * NW * D <= EXT * VR, "output rows are staged in the V tile");
   static_assert(NT == 0 || kKtLds, "register-resident softmax expects Kt in LDS");
+  static_assert(!kKtSplit || (NT == 0 && !kKtLds && NW == 4 && !kS),
+                "split Kt: bf16 online-softmax shapes with 4-wave blocks");
+  constexpr int kMaxT = kKtSplit ? split_tiles<D>() : 1;  // landmark tiles held (split Kt)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r32 = lane & 31, h = lane >> 5;
   const int mp = NT > 0 ? 32 * NT : a.mp;
@@ -98,7 +110,8 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   uint16_t* un = kl + (kKtLds ? (size_t)2 * mp * KR : 0);
   uint16_t* wtl = un;                                  // [2][D][YS]  W^T hi, lo
   float* wgt = reinterpret_cast<float*>(un + (size_t)2 * D * YS);  // [C][mp]
-  uint16_t* vt = un;                                   // [EXT][VR] V rows (hi)
+  uint16_t* ksp = un;                                  // [mp][KR] Kt hi (kKtSplit)
+  uint16_t* vt = un + (kKtSplit ? (size_t)mp * KR : 0);  // [EXT][VR] V rows (hi)
   uint16_t* vt_lo = vt + (size_t)EXT * VR;             // V rows lo (fp32 input only)
   const bool taps = grp == 0;
   const int C = a.C;
@@ -137,9 +150,14 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
       qb[s] = Input<Tin>::load8(Q + (size_t)tq * D + 16 * s + 8 * h, tq < t_valid);
   };
   // scores of landmark tile lt (landmarks x tokens)
+  bf16x8 klo[kMaxT][KD];  // this lane's Kt lo fragments (kKtSplit)
   auto scores = [&](int lt, const Pair8* qb) -> f32x16 {
     f32x16 S = zero16();
-    if constexpr (kKtLds) {
+    if constexpr (kKtSplit) {
+      const uint16_t* kp = ksp + (size_t)(32 * lt + r32) * KR + 8 * h;
+#pragma unroll
+      for (int s = 0; s < KD; ++s) S = mfma_pair<true, false>(Pair8{ld8(kp + 16 * s), klo[lt][s]}, qb[s], S);
+    } else if constexpr (kKtLds) {
       const uint16_t* kp = kl + (size_t)(32 * lt + r32) * KR + 8 * h;
 #pragma unroll
       for (int s = 0; s < KD; ++s) {
@@ -178,6 +196,13 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   // set-up costs about one memory round trip. The landmark operands go first and the
   // first V rows and Q after them: loads retire in order, so the merge below waits only
   // for the landmark data while the token rows are still arriving.
+  // Online-softmax shapes (NT = 0): the head's Y^T planes were formed once for the head
+  // (output_ystage_kernel) in this LDS image's layout; LDS-DMA copies them straight in,
+  // 1 KiB per wave instruction, completed before the token loop.
+  if constexpr (NT == 0) {
+    const uint16_t* ys = a.yt + (size_t)bh * 2 * D * YS;
+    for (int b = wave; b < D * YS / 256; b += NW) dma16(ys + 512 * b + 8 * lane, yl + 512 * b);
+  }
   Chunk<Tin> vc[NCH];
   Pair8 qb[KD];
   float wt0 = 0.f, wt1 = 0.f;  // conv taps `lane` and `lane + 64` of this head (wave 0)
@@ -194,7 +219,7 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   const int ntj = D / 32, ntiles = (mp / 32) * ntj;
   // running max / sum of landmark tid in the first kCB chunks
   float cm[kCB], cl[kCB];
-  if (tid < mp) {
+  if (NT > 0 && tid < mp) {
 #pragma unroll
     for (int c = 0; c < kCB; ++c) {
       cm[c] = c < C ? pml[(size_t)(2 * c) * mp + tid] : kNegBig;
@@ -240,11 +265,28 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
     }
   }
 
+  // split Kt: the lane's lo fragments, and a share of the hi rows to stage after Y
+  constexpr int KHS = kKtSplit ? (kMaxT * 32 * (D / 8) + NTH - 1) / NTH : 1;
+  bf16x8 khs[KHS];
+  if constexpr (kKtSplit) {
+#pragma unroll
+    for (int lt = 0; lt < kMaxT; ++lt)
+#pragma unroll
+      for (int s = 0; s < KD; ++s)
+        klo[lt][s] = 32 * lt < mp ? ld8(khl + (size_t)mp * D + (size_t)(32 * lt + r32) * D + 16 * s + 8 * h)
+                                  : zero8();
+#pragma unroll
+    for (int u = 0; u < KHS; ++u) {
+      const int e = tid + NTH * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      khs[u] = row < mp ? ld8(khl + (size_t)row * D + c8) : zero8();
+    }
+  }
+
   load_v(t_begin, vc);
   load_q(t_begin, qb);
 
   // chunk weights per landmark: exp2(M_c - M*) / sum_c exp2(M_c - M*) L_c
-  if (tid < mp) {
+  if (NT > 0 && tid < mp) {
     const int j = tid;
     if (j >= a.m) {
       for (int c = 0; c < C; ++c) wgt[c * mp + j] = 0.f;
@@ -357,11 +399,6 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
         put_w(f, j, acc);
       }
     }
-  } else {
-    for (int e = tid; e < D * mp / 4; e += NTH) {
-      const int f = e / (mp / 4), j = (e % (mp / 4)) * 4;
-      put_w(f, j, merge_rest(f, j, f32x4{0.f, 0.f, 0.f, 0.f}, 0));
-    }
   }
   __syncthreads();
   // Y = Z W: A operand Z rows (global hi/lo), B operand W read along landmarks (W^T);
@@ -395,15 +432,17 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
         put_y(row0, col0, yv);
       }
     }
-  } else {
-    for (int t = wave; t < ntiles; t += NW) {
-      const int row0 = 32 * (t / ntj), col0 = 32 * (t % ntj);
-      put_y(row0, col0,
-            gemm_tile_rt(zr, zr + P, mp, wtl, wtl + (size_t)D * YS, YS, row0, col0, mp, lane));
+  }
+  __syncthreads();  // the V rows (and the split Kt hi rows) take over the W^T region
+  if constexpr (kKtSplit) {
+#pragma unroll
+    for (int u = 0; u < KHS; ++u) {
+      const int e = tid + NTH * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      if (row < mp) st8(ksp + (size_t)row * KR + c8, khs[u]);
     }
   }
-  __syncthreads();  // the V rows take over the W^T region
   store_v(vc);
+  if constexpr (NT == 0) wait_dma_barrier(0);  // every wave's share of the Y^T image landed
   __syncthreads();
 
   for (int T0 = t_begin; T0 < t_end; T0 += STEP) {
@@ -457,35 +496,59 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
         }
     } else {
       float M = kNegBig, L = 0.f;
-      for (int lt = 0; lt < mp / 32; ++lt) {
+      auto online_tile = [&](int lt) {
         const f32x16 S = scores(lt, qb);
         // without a register prefetch, the next step's Q goes into qb as soon as the
         // last scores are formed, in flight during the products below
         if constexpr (!kQPre)
           if (more && lt == mp / 32 - 1) load_q(T0 + STEP, qb);
-        float x[16];
+        const bool full = 32 * lt + 32 <= a.m;  // no padded landmark in this tile
         float mx = kNegBig;
+        if (full) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          x[rr] = S[rr] * score_scale;
-          if (score_landmark(lt, rr, h) < a.m) mx = fmaxf(mx, x[rr]);
+          for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, S[rr]);
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr)
+            if (score_landmark(lt, rr, h) < a.m) mx = fmaxf(mx, S[rr]);
         }
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mn = fmaxf(M, mx);
-        const float corr = fast_exp2(M - mn);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * score_scale;  // the scale is positive
+        // lazy rescaling: the reference maximum M moves only when some lane's maximum
+        // passes it by more than 8 (probabilities then stay <= 256); the state (M, L,
+        // acc) is exact for any reference point
+        if (__any(mx > M + 8.f)) {
+          const float mn = fmaxf(M, mx);
+          const float corr = fast_exp2(M - mn);
+          L *= corr;
+#pragma unroll
+          for (int f = 0; f < FT; ++f) oacc[f] *= corr;
+          M = mn;
+        }
         float p[16];
         float ps = 0.f;
+        if (full) {
 #pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-          p[rr] = score_landmark(lt, rr, h) < a.m ? fast_exp2(x[rr] - mn) : 0.f;
-          ps += p[rr];
+          for (int rr = 0; rr < 16; ++rr) {
+            p[rr] = fast_exp2(fmaf(S[rr], score_scale, -M));
+            ps += p[rr];
+          }
+        } else {
+#pragma unroll
+          for (int rr = 0; rr < 16; ++rr) {
+            p[rr] = score_landmark(lt, rr, h) < a.m ? fast_exp2(fmaf(S[rr], score_scale, -M)) : 0.f;
+            ps += p[rr];
+          }
         }
-        L = L * corr + ps;
-        M = mn;
-#pragma unroll
-        for (int f = 0; f < FT; ++f) oacc[f] *= corr;
+        L += ps;
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2) add_py(oacc, lt, s2, &p[8 * s2]);
+      };
+      if constexpr (kKtSplit) {
+#pragma unroll
+        for (int lt = 0; lt < kMaxT; ++lt)
+          if (32 * lt < mp) online_tile(lt);
+      } else {
+        for (int lt = 0; lt < mp / 32; ++lt) online_tile(lt);
       }
       L += __shfl_xor(L, 32);
       const float inv = 1.f / L;
@@ -583,65 +646,187 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   }
 }
 
+// Y^T staging for the online-softmax variants (NT = 0), once per head instead of in
+// every output block: block (head, feature tile of 32) merges the C partial context
+// states into W^T rows f0 .. f0+31 (chunk weights exp2(M_c - M*) / sum_c exp2(M_c - M*) L_c
+// per landmark, chunks in fixed order), then each wave forms one 32-landmark row tile of
+// Y = Z W on MFMA and writes it as the output kernel's LDS image of Y^T: [2][D][mp + 8]
+// hi/lo bf16 with landmark i at (i & ~15) | kslot_perm(i & 15).
+template <int D>
+__global__ __launch_bounds__(512) void output_ystage_kernel(OutArgs a) {
+  __shared__ __align__(16) float wgt[kMaxChunks * 256];      // [C][mp]
+  __shared__ __align__(16) uint16_t wt[2 * 32 * (256 + 8)];  // W^T rows of the tile, hi/lo
+  const int mp = a.mp, YS = mp + 8, C = a.C;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nth = blockDim.x;
+  const int bh = blockIdx.x / (D / 32), f0 = 32 * (blockIdx.x % (D / 32));
+  const float* pml = a.part_ml + (size_t)bh * C * 2 * mp;
+  const float* pw = a.part_w + (size_t)bh * C * D * mp;
+  // chunk weights of landmark j (thread j): every chunk's (max, sum) loaded at once
+  if (tid < mp) {
+    const int j = tid;
+    float cm[kMaxChunks], cl[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      cm[c] = c < C ? pml[(size_t)(2 * c) * mp + j] : kNegBig;
+      cl[c] = c < C ? pml[(size_t)(2 * c + 1) * mp + j] : 0.f;
+    }
+    float ms = kNegBig;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) ms = fmaxf(ms, cm[c]);
+    float den = 0.f;
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      cm[c] = c < C ? fast_exp2(cm[c] - ms) : 0.f;
+      den += cm[c] * cl[c];
+    }
+    const float inv = j < a.m ? 1.f / den : 0.f;  // padded landmarks weigh nothing
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < C) wgt[c * mp + j] = cm[c] * inv;
+  }
+  __syncthreads();
+  // W^T[f][j] = sum_c wgt[c][j] partial_c[f][j]: four landmarks per output, all C chunk
+  // loads of an output in flight together
+  for (int e = tid; e < 32 * (mp / 4); e += nth) {
+    const int fl = e / (mp / 4), j = (e % (mp / 4)) * 4, f = f0 + fl;
+    f32x4 v[kMaxChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      v[c] = c < C ? *reinterpret_cast<const f32x4*>(pw + ((size_t)c * D + f) * mp + j)
+                   : f32x4{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c)
+      if (c < C) acc += *reinterpret_cast<const f32x4*>(wgt + c * mp + j) * v[c];
+    uint16_t hb[4], lb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) split1(acc[q], hb[q], lb[q]);
+    *reinterpret_cast<u32x2*>(wt + (size_t)fl * YS + j) =
+        u32x2{(uint32_t)hb[0] | ((uint32_t)hb[1] << 16), (uint32_t)hb[2] | ((uint32_t)hb[3] << 16)};
+    *reinterpret_cast<u32x2*>(wt + (size_t)32 * YS + (size_t)fl * YS + j) =
+        u32x2{(uint32_t)lb[0] | ((uint32_t)lb[1] << 16), (uint32_t)lb[2] | ((uint32_t)lb[3] << 16)};
+    if (a.w_tap != nullptr)  // each feature tile writes its own columns
+#pragma unroll
+      for (int q = 0; q < 4; ++q) a.w_tap[((size_t)bh * mp + j + q) * D + f] = acc[q];
+  }
+  __syncthreads();
+  // Y rows 32 wave .. + 31, columns f0 .. f0 + 31: A = Z rows (hi/lo), B read along the
+  // landmarks from the W^T planes
+  const int row0 = 32 * wave;
+  if (row0 >= mp) return;
+  const uint16_t* zr = a.z_hl + (size_t)bh * 2 * mp * mp;
+  const f32x16 yv = gemm_tile_rt(zr, zr + (size_t)mp * mp, mp, wt, wt + (size_t)32 * YS, YS,
+                                 row0, 0, mp, lane);
+  uint16_t* yt = a.yt + (size_t)bh * 2 * D * YS;
+  const int f = f0 + (lane & 31);
+#pragma unroll
+  for (int rr = 0; rr < 16; ++rr) {
+    const int i = acc_row(row0, rr, lane);
+    const int ip = (i & ~15) | kslot_perm(i & 15);
+    uint16_t hb, lb;
+    split1(yv[rr], hb, lb);
+    yt[(size_t)f * YS + ip] = hb;
+    yt[(size_t)D * YS + (size_t)f * YS + ip] = lb;
+    if (a.y_tap != nullptr) a.y_tap[((size_t)bh * mp + i) * D + f] = yv[rr];
+  }
+}
+
 // ------------------------------------------------------------------ host side
 // LDS budget of one block; Kt goes to LDS only when everything fits in 160 KiB.
 constexpr size_t kLdsLimit = 160 * 1024;
 
-static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, bool kt_lds, int nw) {
+// Where Kt lives for the scores: the whole hi/lo copy in LDS, split (hi plane in LDS,
+// lo plane in registers), or read from L2 every step.
+enum class KtPlace { kLds, kSplit, kL2 };
+
+// A block's LDS. ypre: an online-softmax variant, whose Y^T is staged per head (no W^T
+// merge region).
+static size_t lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C, KtPlace kt, int nw,
+                        bool ypre) {
   const size_t ext = 32 * (size_t)nw - 32 + 16 * (size_t)conv_ksteps;
   const size_t yl = (size_t)2 * d * (mp + 8) * 2;
   const size_t wl = (size_t)conv_ksteps * 2 * 64 * 8 * 2;
-  const size_t kl = kt_lds ? (size_t)2 * mp * (d + 8) * 2 : 0;
-  const size_t wtl = (size_t)2 * d * (mp + 8) * 2 + (size_t)C * mp * 4;  // W^T + chunk weights
-  const size_t vt = (bf16 ? 1 : 2) * ext * (size_t)(d + 8) * 2;        // shares wtl's region
+  const size_t kl = kt == KtPlace::kLds ? (size_t)2 * mp * (d + 8) * 2 : 0;
+  const size_t wtl = ypre ? 0 : (size_t)2 * d * (mp + 8) * 2 + (size_t)C * mp * 4;  // W^T + chunk weights
+  // after the prologue: the split Kt hi rows, then the V rows
+  const size_t vt = (kt == KtPlace::kSplit ? (size_t)mp * (d + 8) * 2 : 0) +
+                    (bf16 ? 1 : 2) * ext * (size_t)(d + 8) * 2;
   return yl + wl + kl + (wtl > vt ? wtl : vt);
 }
 
-static bool kt_in_lds(bool bf16, int d, int mp, int conv_ksteps, int C) {
-  return lds_bytes(bf16, d, mp, conv_ksteps, C, true, 4) <= kLdsLimit;
+static int split_tiles_host(int d) { return std::min(8, 16384 / (32 * d)); }
+
+struct OutShape {
+  KtPlace kt;
+  int nw;
+  size_t lds;
+  bool ypre;  // online softmax (NT = 0): Y^T staged per head by output_ystage_kernel
+};
+
+// Kernel shape for a problem. m <= 64 with the usual conv width (k-steps 4) and Kt in LDS
+// runs the register-resident softmax, whose blocks merge the context states and form Y
+// themselves (cheap at that size). Every other shape runs the online softmax over
+// landmark tiles on Y^T staged once per head. Waves per block: those shapes usually fill
+// a CU's LDS with one block. Where Kt fits beside Y^T the block takes 8 waves and
+// 256-token steps if the larger V tile still fits (and registers allow two waves per
+// SIMD: bf16, d <= 64). Where it does not fit, bf16 shapes hold Kt split (hi plane in
+// LDS, lo plane in registers) in a 4-wave block, whose one wave per SIMD has the whole
+// register file; fp32 shapes read Kt from L2.
+static OutShape out_shape(bool bf16, int d, int mp, int ks, int C) {
+  if (ks == 4 && mp <= 64 && lds_bytes(bf16, d, mp, ks, C, KtPlace::kLds, 4, false) <= kLdsLimit)
+    return {KtPlace::kLds, 4, lds_bytes(bf16, d, mp, ks, C, KtPlace::kLds, 4, false), false};
+  auto lds = [&](KtPlace kt, int nw) { return lds_bytes(bf16, d, mp, ks, C, kt, nw, true); };
+  if (lds(KtPlace::kLds, 4) <= kLdsLimit) {
+    int nw = 4;
+    if (bf16 && mp > 64 && 2 * lds(KtPlace::kLds, 4) > kLdsLimit && lds(KtPlace::kLds, 8) <= kLdsLimit)
+      nw = 8;
+    return {KtPlace::kLds, nw, lds(KtPlace::kLds, nw), true};
+  }
+  if (bf16 && mp > 64 && mp / 32 <= split_tiles_host(d) &&
+      lds(KtPlace::kSplit, 4) <= kLdsLimit)
+    return {KtPlace::kSplit, 4, lds(KtPlace::kSplit, 4), true};
+  int nw = 4;
+  if (bf16 && mp > 64 && 2 * lds(KtPlace::kL2, 4) > kLdsLimit && lds(KtPlace::kL2, 8) <= kLdsLimit)
+    nw = 8;
+  return {KtPlace::kL2, nw, lds(KtPlace::kL2, nw), true};
 }
 
-// Waves per block. The online-softmax shapes (m > 64) usually fill a CU's LDS with one
-// 4-wave block, leaving one wave per SIMD to hide every load and product latency; where
-// the larger V tile of an 8-wave block still fits (and its registers allow two waves per
-// SIMD: bf16, d <= 64) the block takes 8 waves and 256-token steps.
-static int waves_per_block(bool bf16, int d, int mp, int conv_ksteps, int C) {
-  if (!bf16 || mp <= 64) return 4;
-  const bool kt = kt_in_lds(bf16, d, mp, conv_ksteps, C);
-  if (2 * lds_bytes(bf16, d, mp, conv_ksteps, C, kt, 4) <= kLdsLimit) return 4;
-  return lds_bytes(bf16, d, mp, conv_ksteps, C, kt, 8) <= kLdsLimit ? 8 : 4;
+bool output_stages_y(bool bf16, int d, int mp, int conv_ksteps, int C) {
+  return out_shape(bf16, d, mp, conv_ksteps, C).ypre;
 }
 
 size_t output_lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C) {
-  return lds_bytes(bf16, d, mp, conv_ksteps, C, kt_in_lds(bf16, d, mp, conv_ksteps, C),
-                   waves_per_block(bf16, d, mp, conv_ksteps, C));
+  return out_shape(bf16, d, mp, conv_ksteps, C).lds;
 }
 
 int output_step_tokens(bool bf16, int d, int mp, int conv_ksteps, int C) {
-  return 32 * waves_per_block(bf16, d, mp, conv_ksteps, C);
+  return 32 * out_shape(bf16, d, mp, conv_ksteps, C).nw;
 }
 
 // Kernel variant for a shape: register-resident softmax for m <= 64 with the usual
 // conv width (k-steps 4), online softmax otherwise.
 template <typename Tin, int D, int KS>
-static const void* pick_kernel(const OutArgs& a, bool kt_lds, int nw) {
+static const void* pick_kernel(const OutArgs& a, const OutShape& sh) {
+  const bool kt_lds = sh.kt == KtPlace::kLds;
   if constexpr (KS == 4) {
-    if (a.mp <= 64 && kt_lds) {
+    if (!sh.ypre) {  // register-resident softmax: mp <= 64, Kt in LDS
       const bool full = a.m == a.mp;
       if (a.mp == 32)
-        return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true, 4>)
-                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false, 4>);
-      return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true, 4>)
-                  : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4>);
+        return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true, 4, false>)
+                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false, 4, false>);
+      return full ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true, 4, false>)
+                  : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4, false>);
     }
   }
   if constexpr (!Input<Tin>::kSplit) {
-    if (nw == 8)
-      return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8>)
-                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8>);
+    if (sh.kt == KtPlace::kSplit)
+      return reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4, true>);
+    if (sh.nw == 8)
+      return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8, false>)
+                    : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8, false>);
   }
-  return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 4>)
-                : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4>);
+  return kt_lds ? reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 4, false>)
+                : reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4, false>);
 }
 
 template <typename Tin, int D, int KS>
@@ -651,10 +836,10 @@ static int blocks_per_cu_t(int mp, int m, int C, size_t lds) {
   a.mp = mp;
   a.m = m;
   a.C = C;
-  const int nw = waves_per_block(kBf16, D, mp, KS, C);
-  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, mp, KS, C), nw);
+  const OutShape sh = out_shape(kBf16, D, mp, KS, C);
+  const void* fn = pick_kernel<Tin, D, KS>(a, sh);
   int nb = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * nw, lds) != hipSuccess) {
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, 64 * sh.nw, lds) != hipSuccess) {
     (void)hipGetLastError();
     return 0;
   }
@@ -682,11 +867,17 @@ int output_blocks_per_cu(bool bf16, int d, int ks, int mp, int m, int C, size_t 
 template <typename Tin, int D, int KS>
 static hipError_t launch_t(const OutArgs& a, hipStream_t s) {
   constexpr bool kBf16 = !Input<Tin>::kSplit;
-  const size_t lds = output_lds_bytes(kBf16, D, a.mp, KS, a.C);
-  const int nw = waves_per_block(kBf16, D, a.mp, KS, a.C);
-  const void* fn = pick_kernel<Tin, D, KS>(a, kt_in_lds(kBf16, D, a.mp, KS, a.C), nw);
+  const OutShape sh = out_shape(kBf16, D, a.mp, KS, a.C);
+  const void* fn = pick_kernel<Tin, D, KS>(a, sh);
   void* args[] = {const_cast<OutArgs*>(&a)};
-  return hipLaunchKernel(fn, dim3(a.BH * a.G), dim3(64 * nw), args, lds, s);
+  if (sh.ypre) {
+    if (a.C > kMaxChunks || a.mp > 256) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(output_ystage_kernel<D>, dim3(a.BH * (D / 32)), dim3(64 * (a.mp / 32)), 0,
+                       s, a);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipLaunchKernel(fn, dim3(a.BH * a.G), dim3(64 * sh.nw), args, sh.lds, s);
 }
 
 template <typename Tin, int D>
@@ -709,19 +900,20 @@ hipError_t launch_output(bool bf16, int d, int ks, const OutArgs& a, hipStream_t
 
 template <typename Tin, int D, int KS>
 static hipError_t attr_t(size_t bytes) {
-  const void* fns[8] = {
-      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 4>),
-      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4>)};
+  const void* fns[9] = {
+      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 4, false>),
+      reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4, false>)};
   int nf = 2;
   if constexpr (KS == 4) {
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true, 4>);
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false, 4>);
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true, 4>);
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, true, 4, false>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 1, false, 4, false>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, true, 4, false>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 2, false, 4, false>);
   }
   if constexpr (!Input<Tin>::kSplit) {
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8>);
-    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, true, 0, false, 8, false>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 8, false>);
+    fns[nf++] = reinterpret_cast<const void*>(&output_kernel<Tin, D, KS, false, 0, false, 4, true>);
   }
   for (int i = 0; i < nf; ++i) {
     const hipError_t e =

@@ -76,7 +76,7 @@ bool uneven_chunks(int BH, int C, int npinv, int ncu, int slots_per_cu) {
 
 // Byte offsets of the workspace's sub-buffers (256-byte aligned).
 struct WsLayout {
-  size_t qt, kt, qhl, khl, as, z, pl, own, apart, zhl, pw, pml, w, y;
+  size_t qt, kt, qhl, khl, as, z, pl, own, apart, zhl, pw, pml, w, y, yt;
 };
 
 struct nys_attn_plan {
@@ -182,6 +182,7 @@ static nys_status plan_init(nys_attn_plan* p, int B, int H, int n, int d, int m,
   p->chunk = (int)round_up(std::max<long long>(step, ((long long)n + nc - 1) / nc), step);
   p->chunk = (int)std::min<long long>(p->chunk, round_up(n, step));
   p->C = ceil_div(n, p->chunk);
+  if (p->C > nys::kMaxChunks) return fail(NYS_E_UNSUPPORTED, "too many context chunks");
   c.chunk = p->chunk; c.C = p->C;
   const size_t out_lds = nys::output_lds_bytes(bf16, d, p->mp, p->ks, p->C);
   if (out_lds > max_lds) return fail(NYS_E_UNSUPPORTED, "shape needs more LDS than the device offers");
@@ -229,6 +230,7 @@ static nys_status plan_init(nys_attn_plan* p, int B, int H, int n, int d, int m,
   L.apart = take(p->mp > 64 ? BHs * (mp / 32) * (mp + 1) * 4 : 0);
   L.zhl = take(BHs * 2 * P * 2);
   L.pw = take(BHs * p->C * mp * dd * 4); L.pml = take(BHs * p->C * 2 * mp * 4);
+  L.yt = take(nys::output_stages_y(bf16, d, p->mp, p->ks, p->C) ? BHs * 2 * dd * (mp + 8) * 2 : 0);
   L.w = take(debug_taps ? BHs * mp * dd * 4 : 0);
   L.y = take(debug_taps ? BHs * mp * dd * 4 : 0);
   p->ws_bytes = off;
@@ -277,6 +279,7 @@ static void plan_bind(nys_attn_plan* p, char* ws) {
   c.part_w = F(L.pw); c.part_ml = F(L.pml);
   nys::OutArgs& o = p->out;
   o.kt = F(L.kt); o.kt_hl = U(L.khl); o.z_hl = U(L.zhl); o.part_w = F(L.pw); o.part_ml = F(L.pml);
+  o.yt = U(L.yt);
   o.w_tap = p->debug_taps ? F(L.w) : nullptr;  // enabled per call (debug forwards only)
   o.y_tap = p->debug_taps ? F(L.y) : nullptr;
 }
