@@ -39,50 +39,44 @@ namespace nys {
 constexpr int kBwdThreads = 256;  // landmark-sized kernels and the final pass
 
 // ------------------------------------------------------------------ fp32 block products
-// C[M][N] = alpha op(A) op(B) + beta C. op(A) is A stored [M][K] (lda) or, with TA, A
-// stored [K][M]; op(B) is B stored [K][N] (ldb) or, with TB, B stored [N][K]. Each
-// thread owns 4 x 4 outputs and reads its operands as 16-byte runs, four k at a time:
-// M, N, K multiples of 4, lda and ldb multiples of 4, A and B 16-byte aligned. C must
-// not alias A or B; no barrier inside.
+// C[M][N] = alpha op(A) op(B) + beta C on fp32 MFMA (v_mfma_f32_32x32x2_f32, products
+// and sums in fp32). op(A) is A stored [M][K] (lda) or, with TA, A stored [K][M]; op(B)
+// is B stored [K][N] (ldb) or, with TB, B stored [N][K]. Each wave forms whole 32 x 32
+// output tiles; the two k-slots of the MFMA take the two halves of the k range, so a lane
+// reads four consecutive k of a k-contiguous operand as one 16-byte load. M and N
+// multiples of 32, K a multiple of 8, lda and ldb multiples of 4, A and B 16-byte
+// aligned. C must not alias A or B; no barrier inside.
 template <bool TA, bool TB>
 __device__ void blk_mm(float* C, int ldc, const float* A, int lda, const float* B, int ldb,
                        int M, int N, int K, float alpha, float beta) {
-  const int nb = N >> 2, total = (M >> 2) * nb;
-  for (int blk = threadIdx.x; blk < total; blk += blockDim.x) {
-    const int i0 = (blk / nb) * 4, j0 = (blk % nb) * 4;
-    float acc[4][4];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int r32 = lane & 31, kb = (lane >> 5) * (K / 2);
+  const int tn = N / 32, tiles = (M / 32) * tn;
+  for (int t = wave; t < tiles; t += nw) {
+    const int i0 = 32 * (t / tn), j0 = 32 * (t % tn);
+    f32x16 acc = zero16();
+    for (int s = kb; s < kb + K / 2; s += 4) {
+      f32x4 av, bv;
+      if (TA) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+        for (int q = 0; q < 4; ++q) av[q] = A[(s + q) * lda + i0 + r32];
+      } else {
+        av = *reinterpret_cast<const f32x4*>(A + (i0 + r32) * lda + s);
+      }
+      if (TB) {
+        bv = *reinterpret_cast<const f32x4*>(B + (j0 + r32) * ldb + s);
+      } else {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-    for (int k = 0; k < K; k += 4) {
-      float av[4][4], bv[4][4];  // av[r][kk] = op(A)[i0 + r][k + kk], bv[kk][c] = op(B)[k + kk][j0 + c]
-#pragma unroll
-      for (int x = 0; x < 4; ++x) {
-        const f32x4 ra = TA ? *reinterpret_cast<const f32x4*>(A + (k + x) * lda + i0)
-                            : *reinterpret_cast<const f32x4*>(A + (i0 + x) * lda + k);
-        const f32x4 rb = TB ? *reinterpret_cast<const f32x4*>(B + (j0 + x) * ldb + k)
-                            : *reinterpret_cast<const f32x4*>(B + (k + x) * ldb + j0);
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          if (TA) av[y][x] = ra[y]; else av[x][y] = ra[y];
-          if (TB) bv[y][x] = rb[y]; else bv[x][y] = rb[y];
-        }
+        for (int q = 0; q < 4; ++q) bv[q] = B[(s + q) * ldb + j0 + r32];
       }
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int c = 0; c < 4; ++c) acc[r][c] += av[r][kk] * bv[kk][c];
+      for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av[q], bv[q], acc, 0, 0, 0);
     }
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float* p = C + (i0 + r) * ldc + j0 + c;
-        *p = beta != 0.f ? alpha * acc[r][c] + beta * *p : alpha * acc[r][c];
-      }
+    for (int rr = 0; rr < 16; ++rr) {
+      float* p = C + acc_row(i0, rr, lane) * ldc + j0 + r32;
+      *p = beta != 0.f ? alpha * acc[rr] + beta * *p : alpha * acc[rr];
+    }
   }
 }
 
@@ -379,16 +373,19 @@ template <int D, int MP, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
   constexpr int T = 32 * NW, LT = MP / 32, FT = D / 32;
   constexpr int NRED = 2 * LT * FT, RPW = (NRED + NW - 1) / NW;
+  // LDS rows padded by 16 bytes: the transposed tile stores and the 16-byte row reads of
+  // 32 lanes then spread over the banks instead of meeting in one
+  constexpr int TP = T + 8, DP = D + 8, MPP = MP + 8;
   extern __shared__ __align__(16) char lds[];
-  uint16_t* ft_hi = reinterpret_cast<uint16_t*>(lds);  // F^T   [MP][T]
-  uint16_t* ft_lo = ft_hi + MP * T;
-  uint16_t* st_hi = ft_lo + MP * T;                     // dSF^T [MP][T]
-  uint16_t* st_lo = st_hi + MP * T;
-  uint16_t* qR = st_lo + MP * T;                        // Q     [T][D] (step's tokens)
-  uint16_t* oR = qR + T * D;                            // dO    [T][D]
+  uint16_t* ft_hi = reinterpret_cast<uint16_t*>(lds);  // F^T   [MP][TP]
+  uint16_t* ft_lo = ft_hi + MP * TP;
+  uint16_t* st_hi = ft_lo + MP * TP;                    // dSF^T [MP][TP]
+  uint16_t* st_lo = st_hi + MP * TP;
+  uint16_t* qR = st_lo + MP * TP;                       // Q     [T][DP] (step's tokens)
+  uint16_t* oR = qR + T * DP;                           // dO    [T][DP]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
-  uint16_t* ds_hi = oR + T * D + wave * 2 * 32 * MP;    // dSF   [32][MP] per wave
-  uint16_t* ds_lo = ds_hi + 32 * MP;
+  uint16_t* ds_hi = oR + T * DP + wave * 2 * 32 * MPP;  // dSF   [32][MPP] per wave
+  uint16_t* ds_lo = ds_hi + 32 * MPP;
   int bh, c;
   xcd_map(blockIdx.x, a.BH, a.C, bh, c);
   const int m = a.m, L = valid_length(a.lengths, bh, a.H, a.n, a.m);
@@ -419,8 +416,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
         qv = *reinterpret_cast<const u32x4*>(q + (size_t)tok * D + f8);
         ov = *reinterpret_cast<const u32x4*>(dO + (size_t)tok * D + f8);
       }
-      *reinterpret_cast<u32x4*>(qR + (32 * wave + i) * D + f8) = qv;
-      *reinterpret_cast<u32x4*>(oR + (32 * wave + i) * D + f8) = ov;
+      *reinterpret_cast<u32x4*>(qR + (32 * wave + i) * DP + f8) = qv;
+      *reinterpret_cast<u32x4*>(oR + (32 * wave + i) * DP + f8) = ov;
     }
     // S = Q Kt^T and dF = dO Y^T for 32 tokens: lane = landmark, registers = tokens
     const int trow = min(tw + r32, L - 1);
@@ -466,15 +463,15 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
     }
 #pragma unroll
     for (int lt = 0; lt < LT; ++lt) {
-      store_cols_hl(ft_hi, ft_lo, T, 32 * wave, 32 * lt, sc[lt], lane);
-      store_cols_hl(st_hi, st_lo, T, 32 * wave, 32 * lt, df[lt], lane);
-      store_rows_hl(ds_hi, ds_lo, MP, 0, 32 * lt, df[lt], lane);
+      store_cols_hl(ft_hi, ft_lo, TP, 32 * wave, 32 * lt, sc[lt], lane);
+      store_cols_hl(st_hi, st_lo, TP, 32 * wave, 32 * lt, df[lt], lane);
+      store_rows_hl(ds_hi, ds_lo, MPP, 0, 32 * lt, df[lt], lane);
     }
     // dQ (first term) = s dSF Kt for the wave's 32 tokens
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
       const size_t br = (size_t)(32 * ft + r32) * MP;
-      const f32x16 acc = mma_rows<MP, true, true>(zero16(), ds_hi + r32 * MP, ds_lo + r32 * MP,
+      const f32x16 acc = mma_rows<MP, true, true>(zero16(), ds_hi + r32 * MPP, ds_lo + r32 * MPP,
                                                   kT_hi + br, kT_lo + br, h);
 #pragma unroll
       for (int rr = 0; rr < 16; ++rr) {
@@ -489,9 +486,9 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
       const int ti = wave + NW * u;
       if (ti < NRED) {
         const int which = ti / (LT * FT), rem = ti % (LT * FT), at = rem / FT, bt = rem % FT;
-        const uint16_t* ah = (which == 0 ? ft_hi : st_hi) + (32 * at + r32) * T;
-        const uint16_t* alo = (which == 0 ? ft_lo : st_lo) + (32 * at + r32) * T;
-        red[u] = mma_rows_btr<T, true>(red[u], ah, alo, which == 0 ? oR : qR, D, 32 * bt, lane);
+        const uint16_t* ah = (which == 0 ? ft_hi : st_hi) + (32 * at + r32) * TP;
+        const uint16_t* alo = (which == 0 ? ft_lo : st_lo) + (32 * at + r32) * TP;
+        red[u] = mma_rows_btr<T, true>(red[u], ah, alo, which == 0 ? oR : qR, DP, 32 * bt, lane);
       }
     }
     __syncthreads();
@@ -661,11 +658,12 @@ template <int D, int MP, int NW>
 __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
   constexpr int T = 32 * NW, LT = MP / 32, FT = D / 32;
   constexpr int NRED = LT * FT, RPW = (NRED + NW - 1) / NW;
+  constexpr int TP = T + 8, DP = D + 8;  // LDS rows padded by 16 bytes (bank spread)
   extern __shared__ __align__(16) char lds[];
-  uint16_t* sT_hi = reinterpret_cast<uint16_t*>(lds);  // dSB [MP][T] (landmark rows)
-  uint16_t* sT_lo = sT_hi + MP * T;
-  uint16_t* kR = sT_lo + MP * T;                        // K   [T][D] (step's tokens)
-  float* smx = reinterpret_cast<float*>(kR + T * D);   // per landmark: max, 1/sum, D_B
+  uint16_t* sT_hi = reinterpret_cast<uint16_t*>(lds);  // dSB [MP][TP] (landmark rows)
+  uint16_t* sT_lo = sT_hi + MP * TP;
+  uint16_t* kR = sT_lo + MP * TP;                       // K   [T][DP] (step's tokens)
+  float* smx = reinterpret_cast<float*>(kR + T * DP);  // per landmark: max, 1/sum, D_B
   float* sinv = smx + MP;
   float* sdb = sinv + MP;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5, r32 = lane & 31;
@@ -706,7 +704,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
       const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, t = tw + i;
       u32x4 kv{0u, 0u, 0u, 0u};
       if (t < te) kv = *reinterpret_cast<const u32x4*>(kk + (size_t)t * D + f8);
-      *reinterpret_cast<u32x4*>(kR + (32 * wave + i) * D + f8) = kv;
+      *reinterpret_cast<u32x4*>(kR + (32 * wave + i) * DP + f8) = kv;
     }
     const int trow = min(tok, L - 1);
     f32x16 sb[LT], db[LT];  // B and dSB: landmark rows, this lane's token
@@ -728,7 +726,7 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
         sb[lt][rr] = b;
         db[lt][rr] = v ? b * (db[lt][rr] - sdb[j]) : 0.f;
       }
-      store_rows_hl(sT_hi, sT_lo, T, 32 * lt, 32 * wave, db[lt], lane);
+      store_rows_hl(sT_hi, sT_lo, TP, 32 * lt, 32 * wave, db[lt], lane);
     }
     // B operands from the registers: k-step s covers landmarks 16 s .. 16 s + 15, held in
     // registers 8 (s % 2) .. 8 (s % 2) + 7 of tile s / 2
@@ -777,8 +775,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
       const int ti = wave + NW * u;
       if (ti < NRED) {
         const int at = ti / FT, bt = ti % FT;
-        red[u] = mma_rows_btr<T, true>(red[u], sT_hi + (32 * at + r32) * T,
-                                       sT_lo + (32 * at + r32) * T, kR, D, 32 * bt, lane);
+        red[u] = mma_rows_btr<T, true>(red[u], sT_hi + (32 * at + r32) * TP,
+                                       sT_lo + (32 * at + r32) * TP, kR, DP, 32 * bt, lane);
       }
     }
     __syncthreads();
@@ -849,38 +847,48 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   const float* dvp = a.dv_part + (size_t)bh * a.n * D;
   uint16_t* dq = a.dq + (size_t)bh * a.n * D;
   uint16_t* dv = a.dv + (size_t)bh * a.n * D;
-  auto rd = [](const uint16_t* p) { return __uint_as_float((uint32_t)*p << 16); };
-  // thread = (feature f, token i): dQ and dV
-  constexpr int NE = kFinTok * D / kBwdThreads, NB = 8;
-  for (int u0 = 0; u0 < NE; u0 += NB) {
-    float pq[NB], pv[NB];
+  // thread = (token i, features f0 .. f0 + 7): dQ and dV, 16-byte loads and stores; the
+  // transposed conv reads one 16-byte dO run per tap
+  constexpr int NE8 = kFinTok * (D / 8) / kBwdThreads;
+  auto cvt8 = [](const float* x) {
+    u32x4 r;
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int e = threadIdx.x + kBwdThreads * (u0 + u), i = e / D, f = e % D, t = t0 + i;
-      pq[u] = t < tv ? dqp[(size_t)t * D + f] : 0.f;
-      pv[u] = t < tv ? dvp[(size_t)t * D + f] : 0.f;
-    }
+    for (int e = 0; e < 4; ++e) r[e] = __builtin_bit_cast(uint32_t, bf16_rne2(x[2 * e], x[2 * e + 1]));
+    return r;
+  };
+#pragma unroll 2
+  for (int u = 0; u < NE8; ++u) {
+    const int e = threadIdx.x + kBwdThreads * u, i = e / (D / 8), f0 = (e % (D / 8)) * 8;
+    const int t = t0 + i;
+    if (t >= t1) continue;
+    u32x4 oq{0u, 0u, 0u, 0u}, ov{0u, 0u, 0u, 0u};
+    if (t < tv) {
+      const f32x4 q0 = *reinterpret_cast<const f32x4*>(dqp + (size_t)t * D + f0);
+      const f32x4 q1 = *reinterpret_cast<const f32x4*>(dqp + (size_t)t * D + f0 + 4);
+      const f32x4 v0 = *reinterpret_cast<const f32x4*>(dvp + (size_t)t * D + f0);
+      const f32x4 v1 = *reinterpret_cast<const f32x4*>(dvp + (size_t)t * D + f0 + 4);
+      const float* sqr = sq + srow[i] + f0;
+      float xq[8], acc[8];
 #pragma unroll
-    for (int u = 0; u < NB; ++u) {
-      const int e = threadIdx.x + kBwdThreads * (u0 + u), i = e / D, f = e % D, t = t0 + i;
-      if (t >= t1) continue;
-      uint16_t oq = 0, ov = 0;
-      if (t < tv) {
-        oq = __builtin_bit_cast(uint16_t, bf16_rne(pq[u] + sq[srow[i] + f]));
-        // d out[t'] / d V[t] = w[k] for t' = t - k + half; eight independent partial sums
-        const uint16_t* op = so + (i + 2 * half) * D + f;
-        float ps[8] = {pv[u], 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        int k = 0;
-        for (; k + 8 <= W; k += 8)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) ps[j] += sw[k + j] * rd(op - (k + j) * D);
-        for (; k < W; ++k) ps[0] += sw[k] * rd(op - k * D);
-        const float acc = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
-        ov = __builtin_bit_cast(uint16_t, bf16_rne(acc));
+      for (int q = 0; q < 4; ++q) {
+        xq[q] = q0[q] + sqr[q];
+        xq[4 + q] = q1[q] + sqr[4 + q];
+        acc[q] = v0[q];
+        acc[4 + q] = v1[q];
       }
-      dq[(size_t)t * D + f] = oq;
-      dv[(size_t)t * D + f] = ov;
+      // d out[t'] / d V[t] = w[k] for t' = t - k + half: staged row i + 2 half - k
+      const uint16_t* op = so + (i + 2 * half) * D + f0;
+      for (int k = 0; k < W; ++k) {
+        const bf16x8 r = ld8(op - k * D);
+        const float wk = sw[k];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc[q] += wk * (float)r[q];  // exact widening
+      }
+      oq = cvt8(xq);
+      ov = cvt8(acc);
     }
+    *reinterpret_cast<u32x4*>(dq + (size_t)t * D + f0) = oq;
+    *reinterpret_cast<u32x4*>(dv + (size_t)t * D + f0) = ov;
   }
   // dw[k] = sum over rows i < tv - t0 of G[i][i + k], G = dO_tile V_ext^T on MFMA (wave w:
   // rows 32 w .. 32 w + 31, the column tiles that meet the band 0 <= j - i < W)
@@ -932,8 +940,9 @@ struct BwdShape {
   static constexpr size_t l1 = (5 * MP * (MP + 4) + 2 * MP * (D + 4)) * 4;
   static constexpr size_t l2a = 9 * MP * (MP + 4), l2b = 3 * MP * (D + 4) + 2 * MP * (MP + 4);
   static constexpr size_t l2 = (l2a > l2b ? l2a : l2b) * 4;
-  static constexpr size_t p1 = ((size_t)4 * MP * T + 2 * D * T + NW * 2 * 32 * MP) * 2;
-  static constexpr size_t p2 = ((size_t)2 * MP * T + (size_t)T * D) * 2 + 3 * MP * 4;
+  static constexpr size_t p1 =
+      ((size_t)4 * MP * (T + 8) + 2 * (D + 8) * T + NW * 2 * 32 * (MP + 8)) * 2;
+  static constexpr size_t p2 = ((size_t)2 * MP * (T + 8) + (size_t)T * (D + 8)) * 2 + 3 * MP * 4;
   static constexpr size_t fin =
       (size_t)2 * kFinRows * D * 2 + ((size_t)MP * D + 65 + 4 * 65 + kFinTok) * 4;
 };
