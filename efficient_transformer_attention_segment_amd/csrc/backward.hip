@@ -655,7 +655,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_land_bwd_kernel(BwdArgs a) {
 // landmarks in that register order (kslot_perm). Only dSB^T goes through LDS, for the
 // reduction over tokens.
 template <int D, int MP, int NW>
-__global__ __launch_bounds__(64 * NW) void bwd_pass2_kernel(BwdArgs a) {
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void bwd_pass2_kernel(BwdArgs a) {
   constexpr int T = 32 * NW, LT = MP / 32, FT = D / 32;
   constexpr int NRED = LT * FT, RPW = (NRED + NW - 1) / NW;
   constexpr int TP = T + 8, DP = D + 8;  // LDS rows padded by 16 bytes (bank spread)
