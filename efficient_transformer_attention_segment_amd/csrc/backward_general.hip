@@ -42,6 +42,11 @@ struct GemmArgs {
   int mask;
   const int* lengths;
   int H, n, m;
+  // split over K (nsplit > 1): block z covers batch entry z % nbatch and k range
+  // [kchunk (z / nbatch), + kchunk), writing its raw partial product to part
+  // [nsplit][nbatch][M][N]; split_reduce_kernel then forms C
+  float* part;
+  int nsplit, kchunk, nbatch;
 };
 
 template <typename T>
@@ -54,17 +59,22 @@ __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p) {
 }
 
 constexpr int kGT = 64, kGK = 16, kGS = kGT + 4;
+constexpr int kSplitBlocks = 1024, kSplitMin = 512;  // split-K targets (see Runner::gemm)
 
 template <typename TAe, typename TBe, bool TA, bool TB>
 __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) float As[kGK][kGS];
   __shared__ __align__(16) float Bs[kGK][kGS];
-  const int b = blockIdx.z, tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int split = g.nsplit > 1 ? (int)blockIdx.z / g.nbatch : 0;
+  const int b = g.nsplit > 1 ? (int)blockIdx.z % g.nbatch : (int)blockIdx.z;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const int row0 = blockIdx.y * kGT, col0 = blockIdx.x * kGT;
   const int L = valid_length(g.lengths, b, g.H, g.n, g.m);
   const int lm = (g.mask & 1) ? min(g.M, L) : g.M;
   const int ln = (g.mask & 2) ? min(g.N, L) : g.N;
-  const int lk = (g.mask & 4) ? min(g.K, L) : g.K;
+  const int lk0 = (g.mask & 4) ? min(g.K, L) : g.K;
+  const int kbeg = split * g.kchunk;
+  const int lk = g.nsplit > 1 ? min(lk0, kbeg + g.kchunk) : lk0;
   const TAe* A = static_cast<const TAe*>(g.A) + (size_t)b * g.sA;
   const TBe* B = static_cast<const TBe*>(g.B) + (size_t)b * g.sB;
   float acc[4][4];
@@ -72,7 +82,7 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  for (int k0 = 0; k0 < lk; k0 += kGK) {
+  for (int k0 = g.nsplit > 1 ? kbeg : 0; k0 < lk; k0 += kGK) {
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int e = tid + 256 * u;
@@ -101,6 +111,20 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     }
     __syncthreads();
   }
+  if (g.nsplit > 1) {  // raw partial; the reduction applies the epilogue
+    float* P = g.part + ((size_t)split * g.nbatch + b) * g.M * g.N;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = row0 + 4 * ty + r;
+      if (i >= g.M) continue;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int j = col0 + 4 * tx + c;
+        if (j < g.N) P[(size_t)i * g.N + j] = acc[r][c];
+      }
+    }
+    return;
+  }
   float* C = g.C + (size_t)b * g.sC;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
@@ -118,6 +142,26 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
       *p = v;
     }
   }
+}
+
+// C = alpha sum_s part[s] + beta C + diag I for a product split over K, the splits added
+// in a fixed order (one thread per element of C).
+__global__ __launch_bounds__(256) void split_reduce_kernel(GemmArgs g) {
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long mn = (long long)g.M * g.N;
+  if (e >= mn * g.nbatch) return;
+  const int b = (int)(e / mn), r = (int)(e % mn), i = r / g.N, j = r % g.N;
+  const int L = valid_length(g.lengths, b, g.H, g.n, g.m);
+  const int lm = (g.mask & 1) ? min(g.M, L) : g.M;
+  const int ln = (g.mask & 2) ? min(g.N, L) : g.N;
+  float v = 0.f;
+  for (int sp = 0; sp < g.nsplit; ++sp) v += g.part[((size_t)sp * g.nbatch + b) * mn + r];
+  float* p = g.C + (size_t)b * g.sC + (size_t)i * g.ldc + j;
+  v *= g.alpha;
+  if (g.beta != 0.f) v += g.beta * *p;
+  if (i == j && i < g.diag_n) v += g.diag;
+  if (i >= lm || j >= ln) v = 0.f;
+  *p = v;
 }
 
 // ------------------------------------------------------------------ row kernels
@@ -391,10 +435,29 @@ struct Runner {
             float diag = 0.f, int diag_n = 0) {
     if (err != hipSuccess) return;
     GemmArgs g{A, B, C, sA, sB, sC, lda, ldb, ldc, M, N, K, alpha, beta, diag, diag_n, mask,
-               a.lengths, a.H, a.n, a.m};
-    const dim3 grid((N + kGT - 1) / kGT, (M + kGT - 1) / kGT, a.BH);
+               a.lengths, a.H, a.n, a.m, nullptr, 1, 0, a.BH};
+    // products over the token dimension have few output tiles per head and a long k loop:
+    // split k so that about kSplitBlocks blocks share it (at least kSplitMin tokens each)
+    const int tiles = ((N + kGT - 1) / kGT) * ((M + kGT - 1) / kGT);
+    if ((mask & 4) && a.nsplit > 1 && (long long)M * N <= (long long)a.mp * a.d) {
+      const int want = (kSplitBlocks + tiles * a.BH - 1) / (tiles * a.BH);
+      const int sp = std::min({a.nsplit, want, std::max(1, K / kSplitMin)});
+      if (sp > 1) {
+        g.nsplit = sp;
+        g.kchunk = (K + sp - 1) / sp;
+        g.kchunk = (g.kchunk + kGK - 1) / kGK * kGK;
+        g.part = a.ksplit;
+      }
+    }
+    const dim3 grid((N + kGT - 1) / kGT, (M + kGT - 1) / kGT, a.BH * g.nsplit);
     hipLaunchKernelGGL((gemm_kernel<TAe, TBe, TA, TB>), grid, dim3(256), 0, s, g);
     err = hipGetLastError();
+    if (err == hipSuccess && g.nsplit > 1) {
+      const long long total = (long long)a.BH * M * N;
+      hipLaunchKernelGGL(split_reduce_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0,
+                         s, g);
+      err = hipGetLastError();
+    }
   }
   void softmax(float* X, int rows, int cols, int rmode, int cmode, float scale) {
     if (err != hipSuccess) return;

@@ -151,6 +151,8 @@ struct GenBwdArgs {
   float* alpha;
   int* amax;
   float* dw_part;
+  float* ksplit;  // [nsplit][BH][mp][d] partial products of the token-dimension products
+  int nsplit;     // most k-splits ksplit holds (1: no split)
   int B, H, BH, n, d, m, mp, W, iters, dw_chunk;
   float scale;
   bool bf16;

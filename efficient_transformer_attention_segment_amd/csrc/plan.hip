@@ -663,6 +663,9 @@ static size_t carve_general(nys_attn_plan* p, char* base) {
   g.alpha = take(BHs * 4);
   g.amax = reinterpret_cast<int*>(take(BHs * 2));
   g.dw_part = take(BHs * nch * p->W);
+  // split-K scratch: up to 32 splits of at least 512 tokens, while B*H*splits fits a grid z
+  g.nsplit = (int)std::max<size_t>(1, std::min<size_t>({32, n / 512, 65535 / std::max<size_t>(BHs, 1)}));
+  g.ksplit = take(g.nsplit > 1 ? (size_t)g.nsplit * BHs * mp * dd : 0);
   g.B = p->B; g.H = p->H; g.BH = p->BH; g.n = p->n; g.d = p->d; g.m = p->m; g.mp = p->mp;
   g.W = p->W; g.iters = p->iters; g.dw_chunk = kDwChunk;
   g.scale = p->ctx.scale;
