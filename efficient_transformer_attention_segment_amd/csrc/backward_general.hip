@@ -337,6 +337,31 @@ __global__ __launch_bounds__(256) void segment_scatter_kernel(float* dX, const f
 }
 
 // dV[t] += sum_k w[h][k] dO[t - k + half] over the valid tokens (the transposed conv).
+// Eight consecutive elements of a token row as floats (bf16 bits or fp32), one or two
+// 16-byte loads; p 16-byte aligned (bf16) or 32-byte aligned (fp32).
+template <typename T>
+__device__ __forceinline__ void ld8f(const T* p, float* x) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4 u = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[2 * q] = __uint_as_float(u[q] << 16);
+      x[2 * q + 1] = __uint_as_float(u[q] & 0xffff0000u);
+    }
+  } else {
+    const f32x4 lo = *reinterpret_cast<const f32x4*>(p), hi = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      x[q] = lo[q];
+      x[4 + q] = hi[q];
+    }
+  }
+}
+
+constexpr int kMaxConvW = 65;  // widest conv the plan accepts
+
+// dV[t] += sum_k w[k] dO[t - k + half] over the valid rows (the conv's transpose); one
+// thread per eight consecutive features of a token.
 template <typename T>
 __global__ __launch_bounds__(256) void conv_transpose_kernel(float* dV, const T* dO,
                                                              const float* w, int n, int d,
@@ -345,44 +370,66 @@ __global__ __launch_bounds__(256) void conv_transpose_kernel(float* dV, const T*
   const int b = blockIdx.y;
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   const int L = valid_length(lengths, b, H, n, m);
-  if (e >= (long long)L * d) return;
-  const int t = (int)(e / d), f = (int)(e % d), half = (W - 1) / 2;
+  if (e >= (long long)L * (d / 8)) return;
+  const int t = (int)(e / (d / 8)), f0 = (int)(e % (d / 8)) * 8, half = (W - 1) / 2;
   const float* wh = w + (size_t)(b % H) * W;
-  const T* o = dO + (size_t)b * n * d;
-  float acc = 0.f;
+  const T* o = dO + (size_t)b * n * d + f0;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < W; ++k) {
     const int src = t - k + half;
-    if (src >= 0 && src < L) acc += wh[k] * ld_elem(o + (size_t)src * d + f);
+    if (src >= 0 && src < L) {
+      float x[8];
+      ld8f(o + (size_t)src * d, x);
+      const float wk = wh[k];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) acc[q] += wk * x[q];
+    }
   }
-  dV[((size_t)b * n + t) * d + f] += acc;
+  f32x4* p = reinterpret_cast<f32x4*>(dV + ((size_t)b * n + t) * d + f0);
+  p[0] += f32x4{acc[0], acc[1], acc[2], acc[3]};
+  p[1] += f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
 // Partial conv-weight gradient of one (head, token chunk): part[b][chunk][k] =
-// sum over the chunk's valid t of dO[t] . V[t + k - half] (V zero outside [0, L)).
+// sum over the chunk's valid t of dO[t] . V[t + k - half] (V zero outside [0, L)). One
+// thread per eight consecutive features of a token; the per-tap sums stay in registers.
 template <typename T>
 __global__ __launch_bounds__(256) void dw_partial_kernel(float* part, const T* dO, const T* V,
                                                          int n, int d, int W, int H, int m,
                                                          const int* lengths, int chunk,
                                                          int nchunks) {
-  __shared__ float red[4][72];
+  __shared__ float red[4][kMaxConvW + 7];
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int L = valid_length(lengths, b, H, n, m);
   const int t0 = c * chunk, t1 = min(t0 + chunk, L), half = (W - 1) / 2;
   const T* o = dO + (size_t)b * n * d;
   const T* v = V + (size_t)b * n * d;
-  float acc[72];
-  for (int k = 0; k < W; ++k) acc[k] = 0.f;
-  for (long long e = tid; e < (long long)max(0, t1 - t0) * d; e += 256) {
-    const int t = t0 + (int)(e / d), f = (int)(e % d);
-    const float go = ld_elem(o + (size_t)t * d + f);
-    for (int k = 0; k < W; ++k) {
+  float acc[kMaxConvW];
+#pragma unroll
+  for (int k = 0; k < kMaxConvW; ++k) acc[k] = 0.f;
+  for (long long e = tid; e < (long long)max(0, t1 - t0) * (d / 8); e += 256) {
+    const int t = t0 + (int)(e / (d / 8)), f0 = (int)(e % (d / 8)) * 8;
+    float go[8];
+    ld8f(o + (size_t)t * d + f0, go);
+#pragma unroll
+    for (int k = 0; k < kMaxConvW; ++k) {
       const int src = t + k - half;
-      if (src >= 0 && src < L) acc[k] += go * ld_elem(v + (size_t)src * d + f);
+      if (k < W && src >= 0 && src < L) {
+        float x[8];
+        ld8f(v + (size_t)src * d + f0, x);
+        float s8 = 0.f;
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s8 += go[q] * x[q];
+        acc[k] += s8;
+      }
     }
   }
-  for (int k = 0; k < W; ++k) {
-    const float s = wave_sum(acc[k]);
-    if ((tid & 63) == 0) red[tid >> 6][k] = s;
+#pragma unroll
+  for (int k = 0; k < kMaxConvW; ++k) {
+    if (k < W) {
+      const float s = wave_sum(acc[k]);
+      if ((tid & 63) == 0) red[tid >> 6][k] = s;
+    }
   }
   __syncthreads();
   if (tid < W)
@@ -612,7 +659,8 @@ hipError_t run(const GenBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(segment_scatter_kernel, tok, dim3(256), 0, s, a.dK, a.dKt, n, d, mp, m,
                      a.lengths, a.H);
   // conv skip: dV += conv^T(dO); dw
-  hipLaunchKernelGGL((conv_transpose_kernel<T>), tok, dim3(256), 0, s, a.dV, dO, a.conv_w, n, d,
+  const dim3 tok8((unsigned)((nd / 8 + 255) / 256), BH);
+  hipLaunchKernelGGL((conv_transpose_kernel<T>), tok8, dim3(256), 0, s, a.dV, dO, a.conv_w, n, d,
                      a.W, a.H, m, a.lengths);
   const int nch = (n + a.dw_chunk - 1) / a.dw_chunk;
   hipLaunchKernelGGL((dw_partial_kernel<T>), dim3(nch, BH), dim3(256), 0, s, a.dw_part, dO, v, n,
