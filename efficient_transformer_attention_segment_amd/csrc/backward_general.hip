@@ -27,6 +27,9 @@ namespace nys {
 // C[b] = alpha op(A[b]) op(B[b]) + beta C[b] + diag I (diagonal entries i = j < diag_n),
 // C fp32 M x N (ldc), op(A) M x K: A stored [M][K] (lda) or, with TA, [K][M]; op(B)
 // K x N: B stored [K][N] (ldb) or, with TB, [N][K]. Element types float or bf16 bits.
+// 64 x 64 output tiles per block, 32-deep k slabs staged in LDS (the next slab loaded into
+// registers meanwhile), each wave forming a 32 x 32 quarter on fp32 MFMA
+// (v_mfma_f32_32x32x2_f32).
 // Token masking (mask bits: 1 = M, 2 = N, 4 = K is a token dimension): indices at or
 // past the batch entry's valid length read as zero (those memory rows are never read)
 // and C entries in masked rows / columns are written as zero.
@@ -58,7 +61,7 @@ __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p) {
   return __uint_as_float((uint32_t)*p << 16);
 }
 
-constexpr int kGT = 64, kGK = 16, kGS = kGT + 4;
+constexpr int kGT = 64, kGK = 32, kGS = kGT + 4;
 constexpr int kSplitBlocks = 1024, kSplitMin = 512;  // split-K targets (see Runner::gemm)
 
 template <typename TAe, typename TBe, bool TA, bool TB>
@@ -67,7 +70,8 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   __shared__ __align__(16) float Bs[kGK][kGS];
   const int split = g.nsplit > 1 ? (int)blockIdx.z / g.nbatch : 0;
   const int b = g.nsplit > 1 ? (int)blockIdx.z % g.nbatch : (int)blockIdx.z;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r32 = lane & 31;
+  const int wr = wave >> 1, wc = wave & 1;  // this wave's 32 x 32 quarter of the tile
   const int row0 = blockIdx.y * kGT, col0 = blockIdx.x * kGT;
   const int L = valid_length(g.lengths, b, g.H, g.n, g.m);
   const int lm = (g.mask & 1) ? min(g.M, L) : g.M;
@@ -77,70 +81,69 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const int lk = g.nsplit > 1 ? min(lk0, kbeg + g.kchunk) : lk0;
   const TAe* A = static_cast<const TAe*>(g.A) + (size_t)b * g.sA;
   const TBe* B = static_cast<const TBe*>(g.B) + (size_t)b * g.sB;
-  float acc[4][4];
+  f32x16 acc = zero16();
+  // the next slab's elements are loaded into registers while the current one is used
+  constexpr int U = kGT * kGK / 256;
+  float ra[U], rb[U];
+  auto fetch = [&](int k0) {
 #pragma unroll
-  for (int r = 0; r < 4; ++r)
-#pragma unroll
-    for (int c = 0; c < 4; ++c) acc[r][c] = 0.f;
-  for (int k0 = g.nsplit > 1 ? kbeg : 0; k0 < lk; k0 += kGK) {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < U; ++u) {
       const int e = tid + 256 * u;
-      // A tile: 64 rows x 16 k, threads along the stored contiguous index
+      // A tile: 64 rows x kGK k, threads along the stored contiguous index
       const int ai = TA ? e % kGT : e / kGK, ak = TA ? e / kGT : e % kGK;
       const int i = row0 + ai, k = k0 + ak;
-      As[ak][ai] = (i < lm && k < lk)
-                       ? ld_elem(A + (TA ? (size_t)k * g.lda + i : (size_t)i * g.lda + k))
-                       : 0.f;
-      // B tile: 16 k x 64 columns
+      ra[u] = (i < lm && k < lk)
+                  ? ld_elem(A + (TA ? (size_t)k * g.lda + i : (size_t)i * g.lda + k))
+                  : 0.f;
+      // B tile: kGK k x 64 columns
       const int bk = TB ? e % kGK : e / kGT, bj = TB ? e / kGK : e % kGT;
-      const int j = col0 + bj, kb = k0 + bk;
-      Bs[bk][bj] = (j < ln && kb < lk)
-                       ? ld_elem(B + (TB ? (size_t)j * g.ldb + kb : (size_t)kb * g.ldb + j))
-                       : 0.f;
+      const int jj = col0 + bj, kb = k0 + bk;
+      rb[u] = (jj < ln && kb < lk)
+                  ? ld_elem(B + (TB ? (size_t)jj * g.ldb + kb : (size_t)kb * g.ldb + jj))
+                  : 0.f;
+    }
+  };
+  const int kstart = g.nsplit > 1 ? kbeg : 0;
+  if (kstart < lk) fetch(kstart);
+  for (int k0 = kstart; k0 < lk; k0 += kGK) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int e = tid + 256 * u;
+      As[TA ? e / kGT : e % kGK][TA ? e % kGT : e / kGK] = ra[u];
+      Bs[TB ? e % kGK : e / kGT][TB ? e / kGK : e % kGT] = rb[u];
     }
     __syncthreads();
+    if (k0 + kGK < lk) fetch(k0 + kGK);
+    // fp32 MFMA over the slab: lane half h takes k-slot h of each pair of k
 #pragma unroll
-    for (int kk = 0; kk < kGK; ++kk) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(&As[kk][4 * ty]);
-      const f32x4 bv = *reinterpret_cast<const f32x4*>(&Bs[kk][4 * tx]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 4; ++c) acc[r][c] += av[r] * bv[c];
+    for (int kk = 0; kk < kGK; kk += 2) {
+      const float av = As[kk + (lane >> 5)][32 * wr + r32];
+      const float bv = Bs[kk + (lane >> 5)][32 * wc + r32];
+      acc = __builtin_amdgcn_mfma_f32_32x32x2f32(av, bv, acc, 0, 0, 0);
     }
     __syncthreads();
   }
+  const int j = col0 + 32 * wc + r32;  // the lane's column; rows from acc_row
   if (g.nsplit > 1) {  // raw partial; the reduction applies the epilogue
     float* P = g.part + ((size_t)split * g.nbatch + b) * g.M * g.N;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = row0 + 4 * ty + r;
-      if (i >= g.M) continue;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int j = col0 + 4 * tx + c;
-        if (j < g.N) P[(size_t)i * g.N + j] = acc[r][c];
-      }
+    for (int rr = 0; rr < 16; ++rr) {
+      const int i = acc_row(row0 + 32 * wr, rr, lane);
+      if (i < g.M && j < g.N) P[(size_t)i * g.N + j] = acc[rr];
     }
     return;
   }
   float* C = g.C + (size_t)b * g.sC;
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int i = row0 + 4 * ty + r;
-    if (i >= g.M) continue;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int j = col0 + 4 * tx + c;
-      if (j >= g.N) continue;
-      float* p = C + (size_t)i * g.ldc + j;
-      float v = g.alpha * acc[r][c];
-      if (g.beta != 0.f) v += g.beta * *p;
-      if (i == j && i < g.diag_n) v += g.diag;
-      if (i >= lm || j >= ln) v = 0.f;
-      *p = v;
-    }
+  for (int rr = 0; rr < 16; ++rr) {
+    const int i = acc_row(row0 + 32 * wr, rr, lane);
+    if (i >= g.M || j >= g.N) continue;
+    float* p = C + (size_t)i * g.ldc + j;
+    float v = g.alpha * acc[rr];
+    if (g.beta != 0.f) v += g.beta * *p;
+    if (i == j && i < g.diag_n) v += g.diag;
+    if (i >= lm || j >= ln) v = 0.f;
+    *p = v;
   }
 }
 
