@@ -61,6 +61,19 @@ __device__ __forceinline__ float ld_elem<uint16_t>(const uint16_t* p) {
   return __uint_as_float((uint32_t)*p << 16);
 }
 
+// Four consecutive elements as floats in one load (8 bytes of bf16 or 16 of fp32); p
+// aligned to four elements.
+template <typename T>
+__device__ __forceinline__ f32x4 ld4f(const T* p) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x2 u = *reinterpret_cast<const u32x2*>(p);
+    return f32x4{__uint_as_float(u[0] << 16), __uint_as_float(u[0] & 0xffff0000u),
+                 __uint_as_float(u[1] << 16), __uint_as_float(u[1] & 0xffff0000u)};
+  } else {
+    return *reinterpret_cast<const f32x4*>(p);
+  }
+}
+
 constexpr int kGT = 64, kGK = 32, kGS = kGT + 4;
 constexpr int kSplitBlocks = 1024, kSplitMin = 512;  // split-K targets (see Runner::gemm)
 
@@ -83,34 +96,55 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   const TBe* B = static_cast<const TBe*>(g.B) + (size_t)b * g.sB;
   f32x16 acc = zero16();
   // the next slab's elements are loaded into registers while the current one is used
-  constexpr int U = kGT * kGK / 256;
-  float ra[U], rb[U];
+  // each thread fetches runs of four elements along the operand's stored contiguous
+  // index (one vector load when all four are in range, else element by element)
+  constexpr int U4 = kGT * kGK / 1024;
+  f32x4 ra[U4], rb[U4];
+  auto run4 = [](const auto* p, bool all, int nvalid) {
+    if (all && (reinterpret_cast<uintptr_t>(p) & (4 * sizeof(*p) - 1)) == 0) return ld4f(p);
+    f32x4 x{0.f, 0.f, 0.f, 0.f};
+    for (int q = 0; q < nvalid; ++q) x[q] = ld_elem(p + q);
+    return x;
+  };
   auto fetch = [&](int k0) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = tid + 256 * u;
-      // A tile: 64 rows x kGK k, threads along the stored contiguous index
+    for (int u = 0; u < U4; ++u) {
+      const int e = 4 * (tid + 256 * u);
+      // A tile: 64 rows x kGK k
       const int ai = TA ? e % kGT : e / kGK, ak = TA ? e / kGT : e % kGK;
       const int i = row0 + ai, k = k0 + ak;
-      ra[u] = (i < lm && k < lk)
-                  ? ld_elem(A + (TA ? (size_t)k * g.lda + i : (size_t)i * g.lda + k))
-                  : 0.f;
+      if (TA) {  // run over i at fixed k
+        const int nv = k < lk ? max(0, min(4, lm - i)) : 0;
+        ra[u] = nv > 0 ? run4(A + (size_t)k * g.lda + i, nv == 4, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {  // run over k at fixed i
+        const int nv = i < lm ? max(0, min(4, lk - k)) : 0;
+        ra[u] = nv > 0 ? run4(A + (size_t)i * g.lda + k, nv == 4, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
       // B tile: kGK k x 64 columns
       const int bk = TB ? e % kGK : e / kGT, bj = TB ? e / kGK : e % kGT;
       const int jj = col0 + bj, kb = k0 + bk;
-      rb[u] = (jj < ln && kb < lk)
-                  ? ld_elem(B + (TB ? (size_t)jj * g.ldb + kb : (size_t)kb * g.ldb + jj))
-                  : 0.f;
+      if (TB) {  // run over k at fixed column
+        const int nv = jj < ln ? max(0, min(4, lk - kb)) : 0;
+        rb[u] = nv > 0 ? run4(B + (size_t)jj * g.ldb + kb, nv == 4, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
+      } else {  // run over columns at fixed k
+        const int nv = kb < lk ? max(0, min(4, ln - jj)) : 0;
+        rb[u] = nv > 0 ? run4(B + (size_t)kb * g.ldb + jj, nv == 4, nv) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
     }
   };
   const int kstart = g.nsplit > 1 ? kbeg : 0;
   if (kstart < lk) fetch(kstart);
   for (int k0 = kstart; k0 < lk; k0 += kGK) {
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int e = tid + 256 * u;
-      As[TA ? e / kGT : e % kGK][TA ? e % kGT : e / kGK] = ra[u];
-      Bs[TB ? e % kGK : e / kGT][TB ? e / kGK : e % kGT] = rb[u];
+    for (int u = 0; u < U4; ++u) {
+      const int e = 4 * (tid + 256 * u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (TA) As[e / kGT][e % kGT + q] = ra[u][q];
+        else As[e % kGK + q][e / kGK] = ra[u][q];
+        if (TB) Bs[e % kGK + q][e / kGK] = rb[u][q];
+        else Bs[e / kGT][e % kGT + q] = rb[u][q];
+      }
     }
     __syncthreads();
     if (k0 + kGK < lk) fetch(k0 + kGK);
@@ -193,17 +227,49 @@ __global__ __launch_bounds__(256) void row_softmax_kernel(RowArgs a, int nrows_t
   const int L = valid_length(a.lengths, b, a.H, a.n, a.m);
   const int vr = extent(a.rmode, a.rows, a.m, L), vc = extent(a.cmode, a.cols, a.m, L);
   float* x = a.X + (size_t)row * a.cols;
-  if (r >= vr) {
-    for (int j = lane; j < a.cols; j += 64) x[j] = 0.f;
+  if (a.cols % 4 != 0) {  // rows not 16-byte aligned: one element per lane and access
+    if (r >= vr) {
+      for (int j = lane; j < a.cols; j += 64) x[j] = 0.f;
+      return;
+    }
+    float mx = kNegBig;
+    for (int j = lane; j < vc; j += 64) mx = fmaxf(mx, a.scale * x[j]);
+    mx = wave_max(mx);
+    float sum = 0.f;
+    for (int j = lane; j < vc; j += 64) sum += expf(a.scale * x[j] - mx);
+    const float inv = 1.f / wave_sum(sum);
+    for (int j = lane; j < a.cols; j += 64) x[j] = j < vc ? expf(a.scale * x[j] - mx) * inv : 0.f;
     return;
   }
+  if (r >= vr) {
+    for (int j = 4 * lane; j < a.cols; j += 256)
+      *reinterpret_cast<f32x4*>(x + j) = f32x4{0.f, 0.f, 0.f, 0.f};
+    return;
+  }
+  // four consecutive columns per lane and access (cols is a multiple of 4)
   float mx = kNegBig;
-  for (int j = lane; j < vc; j += 64) mx = fmaxf(mx, a.scale * x[j]);
+  for (int j = 4 * lane; j < vc; j += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(x + j);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (j + q < vc) mx = fmaxf(mx, a.scale * v[q]);
+  }
   mx = wave_max(mx);
   float sum = 0.f;
-  for (int j = lane; j < vc; j += 64) sum += expf(a.scale * x[j] - mx);
+  for (int j = 4 * lane; j < vc; j += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(x + j);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (j + q < vc) sum += expf(a.scale * v[q] - mx);
+  }
   const float inv = 1.f / wave_sum(sum);
-  for (int j = lane; j < a.cols; j += 64) x[j] = j < vc ? expf(a.scale * x[j] - mx) * inv : 0.f;
+  for (int j = 4 * lane; j < a.cols; j += 256) {
+    const f32x4 v = *reinterpret_cast<const f32x4*>(x + j);
+    f32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = j + q < vc ? expf(a.scale * v[q] - mx) * inv : 0.f;
+    *reinterpret_cast<f32x4*>(x + j) = o;
+  }
 }
 
 // In place on the upstream gradient dP of a row softmax P: X <- P o (X - rowsum(P o X)),
@@ -217,14 +283,37 @@ __global__ __launch_bounds__(256) void row_dsoftmax_kernel(RowArgs a, int nrows_
   const int vr = extent(a.rmode, a.rows, a.m, L), vc = extent(a.cmode, a.cols, a.m, L);
   float* x = a.X + (size_t)row * a.cols;
   const float* p = a.P + (size_t)row * a.cols;
+  if (a.cols % 4 != 0) {  // rows not 16-byte aligned: one element per lane and access
+    if (r >= vr) {
+      for (int j = lane; j < a.cols; j += 64) x[j] = 0.f;
+      return;
+    }
+    float dot = 0.f;
+    for (int j = lane; j < vc; j += 64) dot += p[j] * x[j];
+    dot = wave_sum(dot);
+    for (int j = lane; j < a.cols; j += 64) x[j] = j < vc ? p[j] * (x[j] - dot) : 0.f;
+    return;
+  }
   if (r >= vr) {
-    for (int j = lane; j < a.cols; j += 64) x[j] = 0.f;
+    for (int j = 4 * lane; j < a.cols; j += 256)
+      *reinterpret_cast<f32x4*>(x + j) = f32x4{0.f, 0.f, 0.f, 0.f};
     return;
   }
   float dot = 0.f;
-  for (int j = lane; j < vc; j += 64) dot += p[j] * x[j];
+  for (int j = 4 * lane; j < vc; j += 256) {
+    const f32x4 pv = *reinterpret_cast<const f32x4*>(p + j), xv = *reinterpret_cast<const f32x4*>(x + j);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (j + q < vc) dot += pv[q] * xv[q];
+  }
   dot = wave_sum(dot);
-  for (int j = lane; j < a.cols; j += 64) x[j] = j < vc ? p[j] * (x[j] - dot) : 0.f;
+  for (int j = 4 * lane; j < a.cols; j += 256) {
+    const f32x4 pv = *reinterpret_cast<const f32x4*>(p + j), xv = *reinterpret_cast<const f32x4*>(x + j);
+    f32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) o[q] = j + q < vc ? pv[q] * (xv[q] - dot) : 0.f;
+    *reinterpret_cast<f32x4*>(x + j) = o;
+  }
 }
 
 // ------------------------------------------------------------------ landmark kernels
@@ -329,17 +418,19 @@ __global__ __launch_bounds__(256) void segment_scatter_kernel(float* dX, const f
                                                               int n, int d, int mp, int m,
                                                               const int* lengths, int H) {
   const int b = blockIdx.y;
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // four features each
   const int L = valid_length(lengths, b, H, n, m);
-  if (e >= (long long)L * d) return;
-  const int t = (int)(e / d), f = (int)(e % d);
+  if (e >= (long long)L * (d / 4)) return;
+  const int t = (int)(e / (d / 4)), f = (int)(e % (d / 4)) * 4;
   const int j = (int)(((long long)t * m) / L);
   const int start = (int)(((long long)j * L + m - 1) / m);
   const int end = (int)(((long long)(j + 1) * L + m - 1) / m);
-  dX[((size_t)b * n + t) * d + f] += dXt[((size_t)b * mp + j) * d + f] / (float)(end - start);
+  const float inv = 1.f / (float)(end - start);
+  f32x4* px = reinterpret_cast<f32x4*>(dX + ((size_t)b * n + t) * d + f);
+  const f32x4 g = *reinterpret_cast<const f32x4*>(dXt + ((size_t)b * mp + j) * d + f);
+  *px += g * inv;
 }
 
-// dV[t] += sum_k w[h][k] dO[t - k + half] over the valid tokens (the transposed conv).
 // Eight consecutive elements of a token row as floats (bf16 bits or fp32), one or two
 // 16-byte loads; p 16-byte aligned (bf16) or 32-byte aligned (fp32).
 template <typename T>
@@ -455,13 +546,18 @@ template <typename T>
 __global__ __launch_bounds__(256) void store_grad_kernel(T* out, const float* src, int n, int d,
                                                          int H, int m, const int* lengths) {
   const int b = blockIdx.y;
-  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (long long)n * d) return;
+  const long long e = (long long)blockIdx.x * 256 + threadIdx.x;  // four elements each
+  if (e >= (long long)n * d / 4) return;
   const int L = valid_length(lengths, b, H, n, m);
-  const size_t o = (size_t)b * n * d + e;
-  const float v = e / d < L ? src[o] : 0.f;
-  if constexpr (sizeof(T) == 4) out[o] = v;
-  else out[o] = __builtin_bit_cast(uint16_t, bf16_rne(v));
+  const size_t o = (size_t)b * n * d + 4 * e;
+  const f32x4 v = (4 * e) / d < L ? *reinterpret_cast<const f32x4*>(src + o) : f32x4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4*>(out + o) = v;
+  } else {
+    const bf16x2 lo = bf16_rne2(v[0], v[1]), hi = bf16_rne2(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(out + o) =
+        u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  }
 }
 
 // Zero `count` floats.
@@ -657,9 +753,10 @@ hipError_t run(const GenBwdArgs& a, hipStream_t s) {
   if (r.err != hipSuccess) return r.err;
   // segment means: dQ += dQt[seg] / |seg|, dK += dKt[seg] / |seg|
   const dim3 tok((unsigned)((nd + 255) / 256), BH);
-  hipLaunchKernelGGL(segment_scatter_kernel, tok, dim3(256), 0, s, a.dQ, a.dQt, n, d, mp, m,
+  const dim3 tok4((unsigned)((nd / 4 + 255) / 256), BH);
+  hipLaunchKernelGGL(segment_scatter_kernel, tok4, dim3(256), 0, s, a.dQ, a.dQt, n, d, mp, m,
                      a.lengths, a.H);
-  hipLaunchKernelGGL(segment_scatter_kernel, tok, dim3(256), 0, s, a.dK, a.dKt, n, d, mp, m,
+  hipLaunchKernelGGL(segment_scatter_kernel, tok4, dim3(256), 0, s, a.dK, a.dKt, n, d, mp, m,
                      a.lengths, a.H);
   // conv skip: dV += conv^T(dO); dw
   const dim3 tok8((unsigned)((nd / 8 + 255) / 256), BH);
@@ -671,11 +768,11 @@ hipError_t run(const GenBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(dw_reduce_kernel, dim3(a.H), dim3(128), 0, s, a.dconv_w, a.dw_part, a.B, a.H,
                      a.W, nch);
   // outputs in the I/O type, padding rows zero
-  hipLaunchKernelGGL((store_grad_kernel<T>), tok, dim3(256), 0, s, static_cast<T*>(a.dq), a.dQ,
+  hipLaunchKernelGGL((store_grad_kernel<T>), tok4, dim3(256), 0, s, static_cast<T*>(a.dq), a.dQ,
                      n, d, a.H, m, a.lengths);
-  hipLaunchKernelGGL((store_grad_kernel<T>), tok, dim3(256), 0, s, static_cast<T*>(a.dk), a.dK,
+  hipLaunchKernelGGL((store_grad_kernel<T>), tok4, dim3(256), 0, s, static_cast<T*>(a.dk), a.dK,
                      n, d, a.H, m, a.lengths);
-  hipLaunchKernelGGL((store_grad_kernel<T>), tok, dim3(256), 0, s, static_cast<T*>(a.dv), a.dV,
+  hipLaunchKernelGGL((store_grad_kernel<T>), tok4, dim3(256), 0, s, static_cast<T*>(a.dv), a.dV,
                      n, d, a.H, m, a.lengths);
   return hipGetLastError();
 }

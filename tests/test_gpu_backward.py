@@ -47,6 +47,10 @@ CASES = {
                                                seed=316), [300, 123]),
     "general_f32_m160_iters0_w65": (gen.Config("g7", 1, 1, 640, 32, 160, conv_width=65,
                                                pinv_iters=0, dtype=gen.F32, seed=317), None),
+    # n not a multiple of 4: rows of the n-wide matrices are not 16-byte aligned, so the
+    # row kernels and the product's operand fetch take their element-wise paths
+    "general_m96_n131_ragged": (gen.Config("g8", 2, 1, 131, 64, 96, seed=318), [131, 101]),
+    "general_f32_m40_n203": (gen.Config("g9", 1, 2, 203, 32, 40, dtype=gen.F32, seed=319), None),
 }
 
 
