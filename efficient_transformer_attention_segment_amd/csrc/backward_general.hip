@@ -454,8 +454,14 @@ __device__ __forceinline__ void ld8f(const T* p, float* x) {
 
 constexpr int kMaxConvW = 65;  // widest conv the plan accepts
 
+// Tokens per thread in the conv kernels: a thread reads the W + kConvTok - 1 rows its
+// kConvTok tokens need once, and every tap index below is a compile-time function of two
+// unrolled loop counters.
+constexpr int kConvTok = 4;
+
 // dV[t] += sum_k w[k] dO[t - k + half] over the valid rows (the conv's transpose); one
-// thread per eight consecutive features of a token.
+// thread per kConvTok consecutive tokens x eight consecutive features. Row j of the
+// thread's window is dO[t0 - half + j]; it meets token t0 + r through tap r - j + 2 half.
 template <typename T>
 __global__ __launch_bounds__(256) void conv_transpose_kernel(float* dV, const T* dO,
                                                              const float* w, int n, int d,
@@ -464,29 +470,43 @@ __global__ __launch_bounds__(256) void conv_transpose_kernel(float* dV, const T*
   const int b = blockIdx.y;
   const long long e = (long long)blockIdx.x * 256 + threadIdx.x;
   const int L = valid_length(lengths, b, H, n, m);
-  if (e >= (long long)L * (d / 8)) return;
-  const int t = (int)(e / (d / 8)), f0 = (int)(e % (d / 8)) * 8, half = (W - 1) / 2;
+  const int groups = (L + kConvTok - 1) / kConvTok;
+  if (e >= (long long)groups * (d / 8)) return;
+  const int t0 = (int)(e / (d / 8)) * kConvTok, f0 = (int)(e % (d / 8)) * 8, half = (W - 1) / 2;
   const float* wh = w + (size_t)(b % H) * W;
   const T* o = dO + (size_t)b * n * d + f0;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < W; ++k) {
-    const int src = t - k + half;
-    if (src >= 0 && src < L) {
+  float acc[kConvTok][8] = {};
+#pragma unroll
+  for (int j = 0; j < kMaxConvW + kConvTok - 1; ++j) {
+    const int src = t0 - half + j;
+    if (j < W + kConvTok - 1 && src >= 0 && src < L) {
       float x[8];
       ld8f(o + (size_t)src * d, x);
-      const float wk = wh[k];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) acc[q] += wk * x[q];
+      for (int r = 0; r < kConvTok; ++r) {
+        const int k = r - j + 2 * half;  // tap joining row j to token t0 + r
+        if (k >= 0 && k < W) {
+          const float wk = wh[k];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[r][q] += wk * x[q];
+        }
+      }
     }
   }
-  f32x4* p = reinterpret_cast<f32x4*>(dV + ((size_t)b * n + t) * d + f0);
-  p[0] += f32x4{acc[0], acc[1], acc[2], acc[3]};
-  p[1] += f32x4{acc[4], acc[5], acc[6], acc[7]};
+#pragma unroll
+  for (int r = 0; r < kConvTok; ++r) {
+    if (t0 + r >= L) break;
+    f32x4* p = reinterpret_cast<f32x4*>(dV + ((size_t)b * n + t0 + r) * d + f0);
+    p[0] += f32x4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+    p[1] += f32x4{acc[r][4], acc[r][5], acc[r][6], acc[r][7]};
+  }
 }
 
 // Partial conv-weight gradient of one (head, token chunk): part[b][chunk][k] =
 // sum over the chunk's valid t of dO[t] . V[t + k - half] (V zero outside [0, L)). One
-// thread per eight consecutive features of a token; the per-tap sums stay in registers.
+// thread per kConvTok consecutive tokens x eight consecutive features; row j of the
+// thread's V window is V[t0 - half + j], which meets token t0 + r through tap j - r, so the
+// per-tap sums stay in registers.
 template <typename T>
 __global__ __launch_bounds__(256) void dw_partial_kernel(float* part, const T* dO, const T* V,
                                                          int n, int d, int W, int H, int m,
@@ -495,26 +515,41 @@ __global__ __launch_bounds__(256) void dw_partial_kernel(float* part, const T* d
   __shared__ float red[4][kMaxConvW + 7];
   const int b = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
   const int L = valid_length(lengths, b, H, n, m);
-  const int t0 = c * chunk, t1 = min(t0 + chunk, L), half = (W - 1) / 2;
+  const int t0c = c * chunk, t1 = min(t0c + chunk, L), half = (W - 1) / 2;
   const T* o = dO + (size_t)b * n * d;
   const T* v = V + (size_t)b * n * d;
   float acc[kMaxConvW];
 #pragma unroll
   for (int k = 0; k < kMaxConvW; ++k) acc[k] = 0.f;
-  for (long long e = tid; e < (long long)max(0, t1 - t0) * (d / 8); e += 256) {
-    const int t = t0 + (int)(e / (d / 8)), f0 = (int)(e % (d / 8)) * 8;
-    float go[8];
-    ld8f(o + (size_t)t * d + f0, go);
+  const int groups = (max(0, t1 - t0c) + kConvTok - 1) / kConvTok;
+  for (long long e = tid; e < (long long)groups * (d / 8); e += 256) {
+    const int t0 = t0c + (int)(e / (d / 8)) * kConvTok, f0 = (int)(e % (d / 8)) * 8;
+    float go[kConvTok][8];
 #pragma unroll
-    for (int k = 0; k < kMaxConvW; ++k) {
-      const int src = t + k - half;
-      if (k < W && src >= 0 && src < L) {
+    for (int r = 0; r < kConvTok; ++r) {
+      if (t0 + r < t1) {
+        ld8f(o + (size_t)(t0 + r) * d + f0, go[r]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) go[r][q] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kMaxConvW + kConvTok - 1; ++j) {
+      const int src = t0 - half + j;
+      if (j < W + kConvTok - 1 && src >= 0 && src < L) {
         float x[8];
         ld8f(v + (size_t)src * d + f0, x);
-        float s8 = 0.f;
 #pragma unroll
-        for (int q = 0; q < 8; ++q) s8 += go[q] * x[q];
-        acc[k] += s8;
+        for (int r = 0; r < kConvTok; ++r) {
+          const int k = j - r;  // compile-time: tap joining token t0 + r to row j
+          if (k >= 0 && k < kMaxConvW && k < W) {
+            float s8 = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) s8 += go[r][q] * x[q];
+            acc[k] += s8;
+          }
+        }
       }
     }
   }
@@ -759,8 +794,8 @@ hipError_t run(const GenBwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(segment_scatter_kernel, tok4, dim3(256), 0, s, a.dK, a.dKt, n, d, mp, m,
                      a.lengths, a.H);
   // conv skip: dV += conv^T(dO); dw
-  const dim3 tok8((unsigned)((nd / 8 + 255) / 256), BH);
-  hipLaunchKernelGGL((conv_transpose_kernel<T>), tok8, dim3(256), 0, s, a.dV, dO, a.conv_w, n, d,
+  const dim3 tokc((unsigned)(((n + kConvTok - 1) / kConvTok * (long long)(d / 8) + 255) / 256), BH);
+  hipLaunchKernelGGL((conv_transpose_kernel<T>), tokc, dim3(256), 0, s, a.dV, dO, a.conv_w, n, d,
                      a.W, a.H, m, a.lengths);
   const int nch = (n + a.dw_chunk - 1) / a.dw_chunk;
   hipLaunchKernelGGL((dw_partial_kernel<T>), dim3(nch, BH), dim3(256), 0, s, a.dw_part, dO, v, n,
