@@ -173,32 +173,53 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
     f32x16 sc = zero16();
 #pragma unroll
     for (int s = 0; s < D / 16; ++s) sc = mfma(ld8(krow + 16 * s + 8 * h), qb[s], sc);
+    // no key past the chunk's end and, causal, none after any of the wave's queries: no
+    // masks (the scale is positive, so the maximum is taken on the raw scores)
+    const bool full = k0 + 32 <= t1 && (!a.causal || k0 + 31 <= q0);
     float mx = kNegBig;
+    if (full) {
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const int key = k0 + fl_row(rr, h);
-      const bool ok = key < t1 && (!a.causal || key <= qi);
-      sc[rr] = ok ? sc[rr] * sl : kNegBig;
-      mx = fmaxf(mx, sc[rr]);
+      for (int rr = 0; rr < 16; ++rr) mx = fmaxf(mx, sc[rr]);
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        const int key = k0 + fl_row(rr, h);
+        if (!(key < t1 && (!a.causal || key <= qi))) sc[rr] = kNegBig;
+        mx = fmaxf(mx, sc[rr]);
+      }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mn = fmaxf(mrow, mx), corr = fast_exp2(mrow - mn);
-    float ps = 0.f, pe[16];
+    mx = mx > 0.5f * kNegBig ? mx * sl : kNegBig;
+    // lazy rescaling: the reference maximum moves only when some lane's maximum passes it
+    // by more than 8 (log2 units; probabilities stay <= 256); exact for any reference
+    if (__any(mx > mrow + 8.f)) {
+      const float mn = fmaxf(mrow, mx), corr = fast_exp2(mrow - mn);
+      lrow *= corr;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      pe[rr] = sc[rr] > 0.5f * kNegBig ? fast_exp2(sc[rr] - mn) : 0.f;
-      ps += pe[rr];
+      for (int f = 0; f < FT; ++f) o[f] *= corr;
+      mrow = mn;
+    }
+    float ps = 0.f, pe[16];
+    if (full) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        pe[rr] = fast_exp2(fmaf(sc[rr], sl, -mrow));
+        ps += pe[rr];
+      }
+    } else {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) {
+        pe[rr] = sc[rr] > 0.5f * kNegBig ? fast_exp2(fmaf(sc[rr], sl, -mrow)) : 0.f;
+        ps += pe[rr];
+      }
     }
     Pair8 pb[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) pb[s2] = split8(pe + 8 * s2);
     ps += __shfl_xor(ps, 32);
-    lrow = lrow * corr + ps;
-    mrow = mn;
+    lrow += ps;
 #pragma unroll
     for (int f = 0; f < FT; ++f) {
-#pragma unroll
-      for (int rr = 0; rr < 16; ++rr) o[f][rr] *= corr;
 #pragma unroll
       for (int s2 = 0; s2 < 2; ++s2) {
         const uint16_t* base = vS + 32 * f + trc;
