@@ -838,7 +838,7 @@ __device__ __forceinline__ void flash_reg_body(const CtxArgs& a, int blk, char* 
       const float corr = fast_exp2(M - mn);
       L *= corr;
 #pragma unroll
-      for (int f = 0; f < FT; ++f) wacc[f] *= corr;
+      for (int f = 0; f < FT; ++f) scale_in_place(wacc[f], corr);
       M = mn;
     }
     float p[16];
@@ -992,7 +992,7 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
       const float corr = fast_exp2(M - mn);
       L *= corr;
 #pragma unroll
-      for (int f = 0; f < FT; ++f) wacc[f] *= corr;
+      for (int f = 0; f < FT; ++f) scale_in_place(wacc[f], corr);
       M = mn;
     }
     float p[16];

@@ -196,7 +196,7 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
       const float mn = fmaxf(mrow, mx), corr = fast_exp2(mrow - mn);
       lrow *= corr;
 #pragma unroll
-      for (int f = 0; f < FT; ++f) o[f] *= corr;
+      for (int f = 0; f < FT; ++f) scale_in_place(o[f], corr);
       mrow = mn;
     }
     float ps = 0.f, pe[16];

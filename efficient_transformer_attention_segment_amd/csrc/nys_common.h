@@ -45,6 +45,22 @@ __device__ __forceinline__ f32x16 mfma_pair(const Pair8& a, const Pair8& b, f32x
   return mfma(a.hi, b.hi, c);
 }
 
+// v *= s with every element scaled in its own register: a plain multiply inside a
+// rarely taken branch lets the register allocator place the scaled accumulator elsewhere
+// and copy it back on every loop iteration. The compiler's hazard checks do not look
+// inside asm, so the wait states are explicit. The leading s_nop reads v[0] and s, so the
+// MFMA that wrote v and the v_exp that produced s both come before it: it covers the
+// MFMA-result and transcendental-result read hazards. The trailing one reads v[15], the
+// last element scaled, so the next MFMA that accumulates into v comes after it: it covers
+// the VALU-write to MFMA-read hazard. (Tying the whole vector instead brings the copies
+// back.)
+__device__ __forceinline__ void scale_in_place(f32x16& v, float s) {
+  asm volatile("s_nop 15" : "+v"(v[0]), "+v"(s));
+#pragma unroll
+  for (int i = 0; i < 16; ++i) asm volatile("v_mul_f32 %0, %0, %1" : "+v"(v[i]) : "v"(s));
+  asm volatile("s_nop 4" : "+v"(v[15]));
+}
+
 __device__ __forceinline__ f32x16 zero16() {
   f32x16 z;
 #pragma unroll
