@@ -895,7 +895,10 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
   constexpr int KD = D / 16;       // k-steps over features
   constexpr int FT = D / 32;       // feature tiles of the accumulator
   constexpr int CPR = D / 8;       // 16-byte chunks per row
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  // the wave index read into a scalar register: everything derived from it (the wave's
+  // landmark and token groups, LDS destinations, the partial-step test) stays scalar
+  const int tid = threadIdx.x, lane = tid & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, h = lane >> 5;
   const int LG = a.LG, TG = a.TG, g = wave % LG, tg = wave / LG;
   const int mp = a.mp;
@@ -910,10 +913,29 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
   const int real = step * CPR;
   const int nsteps = c1 > c0 ? (c1 - c0 + step - 1) / step : 0;
   uint16_t* ring = reinterpret_cast<uint16_t*>(lds);
-  auto issue = [&](int t) {
+  // Instruction i of a wave moves 16-byte chunk s = 64 (i nw + wave) + lane of the step:
+  // row s / CPR, chunk (s % CPR) ^ chunk_key(row). The key repeats every 8 rows, so when
+  // an instruction covers a multiple of 8 rows (RI), the lane's chunk is the same for
+  // every i and its source offset grows by RI rows per instruction.
+  const int RI = 64 * nw / CPR;
+  const bool uniform_rows = RI % 8 == 0 && real == NI * 64 * nw;
+  const int r0 = (64 * wave + lane) / CPR;
+  const uint32_t lane_bytes = 2u * (uint32_t)(r0 * D + 8 * ((lane % CPR) ^ chunk_key<CPR>(r0)));
+  const uint32_t inst_bytes = 2u * (uint32_t)(RI * D);
+  auto issue = [&](int t, int slot) {
     const int base = c0 + t * step;
-    uint16_t* dk = ring + (size_t)(t % S) * 2 * tile_elems;
+    uint16_t* dk = ring + (size_t)slot * 2 * tile_elems;
     uint16_t* dv = dk + tile_elems;
+    if (uniform_rows && base + step <= c1) {  // a whole step: no row is clamped
+      const uint16_t* kb = K + (size_t)base * D;
+      const uint16_t* vb = V + (size_t)base * D;
+      for (int i = 0; i < NI; ++i) {
+        const int b = i * nw + wave;
+        dma16_s(kb, lane_bytes + i * inst_bytes, dk + 512 * b);
+        dma16_s(vb, lane_bytes + i * inst_bytes, dv + 512 * b);
+      }
+      return;
+    }
     for (int i = 0; i < NI; ++i) {
       const int b = i * nw + wave, s = 64 * b + lane;
       const int r = s / CPR, ch = (s % CPR) ^ chunk_key<CPR>(r);
@@ -924,7 +946,7 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
     }
   };
   // ring prologue first: its loads overlap the landmark operand set-up below
-  for (int t = 0; t < S - 1 && t < nsteps; ++t) issue(t);
+  for (int t = 0; t < S - 1 && t < nsteps; ++t) issue(t, t);
 
   // landmark operand, with s*log2(e) folded in so the scores come out in log2 units
   Pair8 qb[KD];
@@ -953,14 +975,17 @@ __device__ __forceinline__ void flash_ring_body(const CtxArgs& a, int blk, char*
   const int trcol = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
   const int krow = 32 * tg + r32;
 
+  int cslot = 0, islot = S - 1;  // ring slots of tile t and of tile t + S - 1
   for (int t = 0; t < nsteps; ++t) {
     // tile t is complete once only the DMA of later tiles is outstanding (any other
     // younger load only makes the count conservative)
     wait_dma_barrier(2 * NI * min(nsteps - 1 - t, S - 2));
-    if (t + S - 1 < nsteps) issue(t + S - 1);  // refills the slot consumed at t - 1
+    if (t + S - 1 < nsteps) issue(t + S - 1, islot);  // refills the slot consumed at t - 1
+    islot = islot + 1 == S ? 0 : islot + 1;
     const int base = c0 + t * step;
-    const uint16_t* kt = ring + (size_t)(t % S) * 2 * tile_elems;
+    const uint16_t* kt = ring + (size_t)cslot * 2 * tile_elems;
     const uint16_t* vt = kt + tile_elems;
+    cslot = cslot + 1 == S ? 0 : cslot + 1;
 
     // scores (log2 units): rows = 32 tokens, columns = 32 landmarks
     f32x16 Sc = zero16();

@@ -268,6 +268,15 @@ __device__ __forceinline__ void dma16(const void* src, void* dst_lds) {
                : "memory", "m0");
 }
 
+// Same DMA with a wave-uniform base in SGPRs and a 32-bit per-lane byte offset: no 64-bit
+// address arithmetic per lane. sbase must be wave-uniform.
+__device__ __forceinline__ void dma16_s(const void* sbase, uint32_t voff, void* dst_lds) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst_lds);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(sbase),
+               "s"(m0)
+               : "memory", "m0");
+}
+
 // Wait until at most n vector-memory loads of this wave are outstanding, then a
 // workgroup barrier. Loads complete in issue order, so when the n youngest loads are
 // the DMA of later tiles, every older tile is in LDS; after the barrier that holds for
