@@ -75,7 +75,8 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   static_assert(!kKtSplit || (NT == 0 && !kKtLds && NW == 4 && !kS),
                 "split Kt: bf16 online-softmax shapes with 4-wave blocks");
   constexpr int kMaxT = kKtSplit ? split_tiles<D>() : 1;  // landmark tiles held (split Kt)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the wave index in a scalar register keeps the per-wave row tests scalar
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r32 = lane & 31, h = lane >> 5;
   const int mp = NT > 0 ? 32 * NT : a.mp;
   const int YS = mp + 8;
@@ -457,7 +458,8 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
     }
     const int tq = T0 + 32 * wave + r32;
     const bool qok = tq < t_end;
-    const bool qpad = t_valid < t_end && tq >= t_valid;  // padding row of a cut block
+    const bool cut = t_valid < t_end;        // block-uniform
+    const bool qpad = cut && tq >= t_valid;  // padding row of a cut block
 
     f32x16 oacc[FT];
 #pragma unroll
@@ -484,7 +486,7 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
           ps += e;
         }
       ps += __shfl_xor(ps, 32);
-      const float inv = 1.f / ps;
+      const float inv = __builtin_amdgcn_rcpf(ps);  // ps >= 1 (the maximum contributes 1)
 #pragma unroll
       for (int lt = 0; lt < NT; ++lt)
 #pragma unroll
@@ -551,14 +553,19 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
         for (int lt = 0; lt < mp / 32; ++lt) online_tile(lt);
       }
       L += __shfl_xor(L, 32);
-      const float inv = 1.f / L;
+      const float inv = __builtin_amdgcn_rcpf(L);  // L >= 1 (the maximum contributes 1)
 #pragma unroll
       for (int f = 0; f < FT; ++f) oacc[f] *= inv;
     }
 
-    if (qpad)
+    // only a cut block has padding rows; the empty asm keeps this a scalar branch (the
+    // compiler would otherwise turn the zeroing into selects that every block runs)
+    if (cut) {
+      asm volatile("");
+      if (qpad)
 #pragma unroll
-      for (int f = 0; f < FT; ++f) oacc[f] = zero16();
+        for (int f = 0; f < FT; ++f) oacc[f] = zero16();
+    }
     if (a.attn_tap != nullptr && qok) {
       float* tp = a.attn_tap + ((size_t)bh * a.n + tq) * D + (D / 2) * h;
 #pragma unroll
@@ -584,9 +591,12 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
       }
     }
 
-    if (qpad)
+    if (cut) {
+      asm volatile("");
+      if (qpad)
 #pragma unroll
-      for (int f = 0; f < FT; ++f) oacc[f] = zero16();
+        for (int f = 0; f < FT; ++f) oacc[f] = zero16();
+    }
     if constexpr (kS) {
       if (qok) {
         float* op = static_cast<float*>(a.out) + ((size_t)bh * a.n + tq) * D + (D / 2) * h;
