@@ -788,6 +788,7 @@ static nys_status proj_checks(int B, int H, int n, int d, int d_model) {
   if ((H * d) % 64 != 0) return fail(NYS_E_UNSUPPORTED, "H*d must be a multiple of 64");
   const long long wide = std::max<long long>(d_model, 3LL * H * d);
   if ((long long)B * n * wide >= (1LL << 31)) return fail(NYS_E_UNSUPPORTED, "tensor too large");
+  if (3LL * H * d * d_model >= (1LL << 31)) return fail(NYS_E_UNSUPPORTED, "weights too large");
   return NYS_OK;
 }
 

@@ -31,20 +31,28 @@ constexpr int kPSlabA = kPBM * kPBK, kPSlabB = kPBN * kPBK;  // bf16 elements pe
 constexpr int kPStage = kPSlabA + kPSlabB;
 constexpr int kPDmaPerSlab = 6;  // DMA instructions per wave per stage (4 A + 2 B)
 
-// Source of A-row r's 16-byte chunk at k-offset kk (elements) for the two kernels.
-struct ARowsQkv {
+// A-row sources of the two kernels, split for the DMA's saddr form: a wave-uniform base
+// per 32-wide k-slab (k0) and a per-lane byte offset of row m, chunk kc (k0 + 8 kc .. +7)
+// that is the same for every slab. Byte offsets fit 32 bits (tensors stay below 2^31
+// elements).
+struct ARowsQkv {  // x [M][K]
   const uint16_t* x;
-  int M, K;
-  __device__ __forceinline__ const uint16_t* at(int m, int kk) const {
-    return x + (size_t)m * K + kk;
+  int K;
+  __device__ __forceinline__ const uint16_t* slab(int k0) const { return x + k0; }
+  __device__ __forceinline__ uint32_t lane_bytes(int m, int kc) const {
+    return 2u * ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)kc);
   }
 };
-struct ARowsOut {  // row m = token (b, t), column k = head h = k / d, feature k % d
+struct ARowsOut {  // row m = token (b, t), column k = head k / d, feature k % d
   const uint16_t* o;
   int n, H, d;
-  __device__ __forceinline__ const uint16_t* at(int m, int kk) const {
-    const int b = m / n, t = m - b * n, h = kk / d, f = kk - h * d;
-    return o + (((size_t)b * H + h) * n + t) * d + f;
+  // a 32-wide slab lies in one head (d is a multiple of 32): head k0 / d, features from k0 % d
+  __device__ __forceinline__ const uint16_t* slab(int k0) const {
+    return o + (size_t)(k0 / d) * n * d + (k0 % d);
+  }
+  __device__ __forceinline__ uint32_t lane_bytes(int m, int kc) const {
+    const int b = m / n, t = m - b * n;
+    return 2u * ((uint32_t)((b * H * n + t) * d) + 8u * (uint32_t)kc);
   }
 };
 
@@ -97,24 +105,30 @@ __device__ __forceinline__ void proj_tile(const ARows& arows, const uint16_t* w,
   // one stage: A 1024 and B 512 16-byte chunks = 24 wave instructions, 6 per wave; slot s
   // of an operand holds row s / 4, stored chunk s % 4 (logical chunk (s % 4) ^ key(row))
   auto stage = [&](int t) { return ring + (size_t)(t % kPStages) * kPStage; };
+  // the lane's six DMA sources as byte offsets from the slab bases (rows clamped at M, N)
+  uint32_t aoff[4], boff[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = 64 * (4 * i + wave) + lane, r = s >> 2, c = (s & 3) ^ chunk_key<4>(r);
+    aoff[i] = arows.lane_bytes(min(m0 + r, M - 1), c);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int s = 64 * (4 * i + wave) + lane, r = s >> 2, c = (s & 3) ^ chunk_key<4>(r);
+    boff[i] = 2u * ((uint32_t)min(n0 + r, N - 1) * (uint32_t)K + 8u * (uint32_t)c);
+  }
   auto issue = [&](int t) {
     uint16_t* sa = stage(t);
     uint16_t* sb = sa + kPSlabA;
     // blocks start at different k-slabs (by their slot on the XCD) so that concurrent
     // blocks do not all read the same column window of the 2-byte * K row stride
     const int k0 = ((t + (int)(blockIdx.x >> 3)) % nslab) * kPBK;
+    const uint16_t* abase = arows.slab(k0);
+    const uint16_t* bbase = w + k0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int blk = 4 * i + wave, s = 64 * blk + lane;
-      const int r = s >> 2, c = (s & 3) ^ chunk_key<4>(r);
-      dma16(arows.at(min(m0 + r, M - 1), k0 + 8 * c), sa + 512 * blk);
-    }
+    for (int i = 0; i < 4; ++i) dma16_s(abase, aoff[i], sa + 512 * (4 * i + wave));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int blk = 4 * i + wave, s = 64 * blk + lane;
-      const int r = s >> 2, c = (s & 3) ^ chunk_key<4>(r);
-      dma16(w + (size_t)min(n0 + r, N - 1) * K + k0 + 8 * c, sb + 512 * blk);
-    }
+    for (int i = 0; i < 2; ++i) dma16_s(bbase, boff[i], sb + 512 * (4 * i + wave));
   };
 #pragma unroll
   for (int a = 0; a < 2; ++a)
@@ -211,7 +225,7 @@ __global__ __launch_bounds__(256, 2) void qkv_proj_kernel(ProjArgs a) {
   xcd_map(blockIdx.x, (M + kPBM - 1) / kPBM, (N + kPBN - 1) / kPBN, mb, nb);
   const int m0 = mb * kPBM, n0 = nb * kPBN;
   ProjAcc acc;
-  proj_tile(ARowsQkv{static_cast<const uint16_t*>(a.a), M, K}, static_cast<const uint16_t*>(a.w),
+  proj_tile(ARowsQkv{static_cast<const uint16_t*>(a.a), K}, static_cast<const uint16_t*>(a.w),
             M, N, K, m0, n0, reinterpret_cast<uint16_t*>(lds), acc);
   proj_stage_tile(acc, lds);
   proj_store_tile(lds, m0, n0, M, N,
