@@ -192,10 +192,22 @@ __device__ __forceinline__ void proj_store_tile(const char* lds, int m0, int n0,
   const int chunk = threadIdx.x & 15, r = threadIdx.x >> 4;
   const int nn = n0 + 8 * chunk;
   if (nn >= N) return;
+  const int rows = min(kPBM, M - m0);
+  if (dst.linear(m0, rows)) {  // rows m0 + r + 16 i sit at a fixed stride: one address
+    uint16_t* p = dst(m0 + r, nn);
+    const size_t step = (size_t)16 * dst.row_stride();
+#pragma unroll 4
+    for (int i = 0; i < kPBM / 16; ++i) {
+      if (r + 16 * i >= rows) break;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(lds + stage_off(r + 16 * i, chunk));
+      *reinterpret_cast<u32x4*>(p + i * step) = v;
+    }
+    return;
+  }
 #pragma unroll 4
   for (int i = 0; i < kPBM / 16; ++i) {
     const int m = r + 16 * i;
-    if (m0 + m >= M) break;
+    if (m >= rows) break;
     const u32x4 v = *reinterpret_cast<const u32x4*>(lds + stage_off(m, chunk));
     *reinterpret_cast<u32x4*>(dst(m0 + m, nn)) = v;
   }
@@ -209,6 +221,11 @@ struct DstQkv {  // feature nn of token m -> q, k or v [B][H][n][d]
     const int hd = rem / d, f = rem - hd * d;
     return (which == 0 ? q : which == 1 ? k : v) + (((size_t)b * H + hd) * n + t) * d + f;
   }
+  // tokens m0 .. m0 + rows - 1 of one batch element: consecutive rows d apart
+  __device__ __forceinline__ bool linear(int m0, int rows) const {
+    return m0 / n == (m0 + rows - 1) / n;
+  }
+  __device__ __forceinline__ int row_stride() const { return d; }
 };
 struct DstRows {  // y [M][N]
   uint16_t* y;
@@ -216,6 +233,8 @@ struct DstRows {  // y [M][N]
   __device__ __forceinline__ uint16_t* operator()(int m, int nn) const {
     return y + (size_t)m * N + nn;
   }
+  __device__ __forceinline__ bool linear(int, int) const { return true; }
+  __device__ __forceinline__ int row_stride() const { return N; }
 };
 
 __global__ __launch_bounds__(256, 2) void qkv_proj_kernel(ProjArgs a) {
