@@ -177,7 +177,8 @@ nys_status nys_attn_backward(nys_attn_plan *plan, const void *q, const void *k, 
  *   y     : device bf16 [B][n][d_model], written
  * Preconditions: B, H, n >= 1; d in {32, 64, 128}; d_model >= 64 and a multiple of 64;
  * H*d a multiple of 64; all pointers 16-byte aligned, outputs not overlapping inputs;
- * B*n*max(d_model, 3*H*d) < 2^31. Asynchronous like nys_attn_forward.
+ * B*n*max(d_model, 3*H*d) < 2^31 and 3*H*d*d_model < 2^31 (NYS_E_UNSUPPORTED otherwise).
+ * Asynchronous like nys_attn_forward.
  * Errors: NYS_E_ARG, NYS_E_UNSUPPORTED, NYS_E_DEVICE, NYS_E_LAUNCH. */
 nys_status nys_proj_qkv(const void *x, const void *w_qkv, void *q, void *k, void *v, int B,
                         int H, int n, int d, int d_model, void *stream);
