@@ -805,7 +805,7 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   uint16_t* so = reinterpret_cast<uint16_t*>(lds);   // dO rows t0 - half .. [kFinRows][D]
   uint16_t* sv = so + kFinRows * D;                  // V rows  t0 - half .. [kFinRows][D]
   float* sq = reinterpret_cast<float*>(sv + kFinRows * D);  // dQt / |seg| per segment
-  float* sw = sq + MP * D;                           // conv taps [W]
+  float* sw = sq + a.fin_segs * D;                   // conv taps [W]
   float* sdw = sw + 65;                              // dw sums [W]
   int* srow = reinterpret_cast<int*>(sdw + 4 * 65);  // per token: its dQt row offset
   int bh, c3;
@@ -943,8 +943,10 @@ struct BwdShape {
   static constexpr size_t p1 =
       ((size_t)4 * MP * (T + 8) + 2 * (D + 8) * T + NW * 2 * 32 * (MP + 8)) * 2;
   static constexpr size_t p2 = ((size_t)2 * MP * (T + 8) + (size_t)T * (D + 8)) * 2 + 3 * MP * 4;
-  static constexpr size_t fin =
-      (size_t)2 * kFinRows * D * 2 + ((size_t)MP * D + 65 + 4 * 65 + kFinTok) * 4;
+  static constexpr size_t fin_bytes(int segs) {
+    return (size_t)2 * kFinRows * D * 2 + ((size_t)segs * D + 65 + 4 * 65 + kFinTok) * 4;
+  }
+  static constexpr size_t fin = fin_bytes(MP);  // the most any plan asks for
 };
 
 template <int D, int MP>
@@ -984,7 +986,10 @@ static hipError_t launch_bwd_t(const BwdArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((bwd_land_bwd_kernel<D, MP>), dim3(BH), dim3(kBwdThreads), S::l2, s, a);
   hipLaunchKernelGGL((bwd_pass2_kernel<D, MP, S::NW>), dim3(BH * a.C), dim3(64 * S::NW), S::p2,
                      s, a);
-  hipLaunchKernelGGL((bwd_final_kernel<D>), dim3(BH * a.C3), dim3(kBwdThreads), S::fin, s, a);
+  // the table holds only the segments a token tile can meet: with less LDS per block, three
+  // blocks share a CU at d = 64
+  hipLaunchKernelGGL((bwd_final_kernel<D>), dim3(BH * a.C3), dim3(kBwdThreads),
+                     S::fin_bytes(a.fin_segs), s, a);
   hipLaunchKernelGGL(bwd_dw_kernel, dim3(a.H * a.W), dim3(kBwdThreads), 0, s, a);
   return hipGetLastError();
 }

@@ -120,6 +120,8 @@ struct BwdArgs {
   float* dv_part;           // [BH][n][d]      B^T dW
   float* part_dw;           // [BH][C3][W]
   int B, H, BH, n, d, m, mp, W, iters, chunk, C, chunk3, C3;
+  int fin_segs;  // rows of the final pass's per-segment table: segments one of its token
+                 // tiles can meet (mp with per-sequence lengths, where segments can be short)
   float scale, scale_log2e;
 };
 hipError_t launch_backward(const BwdArgs& a, hipStream_t s);

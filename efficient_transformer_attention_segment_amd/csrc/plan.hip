@@ -762,6 +762,16 @@ extern "C" nys_status nys_attn_backward(nys_attn_plan* p, const void* q, const v
   b.dk = static_cast<uint16_t*>(dk);
   b.dv = static_cast<uint16_t*>(dv);
   b.dconv_w = dconv_w;
+  // Segments a final-pass tile of kFinalTokens tokens can meet: with every sequence of
+  // length n, segments hold at least floor(n / m) tokens, so at most
+  // kFinalTokens / floor(n / m) + 2; with per-sequence lengths a segment can be a single
+  // token, so all of them.
+  {
+    const int per = p->n / p->m;
+    b.fin_segs = (lengths == nullptr && per >= 1)
+                     ? std::min(p->mp, kFinalTokens / per + 2)
+                     : p->mp;
+  }
   const char* what = "";
   hipError_t e = hipSuccess;
   // one stage's launch result (and, with NYS_DEBUG_SYNC, its completion)
