@@ -484,72 +484,62 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
     const uint16_t* kh = a.kt_hl + (size_t)bh * 2 * MP * D;
     at = gemm_tile_k<KD>(kh, kh + MP * D, D, qh, qh + MP * D, D, col0, row0, lane) * a.scale_log2e;
   }
-  // 2. row softmax over the m real landmarks (padded rows/columns become 0). A lane
-  // holds 16 of the row's columns, its partner lane (l ^ 32) the other 16 of the tile.
+  // 2. row softmax over the m real landmarks (padded rows/columns become 0) and
+  // alpha = 1 / (max column abs-sum * max row abs-sum), with two barriers. A lane holds
+  // 16 of its row's columns in the tile, its partner lane (l ^ 32) the other 16. Each
+  // tile leaves its row maximum and its sum of exponentials relative to that maximum;
+  // the row's softmax combines the NT partials, each rescaled by exp(mx_c - M).
+  float mloc = kNegBig;
   if (mine) {
-    float mx = kNegBig;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
-      if (row_tile_col(col0, rr, lane) < m) mx = fmaxf(mx, at[rr]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (h == 0) red_part[irow * NT + tj] = mx;
-  }
-  __syncthreads();
-  float sm = 0.f;
-  if (mine) {
-    float mx = red_part[irow * NT];
-#pragma unroll
-    for (int c = 1; c < NT; ++c) mx = fmaxf(mx, red_part[irow * NT + c]);
+      if (row_tile_col(col0, rr, lane) < m) mloc = fmaxf(mloc, at[rr]);
+    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    float sloc = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      at[rr] = (irow < m && row_tile_col(col0, rr, lane) < m) ? fast_exp2(at[rr] - mx) : 0.f;
-      sm += at[rr];
+      at[rr] = row_tile_col(col0, rr, lane) < m ? fast_exp2(at[rr] - mloc) : 0.f;
+      sloc += at[rr];
     }
-    sm += __shfl_xor(sm, 32);
+    sloc += __shfl_xor(sloc, 32);
+    if (h == 0) {
+      red_part[2 * (irow * NT + tj)] = mloc;
+      red_part[2 * (irow * NT + tj) + 1] = sloc;
+    }
   }
-  __syncthreads();  // every wave has read the maxima
-  if (mine && h == 0) red_part[irow * NT + tj] = sm;
-  __syncthreads();
+  __syncthreads();  // every tile's row partials are in
+  float rsum = 0.f;  // this row's abs-sum: the entries are positive, so sum * (1 / sum)
   if (mine) {
-    float rsum = red_part[irow * NT];
+    float M = kNegBig;
 #pragma unroll
-    for (int c = 1; c < NT; ++c) rsum += red_part[irow * NT + c];
-    const float inv = irow < m ? 1.f / rsum : 0.f;
+    for (int c = 0; c < NT; ++c) M = fmaxf(M, red_part[2 * (irow * NT + c)]);
+    float S = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) at[rr] *= inv;
-  }
-  __syncthreads();
-  // abs row sums (partials per column tile) and abs column sums (partials per row tile)
-  if (mine) {
-    float rs = 0.f;
+    for (int c = 0; c < NT; ++c)
+      S += red_part[2 * (irow * NT + c) + 1] * fast_exp2(red_part[2 * (irow * NT + c)] - M);
+    const float inv = irow < m ? 1.f / S : 0.f;
+    const float sc = fast_exp2(mloc - M) * inv;
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) rs += fabsf(at[rr]);
-    rs += __shfl_xor(rs, 32);
-    if (h == 0) red_part[irow * NT + tj] = rs;
+    for (int rr = 0; rr < 16; ++rr) at[rr] *= sc;
+    rsum = S * inv;
+    // abs column sums of this tile over its 32 rows
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      const float cs = half_sum(fabsf(at[rr]));
+      const float cs = half_sum(at[rr]);
       if (r32 == 0) red_col[ti * MP + row_tile_col(col0, rr, lane)] = cs;
     }
   }
-  __syncthreads();
-  float rmax = 0.f, cmax = 0.f;
-  if (tid < m) {
+  const float rmax_w = wave_max(rsum);
+  if (lane == 0) red[wave] = rmax_w;
+  __syncthreads();  // column partials and every wave's largest row sum are in
+  // every wave forms alpha itself: lane j sums column j's partials (MP <= 64)
+  float csum = 0.f;
+  if (lane < m) {
 #pragma unroll
-    for (int c = 0; c < NT; ++c) {
-      rmax += red_part[tid * NT + c];
-      cmax += red_col[c * MP + tid];
-    }
+    for (int c = 0; c < NT; ++c) csum += red_col[c * MP + lane];
   }
-  rmax = wave_max(rmax);
-  cmax = wave_max(cmax);
-  if (lane == 0) {
-    red[wave] = rmax;
-    red[8 + wave] = cmax;
-  }
-  __syncthreads();
-  rmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  cmax = fmaxf(fmaxf(red[8], red[9]), fmaxf(red[10], red[11]));
+  const float cmax = wave_max(csum);
+  const float rmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float alpha = 1.0f / (cmax * rmax);
   // 3. A_S (fp32 copy and operand planes), Z_0 = alpha A_S^T
   if (mine) {
@@ -1072,7 +1062,7 @@ void context_kernel(CtxArgs a) {
   extern __shared__ __align__(16) char lds[];
   int blk = blockIdx.x;
   if constexpr (MP > 0) {
-    __shared__ float red_part[MP * (MP / 32)];  // [row][column tile]
+    __shared__ float red_part[2 * MP * (MP / 32)];  // [row][column tile][max, sum]
     __shared__ float red_col[(MP / 32) * MP];   // [row tile][column]
     __shared__ float red[16];
     if (blk < a.npinv) {
