@@ -494,14 +494,14 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr)
       if (row_tile_col(col0, rr, lane) < m) mloc = fmaxf(mloc, at[rr]);
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32));
+    mloc = halves_max(mloc);
     float sloc = 0.f;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       at[rr] = row_tile_col(col0, rr, lane) < m ? fast_exp2(at[rr] - mloc) : 0.f;
       sloc += at[rr];
     }
-    sloc += __shfl_xor(sloc, 32);
+    sloc = halves_sum(sloc);
     if (h == 0) {
       red_part[2 * (irow * NT + tj)] = mloc;
       red_part[2 * (irow * NT + tj) + 1] = sloc;
@@ -522,14 +522,17 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) at[rr] *= sc;
     rsum = S * inv;
-    // abs column sums of this tile over its 32 rows
+    // abs column sums of this tile over its 32 rows, all formed before any is stored
+    // (lanes 31 and 63 hold them)
+    float cs[16];
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      const float cs = half_sum(at[rr]);
-      if (r32 == 0) red_col[ti * MP + row_tile_col(col0, rr, lane)] = cs;
+    for (int rr = 0; rr < 16; ++rr) cs[rr] = half_sum_upper(at[rr]);
+    if (r32 == 31) {
+#pragma unroll
+      for (int rr = 0; rr < 16; ++rr) red_col[ti * MP + row_tile_col(col0, rr, lane)] = cs[rr];
     }
   }
-  const float rmax_w = wave_max(rsum);
+  const float rmax_w = wave_max_dpp(rsum);
   if (lane == 0) red[wave] = rmax_w;
   __syncthreads();  // column partials and every wave's largest row sum are in
   // every wave forms alpha itself: lane j sums column j's partials (MP <= 64)
@@ -538,12 +541,12 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
 #pragma unroll
     for (int c = 0; c < NT; ++c) csum += red_col[c * MP + lane];
   }
-  const float cmax = wave_max(csum);
+  const float cmax = wave_max_dpp(csum);
   const float rmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float alpha = 1.0f / (cmax * rmax);
-  // 3. A_S (fp32 copy and operand planes), Z_0 = alpha A_S^T
+  // 3. A_S (operand planes; the fp32 copy only on inspection calls), Z_0 = alpha A_S^T
   if (mine) {
-    store_row_tile_f32<MP>(a.a_s + (size_t)bh * P, row0, col0, at, lane);
+    if (a.fp32_out) store_row_tile_f32<MP>(a.a_s + (size_t)bh * P, row0, col0, at, lane);
     store_row_tile<MP>(plane(kQT), plane(kQT + 1), row0, col0, at, lane);
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {  // element (i, j) of A goes to Z_0[j][i]
@@ -553,7 +556,7 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
       split1(zv, hb, lb);
       plane(kQZ)[swz<MP>(j, irow)] = hb;
       plane(kQZ + 1)[swz<MP>(j, irow)] = lb;
-      if (a.iters == 0) a.z[(size_t)bh * P + (size_t)j * MP + irow] = zv;
+      if (a.iters == 0 && a.fp32_out) a.z[(size_t)bh * P + (size_t)j * MP + irow] = zv;
     }
   }
   __syncthreads();
@@ -596,7 +599,8 @@ __device__ __forceinline__ void pinv_lds_body(const CtxArgs& a, int bh, uint16_t
     if (mine) {  // Z <- Z T / 4, into the X planes
       const f32x16 zv = prod_rows_op<MP>(zrows, plane(pz), plane(pz + 1), col0, lane) * 0.25f;
       store_row_tile<MP>(plane(px), plane(px + 1), row0, col0, zv, lane);
-      if (it == a.iters - 1) store_row_tile_f32<MP>(a.z + (size_t)bh * P, row0, col0, zv, lane);
+      if (it == a.iters - 1 && a.fp32_out)
+        store_row_tile_f32<MP>(a.z + (size_t)bh * P, row0, col0, zv, lane);
     }
     __syncthreads();
     const int nz = px;

@@ -256,6 +256,50 @@ __device__ __forceinline__ float half_sum(float x) {
   return x + __shfl_xor(x, 16);
 }
 
+// Row broadcasts (gfx9 DPP): lane 15 of each row into the next row, lane 31 into rows 2
+// and 3; the row mask picks the rows written, the others keep `old`.
+constexpr int kDppRowBcast15 = 0x142;
+constexpr int kDppRowBcast31 = 0x143;
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_bcast(float old, float x) {
+  return __int_as_float(
+      __builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), kCtrl, kRowMask, 0xf, false));
+}
+
+// Sum over the 32 lanes of a half-wave with DPP steps only, valid in the half's upper
+// row: lanes 16-31 hold the sum of lanes 0-31, lanes 48-63 that of lanes 32-63.
+__device__ __forceinline__ float half_sum_upper(float x) {
+  x += dpp_mov<kDppQuadXor1>(x);
+  x += dpp_mov<kDppQuadXor2>(x);
+  x += dpp_mov<kDppRowRor4>(x);
+  x += dpp_mov<kDppRowRor8>(x);
+  return x + dpp_bcast<kDppRowBcast15, 0xa>(0.f, x);
+}
+
+// Max over all 64 lanes, in every lane: DPP row reductions, two row broadcasts that
+// leave the maximum in lane 63, and a read of that lane.
+__device__ __forceinline__ float wave_max_dpp(float x) {
+  x = fmaxf(x, dpp_mov<kDppQuadXor1>(x));
+  x = fmaxf(x, dpp_mov<kDppQuadXor2>(x));
+  x = fmaxf(x, dpp_mov<kDppRowRor4>(x));
+  x = fmaxf(x, dpp_mov<kDppRowRor8>(x));
+  x = fmaxf(x, dpp_bcast<kDppRowBcast15, 0xa>(x, x));
+  x = fmaxf(x, dpp_bcast<kDppRowBcast31, 0xc>(x, x));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+}
+
+// x[l] combined with x[l ^ 32] (the other half-wave) through v_permlane32_swap, the same
+// value in both lanes of a pair: the swap leaves (x[l], x[l ^ 32]) in every lane, in an
+// order that depends on the half, and both combinations are symmetric.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---------------------------------------------------------------- LDS-DMA staging
 // global_load_lds_dwordx4: every lane moves 16 bytes from its own global address to LDS
 // at (M0 base) + 16 * lane, so one wave instruction fills 1 KiB of LDS contiguously and

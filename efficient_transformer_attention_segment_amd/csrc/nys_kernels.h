@@ -40,6 +40,8 @@ struct CtxArgs {
   int npinv;              // pseudo-inverse blocks at the front of the context grid (0 or BH)
   int ring_ni;            // bf16 context: 1 KiB LDS-DMA loads per wave per K or V tile
   int ring_stages;        // bf16 context: K/V tiles in the LDS ring (2..4)
+  int fp32_out;           // 1: the in-LDS pseudo-inverse (mp <= 64) also stores the fp32
+                          // A_S and Z for inspection; nothing downstream reads them
   float scale;            // 1/sqrt(d)
   float scale_log2e;      // log2(e)/sqrt(d)
 };

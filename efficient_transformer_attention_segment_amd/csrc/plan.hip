@@ -385,6 +385,7 @@ static nys_status forward_impl(nys_attn_plan* p, const void* q, const void* k, c
   o.lengths = lengths;
   o.out = out;
   o.attn_tap = taps ? taps->attn : nullptr;
+  c.fp32_out = taps && (taps->a_s || taps->z);
   if (!taps || (!taps->w && !taps->y)) o.w_tap = o.y_tap = nullptr;
   if (!mark(0) || !chk(nys::launch_segmeans(bf16, p->d, q, k, sg, s), "segment means launch") ||
       !mark(1) || (!p->fused && !chk(nys::launch_pinv(p->d, c, s), "pseudo-inverse launch")) ||
