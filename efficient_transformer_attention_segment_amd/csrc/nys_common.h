@@ -424,6 +424,9 @@ __device__ __forceinline__ f32x16 gemm_tile_k(const uint16_t* ahi, const uint16_
     a[s] = Pair8{ld8(ahi + oa + 16 * s), ld8(alo + oa + 16 * s)};
     b[s] = Pair8{ld8(bhi + ob + 16 * s), ld8(blo + ob + 16 * s)};
   }
+  // keep the scheduler from sinking loads next to their MFMAs (it would to save registers,
+  // and each group of loads would then cost a memory latency of its own)
+  __builtin_amdgcn_sched_barrier(0);
   f32x16 acc = zero16();
 #pragma unroll
   for (int s = 0; s < KSTEPS; ++s) acc = mfma_pair<true, true>(a[s], b[s], acc);
