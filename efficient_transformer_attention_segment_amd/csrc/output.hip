@@ -211,8 +211,9 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   float wt0 = 0.f, wt1 = 0.f;  // conv taps `lane` and `lane + 64` of this head (wave 0)
   if (tid < 64) {
     const float* w = a.conv_w + (size_t)head * a.W;
-    wt0 = lane < a.W ? w[lane] : 0.f;
-    wt1 = lane + 64 < a.W ? w[lane + 64] : 0.f;
+    // clamped reads: the operand below takes only taps below W from these lanes
+    wt0 = w[lane < a.W ? lane : a.W - 1];
+    wt1 = w[lane + 64 < a.W ? lane + 64 : a.W - 1];
   }
   constexpr int kCB = 4;  // chunk states per load batch
   const float* pml = a.part_ml + (size_t)bh * C * 2 * mp;
@@ -220,13 +221,18 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   const uint16_t* zr = a.z_hl + (size_t)bh * 2 * mp * mp;
   const size_t P = (size_t)mp * mp;
   const int ntj = D / 32, ntiles = (mp / 32) * ntj;
-  // running max / sum of landmark tid in the first kCB chunks
+  // Running max / sum of landmark tid in the first kCB chunks. No prologue load sits
+  // under a condition: the compiler turns one into a branch whose zero-filled registers it
+  // guards with a wait for every load issued so far, so the set-up would take several
+  // memory round trips. Slots past C repeat chunk C - 1 (zero weight below; its maximum is
+  // already among the others); slots past an element count load in bounds, unused.
   float cm[kCB], cl[kCB];
   if (NT > 0 && tid < mp) {
 #pragma unroll
     for (int c = 0; c < kCB; ++c) {
-      cm[c] = c < C ? pml[(size_t)(2 * c) * mp + tid] : kNegBig;
-      cl[c] = c < C ? pml[(size_t)(2 * c + 1) * mp + tid] : 0.f;
+      const int cc = c < C ? c : C - 1;
+      cm[c] = pml[(size_t)(2 * cc) * mp + tid];
+      cl[c] = pml[(size_t)(2 * cc + 1) * mp + tid];
     }
   }
   // register-resident softmax shapes (mp = 32 NT): partial W^T of the first kCB chunks
@@ -241,30 +247,31 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   if constexpr (NT > 0) {
 #pragma unroll
     for (int u = 0; u < UP; ++u) {
-      const int e = tid + NTH * u, f = e / (mp / 4), j = (e % (mp / 4)) * 4;
+      const int e0 = tid + NTH * u, e = e0 < D * mp / 4 ? e0 : 0;
+      const int f = e / (mp / 4), j = (e % (mp / 4)) * 4;
 #pragma unroll
-      for (int c = 0; c < kCB; ++c)
-        pv[u][c] = (e < D * mp / 4 && c < C)
-                       ? *reinterpret_cast<const f32x4*>(pw + ((size_t)c * D + f) * mp + j)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int c = 0; c < kCB; ++c) {
+        const int cc = c < C ? c : C - 1;
+        pv[u][c] = *reinterpret_cast<const f32x4*>(pw + ((size_t)cc * D + f) * mp + j);
+      }
     }
 #pragma unroll
     for (int u = 0; u < TPY; ++u) {
-      const int t = wave + NW * u;
-      const int row0 = 32 * (t / ntj);
+      const int t = wave + NW * u, tc = t < ntiles ? t : ntiles - 1;
+      const int row0 = 32 * (tc / ntj);
 #pragma unroll
       for (int s = 0; s < KM; ++s) {
         const size_t o = (size_t)(row0 + r32) * mp + 16 * s + 8 * h;
-        za[u][s] = t < ntiles ? Pair8{ld8(zr + o), ld8(zr + P + o)} : Pair8{zero8(), zero8()};
+        za[u][s] = Pair8{ld8(zr + o), ld8(zr + P + o)};
       }
     }
 #pragma unroll
     for (int u = 0; u < KU; ++u) {
-      const int e = tid + NTH * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
+      const int e0 = tid + NTH * u, e = e0 < mp * (D / 8) ? e0 : 0;
+      const int row = e / (D / 8), c8 = (e % (D / 8)) * 8;
       const float* ks = a.kt + ((size_t)bh * mp + row) * D + c8;
-      const bool ok = e < mp * (D / 8);
-      kx[u][0] = ok ? *reinterpret_cast<const f32x4*>(ks) : f32x4{0.f, 0.f, 0.f, 0.f};
-      kx[u][1] = ok ? *reinterpret_cast<const f32x4*>(ks + 4) : f32x4{0.f, 0.f, 0.f, 0.f};
+      kx[u][0] = *reinterpret_cast<const f32x4*>(ks);
+      kx[u][1] = *reinterpret_cast<const f32x4*>(ks + 4);
     }
   }
 
@@ -275,7 +282,7 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
 #pragma unroll
     for (int u = 0; u < KHS; ++u) {
       const int e = tid + NTH * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
-      khs[u] = row < mp ? ld8(khl + (size_t)row * D + c8) : zero8();
+      khs[u] = ld8(khl + (size_t)(row < mp ? row : mp - 1) * D + c8);
     }
   }
 
