@@ -407,18 +407,11 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
 
   for (int t0 = tb; t0 < te; t0 += T) {
     const int tw = t0 + 32 * wave;
-    // this wave's Q and dO rows, row-major (zeros past the chunk's valid end)
-#pragma unroll
-    for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
-      const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, tok = tw + i;
-      u32x4 qv{0u, 0u, 0u, 0u}, ov{0u, 0u, 0u, 0u};
-      if (tok < te) {
-        qv = *reinterpret_cast<const u32x4*>(q + (size_t)tok * D + f8);
-        ov = *reinterpret_cast<const u32x4*>(dO + (size_t)tok * D + f8);
-      }
-      *reinterpret_cast<u32x4*>(qR + (32 * wave + i) * DP + f8) = qv;
-      *reinterpret_cast<u32x4*>(oR + (32 * wave + i) * DP + f8) = ov;
-    }
+    // this wave's Q and dO rows, row-major (zeros past the chunk's valid end), staged for
+    // the reduction at the end of the step
+    Rows32<D> rq, ro;
+    rq.load(q, tw, te, lane);
+    ro.load(dO, tw, te, lane);
     // S = Q Kt^T and dF = dO Y^T for 32 tokens: lane = landmark, registers = tokens
     const int trow = min(tw + r32, L - 1);
     f32x16 sc[LT], df[LT];
@@ -479,6 +472,8 @@ __global__ __launch_bounds__(64 * NW) void bwd_pass1_kernel(BwdArgs a) {
         if (tok < te) dqp[(size_t)tok * D + 32 * ft + r32] = a.scale * acc[rr];
       }
     }
+    rq.store(qR + 32 * wave * DP, DP, tw, te, lane);
+    ro.store(oR + 32 * wave * DP, DP, tw, te, lane);
     __syncthreads();
     // partial dY = F^T dO and dSF^T Q over the step's T tokens
 #pragma unroll
@@ -699,13 +694,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void bwd_pass2_kernel(Bwd
   for (int t0 = tb; t0 < te; t0 += T) {
     const int tw = t0 + 32 * wave, tok = tw + r32;  // the lane's token
     const bool tv = tok < te;
-#pragma unroll
-    for (int idx = lane; idx < 32 * (D / 8); idx += 64) {
-      const int i = idx / (D / 8), f8 = (idx % (D / 8)) * 8, t = tw + i;
-      u32x4 kv{0u, 0u, 0u, 0u};
-      if (t < te) kv = *reinterpret_cast<const u32x4*>(kk + (size_t)t * D + f8);
-      *reinterpret_cast<u32x4*>(kR + (32 * wave + i) * DP + f8) = kv;
-    }
+    Rows32<D> rk;  // the wave's K rows, staged for the reduction below
+    rk.load(kk, tw, te, lane);
     const int trow = min(tok, L - 1);
     f32x16 sb[LT], db[LT];  // B and dSB: landmark rows, this lane's token
 #pragma unroll
@@ -769,6 +759,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void bwd_pass2_kernel(Bwd
         }
       }
     }
+    rk.store(kR + 32 * wave * DP, DP, tw, te, lane);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < RPW; ++u) {
@@ -814,16 +805,34 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   const int t0 = c3 * kFinTok, t1 = min(t0 + kFinTok, a.n), tv = min(t1, L);
   const uint16_t* dO = a.dout + (size_t)bh * a.n * D;
   const uint16_t* vv = a.v + (size_t)bh * a.n * D;
-#pragma unroll 4
-  for (int e = threadIdx.x; e < kFinRows * (D / 8); e += blockDim.x) {
-    const int r = e / (D / 8), f8 = (e % (D / 8)) * 8, tok = t0 - half + r;
-    u32x4 ov{0u, 0u, 0u, 0u}, vw{0u, 0u, 0u, 0u};
-    if (r < R && tok >= 0 && tok < L) {
-      ov = *reinterpret_cast<const u32x4*>(dO + (size_t)tok * D + f8);
-      vw = *reinterpret_cast<const u32x4*>(vv + (size_t)tok * D + f8);
+  // staged rows, zeros outside [0, L) and past R: loads from rows clamped into [0, L) in
+  // batches of kSB per thread, every load of a batch in flight before its first LDS write
+  // (a load under a condition compiles into a branch closed by a wait for everything)
+  {
+    constexpr int NST = (kFinRows * (D / 8) + kBwdThreads - 1) / kBwdThreads, kSB = 3;
+#pragma unroll
+    for (int u0 = 0; u0 < NST; u0 += kSB) {
+      u32x4 ov[kSB], vw[kSB];
+#pragma unroll
+      for (int u = 0; u < kSB; ++u) {
+        const int e = threadIdx.x + kBwdThreads * (u0 + u < NST ? u0 + u : 0);
+        const int r = e / (D / 8), f8 = (e % (D / 8)) * 8, tok = t0 - half + r;
+        const int tc = tok < 0 ? 0 : (tok < L ? tok : L - 1);
+        ov[u] = *reinterpret_cast<const u32x4*>(dO + (size_t)tc * D + f8);
+        vw[u] = *reinterpret_cast<const u32x4*>(vv + (size_t)tc * D + f8);
+      }
+#pragma unroll
+      for (int u = 0; u < kSB; ++u) {
+        const int e = threadIdx.x + kBwdThreads * (u0 + u);
+        const int r = e / (D / 8), f8 = (e % (D / 8)) * 8, tok = t0 - half + r;
+        asm volatile("" : "+v"(ov[u]), "+v"(vw[u]));
+        const bool ok = r < R && tok >= 0 && tok < L;
+        if (u0 + u < NST && e < kFinRows * (D / 8)) {
+          *reinterpret_cast<u32x4*>(so + r * D + f8) = ok ? ov[u] : u32x4{0u, 0u, 0u, 0u};
+          *reinterpret_cast<u32x4*>(sv + r * D + f8) = ok ? vw[u] : u32x4{0u, 0u, 0u, 0u};
+        }
+      }
     }
-    *reinterpret_cast<u32x4*>(so + r * D + f8) = ov;
-    *reinterpret_cast<u32x4*>(sv + r * D + f8) = vw;
   }
   const int j0 = tv > t0 ? seg_of(t0, L, m) : 0;
   const int j1 = tv > t0 ? seg_of(tv - 1, L, m) : -1;
@@ -831,8 +840,17 @@ __global__ __launch_bounds__(kBwdThreads) void bwd_final_kernel(BwdArgs a) {
   const float* p2 = a.part2 + (size_t)bh * a.C * MP * D;
   for (int e = threadIdx.x; e < (j1 - j0 + 1) * D; e += blockDim.x) {
     const int j = j0 + e / D, f = e % D;
+    // chunk partials summed in chunk order, four loads in flight at a time
     float acc = 0.f;
-    for (int c = 0; c < a.C; ++c) acc += p2[((size_t)c * MP + j) * D + f];
+    int c = 0;
+    for (; c + 4 <= a.C; c += 4) {
+      float x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) x[u] = p2[((size_t)(c + u) * MP + j) * D + f];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) acc += x[u];
+    }
+    for (; c < a.C; ++c) acc += p2[((size_t)c * MP + j) * D + f];
     const float len = (float)(seg_start(j + 1, L, m) - seg_start(j, L, m));
     sq[(j - j0) * D + f] = (dqt[(size_t)j * D + f] + a.scale * acc) / len;
   }

@@ -205,6 +205,34 @@ struct Chunk<float> {
   }
 };
 
+// 32 consecutive rows of a row-major bf16 [n][D] matrix, staged into LDS by one wave in two
+// phases: load() issues every load, each from a row clamped into [0, end) (end >= 1), and
+// store() writes them, zeros for rows at or past end. A load under a condition compiles
+// into a branch that the compiler closes with a wait for everything in flight, so staging
+// rows one conditional load at a time costs a memory round trip per load.
+template <int D>
+struct Rows32 {
+  static constexpr int NL = D / 16;  // 16-byte chunks per lane
+  u32x4 v[NL];
+  __device__ __forceinline__ void load(const uint16_t* src, int t0, int end, int lane) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = lane + 64 * u, i = idx / (D / 8), f8 = (idx % (D / 8)) * 8;
+      const int t = t0 + i < end ? t0 + i : end - 1;
+      v[u] = *reinterpret_cast<const u32x4*>(src + (size_t)t * D + f8);
+    }
+  }
+  __device__ __forceinline__ void store(uint16_t* dst, int ldr, int t0, int end, int lane) {
+#pragma unroll
+    for (int u = 0; u < NL; ++u) {
+      const int idx = lane + 64 * u, i = idx / (D / 8), f8 = (idx % (D / 8)) * 8;
+      asm volatile("" : "+v"(v[u]));  // the select stays here, not next to the load
+      const u32x4 x = t0 + i < end ? v[u] : u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4*>(dst + (size_t)i * ldr + f8) = x;
+    }
+  }
+};
+
 // Position of logical index t inside a 16-wide k-step when an accumulator's rows are
 // reused as the k dimension of the next product. Accumulator register r of lane half h
 // holds row 8*(r/4) + 4*h + (r%4); read as eight k-slots per half for one 16-row step,
