@@ -100,6 +100,14 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
   // index (one vector load when all four are in range, else element by element)
   constexpr int U4 = kGT * kGK / 1024;
   f32x4 ra[U4], rb[U4];
+  // Interior slabs (every run in range, 4-element aligned runs) load without conditions;
+  // edge slabs take the element-wise path. A load under a condition compiles into a branch
+  // that the compiler closes with a wait for everything in flight, so a slab loaded that
+  // way takes several memory round trips.
+  const bool runs_aligned =
+      ((g.lda | g.ldb) & 3) == 0 && (reinterpret_cast<uintptr_t>(A) & (4 * sizeof(TAe) - 1)) == 0 &&
+      (reinterpret_cast<uintptr_t>(B) & (4 * sizeof(TBe) - 1)) == 0;
+  const bool tile_in = runs_aligned && row0 + kGT <= lm && col0 + kGT <= ln;
   auto run4 = [](const auto* p, bool all, int nvalid) {
     if (all && (reinterpret_cast<uintptr_t>(p) & (4 * sizeof(*p) - 1)) == 0) return ld4f(p);
     f32x4 x{0.f, 0.f, 0.f, 0.f};
@@ -107,6 +115,19 @@ __global__ __launch_bounds__(256) void gemm_kernel(GemmArgs g) {
     return x;
   };
   auto fetch = [&](int k0) {
+    if (tile_in && k0 + kGK <= lk) {
+#pragma unroll
+      for (int u = 0; u < U4; ++u) {
+        const int e = 4 * (tid + 256 * u);
+        const int ai = TA ? e % kGT : e / kGK, ak = TA ? e / kGT : e % kGK;
+        const int i = row0 + ai, k = k0 + ak;
+        ra[u] = ld4f(TA ? A + (size_t)k * g.lda + i : A + (size_t)i * g.lda + k);
+        const int bk = TB ? e % kGK : e / kGT, bj = TB ? e / kGK : e % kGT;
+        const int jj = col0 + bj, kb = k0 + bk;
+        rb[u] = ld4f(TB ? B + (size_t)jj * g.ldb + kb : B + (size_t)kb * g.ldb + jj);
+      }
+      return;
+    }
 #pragma unroll
     for (int u = 0; u < U4; ++u) {
       const int e = 4 * (tid + 256 * u);
