@@ -35,6 +35,42 @@ __device__ __forceinline__ bf16x8 fl_tr8(const uint16_t* tile, int ld, int k, in
   return lds_tr16x2(tile + (k + trj) * ld + trc, tile + (k + 4 + trj) * ld + trc);
 }
 
+// Rows [t0, t0 + C) of NM row-major bf16 [n][D] matrices into LDS (row strides ld[]),
+// zeros at and past t1 (> t0). Each thread's loads go out in batches of kB, every load of
+// a batch in flight before its first LDS write, from rows clamped below t1: a load under a
+// condition compiles into a branch that the compiler closes with a wait for everything in
+// flight, so the rows would arrive one memory round trip at a time.
+template <int D, int C, int NTH, int NM>
+__device__ __forceinline__ void stage_chunk_rows(const uint16_t* const (&src)[NM],
+                                                 uint16_t* const (&dst)[NM], const int (&ld)[NM],
+                                                 int t0, int t1) {
+  constexpr int TOT = C * (D / 8), PER = (TOT + NTH - 1) / NTH, kB = 4;
+#pragma unroll
+  for (int u0 = 0; u0 < PER; u0 += kB) {
+    u32x4 x[kB][NM];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int e0 = threadIdx.x + NTH * (u0 + u), e = e0 < TOT ? e0 : 0;
+      const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = min(t0 + i, t1 - 1);
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt)
+        x[u][mt] = *reinterpret_cast<const u32x4*>(src[mt] + (size_t)t * D + f8);
+    }
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      const int e = threadIdx.x + NTH * (u0 + u);
+      const int i = e / (D / 8), f8 = (e % (D / 8)) * 8;
+#pragma unroll
+      for (int mt = 0; mt < NM; ++mt) {
+        asm volatile("" : "+v"(x[u][mt]));  // the select stays here, not next to the load
+        if (u0 + u < PER && e < TOT)
+          *reinterpret_cast<u32x4*>(dst[mt] + i * ld[mt] + f8) =
+              t0 + i < t1 ? x[u][mt] : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------ chunk states
 // S_g^T = V_g^T K_g: the chunk's K and V rows are staged row-major (16-byte writes) and
 // both operands, which contract over tokens, come from LDS transpose reads.
@@ -48,17 +84,7 @@ __global__ __launch_bounds__(256) void flash_state_kernel(FlashArgs a) {
   const int t0 = g * C, t1 = min(t0 + C, a.n);
   const uint16_t* k = a.k + (size_t)bh * a.n * D;
   const uint16_t* v = a.v + (size_t)bh * a.n * D;
-#pragma unroll 4
-  for (int e = threadIdx.x; e < C * (D / 8); e += blockDim.x) {
-    const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = t0 + i;
-    u32x4 kv{0u, 0u, 0u, 0u}, vv{0u, 0u, 0u, 0u};
-    if (t < t1) {
-      kv = *reinterpret_cast<const u32x4*>(k + (size_t)t * D + f8);
-      vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
-    }
-    *reinterpret_cast<u32x4*>(kS + i * D + f8) = kv;
-    *reinterpret_cast<u32x4*>(vS + i * D + f8) = vv;
-  }
+  stage_chunk_rows<D, C, 256, 2>({k, v}, {kS, vS}, {D, D}, t0, t1);
   __syncthreads();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, h = lane >> 5;
   constexpr int FT = D / 32;
@@ -140,17 +166,8 @@ __global__ __launch_bounds__(2 * C) void flash_attend_kernel(FlashArgs a) {
   const uint16_t* q = a.q + (size_t)bh * a.n * D;
   const uint16_t* k = a.k + (size_t)bh * a.n * D;
   const uint16_t* v = a.v + (size_t)bh * a.n * D;
-#pragma unroll 4
-  for (int e = threadIdx.x; e < C * (D / 8); e += blockDim.x) {
-    const int i = e / (D / 8), f8 = (e % (D / 8)) * 8, t = t0 + i;
-    u32x4 vv{0u, 0u, 0u, 0u}, kv{0u, 0u, 0u, 0u};
-    if (t < t1) {
-      vv = *reinterpret_cast<const u32x4*>(v + (size_t)t * D + f8);
-      if constexpr (kKL) kv = *reinterpret_cast<const u32x4*>(k + (size_t)t * D + f8);
-    }
-    *reinterpret_cast<u32x4*>(vS + i * D + f8) = vv;
-    if constexpr (kKL) *reinterpret_cast<u32x4*>(kS + i * LK + f8) = kv;
-  }
+  if constexpr (kKL) stage_chunk_rows<D, C, 2 * C, 2>({v, k}, {vS, kS}, {D, LK}, t0, t1);
+  else stage_chunk_rows<D, C, 2 * C, 1>({v}, {vS}, {D}, t0, t1);
   __syncthreads();
   const int q0 = t0 + 32 * wave;  // this wave's first query
   if (q0 >= t1) return;           // no barrier follows
