@@ -115,7 +115,8 @@ static nys_status validate_shape(int B, int H, int n, int d, int m, int W, int i
   if (iters < 0 || iters > 100) return fail(NYS_E_ARG, "pinv_iters must be in [0, 100]");
   if (dtype != NYS_F32 && dtype != NYS_BF16) return fail(NYS_E_ARG, "unknown dtype");
   if ((long long)n * d >= (1LL << 31)) return fail(NYS_E_UNSUPPORTED, "n*d must be < 2^31");
-  if ((long long)B * H >= (1LL << 24)) return fail(NYS_E_UNSUPPORTED, "B*H too large");
+  // 2 B H m segment tasks are counted in 32 bits (m <= 256)
+  if ((long long)B * H >= (1LL << 23)) return fail(NYS_E_UNSUPPORTED, "B*H must be < 2^23");
   return NYS_OK;
 }
 

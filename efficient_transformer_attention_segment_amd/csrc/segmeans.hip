@@ -18,6 +18,19 @@
 
 namespace nys {
 
+// Wave-uniform index arithmetic: the wave index through readfirstlane, so the task split and
+// the segment bounds run on scalar registers, in 32 bits (divisions by a runtime value in
+// 64 bits on vector registers cost a few hundred instructions before a wave's first load).
+// First row of segment j of m over L rows: ceil(j L / m); the 64-bit form only when m n
+// reaches 2^32.
+__device__ __forceinline__ int seg_first(int j, int L, int m, bool wide) {
+  if (wide) return (int)(((long long)j * L + m - 1) / m);
+  return (int)(((unsigned)j * (unsigned)L + (unsigned)(m - 1)) / (unsigned)m);
+}
+__device__ __forceinline__ bool seg_wide(const SegArgs& a) {
+  return (unsigned long long)a.m * (unsigned long long)a.n >= (1ull << 32);
+}
+
 template <typename Tin, int D>
 __global__ __launch_bounds__(256) void segmeans_kernel(const Tin* __restrict__ q,
                                                        const Tin* __restrict__ k,
@@ -27,15 +40,16 @@ __global__ __launch_bounds__(256) void segmeans_kernel(const Tin* __restrict__ q
   constexpr int RPW = 64 / CPR;          // rows per wave load
   static_assert(CPR >= 1 && CPR <= 64 && (64 % CPR) == 0, "row must tile a wave");
   const int lane = threadIdx.x & 63;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= 2LL * a.BH * a.m) return;  // whole waves only; the kernel has no barrier
-  const int j = (int)(task % a.m);
-  const int bh = (int)((task / a.m) % a.BH);
-  const int which = (int)(task / ((long long)a.m * a.BH));
+  const unsigned task = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (task >= 2u * (unsigned)a.BH * (unsigned)a.m) return;  // whole waves only; no barrier
+  const int j = (int)(task % (unsigned)a.m);
+  const int bh = (int)((task / (unsigned)a.m) % (unsigned)a.BH);
+  const int which = (int)(task / ((unsigned)a.m * (unsigned)a.BH));
   const int c = lane % CPR, r0 = lane / CPR;
   const int L = valid_length(a.lengths, bh, a.H, a.n, a.m);
-  const int start = (int)(((long long)j * L + a.m - 1) / a.m);
-  const int rows = (int)(((long long)(j + 1) * L + a.m - 1) / a.m) - start;
+  const bool wide = seg_wide(a);
+  const int start = seg_first(j, L, a.m, wide);
+  const int rows = seg_first(j + 1, L, a.m, wide) - start;
 
   const Tin* src = (which ? k : q) + ((size_t)bh * a.n + start) * D + c * EPC;
   float acc[EPC];
@@ -99,22 +113,23 @@ __global__ __launch_bounds__(256) void segmeans_short_kernel(const Tin* __restri
   constexpr int CPR = D / EPC;
   static_assert(CPR >= 1 && CPR <= 64 && (64 % CPR) == 0, "row must tile a wave");
   const int lane = threadIdx.x & 63;
-  const int groups = a.m / SPW;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= 2LL * a.BH * groups) return;  // whole waves only; the kernel has no barrier
+  const unsigned groups = (unsigned)(a.m / SPW);
+  const unsigned task = blockIdx.x * 4u + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (task >= 2u * (unsigned)a.BH * groups) return;  // whole waves only; no barrier
   const int j0 = (int)(task % groups) * SPW;
-  const int bh = (int)((task / groups) % a.BH);
-  const int which = (int)(task / ((long long)groups * a.BH));
+  const int bh = (int)((task / groups) % (unsigned)a.BH);
+  const int which = (int)(task / (groups * (unsigned)a.BH));
   const int c = lane % CPR, r = lane / CPR;
   const int L = valid_length(a.lengths, bh, a.H, a.n, a.m);
+  const bool wide = seg_wide(a);
   const Tin* base = (which ? k : q) + (size_t)bh * a.n * D + c * EPC;
   float x[SPW][8];
   int rows[SPW];
 #pragma unroll
   for (int g = 0; g < SPW; ++g) {
     const int j = j0 + g;
-    const int start = (int)(((long long)j * L + a.m - 1) / a.m);
-    rows[g] = (int)(((long long)(j + 1) * L + a.m - 1) / a.m) - start;
+    const int start = seg_first(j, L, a.m, wide);
+    rows[g] = seg_first(j + 1, L, a.m, wide) - start;
     const Tin* src = base + (size_t)(start + r) * D;
     if constexpr (EPC == 8) {
       Input<Tin>::load_raw(src, r < rows[g], x[g]);
@@ -169,14 +184,15 @@ __global__ __launch_bounds__(64 * WPS) void segmeans_split_kernel(const Tin* __r
   constexpr int EPC = 16 / sizeof(Tin), CPR = D / EPC, RPW = 64 / CPR;
   __shared__ float part[WPS][CPR][EPC];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const long long task = blockIdx.x;  // (matrix, head, segment)
-  const int j = (int)(task % a.m);
-  const int bh = (int)((task / a.m) % a.BH);
-  const int which = (int)(task / ((long long)a.m * a.BH));
+  const unsigned task = blockIdx.x;  // (matrix, head, segment)
+  const int j = (int)(task % (unsigned)a.m);
+  const int bh = (int)((task / (unsigned)a.m) % (unsigned)a.BH);
+  const int which = (int)(task / ((unsigned)a.m * (unsigned)a.BH));
   const int c = lane % CPR, r0 = lane / CPR;
   const int L = valid_length(a.lengths, bh, a.H, a.n, a.m);
-  const int start = (int)(((long long)j * L + a.m - 1) / a.m);
-  const int rows = (int)(((long long)(j + 1) * L + a.m - 1) / a.m) - start;
+  const bool wide = seg_wide(a);
+  const int start = seg_first(j, L, a.m, wide);
+  const int rows = seg_first(j + 1, L, a.m, wide) - start;
   const Tin* src = (which ? k : q) + ((size_t)bh * a.n + start) * D + c * EPC;
   float acc[8];
 #pragma unroll

@@ -73,7 +73,7 @@ typedef struct {
  *   n >= 1; 1 <= m <= 256, m <= n (m need not divide n);
  *   d in {32, 64, 128} (other positive d: NYS_E_UNSUPPORTED);
  *   conv_width odd, 1 <= conv_width <= 65;
- *   0 <= pinv_iters <= 100;  dtype NYS_F32 or NYS_BF16; n*d < 2^31.
+ *   0 <= pinv_iters <= 100;  dtype NYS_F32 or NYS_BF16; n*d < 2^31; B*H < 2^23.
  * Shapes whose kernels need more LDS than the device offers (fp32 with d = 128 and
  * m > 96) are NYS_E_UNSUPPORTED.
  * On success *plan is set; on failure *plan = NULL (when plan itself is non-NULL).
