@@ -53,6 +53,7 @@ def _create(*args):
     ((1, 1, 64, 48, 8, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),   # d not built
     ((1, 1, 1024, 32, 512, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),  # m > 256
     ((1, 1, 64, 32, 8, 67, 6, 1), _lib.NYS_E_UNSUPPORTED),   # conv width > 65
+    ((1 << 12, 1 << 11, 64, 32, 8, 33, 6, 1), _lib.NYS_E_UNSUPPORTED),  # B*H = 2^23
 ])
 def test_create_rejects_before_any_device_call(args, status):
     st, plan = _create(*args)
