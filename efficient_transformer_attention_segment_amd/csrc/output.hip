@@ -58,11 +58,10 @@ constexpr int split_tiles() {
 // NW: waves per block (4, or 8 where one block fills a CU's LDS); a step covers 32 NW
 // tokens. kKtSplit (bf16 online-softmax shapes whose Kt does not fit beside Y^T): Kt is
 // the same for every step, so its hi plane is kept in LDS (staged after Y is formed, in
-// the region the W^T merge used) instead of being read from L2 every step, and the scores
-// use Kt rounded to bf16 (the hi plane alone). Holding the lo plane's fragments in
-// registers took 128 per lane and made the kernel spill; the rounding moves a landmark
-// key by at most 2^-9 of itself, a score by a few 1e-4 log2 units at these shapes
-// (landmarks are means over whole segments), far inside the bf16 tolerance.
+// the region the W^T merge used) and each lane keeps its fragments of the lo plane in
+// registers for the whole block, instead of reading Kt from L2 every step. (Scores on the
+// hi plane alone, Kt rounded to bf16, were faster but lost 0.1 of the attention's scale on
+// clustered inputs at m = 256 and at d = 128.)
 template <typename Tin, int D, int KS, bool kKtLds, int NT, bool kFull, int NW, bool kKtSplit>
 __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
   extern __shared__ __align__(16) char lds[];
@@ -154,12 +153,13 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
       qb[s] = Input<Tin>::load8(Q + (size_t)tq * D + 16 * s + 8 * h, tq < t_valid);
   };
   // scores of landmark tile lt (landmarks x tokens)
+  bf16x8 klo[kMaxT][KD];  // this lane's Kt lo fragments (kKtSplit)
   auto scores = [&](int lt, const Pair8* qb) -> f32x16 {
     f32x16 S = zero16();
     if constexpr (kKtSplit) {
       const uint16_t* kp = ksp + (size_t)(32 * lt + r32) * KR + 8 * h;
 #pragma unroll
-      for (int s = 0; s < KD; ++s) S = mfma(ld8(kp + 16 * s), qb[s].hi, S);
+      for (int s = 0; s < KD; ++s) S = mfma_pair<true, false>(Pair8{ld8(kp + 16 * s), klo[lt][s]}, qb[s], S);
     } else if constexpr (kKtLds) {
       const uint16_t* kp = kl + (size_t)(32 * lt + r32) * KR + 8 * h;
 #pragma unroll
@@ -275,10 +275,16 @@ __global__ __launch_bounds__(64 * NW) void output_kernel(OutArgs a) {
     }
   }
 
-  // split Kt: a share of the hi rows to stage after Y
+  // split Kt: the lane's lo fragments, and a share of the hi rows to stage after Y
   constexpr int KHS = kKtSplit ? (kMaxT * 32 * (D / 8) + NTH - 1) / NTH : 1;
   bf16x8 khs[KHS];
   if constexpr (kKtSplit) {
+#pragma unroll
+    for (int lt = 0; lt < kMaxT; ++lt)
+#pragma unroll
+      for (int s = 0; s < KD; ++s)
+        klo[lt][s] = ld8(khl + (size_t)mp * D + (size_t)(32 * (32 * lt < mp ? lt : 0) + r32) * D +
+                         16 * s + 8 * h);  // tiles past mp load tile 0, unused
 #pragma unroll
     for (int u = 0; u < KHS; ++u) {
       const int e = tid + NTH * u, row = e / (D / 8), c8 = (e % (D / 8)) * 8;
