@@ -1185,13 +1185,14 @@ static const void* context_fn(bool bf16, int d, int mp, int LG) {
 
 hipError_t launch_context(bool bf16, int d, const CtxArgs& a, hipStream_t s) {
   const void* fn = context_fn(bf16, d, a.mp, a.LG);
+  if (64 * a.LG * a.TG > (a.npinv > 0 ? 256 : 512)) return hipErrorInvalidConfiguration;
   const dim3 grid(a.npinv + a.BH * a.C), block(64 * a.LG * a.TG);
   void* args[] = {const_cast<CtxArgs*>(&a)};
   return hipLaunchKernel(fn, grid, block, args, context_lds_bytes(bf16, d, a), s);
 }
 
 int context_blocks_per_cu(bool bf16, int d, int mp, size_t ctx_lds) {
-  const int LG = mp / 32, TG = LG >= 4 ? 1 : 4 / LG;
+  const int LG = mp / 32, TG = context_token_groups(LG);
   int nb = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, context_fn(bf16, d, mp, LG), 64 * LG * TG,
                                                    ctx_lds) != hipSuccess) {

@@ -216,6 +216,11 @@ size_t context_lds_bytes(bool bf16, int d, const CtxArgs& a);
 size_t output_lds_bytes(bool bf16, int d, int mp, int conv_ksteps, int C);
 hipError_t configure_context(bool bf16, int d, int mp, size_t ctx_lds);
 // Context blocks resident per CU at this LDS size (0 if the runtime cannot tell).
+// Token groups per landmark group in a context block (block = 64 LG TG threads, at most
+// 512, the kernel's launch bound; a step covers 32 TG tokens): four waves for m <= 64; two
+// groups (8 waves, 64-token steps) at exactly four landmark groups, where 32-token steps
+// left the block's loop dominated by its per-step barriers; one above.
+constexpr int context_token_groups(int LG) { return LG == 4 ? 2 : (LG > 4 ? 1 : 4 / LG); }
 int context_blocks_per_cu(bool bf16, int d, int mp, size_t ctx_lds);
 // Output blocks resident per CU at this LDS size (0 if the runtime cannot tell).
 int output_blocks_per_cu(bool bf16, int d, int ks, int mp, int m, int C, size_t lds);

@@ -148,7 +148,7 @@ static nys_status plan_init(nys_attn_plan* p, int B, int H, int n, int d, int m,
   p->BH = B * H;
   p->mp = (int)round_up(m, 32);
   p->LG = p->mp / 32;
-  p->TG = p->LG >= 4 ? 1 : 4 / p->LG;
+  p->TG = nys::context_token_groups(p->LG);
   const int step = 32 * p->TG;
   const long long work = (long long)p->BH * n;
   p->fused = nys::context_fuses_pinv(p->mp);
