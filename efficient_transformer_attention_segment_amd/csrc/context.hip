@@ -49,10 +49,12 @@ __device__ __forceinline__ float block_max(float x, float* red, int tid, int nw)
 // ------------------------------------------------------------------ pinv
 // Variant for 64 < mp <= 256 (one block of 16 waves per head, up to four tiles per wave):
 // hi/lo operand planes in a slice of CtxArgs::planes, 18 of them (row- and column-major
-// copies, a second Z pair and a separate T pair, so that no plane is read and rewritten
-// by one product).
-enum { kPA = 0, kPZr = 2, kPZc = 4, kPXr = 6, kPXc = 8, kPX2T = 10, kGZr1 = 12, kGZc1 = 14,
-       kGT = 16 };
+// copies, double-buffered where one launch reads a matrix while another of its waves
+// writes the next one, so that no plane is read and rewritten by one launch). The
+// multi-launch iteration (pinv_phase_kernel) uses kPZc, Z_0's columns, for the odd
+// iterations' X rows once X_0 is formed, and kPX2r for X^2 rows.
+enum { kPA = 0, kPZr = 2, kPZc = 4, kPXr = 6, kPXc = 8, kPX2T = 10, kGZr1 = 12, kPX2r = 14,
+       kGT = 16, kPXr1 = kPZc };
 static_assert(kPlanes == 18, "plane count");
 
 template <int TPW>
@@ -296,72 +298,121 @@ __device__ __forceinline__ float pinv_alpha(const CtxArgs& a, int bh, int lane) 
   return 1.0f / (wave_max(cmax) * wave_max(rmax));
 }
 
-// One product of an iteration for every head at once (mp > 64): one wave per 32 x 32
-// output tile, operands read from the head's planes in global memory (they stay in the
-// XCD's L2: a head's tiles run on one XCD). The planes written by the strip kernel and
-// by these phases are fragment-major (frag_off), so every operand load reads whole cache
-// lines; only the final Z leaves row-major. Successive phases are ordered by the launch
-// boundaries, so the m x m products of a head spread over many CUs instead of one.
-//   PH 0: X = A Z        -> X rows and columns (hi/lo), fp32 X
-//   PH 1: X^2 = X X      -> X^2 columns (hi/lo), fp32 X^2
-//   PH 2: T = 13I - 15X + 7X^2 - X X^2 -> T columns (hi/lo)
-//   PH 3: Z <- Z T / 4   -> Z rows and columns of the other Z pair; after the last
-//                           iteration fp32 Z and the row-major hi/lo copy for the output
+// The iteration for every head at once (mp > 64): one wave per 32 x 32 output tile,
+// operands read from the head's planes in global memory (they stay in the XCD's L2: a
+// head's tiles run on one XCD). The planes written by the strip kernel and by these
+// launches are fragment-major (frag_off), so every operand load reads whole cache lines;
+// only the final Z leaves row-major. Launch boundaries order the steps, so the m x m
+// products of a head spread over many CUs instead of one.
+// X = A Z is mostly carried along instead of being formed again from each Z: with
+// T_k = 13I - 15X_k + 7X_k^2 - X_k^3, Z_{k+1} = Z_k T_k / 4 gives
+// X_{k+1} = A Z_{k+1} = (13X_k - 15X_k^2 + 7X_k^3 - X_k^4) / 4, a polynomial in X_k. The X
+// chain then takes two dependent launches per iteration, and each Z product runs beside
+// the next iteration's X^2 (the same iterates as forming X = A Z every time, up to
+// rounding). Carried X drifts from A Z by rounding that the iteration no longer corrects
+// (max error of Z 1e-2 of its RMS on clustered inputs, against 3e-4 with X formed from
+// Z every time), so X is formed again as A Z at the refresh iterations (pinv_refresh:
+// the last one and every second one before it, down to half of the count), which brings
+// the error back to the level of the plain iteration.
+//   PH 0:  X_k = A Z_k (k = 0, or a refresh) -> X rows and columns (hi/lo), fp32 X
+//   PH 1:  X_k^2 = X_k X_k -> X^2 rows and columns (hi/lo), fp32 X^2; with kWithZ the
+//          second half of the grid forms Z_k = Z_{k-1} T_{k-1} / 4 -> Z rows; kZOnly
+//          (before a refresh) forms only Z_k, as rows and as columns (into the X^2 row
+//          planes, free until X_k^2)
+//   PH 2:  X^3 = X X^2 and T_k -> T columns (hi/lo); with kMore also X^4 = X^2 X^2 and
+//          X_{k+1} -> X rows (other set) and columns, fp32 X
+//   PH 3:  Z_I = Z_{I-1} T_{I-1} / 4 -> fp32 Z and the row-major hi/lo copy
+// Z_0's planes are unscaled (A_S^T): X_0 and Z_1 take alpha on their products.
+enum { kWithZ = 1, kZOnly = 2, kMore = 1, kRefresh = 1 };
+
+__host__ __device__ constexpr bool pinv_refresh(int k, int iters) {
+  return k >= 1 && 2 * k >= iters && (iters - 1 - k) % 2 == 0;
+}
+
 template <int PH, int KS>
-__global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it) {
+__global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it, int flags) {
   __shared__ float st[32 * kStageLd];
   const int lane = threadIdx.x;
   constexpr int mp = 16 * KS, nt = mp / 32;
+  const int per = a.BH * nt * nt;
+  // PH 1: the Z product (second half of the grid, or all of it)
+  const int half = (PH == 1 && ((flags & kZOnly) || (int)blockIdx.x >= per)) ? 1 : 0;
+  const int bx = (PH == 1 && !(flags & kZOnly)) ? (int)blockIdx.x - half * per : (int)blockIdx.x;
   int bh, t;
-  xcd_map(blockIdx.x, a.BH, nt * nt, bh, t);
+  xcd_map(bx, a.BH, nt * nt, bh, t);
   const size_t P = (size_t)mp * mp;
   const int row0 = 32 * (t / nt), col0 = 32 * (t % nt);
   uint16_t* pl = a.planes + (size_t)bh * kPlanes * P;
   auto plane = [&](int idx) { return pl + (size_t)idx * P; };
+  auto xrows = [&](int k) { return (k & 1) ? kPXr1 : kPXr; };
+  auto zrows = [&](int k) { return (k & 1) ? kGZr1 : kPZr; };
   float* own = a.own + (size_t)bh * 2 * P;
   if constexpr (PH == 0) {
-    const int zc = (it & 1) ? kGZc1 : kPZc;
+    const bool refresh = flags & kRefresh;  // Z_k's columns sit in the X^2 row planes
+    const int zc = refresh ? kPX2r : kPZc, xr = xrows(it);
     f32x16 x = gemm_tile_frag<KS>(plane(kPA), plane(kPA + 1), plane(zc), plane(zc + 1), row0,
                                   col0, lane);
-    if (it == 0) x *= pinv_alpha(a, bh, lane);  // the Z_0 planes are unscaled
+    if (!refresh) x *= pinv_alpha(a, bh, lane);
     stage_tile(st, x, lane);
-    stage_store_frag<false>(plane(kPXr), plane(kPXr + 1), mp, row0, col0, st, lane);
+    stage_store_frag<false>(plane(xr), plane(xr + 1), mp, row0, col0, st, lane);
     stage_store_frag<true>(plane(kPXc), plane(kPXc + 1), mp, row0, col0, st, lane);
     stage_store_f32(own, mp, row0, col0, st, lane);
   } else if constexpr (PH == 1) {
-    const f32x16 x2 = gemm_tile_frag<KS>(plane(kPXr), plane(kPXr + 1), plane(kPXc),
-                                         plane(kPXc + 1), row0, col0, lane);
-    stage_tile(st, x2, lane);
-    stage_store_frag<true>(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, st, lane);
-    stage_store_f32(own + P, mp, row0, col0, st, lane);
+    if (half == 0) {
+      const int xr = xrows(it);
+      const f32x16 x2 = gemm_tile_frag<KS>(plane(xr), plane(xr + 1), plane(kPXc),
+                                           plane(kPXc + 1), row0, col0, lane);
+      stage_tile(st, x2, lane);
+      stage_store_frag<false>(plane(kPX2r), plane(kPX2r + 1), mp, row0, col0, st, lane);
+      stage_store_frag<true>(plane(kPX2T), plane(kPX2T + 1), mp, row0, col0, st, lane);
+      stage_store_f32(own + P, mp, row0, col0, st, lane);
+    } else {
+      const int zr = zrows(it - 1), zr_n = zrows(it);
+      const f32x16 zv = gemm_tile_frag<KS>(plane(zr), plane(zr + 1), plane(kGT),
+                                           plane(kGT + 1), row0, col0, lane) *
+                        (it == 1 ? 0.25f * pinv_alpha(a, bh, lane) : 0.25f);
+      stage_tile(st, zv, lane);
+      stage_store_frag<false>(plane(zr_n), plane(zr_n + 1), mp, row0, col0, st, lane);
+      if (flags & kZOnly)
+        stage_store_frag<true>(plane(kPX2r), plane(kPX2r + 1), mp, row0, col0, st, lane);
+    }
   } else if constexpr (PH == 2) {
-    const int j = col0 + (lane & 31);
-    const f32x16 x3 = gemm_tile_frag<KS>(plane(kPXr), plane(kPXr + 1), plane(kPX2T),
+    const int j = col0 + (lane & 31), xr = xrows(it);
+    const bool more = flags & kMore;
+    const f32x16 x3 = gemm_tile_frag<KS>(plane(xr), plane(xr + 1), plane(kPX2T),
                                          plane(kPX2T + 1), row0, col0, lane);
-    f32x16 tv;
+    f32x16 x4 = zero16();
+    if (more)
+      x4 = gemm_tile_frag<KS>(plane(kPX2r), plane(kPX2r + 1), plane(kPX2T), plane(kPX2T + 1),
+                              row0, col0, lane);
+    f32x16 tv, xn;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       const size_t o = (size_t)acc_row(row0, rr, lane) * mp + j;
       const float diag = (acc_row(row0, rr, lane) == j) ? 13.f : 0.f;
-      tv[rr] = diag - 15.f * own[o] + 7.f * own[P + o] - x3[rr];
+      const float x = own[o], x2 = own[P + o];
+      tv[rr] = diag - 15.f * x + 7.f * x2 - x3[rr];
+      xn[rr] = 0.25f * (13.f * x - 15.f * x2 + 7.f * x3[rr] - x4[rr]);
     }
     stage_tile(st, tv, lane);
     stage_store_frag<true>(plane(kGT), plane(kGT + 1), mp, row0, col0, st, lane);
+    if (more) {
+      __syncthreads();  // the staging tile is read out before it takes X_{k+1}
+      const int xr_n = xrows(it + 1);
+      stage_tile(st, xn, lane);
+      stage_store_frag<false>(plane(xr_n), plane(xr_n + 1), mp, row0, col0, st, lane);
+      stage_store_frag<true>(plane(kPXc), plane(kPXc + 1), mp, row0, col0, st, lane);
+      stage_store_f32(own, mp, row0, col0, st, lane);
+    }
   } else {
-    const int zr = (it & 1) ? kGZr1 : kPZr;
-    const int zr_n = (it & 1) ? kPZr : kGZr1, zc_n = (it & 1) ? kPZc : kGZc1;
+    const int zr = zrows(a.iters - 1);
     const f32x16 zv = gemm_tile_frag<KS>(plane(zr), plane(zr + 1), plane(kGT), plane(kGT + 1),
                                          row0, col0, lane) *
-                      (it == 0 ? 0.25f * pinv_alpha(a, bh, lane) : 0.25f);
+                      (a.iters == 1 ? 0.25f * pinv_alpha(a, bh, lane) : 0.25f);
     stage_tile(st, zv, lane);
-    if (it == a.iters - 1) {
-      uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
-      stage_store_rows_hl(dst, dst + P, mp, row0, col0, st, lane);
-      stage_store_f32(a.z + (size_t)bh * P, mp, row0, col0, st, lane);
-    } else {
-      stage_store_frag<false>(plane(zr_n), plane(zr_n + 1), mp, row0, col0, st, lane);
-      stage_store_frag<true>(plane(zc_n), plane(zc_n + 1), mp, row0, col0, st, lane);
-    }
+    uint16_t* dst = a.z_hl + (size_t)bh * 2 * P;
+    stage_store_rows_hl(dst, dst + P, mp, row0, col0, st, lane);
+    stage_store_f32(a.z + (size_t)bh * P, mp, row0, col0, st, lane);
   }
 }
 
@@ -1119,22 +1170,34 @@ static hipError_t launch_pinv_t(const CtxArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   const int tiles = (a.mp / 32) * (a.mp / 32);
   const dim3 grid(a.BH * tiles), block(64);
-  for (int it = 0; it < a.iters && e == hipSuccess; ++it) {
-    switch (a.mp) {
-#define NYS_PHASES(MP)                                                               \
-  case MP:                                                                           \
-    hipLaunchKernelGGL((pinv_phase_kernel<0, MP / 16>), grid, block, 0, s, a, it);   \
-    hipLaunchKernelGGL((pinv_phase_kernel<1, MP / 16>), grid, block, 0, s, a, it);   \
-    hipLaunchKernelGGL((pinv_phase_kernel<2, MP / 16>), grid, block, 0, s, a, it);   \
-    hipLaunchKernelGGL((pinv_phase_kernel<3, MP / 16>), grid, block, 0, s, a, it);   \
+  if (e != hipSuccess) return e;
+  switch (a.mp) {
+#define NYS_PHASES(MP)                                                                   \
+  case MP:                                                                               \
+    hipLaunchKernelGGL((pinv_phase_kernel<0, MP / 16>), grid, block, 0, s, a, 0, 0);     \
+    for (int it = 0; it < a.iters; ++it) {                                               \
+      const bool re = pinv_refresh(it, a.iters), next_re = pinv_refresh(it + 1, a.iters); \
+      if (re) {                                                                          \
+        hipLaunchKernelGGL((pinv_phase_kernel<1, MP / 16>), grid, block, 0, s, a, it,    \
+                           (int)kZOnly);                                                 \
+        hipLaunchKernelGGL((pinv_phase_kernel<0, MP / 16>), grid, block, 0, s, a, it,    \
+                           (int)kRefresh);                                               \
+      }                                                                                  \
+      const bool with_z = it > 0 && !re;                                                 \
+      hipLaunchKernelGGL((pinv_phase_kernel<1, MP / 16>), dim3(grid.x * (with_z ? 2 : 1)), \
+                         block, 0, s, a, it, with_z ? (int)kWithZ : 0);                  \
+      const bool more = it + 1 < a.iters && !next_re;                                    \
+      hipLaunchKernelGGL((pinv_phase_kernel<2, MP / 16>), grid, block, 0, s, a, it,      \
+                         more ? (int)kMore : 0);                                         \
+    }                                                                                    \
+    hipLaunchKernelGGL((pinv_phase_kernel<3, MP / 16>), grid, block, 0, s, a, a.iters, 0); \
     break;
-      NYS_PHASES(96) NYS_PHASES(128) NYS_PHASES(160) NYS_PHASES(192) NYS_PHASES(224)
-      NYS_PHASES(256)
+    NYS_PHASES(96) NYS_PHASES(128) NYS_PHASES(160) NYS_PHASES(192) NYS_PHASES(224)
+    NYS_PHASES(256)
 #undef NYS_PHASES
-      default: return hipErrorInvalidValue;
-    }
-    e = hipGetLastError();
+    default: return hipErrorInvalidValue;
   }
+  if (e == hipSuccess) e = hipGetLastError();
   return e;
 }
 
