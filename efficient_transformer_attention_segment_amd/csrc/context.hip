@@ -379,12 +379,13 @@ __global__ __launch_bounds__(64) void pinv_phase_kernel(CtxArgs a, int it, int f
   } else if constexpr (PH == 2) {
     const int j = col0 + (lane & 31), xr = xrows(it);
     const bool more = flags & kMore;
-    const f32x16 x3 = gemm_tile_frag<KS>(plane(xr), plane(xr + 1), plane(kPX2T),
-                                         plane(kPX2T + 1), row0, col0, lane);
-    f32x16 x4 = zero16();
-    if (more)
-      x4 = gemm_tile_frag<KS>(plane(kPX2r), plane(kPX2r + 1), plane(kPX2T), plane(kPX2T + 1),
-                              row0, col0, lane);
+    f32x16 x3, x4 = zero16();
+    if (more)  // X^3 and X^4 share the columns of X^2
+      gemm_tile_frag2<KS>(plane(xr), plane(xr + 1), plane(kPX2r), plane(kPX2r + 1), plane(kPX2T),
+                          plane(kPX2T + 1), row0, col0, lane, x3, x4);
+    else
+      x3 = gemm_tile_frag<KS>(plane(xr), plane(xr + 1), plane(kPX2T), plane(kPX2T + 1), row0,
+                              col0, lane);
     f32x16 tv, xn;
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {

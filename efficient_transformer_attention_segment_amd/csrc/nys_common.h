@@ -583,6 +583,40 @@ __device__ __forceinline__ f32x16 gemm_tile_frag(const uint16_t* ahi, const uint
   return acc;
 }
 
+// Two tiles at (row0, col0) that share the right operand: C1 = A1 B^T and C2 = A2 B^T, each
+// B fragment loaded once for both products (pipelined like gemm_tile_frag).
+template <int KS, int PF = 4>
+__device__ __forceinline__ void gemm_tile_frag2(const uint16_t* a1hi, const uint16_t* a1lo,
+                                                const uint16_t* a2hi, const uint16_t* a2lo,
+                                                const uint16_t* bhi, const uint16_t* blo,
+                                                int row0, int col0, int lane, f32x16& c1,
+                                                f32x16& c2) {
+  constexpr int R = PF < KS ? PF : KS;
+  const size_t oa = (size_t)(row0 >> 5) * KS * 512 + 8 * lane;
+  const size_t ob = (size_t)(col0 >> 5) * KS * 512 + 8 * lane;
+  Pair8 x[R], y[R], b[R];
+#pragma unroll
+  for (int s = 0; s < R; ++s) {
+    x[s] = Pair8{ld8(a1hi + oa + 512 * s), ld8(a1lo + oa + 512 * s)};
+    y[s] = Pair8{ld8(a2hi + oa + 512 * s), ld8(a2lo + oa + 512 * s)};
+    b[s] = Pair8{ld8(bhi + ob + 512 * s), ld8(blo + ob + 512 * s)};
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  c1 = zero16();
+  c2 = zero16();
+#pragma unroll
+  for (int s = 0; s < KS; ++s) {
+    c1 = mfma_pair<true, true>(x[s % R], b[s % R], c1);
+    c2 = mfma_pair<true, true>(y[s % R], b[s % R], c2);
+    if (s + R < KS) {
+      x[s % R] = Pair8{ld8(a1hi + oa + 512 * (s + R)), ld8(a1lo + oa + 512 * (s + R))};
+      y[s % R] = Pair8{ld8(a2hi + oa + 512 * (s + R)), ld8(a2lo + oa + 512 * (s + R))};
+      b[s % R] = Pair8{ld8(bhi + ob + 512 * (s + R)), ld8(blo + ob + 512 * (s + R))};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // store_rows_hl / store_cols_hl into fragment-major planes of width ld.
 __device__ __forceinline__ void store_rows_hl_frag(uint16_t* hi, uint16_t* lo, int ld, int row0,
                                                    int col0, const f32x16& v, int lane) {
